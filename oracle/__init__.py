@@ -1,0 +1,188 @@
+"""Python access to the pointops oracle (plain single-threaded C, float32).
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the GPU library never does, and this
+package imports nothing from it.
+
+The C source ``pointops_oracle.c`` states which passage of the pages each
+function follows. This module only builds that source with gcc, marshals numpy
+arrays into it and, for large inputs, fans contiguous query-row ranges out over
+host threads (ctypes releases the GIL during the call), each thread running the
+unchanged single-threaded routine, so the result does not depend on the thread
+count.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pointops_oracle.c")
+_BUILD_DIR = os.path.join(_HERE, "_build")
+LIB_PATH = os.path.join(_BUILD_DIR, "libpointops_oracle.so")
+
+# Flags: float32 per-operation rounding, no contraction, no fast-math, no FMA.
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+          "-Wall", "-Wextra", "-Werror"]
+
+_lib = None
+_lock = threading.Lock()
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/_build``; return the library path."""
+    if not force and os.path.exists(LIB_PATH):
+        return LIB_PATH
+    os.makedirs(_BUILD_DIR, exist_ok=True)
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            build()
+        lib = ctypes.CDLL(LIB_PATH)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        i64 = ctypes.c_int64
+        lib.pco_s32.argtypes = [f32p, f32p]
+        lib.pco_s32.restype = ctypes.c_float
+        lib.pco_ball_query_r2.argtypes = [ctypes.c_float]
+        lib.pco_ball_query_r2.restype = ctypes.c_float
+        lib.pco_fps.argtypes = [f32p, i64, i64, i64, i64, i64p]
+        lib.pco_fps.restype = ctypes.c_int
+        lib.pco_knn_rows.argtypes = [f32p, f32p, i64, i64, i64, i64, f32p, i64p, i64, i64]
+        lib.pco_knn_rows.restype = ctypes.c_int
+        lib.pco_ball_query_rows.argtypes = [f32p, f32p, i64, i64, i64, ctypes.c_float, i64,
+                                            f32p, i64p, i64, i64]
+        lib.pco_ball_query_rows.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+class OracleError(ValueError):
+    pass
+
+
+def _f32(a):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def _i64(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise OracleError(f"oracle {what} rejected its arguments (status {rc})")
+
+
+def s32(a, b) -> np.float32:
+    """Squared distance of two 3-vectors in the oracle's float32 order."""
+    lib = _load()
+    a, pa = _f32(a)
+    b, pb = _f32(b)
+    assert a.shape == (3,) and b.shape == (3,)
+    return np.float32(lib.pco_s32(pa, pb))
+
+
+def ball_query_r2(radius) -> np.float32:
+    """R2 = fl32(r32 * r32) for r32 = fl32(radius)."""
+    return np.float32(_load().pco_ball_query_r2(float(np.float32(radius))))
+
+
+def fps(xyz, npoint: int, start_idx: int = 0, threads: int = 1) -> np.ndarray:
+    """Farthest point sampling of (B, N, 3) float32 clouds -> (B, npoint) int64.
+
+    With threads > 1 the independent clouds are split over host threads."""
+    lib = _load()
+    xyz, _ = _f32(xyz)
+    B, N, three = xyz.shape
+    assert three == 3
+    out = np.zeros((B, npoint), dtype=np.int64)
+    if B == 0 or npoint == 0:
+        return out
+
+    def run(b0, b1):
+        sub = np.ascontiguousarray(xyz[b0:b1])
+        o = np.zeros((b1 - b0, npoint), dtype=np.int64)
+        rc = lib.pco_fps(sub.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), b1 - b0, N,
+                         npoint, start_idx, _i64(o))
+        _check(rc, "fps")
+        out[b0:b1] = o
+
+    _fan_out(run, B, threads)
+    return out
+
+
+def _fan_out(run, n, threads):
+    threads = max(1, min(int(threads), n))
+    if threads == 1:
+        run(0, n)
+        return
+    bounds = np.linspace(0, n, threads + 1).astype(np.int64)
+    with ThreadPoolExecutor(threads) as ex:
+        futs = [ex.submit(run, int(bounds[i]), int(bounds[i + 1])) for i in range(threads)
+                if bounds[i + 1] > bounds[i]]
+        for f in futs:
+            f.result()
+
+
+def knn(query, ref, k: int, rows=None, threads: int = 1):
+    """kNN of (B, Q, 3) queries in (B, P, 3) references -> (dist (B,Q,k) f32, idx int64).
+
+    ``rows``: optional (lo, hi) range of flattened query rows (b*Q + i) to compute;
+    other rows are left as NaN / -2 so an unwritten slot is visible."""
+    lib = _load()
+    query, pq = _f32(query)
+    ref, pr = _f32(ref)
+    B, Q, _ = query.shape
+    P = ref.shape[1]
+    assert ref.shape[0] == B and ref.shape[2] == 3 and query.shape[2] == 3
+    dist = np.full((B, Q, k), np.nan, dtype=np.float32)
+    idx = np.full((B, Q, k), -2, dtype=np.int64)
+    lo, hi = (0, B * Q) if rows is None else rows
+    pd = dist.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+    def run(a, b):
+        _check(lib.pco_knn_rows(pq, pr, B, Q, P, k, pd, _i64(idx), lo + a, lo + b), "knn")
+
+    if hi > lo:
+        _fan_out(run, hi - lo, threads)
+    return dist, idx
+
+
+def ball_query(query, ref, radius, K: int, rows=None, threads: int = 1):
+    """First-K Ball Query -> (dist2 (B,Q,K) f32, idx (B,Q,K) int64), radius rounded to f32."""
+    lib = _load()
+    query, pq = _f32(query)
+    ref, pr = _f32(ref)
+    B, Q, _ = query.shape
+    P = ref.shape[1]
+    assert ref.shape[0] == B and ref.shape[2] == 3 and query.shape[2] == 3
+    dist2 = np.full((B, Q, K), np.nan, dtype=np.float32)
+    idx = np.full((B, Q, K), -2, dtype=np.int64)
+    lo, hi = (0, B * Q) if rows is None else rows
+    pd = dist2.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    r32 = float(np.float32(radius))
+
+    def run(a, b):
+        _check(lib.pco_ball_query_rows(pq, pr, B, Q, P, r32, K, pd, _i64(idx), lo + a, lo + b),
+               "ball_query")
+
+    if hi > lo:
+        _fan_out(run, hi - lo, threads)
+    return dist2, idx

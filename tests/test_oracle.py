@@ -1,0 +1,411 @@
+"""Pins for the oracle: what fixes it other than itself.
+
+* the pages' worked example (tests/golden/unit_square.json, with its citation);
+* exact rational evaluation of s32 with per-step float32 rounding, which also
+  shows that the other evaluation orders would give different bits;
+* brute force in float64 on integer and dyadic clouds, where float32
+  arithmetic is exact, so the real-valued definition decides every tie and
+  every radius boundary (numpy lexsort / argmax / nonzero as the library
+  routines);
+* an FPS brute force that recomputes each running minimum from scratch;
+* the FPS bisection closed form on a line, the repeat-0 rule, degenerate
+  clouds;
+* kNN k=1 as an argmin, Ball Query with a radius above / below every distance;
+* invariants on random float clouds;
+* the threshold fl32(fl32(r)^2) and the planted on-radius partners.
+
+None of these calls the GPU library.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from point_cloud_neighbor_amd import workloads as W
+from tests.exact import f32_bits, round_f32, s32_exact, s32_exact_alternatives
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------ helpers
+
+def s_f64(q, x):
+    """Real squared distances (B, Q, P) in float64 (exact for integer/dyadic inputs)."""
+    d = q[:, :, None, :].astype(np.float64) - x[:, None, :, :].astype(np.float64)
+    return (d * d).sum(-1)
+
+
+def s_f32_matrix(q, x):
+    """(B, Q, P) squared distances in float32, one rounding per numpy operation
+    in the order ((dx*dx + dy*dy) + dz*dz); checked against the exact rational
+    evaluation in test_f32_matrix_matches_exact."""
+    d = q[:, :, None, :] - x[:, None, :, :]
+    sq = d * d
+    return (sq[..., 0] + sq[..., 1]) + sq[..., 2]
+
+
+def brute_fps(s_full, start, M):
+    """FPS from a full pairwise matrix: at every step the running minimum is
+    recomputed from scratch over the chosen set; argmax takes the first max."""
+    chosen = [start]
+    for _ in range(1, M):
+        m = s_full[:, chosen].min(axis=1)
+        chosen.append(int(np.argmax(m)))
+    return chosen
+
+
+def brute_knn(s, k):
+    B, Q, P = s.shape
+    idx = np.zeros((B, Q, k), dtype=np.int64)
+    for b in range(B):
+        for i in range(Q):
+            order = np.lexsort((np.arange(P), s[b, i]))
+            idx[b, i] = order[:k]
+    return idx
+
+
+def brute_bq(s, r2, K):
+    B, Q, P = s.shape
+    idx = np.full((B, Q, K), -1, dtype=np.int64)
+    for b in range(B):
+        for i in range(Q):
+            hit = np.nonzero(s[b, i] < r2)[0][:K]
+            idx[b, i, :len(hit)] = hit
+    return idx
+
+
+def gather(xyz, idx):
+    return np.take_along_axis(xyz, idx[..., None].repeat(3, axis=-1), axis=1)
+
+
+# ------------------------------------------------------------------ worked example
+
+def test_worked_example(oracle_mod):
+    with open(os.path.join(GOLDEN, "unit_square.json")) as f:
+        g = json.load(f)
+    xyz = np.array(g["xyz"], dtype=np.float32)
+    assert np.array_equal(xyz, W.unit_square())
+    c = oracle_mod.fps(xyz, g["fps_npoint"], g["fps_start_idx"])
+    assert c.tolist() == g["fps_idx"]
+    centres = gather(xyz, c)
+    d, i = oracle_mod.knn(centres, xyz, g["knn_k"])
+    assert i.tolist() == g["knn_idx"]
+    assert d.tolist() == g["derived"]["knn_dist"]
+    d2, j = oracle_mod.ball_query(centres, xyz, g["bq_radius"], g["bq_K"])
+    assert j.tolist() == g["bq_idx"]
+    assert d2.tolist() == g["derived"]["bq_dist2"]
+
+
+# ------------------------------------------------------------------ s32 arithmetic
+
+def _pairs(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        kind = rng.integers(0, 4)
+        if kind == 0:          # unit cube
+            a, b = rng.random(3, dtype=np.float32), rng.random(3, dtype=np.float32)
+        elif kind == 1:        # wide magnitudes
+            a = (rng.standard_normal(3) * 10.0 ** rng.integers(-3, 4, size=3)).astype(np.float32)
+            b = (a * (1 + rng.standard_normal(3) * 1e-3)).astype(np.float32)
+        elif kind == 2:        # subnormal squares: differences ~1e-20
+            a = (rng.integers(-9, 10, size=3) * 1e-20).astype(np.float32)
+            b = (rng.integers(-9, 10, size=3) * 1.3e-20).astype(np.float32)
+        else:                  # near-cancellation, large coordinates
+            a = (rng.random(3) * 1e4).astype(np.float32)
+            b = np.nextafter(a, np.float32(np.inf) * rng.choice([-1, 1], size=3)).astype(np.float32)
+        out.append((a, b))
+    return out
+
+
+def test_s32_matches_exact_stepwise_rounding(oracle_mod):
+    """s32 equals ((dx*dx + dy*dy) + dz*dz) with each step rounded to float32,
+    including subnormal results; the other orders differ on these inputs."""
+    differ = {"right_to_left": 0, "fma_chain": 0, "one_rounding": 0}
+    subnormal = 0
+    for a, b in _pairs(1, 1500):
+        want = s32_exact(a, b)
+        got = oracle_mod.s32(a, b)
+        assert f32_bits(got) == f32_bits(want), (a, b, got, want)
+        assert f32_bits(oracle_mod.s32(b, a)) == f32_bits(want)
+        if 0 < want < np.finfo(np.float32).tiny:
+            subnormal += 1
+        for name, v in s32_exact_alternatives(a, b).items():
+            differ[name] += f32_bits(v) != f32_bits(want)
+    assert subnormal > 20
+    assert all(n > 0 for n in differ.values()), differ
+
+
+def test_f32_matrix_matches_exact():
+    """The vectorised float32 helper used by the invariant tests is the same
+    function as the exact step-by-step evaluation."""
+    pairs = _pairs(2, 400)
+    q = np.stack([a for a, _ in pairs])[None]
+    x = np.stack([b for _, b in pairs])[None]
+    m = s_f32_matrix(q, x)[0]
+    for n, (a, b) in enumerate(pairs):
+        assert f32_bits(m[n, n]) == f32_bits(s32_exact(a, b))
+
+
+# ------------------------------------------------------------------ exact brute force
+
+CLOUDS = [
+    ("int4", lambda s: W.integer_cloud(s, 2, 37, 0, 4)),      # many exact ties
+    ("int2", lambda s: W.integer_cloud(s, 1, 65, 0, 2)),      # heavy duplication
+    ("int_wide", lambda s: W.integer_cloud(s, 3, 50, -1000, 1000)),
+    ("dyadic", lambda s: W.dyadic_cloud(s, 2, 70, 64)),
+]
+
+
+@pytest.mark.parametrize("name,make", CLOUDS)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_fps_exact_brute_force(oracle_mod, name, make, seed):
+    xyz = make(seed)
+    B, N, _ = xyz.shape
+    s = s_f64(xyz, xyz)
+    for M, start in [(1, 0), (N // 2, N - 1), (N, 3), (N + 7, 5)]:
+        got = oracle_mod.fps(xyz, M, start)
+        for b in range(B):
+            assert got[b].tolist() == brute_fps(s[b], start, M)
+
+
+@pytest.mark.parametrize("name,make", CLOUDS)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_knn_exact_brute_force(oracle_mod, name, make, seed):
+    xyz = make(seed)
+    B, N, _ = xyz.shape
+    q = xyz[:, ::3].copy()
+    s = s_f64(q, xyz)
+    for k in (1, 5, N):
+        d, i = oracle_mod.knn(q, xyz, k)
+        want = brute_knn(s, k)
+        assert np.array_equal(i, want)
+        sel = np.take_along_axis(s, want, axis=-1)
+        # D = sqrtf(s): float64 sqrt rounded once to float32 is the correctly
+        # rounded float32 square root (double is wide enough for sqrt).
+        assert np.array_equal(d, np.sqrt(sel).astype(np.float32))
+
+
+@pytest.mark.parametrize("name,make", CLOUDS)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_ball_query_exact_brute_force(oracle_mod, name, make, seed):
+    xyz = make(seed)
+    q = xyz[:, 1::4].copy()
+    s = s_f64(q, xyz)
+    scale = 64.0 if name == "dyadic" else 1.0
+    radii = [2.0, 1.5, 1.0] if name != "int_wide" else [300.0, 750.5, 1024.0]
+    for r in radii:
+        r = r / scale
+        r2 = float(np.float32(r) * np.float32(r))
+        for K in (1, 3, 16, 200):
+            d2, idx = oracle_mod.ball_query(q, xyz, r, K)
+            want = brute_bq(s, r2, K)
+            assert np.array_equal(idx, want)
+            valid = want >= 0
+            assert np.array_equal(d2[valid], np.take_along_axis(s, np.maximum(want, 0), -1)[valid])
+            assert np.all(f32_bits_arr(d2[~valid]) == 0)
+    # the boundary itself: integer radius 2 has R2 = 4 exactly; s == 4 is out
+    if name.startswith("int"):
+        d2, idx = oracle_mod.ball_query(q, xyz, 2.0, 10 ** 4 // 100)
+        assert not np.any(d2[idx >= 0] >= 4.0)
+
+
+def f32_bits_arr(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+# ------------------------------------------------------------------ closed forms and special cases
+
+def bisection_order(k):
+    """FPS order on the points 0..2^k of a line from start 0: both ends, then
+    the midpoints level by level, each level in increasing order (its
+    candidates tie, and ties go to the smaller index)."""
+    n = 1 << k
+    order = [0, n]
+    step = n
+    while step > 1:
+        half = step // 2
+        order += list(range(half, n, step))
+        step = half
+    return order
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5, 8, 11])
+def test_fps_line_bisection_closed_form(oracle_mod, k):
+    N = (1 << k) + 1
+    xyz = W.line_cloud(N)
+    want = bisection_order(k)
+    assert sorted(want) == list(range(N))
+    got = oracle_mod.fps(xyz, N + 3, 0)
+    assert got[0].tolist() == want + [0, 0, 0]
+
+
+def test_fps_line_first_steps_from_other_start(oracle_mod):
+    N = 1000
+    xyz = W.line_cloud(N)
+    got = oracle_mod.fps(xyz, 3, 10)[0].tolist()
+    # from 10 the farthest is N-1; then the point midway between 10 and N-1
+    # (two points tie when the gap is odd: the smaller wins), unless 0 is farther
+    mid = 10 + (N - 1 - 10) // 2
+    assert got[:2] == [10, N - 1]
+    assert got[2] == (mid if (mid - 10) >= 10 else 0)
+
+
+def test_fps_degenerate_clouds(oracle_mod):
+    same = np.full((2, 9, 3), 0.5, dtype=np.float32)
+    assert oracle_mod.fps(same, 5, 4).tolist() == [[4, 0, 0, 0, 0]] * 2
+    pair = np.zeros((1, 6, 3), dtype=np.float32)
+    pair[0, 3] = 1.0           # two distinct locations, start at a duplicate
+    assert oracle_mod.fps(pair, 4, 1)[0].tolist() == [1, 3, 0, 0]
+    one = np.zeros((1, 1, 3), dtype=np.float32)
+    assert oracle_mod.fps(one, 3, 0)[0].tolist() == [0, 0, 0]
+
+
+def test_knn_k1_is_first_argmin(oracle_mod):
+    xyz = W.integer_cloud(7, 2, 300, 0, 6)
+    q = W.integer_cloud(8, 2, 40, 0, 6)
+    s = s_f64(q, xyz)
+    _, i = oracle_mod.knn(q, xyz, 1)
+    assert np.array_equal(i[..., 0], np.argmin(s, axis=-1))
+
+
+def test_ball_query_radius_extremes(oracle_mod):
+    xyz = W.uniform_cube(3, 2, 200)
+    q = W.uniform_cube(4, 2, 30)
+    d2, idx = oracle_mod.ball_query(q, xyz, 100.0, 17)
+    assert np.array_equal(idx, np.broadcast_to(np.arange(17), idx.shape))
+    # duplicates of the query are the only points below a tiny radius
+    xyz2 = xyz.copy()
+    xyz2[:, 50] = q[:, 0]
+    xyz2[:, 120] = q[:, 0]
+    d2, idx = oracle_mod.ball_query(q[:, :1], xyz2, 1e-20, 4)   # R2 ~ 1e-40, subnormal
+    assert idx[:, 0].tolist() == [[50, 120, -1, -1]] * 2
+    assert np.all(d2 == 0)
+    # r = 1e-30: fl32(r32 * r32) underflows to 0 and nothing is strictly below 0
+    d2, idx = oracle_mod.ball_query(q[:, :1], xyz2, 1e-30, 4)
+    assert np.all(idx == -1)
+
+
+def test_subnormal_distances_kept(oracle_mod):
+    xyz = W.subnormal_cloud(5, 40)
+    q = xyz[:, :5].copy()
+    d, i = oracle_mod.knn(q, xyz, 6)
+    s = s_f32_matrix(q, xyz)
+    assert np.any((s > 0) & (s < np.finfo(np.float32).tiny))
+    assert np.array_equal(i, brute_knn(s.astype(np.float64), 6))
+    # a subnormal radius threshold still separates subnormal distances
+    r = float(np.sqrt(np.float64(np.sort(s[s > 0])[3])))
+    r2 = np.float32(r) * np.float32(r)
+    d2, j = oracle_mod.ball_query(q, xyz, r, 40)
+    assert np.array_equal(j, brute_bq(s.astype(np.float64), float(r2), 40))
+
+
+# ------------------------------------------------------------------ invariants on float clouds
+
+def test_fps_invariants_random(oracle_mod):
+    xyz = W.uniform_cube(11, 2, 1500)
+    M = 300
+    got = oracle_mod.fps(xyz, M, 7)
+    s = s_f32_matrix(xyz, xyz)
+    for b in range(2):
+        c = got[b]
+        assert c[0] == 7
+        assert len(set(c.tolist())) == M
+        assert c.tolist() == brute_fps(s[b], 7, M)
+        sel = [s[b][c[t], c[:t]].min() for t in range(1, M)]
+        assert all(sel[t] <= sel[t - 1] for t in range(1, len(sel)))
+
+
+def test_knn_invariants_random(oracle_mod):
+    xyz = W.sphere_shell(12, 2, 2000)
+    q = W.sphere_shell(13, 2, 50)
+    k = 24
+    d, i = oracle_mod.knn(q, xyz, k)
+    s = s_f32_matrix(q, xyz)
+    for b in range(2):
+        for r in range(50):
+            sel = s[b, r, i[b, r]]
+            keys = list(zip(sel.tolist(), i[b, r].tolist()))
+            assert keys == sorted(keys) and len(set(i[b, r].tolist())) == k
+            mask = np.ones(2000, bool)
+            mask[i[b, r]] = False
+            rest = s[b, r, mask]
+            last = keys[-1]
+            assert np.all((rest > last[0]) | ((rest == last[0]) & (np.nonzero(mask)[0] > last[1])))
+            assert np.array_equal(d[b, r], np.sqrt(sel.astype(np.float64)).astype(np.float32))
+
+
+def test_ball_query_invariants_random(oracle_mod):
+    xyz = W.uniform_cube(14, 2, 3000)
+    q = W.uniform_cube(15, 2, 60)
+    r, K = 0.12, 20
+    d2, idx = oracle_mod.ball_query(q, xyz, r, K)
+    s = s_f32_matrix(q, xyz)
+    r2 = np.float32(r) * np.float32(r)
+    for b in range(2):
+        for row in range(60):
+            v = idx[b, row][idx[b, row] >= 0]
+            n = len(v)
+            assert np.all(np.diff(v) > 0)
+            assert np.all(s[b, row, v] < r2)
+            assert np.array_equal(d2[b, row, :n], s[b, row, v])
+            assert np.all(idx[b, row, n:] == -1) and np.all(f32_bits_arr(d2[b, row, n:]) == 0)
+            hits = np.nonzero(s[b, row] < r2)[0]
+            if n < K:
+                assert np.array_equal(hits, v)
+            else:
+                assert np.array_equal(hits[:K], v)
+
+
+# ------------------------------------------------------------------ thresholds and planted cases
+
+@pytest.mark.parametrize("r", sorted(W.R2_BITS))
+def test_threshold_rule(oracle_mod, r):
+    r32 = Fraction(float(np.float32(r)))
+    want = round_f32(r32 * r32)
+    assert f32_bits(oracle_mod.ball_query_r2(r)) == f32_bits(np.float32(float(want)))
+    assert W.R2_BITS[r] == f32_bits(oracle_mod.ball_query_r2(r))
+
+
+def test_dense_threshold_is_one_ulp_above_flat():
+    # fl32(fl32(r)^2) versus fl32(r*r) with r*r in double: one float32 step apart at r = 0.1
+    r = 0.1
+    dense = f32_bits(np.float32(float(round_f32(Fraction(float(np.float32(r))) ** 2))))
+    flat = f32_bits(np.float32(float(round_f32(Fraction(r) * Fraction(r)))))
+    assert dense == 1008981771 and flat == 1008981770
+
+
+def test_planted_radius_partners(oracle_mod):
+    rng = np.random.default_rng(3)
+    xyz = np.round(rng.random((40, 3)) * 64) / 64
+    xyz = xyz.astype(np.float32)
+    planted = W.plant_radius_partners(rng, xyz, np.arange(10), np.arange(10, 40),
+                                      W.R2_BITS[0.05])
+    r2 = W.bits_to_f32(W.R2_BITS[0.05])
+    for a, v, num in planted:
+        s = oracle_mod.s32(xyz[a], xyz[v])
+        assert Fraction(float(s)) == Fraction(num, 1 << 32)
+        delta = num - (f32_bits(r2) & 0x7FFFFF | 0x800000)
+        assert (s < r2) == (delta < 0)
+        assert f32_bits(s) - f32_bits(r2) == delta
+    d2, idx = oracle_mod.ball_query(xyz[None, :10], xyz[None], 0.05, 40)
+    for a, v, num in planted:
+        inside = v in idx[0, a]
+        assert inside == (num < (f32_bits(r2) & 0x7FFFFF | 0x800000))
+
+
+def test_oracle_rejects_bad_arguments(oracle_mod):
+    xyz = W.uniform_cube(0, 1, 10)
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.fps(xyz, 3, 10)
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.knn(xyz, xyz, 11)
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.ball_query(xyz, xyz, 0.0, 4)
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.ball_query(xyz, xyz, float("nan"), 4)
+    # empty references are legal for Ball Query: every slot is padding
+    d2, idx = oracle_mod.ball_query(xyz, np.zeros((1, 0, 3), np.float32), 0.5, 3)
+    assert np.all(idx == -1) and np.all(d2 == 0)
