@@ -1,0 +1,142 @@
+/*
+ * pointops: dense, batched float32 point-cloud neighbour search on AMD
+ * Instinct MI355X (gfx950), as a C ABI.
+ *
+ * The operations follow the contracts of the "mps-pointops" project page
+ * (PyPI, version 0.5.0), sections "The operators in equations" and
+ * "Contracts", and of its "Numerical contracts" page, section "Selection and
+ * output". All of them evaluate the squared distance of a query q and a
+ * reference x as
+ *
+ *     s32(q, x) = ((dx*dx + dy*dy) + dz*dz),   dx = fl32(q.x - x.x), ...
+ *
+ * with every operation a float32 operation rounded to nearest-even, no fused
+ * multiply-add and float32 subnormals kept (the project page, section "How
+ * the kernels work", fixes this order for FPS and kNN; this library uses it
+ * for Ball Query as well). Results are therefore fully determined, indices
+ * and distance bits included.
+ *
+ * Conventions shared by every entry point:
+ *   - Point buffers are device pointers (memory of the current HIP device) to
+ *     row-major, contiguous float32 arrays of shape (B, n, 3); index outputs
+ *     are int64. The caller owns every buffer; the library never allocates or
+ *     frees device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL: the default stream).
+ *     Calls are asynchronous on that stream. Argument errors are detected on
+ *     the host and returned before anything is launched or written; failures
+ *     during execution surface at the caller's next synchronisation.
+ *   - There is no CPU fallback: an unsupported device or argument is an error.
+ *   - Inputs are read-only and may alias each other (query == ref is fine).
+ *     Outputs must not alias inputs or each other.
+ *   - Sizes are limited to n < 2^31 points per cloud.
+ *   - Non-finite coordinates are outside the contract: the calls still
+ *     terminate and write only inside their outputs, but the results are
+ *     unspecified.
+ *   - Thread safety: the library is stateless apart from a per-device property
+ *     cache and a thread-local error message.
+ */
+#ifndef POINTOPS_H
+#define POINTOPS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum pointops_status {
+    POINTOPS_OK = 0,
+    POINTOPS_INVALID_ARGUMENT = 1, /* a size, index, radius or pointer is out of range */
+    POINTOPS_UNSUPPORTED = 2,      /* valid request beyond a compiled limit (k > KMAX, sizes) */
+    POINTOPS_UNSUPPORTED_DEVICE = 3, /* current device is not gfx950 with 64-wide waves */
+    POINTOPS_HIP_ERROR = 4         /* a HIP runtime call failed; see pointops_last_error() */
+};
+
+/* Largest k accepted by pointops_knn. The project page, section "Contracts",
+ * caps k at a kernel constant and reports an explicit error beyond it; this
+ * library does the same with its own constant. */
+#define POINTOPS_KNN_KMAX 64
+
+/*
+ * Farthest point sampling.
+ * Project page, section "The operators in equations", "Farthest point
+ * sampling"; section "Contracts" (start index, repeat-0 rule).
+ *   c_0 = start_idx; m_j = min over chosen centres u of s32(x_j, x_{c_u});
+ *   c_{t+1} = the smallest j whose m_j equals max_l m_l.
+ * Once every point is taken, all m are 0 and the remaining slots are 0.
+ *
+ *   xyz       (B, N, 3) float32, device.
+ *   B, N, M   clouds, points per cloud, samples per cloud. B == 0 or M == 0 is
+ *             a no-op. M may exceed N. N == 0 with M >= 1 is invalid.
+ *   start_idx first centre of every cloud, 0 <= start_idx < N.
+ *   out_idx   (B, M) int64, device: c_0 .. c_{M-1}.
+ *   out_xyz   (B, M, 3) float32, device, or NULL: the sampled coordinates
+ *             x_{c_t} (bit copies of the input).
+ *   workspace device scratch of at least pointops_fps_workspace_bytes(B, N, M)
+ *             bytes (NULL allowed when that size is 0). Its contents on entry
+ *             do not matter; the call clears what it uses, on `stream`.
+ *             Calls that share a workspace must be ordered (same stream).
+ */
+int pointops_fps(const float *xyz, int64_t B, int64_t N, int64_t M, int64_t start_idx,
+                 int64_t *out_idx, float *out_xyz, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/* Bytes of device workspace pointops_fps needs for this shape (it may be 0). */
+size_t pointops_fps_workspace_bytes(int64_t B, int64_t N, int64_t M);
+
+/*
+ * k nearest neighbours.
+ * Project page, section "The operators in equations", "k nearest neighbors";
+ * "Numerical contracts" page, section "Selection and output".
+ *   For every query i of cloud b: sort the references j by (s32(q_i, x_j), j),
+ *   keep the first k; out_idx = j, out_dist = sqrtf(s32) correctly rounded.
+ *
+ *   query     (B, Q, 3) float32, device.      ref (B, P, 3) float32, device.
+ *   k         1 <= k <= P (INVALID_ARGUMENT otherwise) and
+ *             k <= POINTOPS_KNN_KMAX (UNSUPPORTED otherwise).
+ *   out_dist  (B, Q, k) float32, device.      out_idx (B, Q, k) int64, device.
+ *   B == 0 or Q == 0 is a no-op.
+ */
+int pointops_knn(const float *query, const float *ref, int64_t B, int64_t Q, int64_t P,
+                 int64_t k, float *out_dist, int64_t *out_idx, void *stream);
+
+/*
+ * Dense Ball Query: the first K references within the radius, in input order.
+ * Project page, section "The operators in equations", "Ball Query: first K
+ * within a radius"; "Numerical contracts" page, section "Selection and output".
+ *   R2 = fl32(radius * radius) with radius already a float32 (the caller's
+ *   fl32(r)); J = the references j with s32(q_i, x_j) < R2, in increasing j;
+ *   slot n < min(K, |J|) holds (J[n], s32 of J[n]); the rest hold (-1, +0.0f).
+ *   A zero squared distance is a real match: test out_idx >= 0 for padding.
+ *
+ *   query     (B, Q, 3) float32, device.      ref (B, P, 3) float32, device.
+ *   radius    finite and > 0 (INVALID_ARGUMENT otherwise).
+ *   K         >= 1.  P == 0 is allowed: every slot is padding.
+ *   out_dist2 (B, Q, K) float32, device.      out_idx (B, Q, K) int64, device.
+ *   B == 0 or Q == 0 is a no-op.
+ */
+int pointops_ball_query(const float *query, const float *ref, int64_t B, int64_t Q, int64_t P,
+                        float radius, int64_t K, float *out_dist2, int64_t *out_idx,
+                        void *stream);
+
+/* POINTOPS_OK if `device` is a gfx950 GPU with 64-wide wavefronts (the kernels
+ * assume that width), POINTOPS_UNSUPPORTED_DEVICE otherwise. The entry points
+ * above run this check on the current device (cached per device). */
+int pointops_device_check(int device);
+
+/* A static description of a status code. */
+const char *pointops_status_string(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char *pointops_last_error(void);
+
+/* Library ABI version: 1. */
+int pointops_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POINTOPS_H */

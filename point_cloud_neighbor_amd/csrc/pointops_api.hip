@@ -1,0 +1,276 @@
+// C ABI of the pointops library: argument validation, device check, launch
+// geometry. Declarations and the contract of every entry point are in
+// include/pointops.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/pointops.h"
+
+namespace pointops {
+hipError_t launch_ball_query(const float*, const float*, int64_t, int64_t, int64_t, float,
+                             int64_t, float*, int64_t*, int, hipStream_t);
+hipError_t launch_fps(const float*, int64_t, int64_t, int64_t, int64_t, int64_t*, float*, void*,
+                      int, int, int, uint32_t, hipStream_t);
+hipError_t launch_fps_clear(void*, size_t, hipStream_t);
+size_t fps_workspace_bytes(int64_t B, int64_t G);
+hipError_t launch_knn(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
+                      int64_t*, int, int, hipStream_t);
+}  // namespace pointops
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(POINTOPS_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxPoints = (int64_t)1 << 31;  // indices are int32 internally
+constexpr int64_t kMaxGridY = 65535;
+
+struct DeviceInfo {
+    int checked = 0;  // 0: unknown, 1: supported, -1: unsupported
+    int cus = 0;
+    size_t lds_per_block = 0;
+    char arch[64] = {0};
+};
+
+constexpr int kMaxDevices = 64;
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+int check_device(int device, DeviceInfo** out) {
+    if (device < 0 || device >= kMaxDevices)
+        return fail(POINTOPS_UNSUPPORTED_DEVICE, "device %d out of range", device);
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DeviceInfo& d = g_dev[device];
+    if (d.checked == 0) {
+        hipDeviceProp_t prop;
+        hipError_t e = hipGetDeviceProperties(&prop, device);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+        snprintf(d.arch, sizeof d.arch, "%s", prop.gcnArchName);
+        d.cus = prop.multiProcessorCount;
+        d.lds_per_block = prop.sharedMemPerBlock;
+        const bool gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        const char* force = getenv("POINTOPS_FORCE_UNSUPPORTED_DEVICE");  // test hook
+        d.checked = (gfx950 && prop.warpSize == 64 && !(force && force[0] == '1')) ? 1 : -1;
+    }
+    if (out) *out = &d;
+    if (d.checked != 1)
+        return fail(POINTOPS_UNSUPPORTED_DEVICE,
+                    "device %d (%s) is not a gfx950 GPU with 64-wide wavefronts", device, d.arch);
+    return POINTOPS_OK;
+}
+
+int current_device(DeviceInfo** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    return check_device(dev, out);
+}
+
+long env_long(const char* name, long dflt) {
+    const char* v = getenv(name);
+    if (!v || !*v) return dflt;
+    char* end = nullptr;
+    long x = strtol(v, &end, 10);
+    return (end && *end == 0) ? x : dflt;
+}
+
+// ------------------------------------------------------------------ FPS geometry
+
+struct FpsPlan {
+    int G;      // workgroups per cloud
+    int ppt;    // points per thread
+    int block;  // threads per workgroup
+};
+
+// Points per workgroup for one cloud: enough workgroups that a step's update is
+// short, few enough that the per-step exchange stays cheap and every cloud's
+// workgroups fit on the device at once.
+FpsPlan fps_plan(int64_t B, int64_t N, const DeviceInfo& dev) {
+    const int64_t cus = std::max(1, dev.cus);
+    long g_env = env_long("POINTOPS_FPS_WG_PER_CLOUD", 0);
+    int64_t G;
+    if (g_env > 0) {
+        G = g_env;
+    } else {
+        // target ~4096 points per workgroup, at most one workgroup per CU overall
+        G = (N + 4095) / 4096;
+        G = std::min<int64_t>(G, std::max<int64_t>(1, cus / std::max<int64_t>(B, 1)));
+    }
+    G = std::max<int64_t>(1, std::min<int64_t>(G, N));
+    int64_t slice = (N + G - 1) / G;
+    // every slice non-empty: with slice = ceil(N/G), the last slice starts at
+    // (G-1)*slice, which must be < N
+    while (G > 1 && (G - 1) * slice >= N) {
+        --G;
+        slice = (N + G - 1) / G;
+    }
+    FpsPlan p;
+    p.G = (int)G;
+    p.block = slice <= 1024 ? 256 : 1024;
+    const int64_t per = (slice + p.block - 1) / p.block;
+    int ppt = 1;
+    while (ppt < per) ppt *= 2;
+    if (p.block == 256 && ppt > 4) {
+        p.block = 1024;
+        ppt = 1;
+        while (ppt < (slice + 1023) / 1024) ppt *= 2;
+    }
+    p.ppt = ppt;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pointops_abi_version(void) { return 1; }
+
+const char* pointops_status_string(int status) {
+    switch (status) {
+        case POINTOPS_OK: return "ok";
+        case POINTOPS_INVALID_ARGUMENT: return "invalid argument";
+        case POINTOPS_UNSUPPORTED: return "unsupported (beyond a compiled limit)";
+        case POINTOPS_UNSUPPORTED_DEVICE: return "unsupported device (needs gfx950, wave64)";
+        case POINTOPS_HIP_ERROR: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* pointops_last_error(void) { return g_err; }
+
+int pointops_device_check(int device) {
+    g_err[0] = 0;
+    return check_device(device, nullptr);
+}
+
+size_t pointops_fps_workspace_bytes(int64_t B, int64_t N, int64_t M) {
+    if (B <= 0 || N <= 0 || M <= 0) return 0;
+    DeviceInfo* dev = nullptr;
+    DeviceInfo fallback;
+    fallback.cus = 256;
+    if (current_device(&dev) != POINTOPS_OK) dev = &fallback;
+    g_err[0] = 0;
+    const FpsPlan p = fps_plan(B, N, *dev);
+    return pointops::fps_workspace_bytes(B, p.G);
+}
+
+int pointops_fps(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t start_idx,
+                 int64_t* out_idx, float* out_xyz, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    g_err[0] = 0;
+    if (B < 0 || N < 0 || M < 0) return fail(POINTOPS_INVALID_ARGUMENT, "negative size");
+    if (B == 0 || M == 0) return POINTOPS_OK;
+    if (N == 0) return fail(POINTOPS_INVALID_ARGUMENT, "N == 0 with M >= 1");
+    if (start_idx < 0 || start_idx >= N)
+        return fail(POINTOPS_INVALID_ARGUMENT, "start_idx %lld not in [0, %lld)",
+                    (long long)start_idx, (long long)N);
+    if (N >= kMaxPoints || M >= kMaxPoints)
+        return fail(POINTOPS_UNSUPPORTED, "N and M must be below 2^31");
+    if (!xyz || !out_idx) return fail(POINTOPS_INVALID_ARGUMENT, "null pointer");
+    DeviceInfo* dev = nullptr;
+    int st = current_device(&dev);
+    if (st != POINTOPS_OK) return st;
+    const FpsPlan p = fps_plan(B, N, *dev);
+    const int64_t slice = (N + p.G - 1) / p.G;
+    if (p.ppt > 16 || slice * 12 > (int64_t)std::min<size_t>(dev->lds_per_block, 65536) - 1024)
+        return fail(POINTOPS_UNSUPPORTED,
+                    "cloud of %lld points needs %d workgroups of %lld points; "
+                    "raise POINTOPS_FPS_WG_PER_CLOUD", (long long)N, p.G, (long long)slice);
+    if (B * p.G > (int64_t)dev->cus * 8 && p.G > 1)
+        return fail(POINTOPS_UNSUPPORTED, "B*G = %lld workgroups exceed what runs at once",
+                    (long long)(B * p.G));
+    const size_t need = pointops::fps_workspace_bytes(B, p.G);
+    if (!workspace || workspace_bytes < need)
+        return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
+                    workspace_bytes, need);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = pointops::launch_fps_clear(workspace, need, s);
+    if (e != hipSuccess) return hip_fail(e, "fps workspace clear");
+    const uint32_t spin = (uint32_t)env_long("POINTOPS_FPS_SPIN_LIMIT", 1L << 24);
+    e = pointops::launch_fps(xyz, B, N, M, start_idx, out_idx, out_xyz, workspace, p.G, p.ppt,
+                             p.block, spin, s);
+    if (e != hipSuccess) return hip_fail(e, "fps launch");
+    return POINTOPS_OK;
+}
+
+int pointops_knn(const float* query, const float* ref, int64_t B, int64_t Q, int64_t P,
+                 int64_t k, float* out_dist, int64_t* out_idx, void* stream) {
+    g_err[0] = 0;
+    if (B < 0 || Q < 0 || P < 0) return fail(POINTOPS_INVALID_ARGUMENT, "negative size");
+    if (k < 1 || k > P)
+        return fail(POINTOPS_INVALID_ARGUMENT, "k = %lld must satisfy 1 <= k <= P = %lld",
+                    (long long)k, (long long)P);
+    if (k > POINTOPS_KNN_KMAX)
+        return fail(POINTOPS_UNSUPPORTED, "k = %lld exceeds POINTOPS_KNN_KMAX = %d",
+                    (long long)k, POINTOPS_KNN_KMAX);
+    if (B == 0 || Q == 0) return POINTOPS_OK;
+    if (Q >= kMaxPoints || P >= kMaxPoints) return fail(POINTOPS_UNSUPPORTED, "sizes >= 2^31");
+    if (B > kMaxGridY) return fail(POINTOPS_UNSUPPORTED, "B > %lld", (long long)kMaxGridY);
+    if (!query || !ref || !out_dist || !out_idx)
+        return fail(POINTOPS_INVALID_ARGUMENT, "null pointer");
+    int st = current_device(nullptr);
+    if (st != POINTOPS_OK) return st;
+    int kcap = 1;
+    while (kcap < k) kcap *= 2;
+    int nw = kcap >= 64 ? 2 : 4;
+    const long nw_env = env_long("POINTOPS_KNN_WAVES", 0);
+    if (nw_env == 1 || (nw_env == 4 && kcap < 64) || (nw_env == 2 && kcap == 64)) nw = (int)nw_env;
+    hipError_t e = pointops::launch_knn(query, ref, B, Q, P, k, out_dist, out_idx, kcap, nw,
+                                        (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "knn launch");
+    return POINTOPS_OK;
+}
+
+int pointops_ball_query(const float* query, const float* ref, int64_t B, int64_t Q, int64_t P,
+                        float radius, int64_t K, float* out_dist2, int64_t* out_idx,
+                        void* stream) {
+    g_err[0] = 0;
+    if (B < 0 || Q < 0 || P < 0) return fail(POINTOPS_INVALID_ARGUMENT, "negative size");
+    if (!(radius > 0.0f) || std::isinf(radius))
+        return fail(POINTOPS_INVALID_ARGUMENT, "radius must be finite and > 0");
+    if (K < 1) return fail(POINTOPS_INVALID_ARGUMENT, "K must be >= 1");
+    if (B == 0 || Q == 0) return POINTOPS_OK;
+    if (Q >= kMaxPoints || P >= kMaxPoints || K >= kMaxPoints)
+        return fail(POINTOPS_UNSUPPORTED, "sizes >= 2^31");
+    if (B > kMaxGridY) return fail(POINTOPS_UNSUPPORTED, "B > %lld", (long long)kMaxGridY);
+    if (!query || (!ref && P > 0) || !out_dist2 || !out_idx)
+        return fail(POINTOPS_INVALID_ARGUMENT, "null pointer");
+    DeviceInfo* dev = nullptr;
+    int st = current_device(&dev);
+    if (st != POINTOPS_OK) return st;
+    // R2 = fl32(r32 * r32), the project page's dense threshold.
+    volatile float r32 = radius;
+    const float r2 = r32 * r32;
+    // Queries per wave: enough waves to fill the device once, and no more than 16.
+    const int64_t rows = B * Q;
+    const int64_t slots = (int64_t)std::max(1, dev->cus) * 4 * 8;
+    int qw = 16;
+    for (int c : {1, 2, 4, 8, 16})
+        if (rows / c <= slots) { qw = c; break; }
+    const long qw_env = env_long("POINTOPS_BQ_QUERIES_PER_WAVE", 0);
+    if (qw_env == 1 || qw_env == 2 || qw_env == 4 || qw_env == 8 || qw_env == 16) qw = (int)qw_env;
+    hipError_t e = pointops::launch_ball_query(query, ref, B, Q, P, r2, K, out_dist2, out_idx,
+                                               qw, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ball_query launch");
+    return POINTOPS_OK;
+}
+
+}  // extern "C"

@@ -96,16 +96,23 @@ def morton_order(xyz: np.ndarray, bits: int = 10) -> np.ndarray:
 
 
 def _three_squares(rng: np.random.Generator, target: int):
-    """Random integers (a, b, c) with a^2 + b^2 + c^2 == target, by search."""
+    """Random integers (a, b, c) with a^2 + b^2 + c^2 == target, by search over
+    batches of random (a, b) with an exact integer square-root test."""
     root = math.isqrt(target)
-    for _ in range(200000):
-        a = int(rng.integers(0, root + 1))
+    for _ in range(100):
+        a = rng.integers(0, root + 1, size=65536, dtype=np.int64)
         rest = target - a * a
-        b = int(rng.integers(0, math.isqrt(rest) + 1))
+        b = np.floor(rng.random(65536) * (np.sqrt(rest.astype(np.float64)) + 1)).astype(np.int64)
         c2 = rest - b * b
-        c = math.isqrt(c2)
-        if c * c == c2:
-            v = np.array([a, b, c], dtype=np.int64)
+        ok = c2 >= 0
+        c = np.floor(np.sqrt(np.where(ok, c2, 0).astype(np.float64))).astype(np.int64)
+        c += (c + 1) * (c + 1) <= c2          # exact integer square root
+        c -= c * c > c2
+        hit = np.nonzero(ok & (c * c == c2))[0]
+        if len(hit):
+            n = hit[0]
+            v = np.array([a[n], b[n], c[n]], dtype=np.int64)
+            assert int(v @ v) == target
             v *= rng.choice([-1, 1], size=3)
             return v[rng.permutation(3)]
     raise RuntimeError(f"no three-square representation found for {target}")

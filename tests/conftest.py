@@ -18,3 +18,15 @@ def oracle_mod():
     import oracle
     oracle.build(force=False)
     return oracle
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    """The GPU path: a visible gfx950 device and the built library. Fails
+    (does not skip) when either is missing, so a GPU run cannot pass silently."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible to torch")
+    from point_cloud_neighbor_amd import ops
+    ops.device_check()
+    return ops

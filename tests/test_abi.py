@@ -1,0 +1,116 @@
+"""The C ABI library loads and exports what include/pointops.h declares, and
+its host-side argument checks answer before anything reaches a device.
+
+Runs without a GPU: none of these calls launches a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pointops.h")
+LIB = os.path.join(ROOT, "point_cloud_neighbor_amd", "libpointops.so")
+
+OK, INVALID, UNSUPPORTED, UNSUPPORTED_DEVICE, HIP_ERROR = range(5)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pointops_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from point_cloud_neighbor_amd import build
+        build.build()
+    lib = ctypes.CDLL(LIB)
+    i64, vp, f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    lib.pointops_fps.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.pointops_knn.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp]
+    lib.pointops_ball_query.argtypes = [vp, vp, i64, i64, i64, f32, i64, vp, vp, vp]
+    lib.pointops_status_string.restype = ctypes.c_char_p
+    lib.pointops_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("pointops_fps", "pointops_fps_workspace_bytes", "pointops_knn",
+                     "pointops_ball_query", "pointops_device_check", "pointops_status_string",
+                     "pointops_last_error", "pointops_abi_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in pointops.h but not exported"
+
+
+def test_status_strings_and_version(lib):
+    assert lib.pointops_abi_version() == 1
+    for code in range(5):
+        assert lib.pointops_status_string(code)
+    assert lib.pointops_status_string(99) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def test_fps_argument_checks(lib):
+    out = FAKE
+    # start index out of range
+    assert lib.pointops_fps(FAKE, 1, 10, 3, 10, out, None, FAKE, 1 << 20, None) == INVALID
+    assert b"start_idx" in lib.pointops_last_error()
+    assert lib.pointops_fps(FAKE, 1, 10, 3, -1, out, None, FAKE, 1 << 20, None) == INVALID
+    # empty cloud with samples requested
+    assert lib.pointops_fps(FAKE, 1, 0, 3, 0, out, None, FAKE, 1 << 20, None) == INVALID
+    assert lib.pointops_fps(FAKE, -1, 10, 3, 0, out, None, FAKE, 1 << 20, None) == INVALID
+    # no-ops: B == 0 or M == 0
+    assert lib.pointops_fps(None, 0, 10, 3, 0, None, None, None, 0, None) == OK
+    assert lib.pointops_fps(None, 2, 10, 0, 0, None, None, None, 0, None) == OK
+    assert lib.pointops_fps(FAKE, 1, 1 << 31, 3, 0, out, None, FAKE, 1 << 20, None) == UNSUPPORTED
+
+
+def test_knn_argument_checks(lib):
+    assert lib.pointops_knn(FAKE, FAKE, 1, 4, 10, 11, FAKE, FAKE, None) == INVALID  # k > P
+    assert lib.pointops_knn(FAKE, FAKE, 1, 4, 10, 0, FAKE, FAKE, None) == INVALID   # k < 1
+    assert lib.pointops_knn(FAKE, FAKE, 1, 4, 100, 65, FAKE, FAKE, None) == UNSUPPORTED
+    assert b"KMAX" in lib.pointops_last_error()
+    assert lib.pointops_knn(None, None, 0, 4, 10, 3, None, None, None) == OK        # B == 0
+    assert lib.pointops_knn(None, None, 2, 0, 10, 3, None, None, None) == OK        # Q == 0
+    assert lib.pointops_knn(FAKE, FAKE, 70000, 4, 10, 3, FAKE, FAKE, None) == UNSUPPORTED
+
+
+def test_ball_query_argument_checks(lib):
+    for r in (0.0, -1.0, float("nan"), float("inf")):
+        assert lib.pointops_ball_query(FAKE, FAKE, 1, 4, 10, r, 3, FAKE, FAKE, None) == INVALID
+    assert lib.pointops_ball_query(FAKE, FAKE, 1, 4, 10, 0.5, 0, FAKE, FAKE, None) == INVALID
+    assert lib.pointops_ball_query(None, None, 0, 4, 10, 0.5, 3, None, None, None) == OK
+    assert lib.pointops_ball_query(None, None, 3, 0, 10, 0.5, 3, None, None, None) == OK
+
+
+def test_no_gpu_means_an_error_not_a_fallback(lib):
+    """Without a usable gfx950 device a well-formed call fails loudly."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; covered by the GPU tests")
+    st = lib.pointops_device_check(0)
+    assert st in (UNSUPPORTED_DEVICE, HIP_ERROR)
+    st = lib.pointops_knn(FAKE, FAKE, 1, 4, 10, 3, FAKE, FAKE, None)
+    assert st in (UNSUPPORTED_DEVICE, HIP_ERROR)
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    from point_cloud_neighbor_amd import ops
+    x = torch.zeros(1, 8, 3)
+    with pytest.raises(ops.PointopsError):
+        ops.knn(x, x, 2)
+    with pytest.raises(ops.PointopsError):
+        ops.ball_query(x, x, 0.5, 2)
+    with pytest.raises(ops.PointopsError):
+        ops.furthest_point_sample(x, 2)

@@ -1,0 +1,263 @@
+"""GPU path versus the oracle, element by element, on seeded inputs that span
+several tiles and ragged tails, plus the edge cases of each operation.
+
+All calls go through the C ABI (via the thin Python binding)."""
+import ctypes
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from point_cloud_neighbor_amd import workloads as W
+from tests.gpu_util import assert_dist_close, assert_idx_equal, dev, gather, host
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def check_fps(gpu, oracle_mod, xyz, M, start=0, what=""):
+    got, gxyz = gpu.furthest_point_sample(dev(xyz), M, start, return_xyz=True)
+    want = oracle_mod.fps(xyz, M, start, threads=4)
+    assert_idx_equal(host(got), want, f"fps {what}")
+    # the sampled coordinates are bit copies of the chosen points
+    assert np.array_equal(host(gxyz).view(np.uint32), gather(xyz, want).view(np.uint32))
+    return want
+
+
+def check_knn(gpu, oracle_mod, q, x, k, what=""):
+    d, i = gpu.knn(dev(q), dev(x), k)
+    wd, wi = oracle_mod.knn(q, x, k, threads=8)
+    assert_idx_equal(host(i), wi, f"knn idx {what}")
+    assert_dist_close(host(d), wd, f"knn dist {what}")
+
+
+def check_bq(gpu, oracle_mod, q, x, r, K, what=""):
+    d2, i = gpu.ball_query(dev(q), dev(x), r, K)
+    wd, wi = oracle_mod.ball_query(q, x, r, K, threads=8)
+    assert_idx_equal(host(i), wi, f"bq idx {what}")
+    assert_dist_close(host(d2), wd, f"bq dist2 {what}")
+
+
+# ------------------------------------------------------------------ the pages' example
+
+def test_worked_example(gpu, oracle_mod):
+    with open(os.path.join(GOLDEN, "unit_square.json")) as f:
+        g = json.load(f)
+    xyz = np.array(g["xyz"], dtype=np.float32)
+    c, cx = gpu.furthest_point_sample(dev(xyz), g["fps_npoint"], g["fps_start_idx"],
+                                      return_xyz=True)
+    assert host(c).tolist() == g["fps_idx"]
+    d, i = gpu.knn(cx, dev(xyz), g["knn_k"])
+    assert host(i).tolist() == g["knn_idx"]
+    assert host(d).tolist() == g["derived"]["knn_dist"]
+    d2, j = gpu.ball_query(cx, dev(xyz), g["bq_radius"], g["bq_K"])
+    assert host(j).tolist() == g["bq_idx"]
+    assert host(d2).tolist() == g["derived"]["bq_dist2"]
+
+
+# ------------------------------------------------------------------ exact (integer / dyadic) clouds
+
+EXACT = [
+    ("int4", lambda s: W.integer_cloud(s, 2, 300, 0, 4)),
+    ("int2", lambda s: W.integer_cloud(s, 1, 1100, 0, 2)),
+    ("int_wide", lambda s: W.integer_cloud(s, 3, 777, -1000, 1000)),
+    ("dyadic", lambda s: W.dyadic_cloud(s, 2, 2049, 64)),
+]
+
+
+@pytest.mark.parametrize("name,make", EXACT)
+def test_exact_clouds_all_ops(gpu, oracle_mod, name, make):
+    xyz = make(0)
+    B, N, _ = xyz.shape
+    for M, start in [(1, 0), (37, N - 1), (N, 5), (N + 9, 2)]:
+        check_fps(gpu, oracle_mod, xyz, M, start, f"{name} M={M}")
+    q = xyz[:, ::5].copy()
+    for k in (1, 3, 16, 17, 64):
+        check_knn(gpu, oracle_mod, q, xyz, k, f"{name} k={k}")
+    scale = 64.0 if name == "dyadic" else (300.0 if name == "int_wide" else 1.0)
+    for r in (1.0, 1.5, 2.0):
+        for K in (1, 31, 64, 65, 300):
+            check_bq(gpu, oracle_mod, q, xyz, r * scale if name != "dyadic" else r / 8, K,
+                     f"{name} r={r} K={K}")
+
+
+# ------------------------------------------------------------------ float clouds, shapes and tails
+
+@pytest.mark.parametrize("B,N", [(1, 1), (1, 2), (1, 63), (1, 64), (2, 65), (1, 1000), (3, 1025),
+                                 (1, 4097), (2, 20000), (1, 70001)])
+def test_fps_shapes(gpu, oracle_mod, B, N):
+    xyz = W.uniform_cube(N, B, N)
+    for M in sorted({1, 2, min(N, 100), N + 3 if N < 2000 else 300}):
+        check_fps(gpu, oracle_mod, xyz, M, N // 3, f"B={B} N={N} M={M}")
+
+
+@pytest.mark.parametrize("G", [2, 3, 7, 16, 33])
+def test_fps_forced_workgroups_per_cloud(gpu, oracle_mod, G, monkeypatch):
+    """The cross-workgroup argmax, forced on mid-sized clouds; twice, same bits."""
+    monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", str(G))
+    xyz = W.sphere_shell(G, 2, 5000 + G)
+    want = check_fps(gpu, oracle_mod, xyz, 700, 11, f"G={G}")
+    again = host(gpu.furthest_point_sample(dev(xyz), 700, 11))
+    assert np.array_equal(again, want)
+
+
+def test_fps_ties_and_duplicates(gpu, oracle_mod, monkeypatch):
+    xyz = W.integer_cloud(5, 2, 3000, 0, 3)      # 27 distinct locations, heavy ties
+    for G in ("1", "5"):
+        monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", G)
+        check_fps(gpu, oracle_mod, xyz, 60, 7, f"dups G={G}")
+    line = W.line_cloud(1025)
+    check_fps(gpu, oracle_mod, line, 1030, 0, "line")
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5, 8, 15, 16, 17, 31, 32, 33, 63, 64])
+def test_knn_k_values(gpu, oracle_mod, k):
+    x = W.uniform_cube(100 + k, 2, 1500)
+    q = W.uniform_cube(200 + k, 2, 130)
+    check_knn(gpu, oracle_mod, q, x, k, f"k={k}")
+
+
+@pytest.mark.parametrize("Q,P,k", [(1, 1, 1), (1, 16, 16), (63, 64, 7), (65, 65, 64),
+                                   (64, 100, 8), (200, 7, 7), (129, 5003, 16), (70, 20011, 32)])
+def test_knn_shapes(gpu, oracle_mod, Q, P, k):
+    x = W.sphere_shell(P, 1, P)
+    q = W.sphere_shell(Q + 1, 1, Q)
+    check_knn(gpu, oracle_mod, q, x, k, f"Q={Q} P={P} k={k}")
+
+
+@pytest.mark.parametrize("env", ["1", "4"])
+def test_knn_wave_split_agrees(gpu, oracle_mod, env, monkeypatch):
+    monkeypatch.setenv("POINTOPS_KNN_WAVES", env)
+    x = W.uniform_cube(9, 1, 3001)
+    check_knn(gpu, oracle_mod, x[:, :97].copy(), x, 16, f"waves={env}")
+
+
+@pytest.mark.parametrize("Q,P,K,r", [(1, 0, 4, 0.5), (5, 1, 1, 0.5), (63, 64, 31, 0.3),
+                                     (65, 65, 33, 0.3), (130, 1000, 64, 0.2),
+                                     (200, 5000, 65, 0.15), (100, 3000, 200, 0.5),
+                                     (64, 4096, 1, 0.05)])
+def test_ball_query_shapes(gpu, oracle_mod, Q, P, K, r):
+    x = W.uniform_cube(P + 1, 2, P)
+    q = W.uniform_cube(Q + 2, 2, Q)
+    check_bq(gpu, oracle_mod, q, x, r, K, f"Q={Q} P={P} K={K} r={r}")
+
+
+@pytest.mark.parametrize("qw", ["1", "2", "4", "8", "16"])
+def test_ball_query_queries_per_wave(gpu, oracle_mod, qw, monkeypatch):
+    monkeypatch.setenv("POINTOPS_BQ_QUERIES_PER_WAVE", qw)
+    x = W.uniform_cube(3, 1, 2500)
+    check_bq(gpu, oracle_mod, x[:, :77].copy(), x, 0.12, 40, f"qw={qw}")
+
+
+def test_ball_query_planted_boundary(gpu, oracle_mod):
+    rng = np.random.default_rng(3)
+    xyz = (np.round(rng.random((400, 3)) * 64) / 64).astype(np.float32)
+    planted = W.plant_radius_partners(rng, xyz, np.arange(40), np.arange(40, 160),
+                                      W.R2_BITS[0.05])
+    x = xyz[None]
+    check_bq(gpu, oracle_mod, x[:, :40].copy(), x, 0.05, 64, "planted")
+    d2, idx = gpu.ball_query(dev(x[:, :40].copy()), dev(x), 0.05, 64)
+    idx = host(idx)[0]
+    m = W.R2_BITS[0.05] & 0x7FFFFF | 0x800000
+    for a, v, num in planted:
+        assert (v in idx[a]) == (num < m), (a, v, num)
+
+
+def test_subnormal_distances(gpu, oracle_mod):
+    x = W.subnormal_cloud(5, 300)
+    q = x[:, :40].copy()
+    check_knn(gpu, oracle_mod, q, x, 9, "subnormal")
+    check_bq(gpu, oracle_mod, q, x, 3e-20, 50, "subnormal")
+    check_fps(gpu, oracle_mod, x, 50, 0, "subnormal")
+
+
+def test_self_queries_and_duplicates(gpu, oracle_mod):
+    x = W.uniform_cube(8, 1, 2000)
+    x[0, 1500] = x[0, 3]      # exact duplicate with a larger index
+    x[0, 10] = x[0, 700]      # and with a smaller one
+    check_knn(gpu, oracle_mod, x, x, 4, "self")
+    check_bq(gpu, oracle_mod, x, x, 0.03, 8, "self")
+
+
+def test_noncontiguous_inputs(gpu, oracle_mod):
+    base = W.uniform_cube(12, 2, 2000)
+    t = dev(base)[:, ::2]                      # a strided view
+    d, i = gpu.knn(t, t, 5)
+    wd, wi = oracle_mod.knn(base[:, ::2].copy(), base[:, ::2].copy(), 5)
+    assert_idx_equal(host(i), wi, "strided")
+
+
+# ------------------------------------------------------------------ unwritten slots, errors
+
+def _raw_lib():
+    from point_cloud_neighbor_amd import ops
+    return ops._load()
+
+
+def test_every_output_slot_written(gpu):
+    """Outputs prefilled with sentinels (NaN bits, index -2) come back with no
+    sentinel left, through the C ABI directly."""
+    lib = _raw_lib()
+    x = dev(W.uniform_cube(21, 2, 3000))
+    q = x[:, :150].contiguous()
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for K in (1, 33, 100):
+        d2 = torch.full((2, 150, K), float("nan"), device="cuda")
+        ix = torch.full((2, 150, K), -2, dtype=torch.int64, device="cuda")
+        assert lib.pointops_ball_query(q.data_ptr(), x.data_ptr(), 2, 150, 3000,
+                                       ctypes.c_float(0.1), K, d2.data_ptr(), ix.data_ptr(), s) == 0
+        assert not torch.isnan(d2).any() and not (ix == -2).any()
+    d = torch.full((2, 150, 20), float("nan"), device="cuda")
+    ix = torch.full((2, 150, 20), -2, dtype=torch.int64, device="cuda")
+    assert lib.pointops_knn(q.data_ptr(), x.data_ptr(), 2, 150, 3000, 20, d.data_ptr(),
+                            ix.data_ptr(), s) == 0
+    assert not torch.isnan(d).any() and not (ix < 0).any()
+    ws = torch.empty(lib.pointops_fps_workspace_bytes(2, 3000, 64), dtype=torch.uint8, device="cuda")
+    o = torch.full((2, 64), -2, dtype=torch.int64, device="cuda")
+    assert lib.pointops_fps(x.data_ptr(), 2, 3000, 64, 0, o.data_ptr(), None, ws.data_ptr(),
+                            ws.numel(), s) == 0
+    assert not (o < 0).any()
+
+
+def test_fps_bounded_wait_terminates(gpu, monkeypatch):
+    """A tiny bound on the cross-workgroup wait (forced from the host) makes the
+    kernel stop early instead of waiting: the call returns, output slots not
+    reached hold -1 and the rest are valid indices."""
+    monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", "8")
+    monkeypatch.setenv("POINTOPS_FPS_SPIN_LIMIT", "0")
+    xyz = dev(W.uniform_cube(4, 1, 20000))
+    out = host(gpu.furthest_point_sample(xyz, 500))
+    torch.cuda.synchronize()
+    assert ((out >= 0) & (out < 20000) | (out == -1)).all()
+    first_bad = np.argmax(out[0] == -1) if (out == -1).any() else 500
+    assert (out[0, first_bad:] == -1).all()
+
+
+def test_unsupported_device_is_an_error(gpu):
+    from point_cloud_neighbor_amd import ops
+    import subprocess, sys
+    code = ("import os, torch; os.environ['POINTOPS_FORCE_UNSUPPORTED_DEVICE']='1';"
+            "from point_cloud_neighbor_amd import ops;"
+            "x=torch.zeros(1,8,3,device='cuda')\n"
+            "try:\n ops.knn(x,x,2); print('NOERR')\n"
+            "except ops.PointopsError as e: print('ERR', e.status)")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))), timeout=120)
+    assert "ERR 3" in r.stdout, r.stdout + r.stderr
+
+
+def test_invalid_arguments_raise(gpu):
+    x = dev(W.uniform_cube(1, 1, 10))
+    with pytest.raises(gpu.PointopsError):
+        gpu.knn(x, x, 11)
+    with pytest.raises(gpu.PointopsError):
+        gpu.knn(x, x, 0)
+    with pytest.raises(gpu.PointopsError):
+        gpu.furthest_point_sample(x, 3, 10)
+    with pytest.raises(gpu.PointopsError):
+        gpu.ball_query(x, x, -1.0, 3)
+    with pytest.raises(gpu.PointopsError):
+        gpu.knn(x.double(), x.double(), 2)

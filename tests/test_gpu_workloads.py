@@ -1,0 +1,126 @@
+"""The five benchmark workloads at full size, in the launch configuration the
+benchmark times. Where the oracle would take too long, whole outputs are
+checked through properties that hold at any size and sampled rows (or an FPS
+prefix, which does not depend on the number of samples) are checked element by
+element against the oracle."""
+import numpy as np
+import pytest
+
+from point_cloud_neighbor_amd import workloads as W
+from tests.gpu_util import assert_dist_close, assert_idx_equal, dev, gather, host
+
+pytestmark = pytest.mark.gpu
+
+THREADS = 8
+
+
+def row_blocks(n, size, count=3):
+    starts = np.linspace(0, max(n - size, 0), count).astype(int)
+    return [(int(s), int(min(n, s + size))) for s in starts]
+
+
+def knn_properties(d, i, P):
+    assert (i >= 0).all() and (i < P).all()
+    assert (np.diff(d, axis=-1) >= 0).all()
+    srt = np.sort(i, axis=-1)
+    assert (np.diff(srt, axis=-1) > 0).all(), "a row repeats an index"
+
+
+def bq_properties(d2, i, K, r2):
+    valid = i >= 0
+    # hits first, padding after; indices strictly increasing among hits
+    assert (valid[..., :-1] | ~valid[..., 1:]).all()
+    inc = np.diff(np.where(valid, i, np.iinfo(np.int64).max), axis=-1)
+    assert (inc[valid[..., 1:]] > 0).all()
+    assert (d2[valid] < r2).all()
+    assert (d2[~valid].view(np.uint32) == 0).all()
+
+
+def test_tiny(gpu, oracle_mod):
+    w = W.workload("tiny")
+    x = w.xyz
+    c, cx = gpu.furthest_point_sample(dev(x), w.fps_m, w.fps_start, return_xyz=True)
+    wc = oracle_mod.fps(x, w.fps_m, w.fps_start)
+    assert_idx_equal(host(c), wc, "tiny fps")
+    centres = gather(x, wc)
+    d, i = gpu.knn(cx, dev(x), w.knn_k)
+    wd, wi = oracle_mod.knn(centres, x, w.knn_k)
+    assert_idx_equal(host(i), wi, "tiny knn")
+    assert_dist_close(host(d), wd, "tiny knn")
+    d2, j = gpu.ball_query(cx, dev(x), w.bq_radius, w.bq_k)
+    wd2, wj = oracle_mod.ball_query(centres, x, w.bq_radius, w.bq_k)
+    assert_idx_equal(host(j), wj, "tiny bq")
+    assert_dist_close(host(d2), wd2, "tiny bq")
+
+
+def test_grouping(gpu, oracle_mod):
+    w = W.workload("grouping")
+    x = w.xyz
+    c, cx = gpu.furthest_point_sample(dev(x), w.fps_m, w.fps_start, return_xyz=True)
+    wc = oracle_mod.fps(x, w.fps_m, w.fps_start, threads=THREADS)
+    assert_idx_equal(host(c), wc, "grouping fps")
+    centres = gather(x, wc)
+    d, i = gpu.knn(cx, dev(x), w.knn_k)
+    wd, wi = oracle_mod.knn(centres, x, w.knn_k, threads=THREADS)
+    assert_idx_equal(host(i), wi, "grouping knn")
+    assert_dist_close(host(d), wd, "grouping knn")
+
+
+def test_large(gpu, oracle_mod):
+    w = W.workload("large")
+    x = w.xyz
+    N = x.shape[1]
+    c = gpu.furthest_point_sample(dev(x), w.fps_m, w.fps_start)
+    wc = oracle_mod.fps(x, w.fps_m, w.fps_start)
+    assert_idx_equal(host(c), wc, "large fps")
+    xd = dev(x)
+    d, i = gpu.knn(xd, xd, w.knn_k)
+    d, i = host(d), host(i)
+    knn_properties(d, i, N)
+    # uniform float32 points are distinct here: each point is its own nearest
+    assert (i[0, :, 0] == np.arange(N)).all() and (d[0, :, 0] == 0).all()
+    for lo, hi in row_blocks(N, 256):
+        wd, wi = oracle_mod.knn(x, x, w.knn_k, rows=(lo, hi), threads=THREADS)
+        assert_idx_equal(i[:, lo:hi], wi[:, lo:hi], f"large knn rows {lo}:{hi}")
+        assert_dist_close(d[:, lo:hi], wd[:, lo:hi], f"large knn rows {lo}:{hi}")
+
+
+def test_sorted_bq(gpu, oracle_mod):
+    w = W.workload("sorted_bq")
+    x = w.xyz
+    N = x.shape[1]
+    xd = dev(x)
+    d2, i = gpu.ball_query(xd, xd, w.bq_radius, w.bq_k)
+    d2, i = host(d2), host(i)
+    r2 = W.bits_to_f32(W.R2_BITS[0.05])
+    bq_properties(d2, i, w.bq_k, r2)
+    blocks = row_blocks(N, 512, 4)
+    # rows holding exact on-radius pairs: a point on the 1/64 grid whose row
+    # includes a partner at exactly the float below R2
+    on_grid = np.nonzero((np.round(x[0] * 64) / 64 == x[0]).all(axis=1))[0]
+    blocks += [(int(a), int(a) + 1) for a in on_grid[:200]]
+    for lo, hi in blocks:
+        wd2, wi = oracle_mod.ball_query(x, x, w.bq_radius, w.bq_k, rows=(lo, hi), threads=THREADS)
+        assert_idx_equal(i[:, lo:hi], wi[:, lo:hi], f"sorted bq rows {lo}:{hi}")
+        assert_dist_close(d2[:, lo:hi], wd2[:, lo:hi], f"sorted bq rows {lo}:{hi}")
+
+
+def test_stress(gpu, oracle_mod):
+    w = W.workload("stress")
+    x = w.xyz
+    N = x.shape[1]
+    c, cx = gpu.furthest_point_sample(dev(x), w.fps_m, w.fps_start, return_xyz=True)
+    c = host(c)
+    prefix = 2048     # the first outputs of FPS do not depend on how many follow
+    wc = oracle_mod.fps(x, prefix, w.fps_start)
+    assert_idx_equal(c[:, :prefix], wc, "stress fps prefix")
+    assert len(np.unique(c)) == w.fps_m   # 1M points, 16384 samples: all distinct
+    d2, i = gpu.ball_query(cx, dev(x), w.bq_radius, w.bq_k)
+    d2, i = host(d2), host(i)
+    bq_properties(d2, i, w.bq_k, W.bits_to_f32(W.R2_BITS[0.03]))
+    centres = gather(x, c)
+    for lo, hi in row_blocks(w.fps_m, 128):
+        wd2, wi = oracle_mod.ball_query(centres, x, w.bq_radius, w.bq_k, rows=(lo, hi),
+                                        threads=THREADS)
+        assert_idx_equal(i[:, lo:hi], wi[:, lo:hi], f"stress bq rows {lo}:{hi}")
+        assert_dist_close(d2[:, lo:hi], wd2[:, lo:hi], f"stress bq rows {lo}:{hi}")
