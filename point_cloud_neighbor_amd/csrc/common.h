@@ -59,6 +59,38 @@ __device__ __forceinline__ int wave_max_i32(int v) {
     return __builtin_amdgcn_readfirstlane(v);
 }
 
+// DPP lane movement (gfx9 encodings): quad_perm, row mirrors, row broadcasts.
+constexpr int kDppQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t src) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Maximum of an unsigned 32-bit value over the 64 lanes of a wave, returned
+// wave-uniform. Lanes exchange through DPP (no LDS traffic): butterflies inside
+// each row of 16 lanes, then row broadcasts carry rows 0-1 and 0-2 into the
+// last row, whose lane 63 holds the maximum.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<kDppQuadSwap1>(v, v));
+    v = max(v, dpp_u32<kDppQuadSwap2>(v, v));
+    v = max(v, dpp_u32<kDppRowHalfMirror>(v, v));
+    v = max(v, dpp_u32<kDppRowMirror>(v, v));
+    v = max(v, dpp_u32<kDppRowBcast15, 0xA>(v, v));
+    v = max(v, dpp_u32<kDppRowBcast31, 0xC>(v, v));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Value of `v` in lane `l` (l wave-uniform).
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int l) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
 // Lane-wise maximum of an unsigned 64-bit key over the 64 lanes of a wave;
 // every lane gets the result.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {

@@ -36,7 +36,7 @@
 namespace pointops {
 
 constexpr int kKnnGroup = 8;     // references tested per threshold check
-constexpr int kKnnBuf = 24;      // candidate slots per lane (>= kKnnGroup + 1)
+constexpr int kKnnBuf = 16;      // candidate slots per lane (>= kKnnGroup + 1)
 
 template <int KCAP>
 struct TopK {
@@ -191,8 +191,9 @@ hipError_t launch_knn(const float* query, const float* ref, int64_t B, int64_t Q
     POINTOPS_KNN_CASE(2, 1) POINTOPS_KNN_CASE(2, 4)
     POINTOPS_KNN_CASE(4, 1) POINTOPS_KNN_CASE(4, 4)
     POINTOPS_KNN_CASE(8, 1) POINTOPS_KNN_CASE(8, 4)
-    POINTOPS_KNN_CASE(16, 1) POINTOPS_KNN_CASE(16, 4)
-    POINTOPS_KNN_CASE(32, 1) POINTOPS_KNN_CASE(32, 4)
+    POINTOPS_KNN_CASE(16, 1) POINTOPS_KNN_CASE(16, 2) POINTOPS_KNN_CASE(16, 4)
+    POINTOPS_KNN_CASE(16, 8)
+    POINTOPS_KNN_CASE(32, 1) POINTOPS_KNN_CASE(32, 2) POINTOPS_KNN_CASE(32, 4)
     POINTOPS_KNN_CASE(64, 1) POINTOPS_KNN_CASE(64, 2)
 #undef POINTOPS_KNN_CASE
     return hipErrorInvalidValue;

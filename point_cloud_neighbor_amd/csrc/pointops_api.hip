@@ -10,6 +10,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <utility>
 
 #include "../../include/pointops.h"
 
@@ -100,19 +101,25 @@ struct FpsPlan {
     int block;  // threads per workgroup
 };
 
-// Points per workgroup for one cloud: enough workgroups that a step's update is
-// short, few enough that the per-step exchange stays cheap and every cloud's
-// workgroups fit on the device at once.
+// Workgroups per cloud. One workgroup per cloud avoids the cross-workgroup
+// exchange (about 1 us per step) and is fastest whenever the cloud fits in one
+// workgroup (16 points per thread, its coordinates in LDS). Larger clouds take
+// about 4096 points per workgroup, at most 128 workgroups (more slots make the
+// exchange slower than the update they save), more only if a slice would not
+// fit, and at most the number of workgroups the device runs at once.
 FpsPlan fps_plan(int64_t B, int64_t N, const DeviceInfo& dev) {
     const int64_t cus = std::max(1, dev.cus);
+    const int64_t max_slice = std::min<int64_t>(16 * 1024, ((int64_t)dev.lds_per_block - 1024) / 12);
     long g_env = env_long("POINTOPS_FPS_WG_PER_CLOUD", 0);
     int64_t G;
     if (g_env > 0) {
         G = g_env;
+    } else if (N <= max_slice) {
+        G = 1;
     } else {
-        // target ~4096 points per workgroup, at most one workgroup per CU overall
-        G = (N + 4095) / 4096;
-        G = std::min<int64_t>(G, std::max<int64_t>(1, cus / std::max<int64_t>(B, 1)));
+        G = std::min<int64_t>((N + 4095) / 4096, 128);
+        G = std::max<int64_t>(G, (N + max_slice - 1) / max_slice);
+        G = std::min<int64_t>(G, std::max<int64_t>(1, 4 * cus / std::max<int64_t>(B, 1)));
     }
     G = std::max<int64_t>(1, std::min<int64_t>(G, N));
     int64_t slice = (N + G - 1) / G;
@@ -124,16 +131,8 @@ FpsPlan fps_plan(int64_t B, int64_t N, const DeviceInfo& dev) {
     }
     FpsPlan p;
     p.G = (int)G;
-    p.block = slice <= 1024 ? 256 : 1024;
-    const int64_t per = (slice + p.block - 1) / p.block;
-    int ppt = 1;
-    while (ppt < per) ppt *= 2;
-    if (p.block == 256 && ppt > 4) {
-        p.block = 1024;
-        ppt = 1;
-        while (ppt < (slice + 1023) / 1024) ppt *= 2;
-    }
-    p.ppt = ppt;
+    p.block = slice > 1024 ? 1024 : 256;
+    p.ppt = (int)((slice + p.block - 1) / p.block);
     return p;
 }
 
@@ -190,7 +189,7 @@ int pointops_fps(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t star
     if (st != POINTOPS_OK) return st;
     const FpsPlan p = fps_plan(B, N, *dev);
     const int64_t slice = (N + p.G - 1) / p.G;
-    if (p.ppt > 16 || slice * 12 > (int64_t)std::min<size_t>(dev->lds_per_block, 65536) - 1024)
+    if (p.ppt > 16 || slice * 12 > (int64_t)dev->lds_per_block - 1024)
         return fail(POINTOPS_UNSUPPORTED,
                     "cloud of %lld points needs %d workgroups of %lld points; "
                     "raise POINTOPS_FPS_WG_PER_CLOUD", (long long)N, p.G, (long long)slice);
@@ -232,7 +231,9 @@ int pointops_knn(const float* query, const float* ref, int64_t B, int64_t Q, int
     while (kcap < k) kcap *= 2;
     int nw = kcap >= 64 ? 2 : 4;
     const long nw_env = env_long("POINTOPS_KNN_WAVES", 0);
-    if (nw_env == 1 || (nw_env == 4 && kcap < 64) || (nw_env == 2 && kcap == 64)) nw = (int)nw_env;
+    if (nw_env == 1 || (nw_env == 2 && kcap >= 16) || (nw_env == 4 && kcap < 64) ||
+        (nw_env == 8 && kcap == 16))
+        nw = (int)nw_env;
     hipError_t e = pointops::launch_knn(query, ref, B, Q, P, k, out_dist, out_idx, kcap, nw,
                                         (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "knn launch");
@@ -259,11 +260,13 @@ int pointops_ball_query(const float* query, const float* ref, int64_t B, int64_t
     // R2 = fl32(r32 * r32), the project page's dense threshold.
     volatile float r32 = radius;
     const float r2 = r32 * r32;
-    // Queries per wave: enough waves to fill the device once, and no more than 16.
+    // Queries per wave: fewer queries per wave until the grid is about one
+    // device-full of waves; at most 8 (measured faster than 16 on 100k x 100k:
+    // the shorter waves balance better).
     const int64_t rows = B * Q;
     const int64_t slots = (int64_t)std::max(1, dev->cus) * 4 * 8;
-    int qw = 16;
-    for (int c : {1, 2, 4, 8, 16})
+    int qw = 8;
+    for (int c : {1, 2, 4, 8})
         if (rows / c <= slots) { qw = c; break; }
     const long qw_env = env_long("POINTOPS_BQ_QUERIES_PER_WAVE", 0);
     if (qw_env == 1 || qw_env == 2 || qw_env == 4 || qw_env == 8 || qw_env == 16) qw = (int)qw_env;
