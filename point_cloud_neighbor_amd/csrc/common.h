@@ -77,12 +77,14 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t src) {
 // each row of 16 lanes, then row broadcasts carry rows 0-1 and 0-2 into the
 // last row, whose lane 63 holds the maximum.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, dpp_u32<kDppQuadSwap1>(v, v));
-    v = max(v, dpp_u32<kDppQuadSwap2>(v, v));
-    v = max(v, dpp_u32<kDppRowHalfMirror>(v, v));
-    v = max(v, dpp_u32<kDppRowMirror>(v, v));
-    v = max(v, dpp_u32<kDppRowBcast15, 0xA>(v, v));
-    v = max(v, dpp_u32<kDppRowBcast31, 0xC>(v, v));
+    // 0 (the identity of max) stands in for lanes a row mask leaves out, which
+    // also lets the compiler fold each lane move into the max instruction
+    v = max(v, dpp_u32<kDppQuadSwap1>(0u, v));
+    v = max(v, dpp_u32<kDppQuadSwap2>(0u, v));
+    v = max(v, dpp_u32<kDppRowHalfMirror>(0u, v));
+    v = max(v, dpp_u32<kDppRowMirror>(0u, v));
+    v = max(v, dpp_u32<kDppRowBcast15, 0xA>(0u, v));
+    v = max(v, dpp_u32<kDppRowBcast31, 0xC>(0u, v));
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 

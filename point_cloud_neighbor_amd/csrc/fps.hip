@@ -43,6 +43,8 @@
 // `spin_limit` polls raises the status word and stops; the others then stop on
 // their own bound; output slots not reached are -1.
 #include <algorithm>
+#include <tuple>
+#include <type_traits>
 #include <utility>
 
 #include "common.h"
@@ -217,6 +219,412 @@ __global__ __launch_bounds__(BLOCK) void fps_kernel(
     }
 }
 
+// ---------------------------------------------------------------- batched FPS
+//
+// The same selection, with far fewer cross-workgroup exchanges. Wave 0 of every
+// workgroup holds no points; the other waves hold the slice. At an exchange
+// each point wave reports its top point (largest key (m, -index)) and a bound:
+// the largest key among its other points. Every workgroup receives the same
+// candidate set C (the reported tops, with coordinates and m) and the largest
+// bound beta over all reports, and wave 0 of each workgroup then runs FPS steps
+// on C alone: it takes the largest key K* in C and folds the new centre into
+// the m of every candidate. Every point outside C has a key below beta, and
+// keys only decrease as centres are added, so whenever K* > beta the candidate
+// is the true next centre of the whole cloud; the first step after an
+// exchange always qualifies (every report's top is in C). When a step does not
+// qualify, or the batch is full, the batch ends. While wave 0 certifies
+// centres, the point waves fold each new centre (read from an LDS list) into
+// their points' m; at the end of the batch every point is up to date and the
+// next exchange starts. All decisions are the ones the plain definition makes,
+// in the same order; only the communication is batched.
+
+constexpr int kFpsMaxBatch = 256;  // centres certified per batch at most
+constexpr uint32_t kNone = 0xFFFFFFFFu;
+
+template <int N_>
+__device__ __forceinline__ uint32_t select_u32(const uint32_t (&v)[N_], int i) {
+    uint32_t r = v[0];
+#pragma unroll
+    for (int s = 1; s < N_; ++s) r = i == s ? v[s] : r;
+    return r;
+}
+
+template <int N_>
+__device__ __forceinline__ float select_f32(const float (&v)[N_], int i) {
+    float r = v[0];
+#pragma unroll
+    for (int s = 1; s < N_; ++s) r = i == s ? v[s] : r;
+    return r;
+}
+
+// Key order: larger m first, then smaller index.
+__device__ __forceinline__ bool key_gt(uint32_t ma, uint32_t ja, uint32_t mb, uint32_t jb) {
+    return ma > mb || (ma == mb && ja < jb);
+}
+
+// Largest key over the lanes of a wave whose `use` flag is set. Lanes must be
+// in increasing index order (the first lane holding the largest m has the
+// smallest index). Returns (m, index) of the winner, (0, kNone) when no lane
+// takes part.
+__device__ __forceinline__ void wave_max_key(uint32_t m, uint32_t j, bool use, uint32_t& om,
+                                             uint32_t& oj, int& olane) {
+    const uint32_t mx = wave_max_u32(use ? m : 0u);
+    const uint64_t mask = ballot(use && m == mx);
+    if (mask == 0) {
+        om = 0;
+        oj = kNone;
+        olane = -1;
+        return;
+    }
+    olane = __builtin_ctzll(mask);
+    om = mx;
+    oj = lane_value(j, olane);
+}
+
+template <int PPT, int BLOCK, int CPL>
+__global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
+    const float* __restrict__ xyz, int N, int M, int start_idx, int G, int slice, int RG,
+    int64_t* __restrict__ out_idx, float* __restrict__ out_xyz, uint64_t* __restrict__ words,
+    int stride, uint32_t* __restrict__ status, uint32_t spin_limit) {
+    constexpr int NW = BLOCK / kWave;
+    // Waves whose index is a multiple of 4 hold no points, so the certifying
+    // wave 0 has its SIMD (waves go round-robin over the 4 SIMDs of a CU) to
+    // itself; the other waves are the point waves.
+    constexpr int NPW = NW - NW / 4;
+    static_assert(NW % 4 == 0 && NPW >= 1 && NPW <= kWave, "wave count");
+    __shared__ float cen[3][kFpsMaxBatch];
+    __shared__ uint32_t cen_j[kFpsMaxBatch];  // index of each certified centre
+    __shared__ int cen_count, cen_done, sh_t, sh_abort;
+    __shared__ uint32_t wt[5][NPW];  // each point wave's top: m, index, x, y, z
+    __shared__ uint32_t wb[2][NPW];  // each point wave's bound: m, index
+    __shared__ uint32_t live_c[5][kWave * CPL];  // compacted live candidates
+    extern __shared__ uint32_t stage[];  // gathered words, G * (5 * RG + 2)
+
+    const int b = blockIdx.x / G;
+    const int g = blockIdx.x - b * G;
+    const int tid = threadIdx.x;
+    const int wave = uniform(tid / kWave);
+    const int lane = tid % kWave;
+    const float* xb = xyz + (size_t)b * N * 3;
+    const int lo = g * slice;
+    const int cnt = min(N, lo + slice) - lo;  // >= 1
+    const bool point_wave = wave % 4 != 0;
+    const int pw = wave - 1 - wave / 4;       // index among the point waves
+    const int u = pw * kWave + lane;          // point-thread id
+    const int wbase = pw * kWave * PPT;       // first slice position of this wave
+
+    float px[PPT], py[PPT], pz[PPT];
+    uint32_t pm[PPT];
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+        const int r = u * PPT + p;
+        const bool real = point_wave && r < cnt;
+        const size_t j = (size_t)lo + (real ? r : 0);
+        px[p] = xb[3 * j + 0];
+        py[p] = xb[3 * j + 1];
+        pz[p] = xb[3 * j + 2];
+        pm[p] = real ? 0x7F800000u : 0u;  // +inf for points, +0 for padding
+    }
+
+    int64_t* ob = out_idx + (size_t)b * M;
+    float* oxb = out_xyz ? out_xyz + (size_t)b * M * 3 : nullptr;
+    uint64_t* cw = words + (size_t)b * 2 * G * stride;
+    if (tid == 0) {
+        const float sx = xb[(size_t)3 * start_idx + 0], sy = xb[(size_t)3 * start_idx + 1],
+                    sz = xb[(size_t)3 * start_idx + 2];
+        cen[0][0] = sx; cen[1][0] = sy; cen[2][0] = sz;
+        cen_count = 1;
+        cen_done = 1;
+        sh_t = 1;
+        sh_abort = 0;
+        if (g == 0) {
+            ob[0] = start_idx;
+            if (oxb) { oxb[0] = sx; oxb[1] = sy; oxb[2] = sz; }
+        }
+    }
+    if (wave == 0) __builtin_amdgcn_s_setprio(3);
+    __syncthreads();
+
+    uint32_t batch = 0;
+    int out_t0 = 0;  // output slot of the current batch's first centre (0: c_0, written above)
+    while (true) {
+        // ---- point waves: fold in the centres of the current batch as they come
+        if (point_wave) {
+            int a = 0;
+            while (true) {
+                const int d = __hip_atomic_load(&cen_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                const int n = __hip_atomic_load(&cen_count, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                for (; a < n; ++a) {
+                    const float cx = cen[0][a], cy = cen[1][a], cz = cen[2][a];
+                    // outputs are written here, not by the certifying wave, so that
+                    // wave never waits on a global store
+                    if (g == 0 && pw == 0 && point_wave && lane == 0 && out_t0 >= 1) {
+                        ob[out_t0 + a] = cen_j[a];
+                        if (oxb) {
+                            oxb[3 * (out_t0 + a) + 0] = cx;
+                            oxb[3 * (out_t0 + a) + 1] = cy;
+                            oxb[3 * (out_t0 + a) + 2] = cz;
+                        }
+                    }
+#pragma unroll
+                    for (int p = 0; p < PPT; ++p)
+                        pm[p] = min(pm[p], f2u(s32(cx, cy, cz, px[p], py[p], pz[p])));
+                }
+                if (d) break;  // done was set after the last count: n is final
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __syncthreads();
+        const int t0 = sh_t;
+        if (t0 >= M || sh_abort) break;
+        ++batch;
+        out_t0 = t0;
+        if (wave == 0) {
+            if (lane == 0) {
+                cen_count = 0;
+                cen_done = 0;
+            }
+        } else if (point_wave) {
+            // ---- point waves: top and bound of this wave
+            uint32_t m1 = pm[0], m2 = 0;
+            int p1 = 0, p2 = -1;
+#pragma unroll
+            for (int p = 1; p < PPT; ++p) {
+                if (pm[p] > m1) {
+                    m2 = m1; p2 = p1; m1 = pm[p]; p1 = p;
+                } else if (p2 < 0 || pm[p] > m2) {
+                    m2 = pm[p]; p2 = p;
+                }
+            }
+            const bool valid = wbase < cnt;  // the wave holds real points
+            uint32_t tm, tj, bm, bj;
+            int tl;
+            wave_max_key(m1, (uint32_t)(lo + wbase + lane * PPT + p1), true, tm, tj, tl);
+            const float sx = select_f32(px, p1), sy = select_f32(py, p1), sz = select_f32(pz, p1);
+            const uint32_t tx = lane_value(f2u(sx), tl), ty = lane_value(f2u(sy), tl),
+                           tz = lane_value(f2u(sz), tl);
+            const uint32_t vm = lane == tl ? m2 : m1;
+            const int vp = lane == tl ? p2 : p1;
+            int bl;
+            wave_max_key(vm, (uint32_t)(lo + wbase + lane * PPT + vp), vp >= 0, bm, bj, bl);
+            if (lane == 0) {
+                const int w = pw;
+                wt[0][w] = tm; wt[1][w] = valid ? tj : kNone; wt[2][w] = tx; wt[3][w] = ty;
+                wt[4][w] = tz;
+                wb[0][w] = valid ? bm : 0u; wb[1][w] = valid ? bj : kNone;
+            }
+        }
+        __syncthreads();
+        if (wave != 0) continue;
+
+        // ---- wave 0: exchange, then certify centres ----------------------------
+        uint32_t cm[CPL], cj[CPL], cxv[CPL], cyv[CPL], czv[CPL];
+        uint32_t beta_m = 0, beta_j = kNone;
+        uint32_t abort = 0;
+        {
+            const bool own = lane < NPW;
+            const uint32_t tm = own ? wt[0][lane] : 0u, tj = own ? wt[1][lane] : kNone;
+            const uint32_t bm = own ? wb[0][lane] : 0u, bj = own ? wb[1][lane] : kNone;
+            const bool tv = tj != kNone;
+            if (G == 1) {
+                // candidates: every wave's top, lane = wave (index order)
+#pragma unroll
+                for (int s = 0; s < CPL; ++s) {
+                    cm[s] = s == 0 ? tm : 0u;
+                    cj[s] = s == 0 ? tj : kNone;
+                    cxv[s] = s == 0 && own ? wt[2][lane] : 0u;
+                    cyv[s] = s == 0 && own ? wt[3][lane] : 0u;
+                    czv[s] = s == 0 && own ? wt[4][lane] : 0u;
+                }
+                int l;
+                wave_max_key(bm, bj, bj != kNone, beta_m, beta_j, l);
+            } else {
+                // publish this workgroup's RG best wave tops (in index order) and
+                // its bound: the best of the wave bounds and the unpublished tops
+                uint64_t sel = 0;
+                for (int r = 0; r < RG; ++r) {
+                    uint32_t om, oj;
+                    int ol;
+                    wave_max_key(tm, tj, tv && !((sel >> lane) & 1ull), om, oj, ol);
+                    if (ol >= 0) sel |= 1ull << ol;
+                }
+                const bool mine = (sel >> lane) & 1ull;
+                const bool unpub = tv && !mine;
+                uint32_t gm, gj;
+                int gl;
+                wave_max_key(unpub && key_gt(tm, tj, bm, bj) ? tm : bm,
+                             unpub && key_gt(tm, tj, bm, bj) ? tj : bj,
+                             unpub || bj != kNone, gm, gj, gl);
+                const uint32_t tag = batch;
+                uint64_t* set = cw + (size_t)(batch & 1) * G * stride;
+                uint64_t* my = set + (size_t)g * stride;
+                const int rank = (int)lanes_below(sel);
+                const int nsel = __popcll(sel);
+                if (mine) {
+                    __hip_atomic_store(&my[rank * 5 + 0], tagged(tm, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&my[rank * 5 + 1], tagged(tj, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&my[rank * 5 + 2], tagged(wt[2][lane], tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&my[rank * 5 + 3], tagged(wt[3][lane], tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&my[rank * 5 + 4], tagged(wt[4][lane], tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                // unused candidate ranks are published as empty, and the bound
+                for (int r = nsel + lane; r < RG; r += kWave) {
+                    __hip_atomic_store(&my[r * 5 + 0], tagged(0u, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&my[r * 5 + 1], tagged(kNone, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&my[r * 5 + 2], tagged(0u, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&my[r * 5 + 3], tagged(0u, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&my[r * 5 + 4], tagged(0u, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                if (lane == 0) {
+                    __hip_atomic_store(&my[RG * 5 + 0], tagged(gm, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&my[RG * 5 + 1], tagged(gj, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                // gather every workgroup's words of this batch into LDS: up to 16
+                // loads per lane in flight per poll, so a poll costs one round trip
+                const int per = RG * 5 + 2;
+                const int total = G * per;  // slots are contiguous: word w of the set
+                for (int w0 = 0; w0 < total && !abort; w0 += 16 * kWave) {
+                    uint32_t spins = 0;
+                    while (true) {
+                        uint64_t v[16];
+#pragma unroll
+                        for (int k = 0; k < 16; ++k) {
+                            const int w = w0 + k * kWave + lane;
+                            v[k] = w < total ? __hip_atomic_load(&set[w], __ATOMIC_RELAXED,
+                                                                 __HIP_MEMORY_SCOPE_AGENT)
+                                             : (uint64_t)tag;
+                        }
+                        bool ready = true;
+#pragma unroll
+                        for (int k = 0; k < 16; ++k) ready &= (uint32_t)v[k] == tag;
+                        if (ballot(!ready) == 0) {
+#pragma unroll
+                            for (int k = 0; k < 16; ++k) {
+                                const int w = w0 + k * kWave + lane;
+                                if (w < total) stage[w] = (uint32_t)(v[k] >> 32);
+                            }
+                            break;
+                        }
+                        if (++spins > spin_limit) { abort = 1; break; }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                }
+                __builtin_amdgcn_s_waitcnt(0);  // LDS writes of this wave complete
+                __builtin_amdgcn_wave_barrier();
+                // candidates: q = wg * RG + r, lane-major (lane q / CPL, slot q % CPL)
+#pragma unroll
+                for (int s = 0; s < CPL; ++s) {
+                    const int q = lane * CPL + s;
+                    const bool in = q < G * RG;
+                    const int off = in ? (q / RG) * per + (q % RG) * 5 : 0;
+                    cm[s] = in ? stage[off + 0] : 0u;
+                    cj[s] = in ? stage[off + 1] : kNone;
+                    cxv[s] = in ? stage[off + 2] : 0u;
+                    cyv[s] = in ? stage[off + 3] : 0u;
+                    czv[s] = in ? stage[off + 4] : 0u;
+                }
+                // beta: the largest bound over the workgroups (lane order = index order)
+                beta_m = 0;
+                beta_j = kNone;
+                for (int base = 0; base < G; base += kWave) {
+                    const int wg = base + lane;
+                    const bool in = wg < G;
+                    const uint32_t m = in ? stage[wg * per + RG * 5 + 0] : 0u;
+                    const uint32_t j = in ? stage[wg * per + RG * 5 + 1] : kNone;
+                    uint32_t om, oj;
+                    int ol;
+                    wave_max_key(m, j, in && j != kNone, om, oj, ol);
+                    if (ol >= 0 && (beta_j == kNone || key_gt(om, oj, beta_m, beta_j))) {
+                        beta_m = om;
+                        beta_j = oj;
+                    }
+                }
+            }
+        }
+        // Keep only the candidates that can still be certified in this batch
+        // (key > beta; keys only decrease), compacted in index order into the
+        // first `used` slots of each lane (lane-major). The best candidate is
+        // always among them: its key is the largest of the cloud.
+        int used = CPL;
+        if (!abort) {
+            bool live[CPL];
+            uint32_t below = 0, total = 0;
+#pragma unroll
+            for (int s = 0; s < CPL; ++s) {
+                live[s] = cj[s] != kNone && key_gt(cm[s], cj[s], beta_m, beta_j);
+                const uint64_t mk = ballot(live[s]);
+                below += lanes_below(mk);
+                total += (uint32_t)__popcll(mk);
+            }
+            // lane-major order of the live entries: all entries of lower lanes
+            // come first, then this lane's in slot order
+            uint32_t q = below;
+#pragma unroll
+            for (int s = 0; s < CPL; ++s) {
+                if (live[s]) {
+                    live_c[0][q] = cm[s]; live_c[1][q] = cj[s]; live_c[2][q] = cxv[s];
+                    live_c[3][q] = cyv[s]; live_c[4][q] = czv[s];
+                    ++q;
+                }
+            }
+            used = (int)((total + kWave - 1) / kWave);  // >= 1: the best is live
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int s = 0; s < CPL; ++s) {
+                const int qq = lane * used + s;
+                const bool in = s < used && qq < (int)total;
+                cm[s] = in ? live_c[0][qq] : 0u;
+                cj[s] = in ? live_c[1][qq] : kNone;
+                cxv[s] = in ? live_c[2][qq] : 0u;
+                cyv[s] = in ? live_c[3][qq] : 0u;
+                czv[s] = in ? live_c[4][qq] : 0u;
+            }
+        }
+        int t = t0;
+        if (!abort) {
+            int nc = 0;
+            while (true) {
+                // largest key among the valid candidates (lane-major = index order)
+                uint32_t lm = 0;
+                int ls = -1;
+#pragma unroll
+                for (int s = 0; s < CPL; ++s)
+                    if (cj[s] != kNone && (ls < 0 || cm[s] > lm)) { lm = cm[s]; ls = s; }
+                uint32_t km, kj;
+                int kl;
+                wave_max_key(lm, select_u32(cj, ls < 0 ? 0 : ls), ls >= 0, km, kj, kl);
+                if (nc > 0 && !key_gt(km, kj, beta_m, beta_j)) break;  // not certified
+                const int s_sel = ls < 0 ? 0 : ls;
+                const float X = u2f(lane_value(select_u32(cxv, s_sel), kl));
+                const float Y = u2f(lane_value(select_u32(cyv, s_sel), kl));
+                const float Z = u2f(lane_value(select_u32(czv, s_sel), kl));
+                if (lane == 0) {
+                    cen[0][nc] = X; cen[1][nc] = Y; cen[2][nc] = Z;
+                    cen_j[nc] = kj;
+                    __hip_atomic_store(&cen_count, nc + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
+                ++nc;
+                ++t;
+#pragma unroll
+                for (int s = 0; s < CPL; ++s)
+                    if (s < used)
+                        cm[s] = min(cm[s], f2u(s32(X, Y, Z, u2f(cxv[s]), u2f(cyv[s]), u2f(czv[s]))));
+                if (t >= M || nc == kFpsMaxBatch) break;
+            }
+        }
+        if (lane == 0) {
+            sh_t = t;
+            sh_abort = (int)abort;
+            __hip_atomic_store(&cen_done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    }
+    if (sh_abort && tid == 0) {
+        atomicOr(status, 1u);
+        if (g == 0)
+            for (int v = sh_t; v < M; ++v) ob[v] = -1;
+    }
+}
+
 // Workspace: a 256-byte header (status word), then two parity sets of G slots
 // per cloud.
 size_t fps_workspace_bytes(int64_t B, int64_t G) {
@@ -267,6 +675,85 @@ hipError_t launch_fps(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t
                                   xyz, (int)N, (int)M, (int)start_idx, G, slice, out_idx, out_xyz,
                                   slots, status, spin_limit);
     return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------- batched launch
+
+// Points per thread for which the batched kernel is built.
+constexpr int kBatchPpt[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16};
+
+int fps_batch_ppt_round(int ppt) {
+    for (int v : kBatchPpt)
+        if (v >= ppt) return v;
+    return -1;
+}
+
+int fps_batch_stride(int rg) { return 5 * rg + 2; }  // words per workgroup, contiguous
+
+size_t fps_batch_workspace_bytes(int64_t B, int64_t G, int rg) {
+    return G > 1 ? 256 + (size_t)B * 2 * (size_t)G * fps_batch_stride(rg) * sizeof(uint64_t) : 256;
+}
+
+size_t fps_batch_lds_bytes(int G, int rg) { return G > 1 ? (size_t)G * (5 * rg + 2) * 4 : 0; }
+
+// The (points per thread, block, candidates per lane) triples that are built.
+template <int PPT_, int BLOCK_, int CPL_>
+struct BatchCfg {
+    static constexpr int PPT = PPT_, BLOCK = BLOCK_, CPL = CPL_;
+};
+
+template <int P>
+using BatchCfgsFor = std::tuple<BatchCfg<P, 1024, 1>, BatchCfg<P, 1024, 2>, BatchCfg<P, 1024, 4>,
+                                BatchCfg<P, 256, 1>>;
+
+using BatchCfgs = decltype(std::tuple_cat(BatchCfgsFor<1>{}, BatchCfgsFor<2>{}, BatchCfgsFor<3>{},
+                                          BatchCfgsFor<4>{}, BatchCfgsFor<5>{}, BatchCfgsFor<6>{},
+                                          BatchCfgsFor<8>{}, BatchCfgsFor<10>{},
+                                          BatchCfgsFor<12>{}, BatchCfgsFor<16>{}));
+
+// Calls fn(Cfg{}) for the built configuration matching the runtime values;
+// false when none does.
+template <typename Fn>
+static bool with_batch_cfg(int ppt, int block, int cpl, Fn&& fn) {
+    return std::apply(
+        [&](auto... cfg) {
+            return ((decltype(cfg)::PPT == ppt && decltype(cfg)::BLOCK == block &&
+                     decltype(cfg)::CPL == cpl && (fn(cfg), true)) ||
+                    ...);
+        },
+        BatchCfgs{});
+}
+
+// Largest number of batched-FPS workgroups that are resident at once.
+hipError_t fps_batch_capacity(int ppt, int block, int cpl, size_t lds, int cus, int* out) {
+    hipError_t e = hipErrorInvalidValue;
+    int per_cu = 0;
+    with_batch_cfg(ppt, block, cpl, [&](auto cfg) {
+        using C = decltype(cfg);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, (const void*)fps_batch_kernel<C::PPT, C::BLOCK, C::CPL>, C::BLOCK, lds);
+    });
+    *out = per_cu * cus;
+    return e;
+}
+
+hipError_t launch_fps_batch(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t start_idx,
+                            int64_t* out_idx, float* out_xyz, void* workspace, int G, int ppt,
+                            int block, int rg, int cpl, uint32_t spin_limit, hipStream_t stream) {
+    const int slice = (int)((N + G - 1) / G);
+    uint32_t* status = (uint32_t*)workspace;
+    uint64_t* words = (uint64_t*)((char*)workspace + 256);
+    const size_t lds = fps_batch_lds_bytes(G, rg);
+    hipError_t e = hipErrorInvalidValue;
+    with_batch_cfg(ppt, block, cpl, [&](auto cfg) {
+        using C = decltype(cfg);
+        hipLaunchKernelGGL((fps_batch_kernel<C::PPT, C::BLOCK, C::CPL>), dim3((unsigned)(B * G)),
+                           dim3(C::BLOCK), lds, stream, xyz, (int)N, (int)M, (int)start_idx, G,
+                           slice, rg, out_idx, out_xyz, words, fps_batch_stride(rg), status,
+                           spin_limit);
+        e = hipGetLastError();
+    });
+    return e;
 }
 
 // Device-side clear of the workspace (a plain fill kernel rather than a memset

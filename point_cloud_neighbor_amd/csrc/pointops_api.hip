@@ -21,6 +21,12 @@ hipError_t launch_fps(const float*, int64_t, int64_t, int64_t, int64_t, int64_t*
                       int, int, int, uint32_t, hipStream_t);
 hipError_t launch_fps_clear(void*, size_t, hipStream_t);
 size_t fps_workspace_bytes(int64_t B, int64_t G);
+hipError_t launch_fps_batch(const float*, int64_t, int64_t, int64_t, int64_t, int64_t*, float*,
+                            void*, int, int, int, int, int, uint32_t, hipStream_t);
+hipError_t fps_batch_capacity(int ppt, int block, int cpl, size_t lds, int cus, int* out);
+size_t fps_batch_workspace_bytes(int64_t B, int64_t G, int rg);
+size_t fps_batch_lds_bytes(int G, int rg);
+int fps_batch_ppt_round(int ppt);
 hipError_t launch_knn(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
                       int64_t*, int, int, hipStream_t);
 }  // namespace pointops
@@ -96,21 +102,31 @@ long env_long(const char* name, long dflt) {
 // ------------------------------------------------------------------ FPS geometry
 
 struct FpsPlan {
-    int G;      // workgroups per cloud
-    int ppt;    // points per thread
-    int block;  // threads per workgroup
+    bool batch;  // certified-batch kernel (default) or one exchange per step
+    int G;       // workgroups per cloud
+    int ppt;     // points per thread
+    int block;   // threads per workgroup
+    int rg;      // candidates each workgroup publishes per exchange (batch, G > 1)
+    int cpl;     // candidates per lane of the certifying wave (batch)
+    int err;     // POINTOPS_OK or why no plan fits
 };
 
-// Workgroups per cloud. One workgroup per cloud avoids the cross-workgroup
-// exchange (about 1 us per step) and is fastest whenever the cloud fits in one
-// workgroup (16 points per thread, its coordinates in LDS). Larger clouds take
-// about 4096 points per workgroup, at most 128 workgroups (more slots make the
-// exchange slower than the update they save), more only if a slice would not
-// fit, and at most the number of workgroups the device runs at once.
-FpsPlan fps_plan(int64_t B, int64_t N, const DeviceInfo& dev) {
+int64_t split_even(int64_t N, int64_t G) {
+    // every slice non-empty: with slice = ceil(N/G) the last slice starts at
+    // (G-1)*slice, which must be < N
+    G = std::max<int64_t>(1, std::min<int64_t>(G, N));
+    while (G > 1 && (G - 1) * ((N + G - 1) / G) >= N) --G;
+    return G;
+}
+
+// One exchange per step. One workgroup per cloud avoids the cross-workgroup
+// exchange and is fastest whenever the cloud fits in one workgroup (16 points
+// per thread, its coordinates in LDS); larger clouds take about 4096 points
+// per workgroup, at most 128 workgroups, more only if a slice would not fit.
+FpsPlan fps_plan_step(int64_t B, int64_t N, const DeviceInfo& dev) {
     const int64_t cus = std::max(1, dev.cus);
     const int64_t max_slice = std::min<int64_t>(16 * 1024, ((int64_t)dev.lds_per_block - 1024) / 12);
-    long g_env = env_long("POINTOPS_FPS_WG_PER_CLOUD", 0);
+    const long g_env = env_long("POINTOPS_FPS_WG_PER_CLOUD", 0);
     int64_t G;
     if (g_env > 0) {
         G = g_env;
@@ -121,19 +137,96 @@ FpsPlan fps_plan(int64_t B, int64_t N, const DeviceInfo& dev) {
         G = std::max<int64_t>(G, (N + max_slice - 1) / max_slice);
         G = std::min<int64_t>(G, std::max<int64_t>(1, 4 * cus / std::max<int64_t>(B, 1)));
     }
-    G = std::max<int64_t>(1, std::min<int64_t>(G, N));
-    int64_t slice = (N + G - 1) / G;
-    // every slice non-empty: with slice = ceil(N/G), the last slice starts at
-    // (G-1)*slice, which must be < N
-    while (G > 1 && (G - 1) * slice >= N) {
-        --G;
-        slice = (N + G - 1) / G;
-    }
-    FpsPlan p;
+    G = split_even(N, G);
+    const int64_t slice = (N + G - 1) / G;
+    FpsPlan p{};
+    p.batch = false;
     p.G = (int)G;
     p.block = slice > 1024 ? 1024 : 256;
     p.ppt = (int)((slice + p.block - 1) / p.block);
+    p.err = POINTOPS_OK;
+    if (p.ppt > 16 || slice * 12 > (int64_t)dev.lds_per_block - 1024)
+        p.err = fail(POINTOPS_UNSUPPORTED, "cloud of %lld points needs %d workgroups of %lld points",
+                     (long long)N, p.G, (long long)slice);
+    else if (B * p.G > cus * 8 && p.G > 1)
+        p.err = fail(POINTOPS_UNSUPPORTED, "B*G = %lld workgroups exceed what runs at once",
+                     (long long)(B * p.G));
     return p;
+}
+
+// Certified batches. About 2304 points per workgroup (12 point waves x 64
+// lanes x 3 points) keeps the per-centre update short; at most 256 workgroups
+// per cloud and, when a cloud spans several workgroups, no more workgroups than
+// the device holds at once (they wait on each other). Each workgroup publishes
+// up to 128 / G of its wave tops per exchange; the certifying wave holds at most
+// 256 candidates.
+FpsPlan fps_plan_batch(int64_t B, int64_t N, const DeviceInfo& dev) {
+    const int cus = std::max(1, dev.cus);
+    const long g_env = env_long("POINTOPS_FPS_WG_PER_CLOUD", 0);
+    const long rg_env = env_long("POINTOPS_FPS_RG", 0);
+    const long block_env = env_long("POINTOPS_FPS_BLOCK", 0);
+    int64_t want = g_env > 0 ? g_env : (N <= 2048 ? 1 : std::min<int64_t>((N + 2303) / 2304, 256));
+    int block = block_env == 256 || block_env == 1024 ? (int)block_env : 0;
+    FpsPlan p{};
+    p.batch = true;
+    for (int attempt = 0; attempt < 8; ++attempt) {
+        const int64_t G = split_even(N, want);
+        const int64_t slice = (N + G - 1) / G;
+        p.G = (int)G;
+        p.block = block ? block : (slice <= 768 ? 256 : 1024);
+        const int npw = p.block / 64 - p.block / 256;  // point waves (every 4th holds none)
+        p.ppt = pointops::fps_batch_ppt_round((int)((slice + npw * 64 - 1) / (npw * 64)));
+        if (p.ppt < 0) {  // more than 16 points per thread
+            if (p.block == 256) { block = 1024; continue; }
+            if (g_env > 0) break;
+            want = (N + 16 * 768 - 1) / (16 * 768);
+            continue;
+        }
+        if (G == 1) {
+            p.rg = npw;
+            p.cpl = 1;
+        } else {
+            if (G > 256) break;
+            int rg = (int)std::max<long>(1, std::min<long>(npw, rg_env > 0 ? rg_env : 128 / G));
+            while (G * rg > 256) --rg;
+            p.rg = rg;
+            const int64_t cand = G * rg;
+            p.cpl = cand <= 64 ? 1 : cand <= 128 ? 2 : 4;
+            if (p.block == 256 && p.cpl > 1) { block = 1024; continue; }
+        }
+        int cap = 0;
+        hipError_t e = pointops::fps_batch_capacity(p.ppt, p.block, p.cpl,
+                                                    pointops::fps_batch_lds_bytes(p.G, p.rg),
+                                                    cus, &cap);
+        if (e != hipSuccess) { p.err = hip_fail(e, "fps occupancy query"); return p; }
+        if (G == 1 || B * G <= cap) {
+            p.err = POINTOPS_OK;
+            return p;
+        }
+        if (g_env > 0) break;
+        want = std::max<int64_t>(1, cap / std::max<int64_t>(B, 1));
+    }
+    p.err = fail(POINTOPS_UNSUPPORTED, "no FPS launch shape fits B=%lld N=%lld", (long long)B,
+                 (long long)N);
+    return p;
+}
+
+// The step kernel wins when a cloud fits one workgroup (no cross-workgroup
+// exchange at all, and certified batches there are only a few steps long); the
+// batched kernel wins once a cloud needs several workgroups.
+FpsPlan fps_plan(int64_t B, int64_t N, const DeviceInfo& dev) {
+    const char* mode = getenv("POINTOPS_FPS_MODE");
+    if (mode && strcmp(mode, "step") == 0) return fps_plan_step(B, N, dev);
+    if (mode && strcmp(mode, "batch") == 0) return fps_plan_batch(B, N, dev);
+    const FpsPlan step = fps_plan_step(B, N, dev);
+    if (step.err == POINTOPS_OK && step.G == 1) return step;
+    g_err[0] = 0;
+    return fps_plan_batch(B, N, dev);
+}
+
+size_t plan_workspace_bytes(int64_t B, const FpsPlan& p) {
+    return p.batch ? pointops::fps_batch_workspace_bytes(B, p.G, p.rg)
+                   : pointops::fps_workspace_bytes(B, p.G);
 }
 
 }  // namespace
@@ -166,9 +259,9 @@ size_t pointops_fps_workspace_bytes(int64_t B, int64_t N, int64_t M) {
     DeviceInfo fallback;
     fallback.cus = 256;
     if (current_device(&dev) != POINTOPS_OK) dev = &fallback;
-    g_err[0] = 0;
     const FpsPlan p = fps_plan(B, N, *dev);
-    return pointops::fps_workspace_bytes(B, p.G);
+    g_err[0] = 0;
+    return p.err == POINTOPS_OK ? plan_workspace_bytes(B, p) : 0;
 }
 
 int pointops_fps(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t start_idx,
@@ -188,24 +281,21 @@ int pointops_fps(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t star
     int st = current_device(&dev);
     if (st != POINTOPS_OK) return st;
     const FpsPlan p = fps_plan(B, N, *dev);
-    const int64_t slice = (N + p.G - 1) / p.G;
-    if (p.ppt > 16 || slice * 12 > (int64_t)dev->lds_per_block - 1024)
-        return fail(POINTOPS_UNSUPPORTED,
-                    "cloud of %lld points needs %d workgroups of %lld points; "
-                    "raise POINTOPS_FPS_WG_PER_CLOUD", (long long)N, p.G, (long long)slice);
-    if (B * p.G > (int64_t)dev->cus * 8 && p.G > 1)
-        return fail(POINTOPS_UNSUPPORTED, "B*G = %lld workgroups exceed what runs at once",
-                    (long long)(B * p.G));
-    const size_t need = pointops::fps_workspace_bytes(B, p.G);
+    if (p.err != POINTOPS_OK) return p.err;
+    const size_t need = plan_workspace_bytes(B, p);
     if (!workspace || workspace_bytes < need)
         return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
                     workspace_bytes, need);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = pointops::launch_fps_clear(workspace, need, s);
     if (e != hipSuccess) return hip_fail(e, "fps workspace clear");
-    const uint32_t spin = (uint32_t)env_long("POINTOPS_FPS_SPIN_LIMIT", 1L << 24);
-    e = pointops::launch_fps(xyz, B, N, M, start_idx, out_idx, out_xyz, workspace, p.G, p.ppt,
-                             p.block, spin, s);
+    const uint32_t spin = (uint32_t)env_long("POINTOPS_FPS_SPIN_LIMIT", 1L << 22);
+    if (p.batch)
+        e = pointops::launch_fps_batch(xyz, B, N, M, start_idx, out_idx, out_xyz, workspace, p.G,
+                                       p.ppt, p.block, p.rg, p.cpl, spin, s);
+    else
+        e = pointops::launch_fps(xyz, B, N, M, start_idx, out_idx, out_xyz, workspace, p.G, p.ppt,
+                                 p.block, spin, s);
     if (e != hipSuccess) return hip_fail(e, "fps launch");
     return POINTOPS_OK;
 }

@@ -94,9 +94,12 @@ def test_fps_shapes(gpu, oracle_mod, B, N):
         check_fps(gpu, oracle_mod, xyz, M, N // 3, f"B={B} N={N} M={M}")
 
 
+@pytest.mark.parametrize("mode", ["batch", "step"])
 @pytest.mark.parametrize("G", [2, 3, 7, 16, 33])
-def test_fps_forced_workgroups_per_cloud(gpu, oracle_mod, G, monkeypatch):
-    """The cross-workgroup argmax, forced on mid-sized clouds; twice, same bits."""
+def test_fps_forced_workgroups_per_cloud(gpu, oracle_mod, G, mode, monkeypatch):
+    """The cross-workgroup exchange, forced on mid-sized clouds, for both the
+    certified-batch kernel and the one-exchange-per-step kernel; twice, same bits."""
+    monkeypatch.setenv("POINTOPS_FPS_MODE", mode)
     monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", str(G))
     xyz = W.sphere_shell(G, 2, 5000 + G)
     want = check_fps(gpu, oracle_mod, xyz, 700, 11, f"G={G}")
@@ -104,13 +107,34 @@ def test_fps_forced_workgroups_per_cloud(gpu, oracle_mod, G, monkeypatch):
     assert np.array_equal(again, want)
 
 
-def test_fps_ties_and_duplicates(gpu, oracle_mod, monkeypatch):
+@pytest.mark.parametrize("mode", ["batch", "step"])
+def test_fps_ties_and_duplicates(gpu, oracle_mod, mode, monkeypatch):
+    monkeypatch.setenv("POINTOPS_FPS_MODE", mode)
     xyz = W.integer_cloud(5, 2, 3000, 0, 3)      # 27 distinct locations, heavy ties
     for G in ("1", "5"):
         monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", G)
         check_fps(gpu, oracle_mod, xyz, 60, 7, f"dups G={G}")
+    monkeypatch.delenv("POINTOPS_FPS_WG_PER_CLOUD")
     line = W.line_cloud(1025)
     check_fps(gpu, oracle_mod, line, 1030, 0, "line")
+
+
+@pytest.mark.parametrize("G,rg,block", [(1, 0, 256), (1, 0, 1024), (4, 1, 1024), (4, 15, 1024),
+                                        (9, 3, 1024), (40, 2, 1024), (70, 1, 1024),
+                                        (130, 1, 1024), (3, 1, 256)])
+def test_fps_batch_shapes(gpu, oracle_mod, G, rg, block, monkeypatch):
+    """Certified-batch kernel over workgroup counts, published candidates per
+    workgroup (1..15) and block sizes, including more candidates than lanes."""
+    monkeypatch.setenv("POINTOPS_FPS_MODE", "batch")
+    monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", str(G))
+    monkeypatch.setenv("POINTOPS_FPS_BLOCK", str(block))
+    if rg:
+        monkeypatch.setenv("POINTOPS_FPS_RG", str(rg))
+    N = min(40 * G + 2000, 60000)
+    xyz = W.uniform_cube(G + 100, 1, N)
+    check_fps(gpu, oracle_mod, xyz, 600, 3, f"batch G={G} rg={rg} block={block}")
+    xi = W.integer_cloud(G, 1, N, 0, 5)
+    check_fps(gpu, oracle_mod, xi, 200, 0, f"batch ints G={G} rg={rg} block={block}")
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 5, 8, 15, 16, 17, 31, 32, 33, 63, 64])
@@ -222,10 +246,12 @@ def test_every_output_slot_written(gpu):
     assert not (o < 0).any()
 
 
-def test_fps_bounded_wait_terminates(gpu, monkeypatch):
+@pytest.mark.parametrize("mode", ["batch", "step"])
+def test_fps_bounded_wait_terminates(gpu, mode, monkeypatch):
     """A tiny bound on the cross-workgroup wait (forced from the host) makes the
     kernel stop early instead of waiting: the call returns, output slots not
     reached hold -1 and the rest are valid indices."""
+    monkeypatch.setenv("POINTOPS_FPS_MODE", mode)
     monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", "8")
     monkeypatch.setenv("POINTOPS_FPS_SPIN_LIMIT", "0")
     xyz = dev(W.uniform_cube(4, 1, 20000))
