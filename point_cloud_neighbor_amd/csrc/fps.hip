@@ -352,8 +352,10 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
         if (point_wave) {
             int a = 0;
             while (true) {
-                const int d = __hip_atomic_load(&cen_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-                const int n = __hip_atomic_load(&cen_count, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                const int d = __hip_atomic_load(&cen_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __asm__ __volatile__("" ::: "memory");
+                const int n = __hip_atomic_load(&cen_count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __asm__ __volatile__("" ::: "memory");
                 for (; a < n; ++a) {
                     const float cx = cen[0][a], cy = cen[1][a], cz = cen[2][a];
                     // outputs are written here, not by the certifying wave, so that
@@ -601,7 +603,11 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 if (lane == 0) {
                     cen[0][nc] = X; cen[1][nc] = Y; cen[2][nc] = Z;
                     cen_j[nc] = kj;
-                    __hip_atomic_store(&cen_count, nc + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    // LDS performs one wave's operations in issue order, so a
+                    // reader that sees the new count also sees the entry; only
+                    // the compiler must keep the order (no wait for completion)
+                    __asm__ __volatile__("" ::: "memory");
+                    __hip_atomic_store(&cen_count, nc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
                 ++nc;
                 ++t;

@@ -110,25 +110,13 @@ __global__ __launch_bounds__(NW* kWave) void knn_kernel(
         lim = top.last() - 1u;
     };
 
-    // References stream through scalar registers, one group ahead of use.
     int j = j0;
-    float nxt[3 * kKnnGroup];
-    if (j + kKnnGroup <= j1) {
-#pragma unroll
-        for (int i = 0; i < 3 * kKnnGroup; ++i) nxt[i] = xb[(size_t)3 * j + i];
-    }
     for (; j + kKnnGroup <= j1; j += kKnnGroup) {
-        float cur[3 * kKnnGroup];
-#pragma unroll
-        for (int i = 0; i < 3 * kKnnGroup; ++i) cur[i] = nxt[i];
-        if (j + 2 * kKnnGroup <= j1) {
-#pragma unroll
-            for (int i = 0; i < 3 * kKnnGroup; ++i) nxt[i] = xb[(size_t)3 * (j + kKnnGroup) + i];
-        }
+        const float* rp = xb + (size_t)3 * j;
         uint32_t u[kKnnGroup];
 #pragma unroll
         for (int r = 0; r < kKnnGroup; ++r)
-            u[r] = f2u(s32(qx, qy, qz, cur[3 * r + 0], cur[3 * r + 1], cur[3 * r + 2]));
+            u[r] = f2u(s32(qx, qy, qz, rp[3 * r + 0], rp[3 * r + 1], rp[3 * r + 2]));
         uint32_t mn = u[0];
 #pragma unroll
         for (int r = 1; r < kKnnGroup; ++r) mn = min(mn, u[r]);

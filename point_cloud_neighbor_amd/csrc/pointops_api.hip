@@ -154,10 +154,11 @@ FpsPlan fps_plan_step(int64_t B, int64_t N, const DeviceInfo& dev) {
     return p;
 }
 
-// Certified batches. About 2304 points per workgroup (12 point waves x 64
-// lanes x 3 points) keeps the per-centre update short; at most 256 workgroups
-// per cloud and, when a cloud spans several workgroups, no more workgroups than
-// the device holds at once (they wait on each other). Each workgroup publishes
+// Certified batches. About 1600 points per workgroup keeps the per-centre
+// update short; at most 128 workgroups per cloud by default (more make the
+// exchange of candidates slower than the update they save; measured on 100k
+// and 1M points) and, when a cloud spans several workgroups, no more
+// workgroups than the device holds at once (they wait on each other). Each workgroup publishes
 // up to 128 / G of its wave tops per exchange; the certifying wave holds at most
 // 256 candidates.
 FpsPlan fps_plan_batch(int64_t B, int64_t N, const DeviceInfo& dev) {
@@ -165,7 +166,7 @@ FpsPlan fps_plan_batch(int64_t B, int64_t N, const DeviceInfo& dev) {
     const long g_env = env_long("POINTOPS_FPS_WG_PER_CLOUD", 0);
     const long rg_env = env_long("POINTOPS_FPS_RG", 0);
     const long block_env = env_long("POINTOPS_FPS_BLOCK", 0);
-    int64_t want = g_env > 0 ? g_env : (N <= 2048 ? 1 : std::min<int64_t>((N + 2303) / 2304, 256));
+    int64_t want = g_env > 0 ? g_env : (N <= 2048 ? 1 : std::min<int64_t>((N + 1599) / 1600, 128));
     int block = block_env == 256 || block_env == 1024 ? (int)block_env : 0;
     FpsPlan p{};
     p.batch = true;
