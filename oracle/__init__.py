@@ -68,6 +68,10 @@ def _load():
         lib.pco_ball_query_rows.argtypes = [f32p, f32p, i64, i64, i64, ctypes.c_float, i64,
                                             f32p, i64p, i64, i64]
         lib.pco_ball_query_rows.restype = ctypes.c_int
+        f64p = ctypes.POINTER(ctypes.c_double)
+        lib.pco_ball_query_backward.argtypes = [f32p, f32p, i64p, f32p, i64, i64, i64, i64,
+                                                f64p, f64p, f64p, f64p]
+        lib.pco_ball_query_backward.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -186,3 +190,25 @@ def ball_query(query, ref, radius, K: int, rows=None, threads: int = 1):
     if hi > lo:
         _fan_out(run, hi - lo, threads)
     return dist2, idx
+
+
+def ball_query_backward(query, ref, idx, grad):
+    """Gradients of L = sum G * S of a Ball Query output, in float64.
+
+    Returns (grad_query (B,Q,3), grad_ref (B,P,3), abs_query, abs_ref) where
+    abs_* is the sum of absolute values of the terms of each output."""
+    lib = _load()
+    query, pq = _f32(query)
+    ref, pr = _f32(ref)
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    grad, pg = _f32(grad)
+    B, Q, _ = query.shape
+    P = ref.shape[1]
+    K = idx.shape[-1]
+    assert idx.shape == (B, Q, K) and grad.shape == (B, Q, K)
+    gq = np.zeros((B, Q, 3)); gx = np.zeros((B, P, 3))
+    aq = np.zeros((B, Q, 3)); ax = np.zeros((B, P, 3))
+    f64 = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    _check(lib.pco_ball_query_backward(pq, pr, _i64(idx), pg, B, Q, P, K, f64(gq), f64(gx),
+                                       f64(aq), f64(ax)), "ball_query_backward")
+    return gq, gx, aq, ax

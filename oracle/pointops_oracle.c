@@ -19,16 +19,18 @@
  *        (r32 = fl32(r), R2 = fl32(r32 * r32), strict s32 < R2, exact ties to
  *        the smaller index, zero distance can be a real match).
  *
- * Arithmetic: float32 throughout, each operation rounded to nearest-even, no
- * fused multiply-add, denormals kept. Build with -O2 -ffp-contract=off and
+ * Arithmetic: float32 for the three selections (the pages fix it), each
+ * operation rounded to nearest-even, no fused multiply-add, denormals kept.
+ * The Ball Query backward, whose precision the pages leave open, is float64. Build with -O2 -ffp-contract=off and
  * never with -ffast-math; the preprocessor checks below refuse builds that
  * would evaluate in a wider type or with fast-math.
  *
  * Parity pins (what fixes this code other than itself) live in the test suite:
  * the pages' worked example, exact integer/dyadic brute force in float64,
  * exact-rational per-step rounding of s32, the bisection closed form of FPS on
- * a line, and invariants. Non-finite inputs are outside the contract and their
- * results are "parity unpinned".
+ * a line, invariants, and for the backward central differences of the
+ * quadratic loss. Non-finite inputs are outside the contract and their results
+ * are "parity unpinned".
  */
 #include <float.h>
 #include <math.h>
@@ -232,4 +234,48 @@ int pco_ball_query(const float *query, const float *ref, int64_t B, int64_t Q, i
                    float radius, int64_t K, float *out_dist2, int64_t *out_idx)
 {
     return pco_ball_query_rows(query, ref, B, Q, P, radius, K, out_dist2, out_idx, 0, B * Q);
+}
+
+/* Ball Query backward, in float64.
+ * [P1] "Ball Query: first K within a radius", the two gradient formulas, and
+ * [P2] "Differentiation": with G = dL/dS for the selected pairs,
+ *   dL/dq_i = 2 * sum over k with I_ik >= 0 of G_ik (q_i - x_{I_ik}),
+ *   dL/dx_j = 2 * sum over (i, k) with I_ik = j of G_ik (x_j - q_i).
+ * Padding slots (I < 0) contribute nothing. Each output also gets the sum of
+ * the absolute values of its terms (abs_q, abs_x), from which a caller bounds
+ * the rounding error of a float32 evaluation. All outputs are overwritten.
+ * Any of grad_q/abs_q or grad_x/abs_x may be NULL to skip that side. */
+int pco_ball_query_backward(const float *query, const float *ref, const int64_t *idx,
+                            const float *grad, int64_t B, int64_t Q, int64_t P, int64_t K,
+                            double *grad_q, double *grad_x, double *abs_q, double *abs_x)
+{
+    if (B < 0 || Q < 0 || P < 0 || K < 1)
+        return PCO_INVALID_ARGUMENT;
+    if (grad_q) memset(grad_q, 0, sizeof(double) * (size_t)(B * Q * 3));
+    if (abs_q) memset(abs_q, 0, sizeof(double) * (size_t)(B * Q * 3));
+    if (grad_x) memset(grad_x, 0, sizeof(double) * (size_t)(B * P * 3));
+    if (abs_x) memset(abs_x, 0, sizeof(double) * (size_t)(B * P * 3));
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t i = 0; i < Q; ++i) {
+            const int64_t row = b * Q + i;
+            const float *q = query + (size_t)row * 3;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t j = idx[(size_t)row * K + k];
+                if (j < 0)
+                    continue;
+                if (j >= P)
+                    return PCO_INVALID_ARGUMENT;
+                const double g = (double)grad[(size_t)row * K + k];
+                const float *x = ref + ((size_t)b * P + (size_t)j) * 3;
+                for (int d = 0; d < 3; ++d) {
+                    const double t = 2.0 * g * ((double)q[d] - (double)x[d]);
+                    if (grad_q) grad_q[(size_t)row * 3 + d] += t;
+                    if (abs_q) abs_q[(size_t)row * 3 + d] += fabs(t);
+                    if (grad_x) grad_x[((size_t)b * P + (size_t)j) * 3 + d] -= t;
+                    if (abs_x) abs_x[((size_t)b * P + (size_t)j) * 3 + d] += fabs(t);
+                }
+            }
+        }
+    }
+    return PCO_OK;
 }

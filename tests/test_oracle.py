@@ -409,3 +409,69 @@ def test_oracle_rejects_bad_arguments(oracle_mod):
     # empty references are legal for Ball Query: every slot is padding
     d2, idx = oracle_mod.ball_query(xyz, np.zeros((1, 0, 3), np.float32), 0.5, 3)
     assert np.all(idx == -1) and np.all(d2 == 0)
+
+
+# ------------------------------------------------------------------ Ball Query backward
+
+def _bq_loss(q, x, idx, G):
+    """L = sum over valid slots of G * s(q_i, x_j), s in float64 from the
+    definition of the squared distance (independent of the gradient formula)."""
+    B, Q, K = idx.shape
+    L = 0.0
+    for b in range(B):
+        for i in range(Q):
+            for k in range(K):
+                j = idx[b, i, k]
+                if j >= 0:
+                    d = q[b, i].astype(np.float64) - x[b, j].astype(np.float64)
+                    L += float(G[b, i, k]) * float((d * d).sum())
+    return L
+
+
+def test_ball_query_backward_matches_central_differences(oracle_mod):
+    """The squared distance is quadratic, so a central difference is its exact
+    derivative; on small-integer coordinates with a dyadic step and dyadic G
+    every float64 operation is exact, so the oracle must agree exactly."""
+    rng = np.random.default_rng(21)
+    x = W.integer_cloud(22, 2, 30, -4, 5)
+    q = W.integer_cloud(23, 2, 7, -4, 5)
+    d2, idx = oracle_mod.ball_query(q, x, 4.0, 6)
+    idx[0, 2, 1] = -1                                   # padding in the middle of a row
+    G = (rng.integers(-8, 9, size=idx.shape) / 4.0).astype(np.float32)
+    gq, gx, aq, ax = oracle_mod.ball_query_backward(q, x, idx, G)
+    h = 0.25
+    for b in range(2):
+        for i in range(q.shape[1]):
+            for d in range(3):
+                qp, qm = q.copy(), q.copy()
+                qp[b, i, d] += h
+                qm[b, i, d] -= h
+                fd = (_bq_loss(qp, x, idx, G) - _bq_loss(qm, x, idx, G)) / (2 * h)
+                assert gq[b, i, d] == fd
+        for j in range(x.shape[1]):
+            for d in range(3):
+                xp, xm = x.copy(), x.copy()
+                xp[b, j, d] += h
+                xm[b, j, d] -= h
+                fd = (_bq_loss(q, xp, idx, G) - _bq_loss(q, xm, idx, G)) / (2 * h)
+                assert gx[b, j, d] == fd
+    assert np.all(aq >= np.abs(gq)) and np.all(ax >= np.abs(gx))
+
+
+def test_ball_query_backward_single_pair_and_accumulation(oracle_mod):
+    # one selected pair: 2 G (q - x) to the query, -2 G (q - x) to the reference
+    q = np.array([[[1.0, 2.0, 3.0]]], dtype=np.float32)
+    x = np.array([[[0.5, 2.5, 1.0], [9.0, 9.0, 9.0]]], dtype=np.float32)
+    idx = np.array([[[0, -1]]], dtype=np.int64)
+    G = np.array([[[3.0, 100.0]]], dtype=np.float32)   # padding slot's gradient ignored
+    gq, gx, _, _ = oracle_mod.ball_query_backward(q, x, idx, G)
+    assert gq[0, 0].tolist() == [3.0, -3.0, 12.0]
+    assert gx[0, 0].tolist() == [-3.0, 3.0, -12.0] and gx[0, 1].tolist() == [0, 0, 0]
+    # two rows selecting the same reference accumulate
+    q2 = np.array([[[1.0, 0, 0], [0, 1.0, 0]]], dtype=np.float32)
+    x2 = np.zeros((1, 1, 3), dtype=np.float32)
+    idx2 = np.zeros((1, 2, 1), dtype=np.int64)
+    G2 = np.ones((1, 2, 1), dtype=np.float32)
+    gq, gx, _, _ = oracle_mod.ball_query_backward(q2, x2, idx2, G2)
+    assert gx[0, 0].tolist() == [-2.0, -2.0, 0.0]
+    assert gq[0].tolist() == [[2.0, 0, 0], [0, 2.0, 0]]
