@@ -121,6 +121,30 @@ int pointops_ball_query(const float *query, const float *ref, int64_t B, int64_t
                         float radius, int64_t K, float *out_dist2, int64_t *out_idx,
                         void *stream);
 
+/*
+ * Ball Query backward: gradients of L through the returned squared distances.
+ * Project page, section "The operators in equations", the gradient formulas
+ * under "Ball Query: first K within a radius"; "Numerical contracts" page,
+ * "Differentiation". With G = dL/dS (B, Q, K):
+ *   grad_query[b,i] = 2 * sum over k with I[b,i,k] >= 0 of G (q_i - x_I),
+ *   grad_ref[b,j]   = 2 * sum over (i,k) with I[b,i,k] = j of G (x_j - q_i).
+ * Indices and the radius are not differentiated.
+ *
+ *   query, ref    the forward inputs, (B, Q, 3) and (B, P, 3) float32, device.
+ *   idx           the forward index output (B, Q, K) int64; slots outside
+ *                 [0, P) (the -1 padding) contribute nothing.
+ *   grad_dist2    G, (B, Q, K) float32, device.
+ *   grad_query    (B, Q, 3) float32, device, overwritten; or NULL to skip.
+ *   grad_ref      (B, P, 3) float32, device, overwritten; or NULL to skip.
+ * float32 arithmetic: each term is 2 * (G * fl32(q - x)); a query's terms are
+ * summed in a fixed order (deterministic); a reference's terms are added with
+ * atomics in no fixed order, so grad_ref may differ between runs in the last
+ * bits. B == 0 or Q == 0 zeroes grad_ref (if given) and returns.
+ */
+int pointops_ball_query_backward(const float *query, const float *ref, const int64_t *idx,
+                                 const float *grad_dist2, int64_t B, int64_t Q, int64_t P,
+                                 int64_t K, float *grad_query, float *grad_ref, void *stream);
+
 /* POINTOPS_OK if `device` is a gfx950 GPU with 64-wide wavefronts (the kernels
  * assume that width), POINTOPS_UNSUPPORTED_DEVICE otherwise. The entry points
  * above run this check on the current device (cached per device). */

@@ -1,19 +1,22 @@
 """MI355X-native dense, batched float32 point-cloud neighbour search.
 
-Three operations over (B, N, 3) float32 device tensors, each a hand-written
-HIP kernel for gfx950 behind the C ABI declared in ``include/pointops.h``:
+Operations over (B, N, 3) float32 device tensors, each a hand-written HIP
+kernel for gfx950 behind the C ABI declared in ``include/pointops.h``:
 
 * ``furthest_point_sample(xyz, npoint, start_idx=0)`` -> int64 (B, npoint)
 * ``knn(query, ref, k)`` -> (Euclidean distance float32, int64 index), (B, Q, k)
 * ``ball_query(query, ref, radius, K)`` -> (squared distance float32,
-  int64 index with -1 padding), (B, Q, K)
+  int64 index with -1 padding), (B, Q, K); the squared distances are
+  differentiable with respect to both coordinate tensors
+* ``ball_query_backward(query, ref, idx, grad_dist2)`` -> (grad_query, grad_ref)
 
 The ops are loaded lazily so that ``workloads`` imports without a GPU; calling
 an op without the built library or a gfx950 device raises, there is no CPU
 fallback.
 """
 
-__all__ = ["furthest_point_sample", "knn", "ball_query", "PointopsError"]
+__all__ = ["furthest_point_sample", "knn", "ball_query", "ball_query_backward",
+           "PointopsError"]
 
 
 def __getattr__(name):

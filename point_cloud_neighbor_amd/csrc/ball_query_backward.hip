@@ -1,0 +1,109 @@
+// Ball Query backward for gfx950.
+//
+// Contract: project page "mps-pointops", section "The operators in equations",
+// the two gradient formulas under "Ball Query: first K within a radius", and
+// the "Numerical contracts" page, "Differentiation": for each selected slot
+// (I >= 0) with G = dL/dS, the query receives 2 G (q - x_I) and the reference
+// receives -2 G (q - x_I); contributions to one reference accumulate, in an
+// order the contract leaves free.
+//
+// Mapping. One wave per query row, lane k on slot k (rows with K > 64 take
+// several passes). Each lane forms its term t = 2 * (G * fl32(q - x)) (the
+// doubling is exact); the query gradient is the sum of the row's terms by a
+// fixed DPP tree (deterministic), the reference gradient is accumulated with
+// float atomics after the output has been zeroed. Slots whose index is not in
+// [0, P) contribute nothing.
+#include <algorithm>
+
+#include "common.h"
+
+namespace pointops {
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float src) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(src), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over the 64 lanes by a fixed tree; the total is returned in every lane.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v = v + dpp_f32<kDppQuadSwap1>(v);
+    v = v + dpp_f32<kDppQuadSwap2>(v);
+    v = v + dpp_f32<kDppRowHalfMirror>(v);
+    v = v + dpp_f32<kDppRowMirror>(v);
+    v = v + dpp_f32<kDppRowBcast15, 0xA>(v);
+    v = v + dpp_f32<kDppRowBcast31, 0xC>(v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+constexpr int kBqBwdWaves = 4;
+
+__global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_kernel(
+    const float* __restrict__ query, const float* __restrict__ ref,
+    const int64_t* __restrict__ idx, const float* __restrict__ grad, int64_t rows, int Q,
+    int P, int K, float* __restrict__ grad_query, float* __restrict__ grad_ref) {
+    const int64_t row = (int64_t)blockIdx.x * kBqBwdWaves + threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (row >= rows) return;  // whole waves leave together
+    const int64_t b = row / Q;
+    const float qx = query[3 * row + 0], qy = query[3 * row + 1], qz = query[3 * row + 2];
+    float sx = 0.f, sy = 0.f, sz = 0.f;
+    for (int k0 = 0; k0 < K; k0 += kWave) {
+        const int k = k0 + lane;
+        if (k >= K) continue;
+        const int64_t j = idx[row * K + k];
+        if (j < 0 || j >= P) continue;
+        const float g = grad[row * K + k];
+        const float* x = ref + (b * P + j) * 3;
+        const float tx = 2.0f * (g * (qx - x[0]));
+        const float ty = 2.0f * (g * (qy - x[1]));
+        const float tz = 2.0f * (g * (qz - x[2]));
+        sx += tx;
+        sy += ty;
+        sz += tz;
+        if (grad_ref) {
+            float* o = grad_ref + (b * P + j) * 3;
+            unsafeAtomicAdd(o + 0, -tx);
+            unsafeAtomicAdd(o + 1, -ty);
+            unsafeAtomicAdd(o + 2, -tz);
+        }
+    }
+    if (grad_query) {
+        sx = wave_sum_f32(sx);
+        sy = wave_sum_f32(sy);
+        sz = wave_sum_f32(sz);
+        if (lane == 0) {
+            grad_query[3 * row + 0] = sx;
+            grad_query[3 * row + 1] = sy;
+            grad_query[3 * row + 2] = sz;
+        }
+    }
+}
+
+__global__ void zero_f32_kernel(float* __restrict__ p, size_t n) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0.0f;
+}
+
+hipError_t launch_ball_query_backward(const float* query, const float* ref, const int64_t* idx,
+                                      const float* grad, int64_t B, int64_t Q, int64_t P,
+                                      int64_t K, float* grad_query, float* grad_ref,
+                                      hipStream_t stream) {
+    if (grad_ref && B * P > 0) {
+        // a fill kernel rather than a memset node, so the call can be captured
+        const size_t n = (size_t)B * P * 3;
+        const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+        hipLaunchKernelGGL(zero_f32_kernel, dim3(blocks), dim3(256), 0, stream, grad_ref, n);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t rows = B * Q;
+    const unsigned blocks = (unsigned)((rows + kBqBwdWaves - 1) / kBqBwdWaves);
+    hipLaunchKernelGGL(ball_query_backward_kernel, dim3(blocks), dim3(kBqBwdWaves * kWave), 0,
+                       stream, query, ref, idx, grad, rows, (int)Q, (int)P, (int)K, grad_query,
+                       grad_ref);
+    return hipGetLastError();
+}
+
+}  // namespace pointops

@@ -29,6 +29,9 @@ size_t fps_batch_lds_bytes(int G, int rg);
 int fps_batch_ppt_round(int ppt);
 hipError_t launch_knn(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
                       int64_t*, int, int, hipStream_t);
+hipError_t launch_ball_query_backward(const float*, const float*, const int64_t*, const float*,
+                                      int64_t, int64_t, int64_t, int64_t, float*, float*,
+                                      hipStream_t);
 }  // namespace pointops
 
 namespace {
@@ -368,3 +371,28 @@ int pointops_ball_query(const float* query, const float* ref, int64_t B, int64_t
 }
 
 }  // extern "C"
+
+extern "C" int pointops_ball_query_backward(const float* query, const float* ref,
+                                            const int64_t* idx, const float* grad_dist2,
+                                            int64_t B, int64_t Q, int64_t P, int64_t K,
+                                            float* grad_query, float* grad_ref, void* stream) {
+    g_err[0] = 0;
+    if (B < 0 || Q < 0 || P < 0) return fail(POINTOPS_INVALID_ARGUMENT, "negative size");
+    if (K < 1) return fail(POINTOPS_INVALID_ARGUMENT, "K must be >= 1");
+    if (Q >= kMaxPoints || P >= kMaxPoints || K >= kMaxPoints)
+        return fail(POINTOPS_UNSUPPORTED, "sizes >= 2^31");
+    if (B > 0 && Q > (int64_t)INT32_MAX * 4 / B)
+        return fail(POINTOPS_UNSUPPORTED, "B * Q above 2^33 rows");
+    if (!grad_query && !grad_ref) return POINTOPS_OK;
+    const bool rows = B > 0 && Q > 0;
+    if ((rows && (!query || !idx || !grad_dist2 || (!ref && P > 0))) ||
+        (grad_ref && B * P > 0 && !ref))
+        return fail(POINTOPS_INVALID_ARGUMENT, "null pointer");
+    int st = current_device(nullptr);
+    if (st != POINTOPS_OK) return st;
+    hipError_t e = pointops::launch_ball_query_backward(
+        query, ref, idx, grad_dist2, rows ? B : 0, rows ? Q : 0, P, K, grad_query, grad_ref,
+        (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ball_query_backward launch");
+    return POINTOPS_OK;
+}

@@ -53,6 +53,9 @@ def _load():
         lib.pointops_knn.restype = ctypes.c_int
         lib.pointops_ball_query.argtypes = [vp, vp, i64, i64, i64, f32, i64, vp, vp, vp]
         lib.pointops_ball_query.restype = ctypes.c_int
+        lib.pointops_ball_query_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp,
+                                                     vp]
+        lib.pointops_ball_query_backward.restype = ctypes.c_int
         lib.pointops_device_check.argtypes = [ctypes.c_int]
         lib.pointops_device_check.restype = ctypes.c_int
         lib.pointops_status_string.argtypes = [ctypes.c_int]
@@ -136,7 +139,18 @@ def knn(query: torch.Tensor, ref: torch.Tensor, k: int):
 def ball_query(query: torch.Tensor, ref: torch.Tensor, radius: float, K: int):
     """First K references within ``radius`` in input order -> (squared distance
     float32, int64 index with -1 padding), (B, Q, K). ``radius`` is rounded to
-    float32 first (the threshold is fl32(fl32(r) * fl32(r)))."""
+    float32 first (the threshold is fl32(fl32(r) * fl32(r))).
+
+    When grad mode is on and ``query`` or ``ref`` requires grad, the squared
+    distances are differentiable with respect to both coordinate tensors (the
+    backward runs ``ball_query_backward``); the indices are not."""
+    if torch.is_grad_enabled() and (getattr(query, "requires_grad", False)
+                                    or getattr(ref, "requires_grad", False)):
+        return _BallQueryFn.apply(query, ref, radius, K)
+    return _ball_query(query, ref, radius, K)
+
+
+def _ball_query(query: torch.Tensor, ref: torch.Tensor, radius: float, K: int):
     lib = _load()
     query = _points(query, "query")
     ref = _points(ref, "ref")
@@ -152,3 +166,56 @@ def ball_query(query: torch.Tensor, ref: torch.Tensor, radius: float, K: int):
                                      idx.data_ptr(), _stream(query.device))
         _check(rc)
     return d2, idx
+
+
+def ball_query_backward(query: torch.Tensor, ref: torch.Tensor, idx: torch.Tensor,
+                        grad_dist2: torch.Tensor, need_query: bool = True,
+                        need_ref: bool = True):
+    """Gradients of L through Ball Query's squared distances, given
+    G = dL/dS (B, Q, K) and the forward's indices -> (grad_query (B, Q, 3) or
+    None, grad_ref (B, P, 3) or None), float32. Slots with a negative index
+    contribute nothing."""
+    lib = _load()
+    query = _points(query, "query")
+    ref = _points(ref, "ref")
+    if query.device != ref.device or query.shape[0] != ref.shape[0]:
+        raise PointopsError(1, "query and ref must share the device and the batch size")
+    B, Q, _ = query.shape
+    P = ref.shape[1]
+    if idx.dim() != 3 or tuple(idx.shape[:2]) != (B, Q) or idx.dtype != torch.int64:
+        raise PointopsError(1, f"idx must be int64 of shape (B, Q, K), got {idx.dtype} "
+                               f"{tuple(idx.shape)}")
+    K = idx.shape[2]
+    if grad_dist2.shape != idx.shape or grad_dist2.dtype != torch.float32:
+        raise PointopsError(1, f"grad_dist2 must be float32 of shape {tuple(idx.shape)}")
+    if idx.device != query.device or grad_dist2.device != query.device:
+        raise PointopsError(1, "idx and grad_dist2 must be on the device of query")
+    idx = idx.contiguous()
+    grad_dist2 = grad_dist2.contiguous()
+    with torch.cuda.device(query.device):
+        gq = torch.empty_like(query) if need_query else None
+        gx = torch.empty_like(ref) if need_ref else None
+        rc = lib.pointops_ball_query_backward(
+            query.data_ptr(), ref.data_ptr(), idx.data_ptr(), grad_dist2.data_ptr(), B, Q, P,
+            K, gq.data_ptr() if gq is not None else None,
+            gx.data_ptr() if gx is not None else None, _stream(query.device))
+        _check(rc)
+    return gq, gx
+
+
+class _BallQueryFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, query, ref, radius, K):
+        d2, idx = _ball_query(query, ref, radius, K)
+        ctx.save_for_backward(query, ref, idx)
+        ctx.mark_non_differentiable(idx)
+        return d2, idx
+
+    @staticmethod
+    def backward(ctx, grad_d2, grad_idx):
+        query, ref, idx = ctx.saved_tensors
+        if grad_d2 is None:
+            return None, None, None, None
+        gq, gx = ball_query_backward(query, ref, idx, grad_d2, ctx.needs_input_grad[0],
+                                     ctx.needs_input_grad[1])
+        return gq, gx, None, None
