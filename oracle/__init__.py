@@ -9,7 +9,8 @@ function follows. This module only builds that source with gcc, marshals numpy
 arrays into it and, for large inputs, fans contiguous query-row ranges out over
 host threads (ctypes releases the GIL during the call), each thread running the
 unchanged single-threaded routine, so the result does not depend on the thread
-count.
+count. Ragged batches are composed here from those routines, one cloud at a
+time (see the section at the end).
 """
 from __future__ import annotations
 
@@ -212,3 +213,71 @@ def ball_query_backward(query, ref, idx, grad):
     _check(lib.pco_ball_query_backward(pq, pr, _i64(idx), pg, B, Q, P, K, f64(gq), f64(gx),
                                        f64(aq), f64(ax)), "ball_query_backward")
     return gq, gx, aq, ax
+
+
+# ------------------------------------------------------------------ ragged batches
+#
+# Project page, section "Flat torch_cluster subset": the clouds of a batch sit
+# back to back in one flat array and are searched independently; returned
+# indices point into the flat input; a cloud with fewer than k references gets
+# only the neighbours it has. A cloud is a segment (off, cnt) of a flat buffer.
+# Each cloud is handed, alone, to the dense routines above; the only additions
+# are the index offset and the padding of missing kNN neighbours, which this
+# library's ragged output marks with (+inf, -1).
+
+def fps_ragged(xyz, x_off, x_cnt, out_off, out_cnt, out_rows, start=None, global_index=True,
+               clouds=None):
+    """FPS of every cloud -> (out_rows,) int64; rows no cloud writes hold -2."""
+    xyz = np.ascontiguousarray(xyz, dtype=np.float32)
+    out = np.full(out_rows, -2, dtype=np.int64)
+    for b in (range(len(x_cnt)) if clouds is None else clouds):
+        m = int(out_cnt[b])
+        if m == 0:
+            continue
+        o, n = int(x_off[b]), int(x_cnt[b])
+        s = 0 if start is None else int(start[b])
+        idx = fps(xyz[None, o:o + n], m, s)[0]
+        out[int(out_off[b]):int(out_off[b]) + m] = idx + (o if global_index else 0)
+    return out
+
+
+def knn_ragged(query, q_off, q_cnt, ref, r_off, r_cnt, k, global_index=True, clouds=None,
+               threads=1):
+    """kNN of every cloud -> (dist, idx), (q_rows, k); rows no cloud writes
+    hold NaN / -2; missing neighbours (cloud smaller than k) are (+inf, -1)."""
+    query = np.ascontiguousarray(query, dtype=np.float32)
+    ref = np.ascontiguousarray(ref, dtype=np.float32)
+    dist = np.full((len(query), k), np.nan, dtype=np.float32)
+    idx = np.full((len(query), k), -2, dtype=np.int64)
+    for b in (range(len(q_cnt)) if clouds is None else clouds):
+        qo, qn, ro, rn = int(q_off[b]), int(q_cnt[b]), int(r_off[b]), int(r_cnt[b])
+        if qn == 0:
+            continue
+        kk = min(k, rn)
+        dist[qo:qo + qn] = np.inf
+        idx[qo:qo + qn] = -1
+        if kk == 0:
+            continue
+        d, i = knn(query[None, qo:qo + qn], ref[None, ro:ro + rn], kk, threads=threads)
+        dist[qo:qo + qn, :kk] = d[0]
+        idx[qo:qo + qn, :kk] = i[0] + (ro if global_index else 0)
+    return dist, idx
+
+
+def ball_query_ragged(query, q_off, q_cnt, ref, r_off, r_cnt, radius, K, global_index=True,
+                      clouds=None, threads=1):
+    """First-K Ball Query of every cloud -> (dist2, idx), (q_rows, K); rows no
+    cloud writes hold NaN / -2."""
+    query = np.ascontiguousarray(query, dtype=np.float32)
+    ref = np.ascontiguousarray(ref, dtype=np.float32)
+    dist2 = np.full((len(query), K), np.nan, dtype=np.float32)
+    idx = np.full((len(query), K), -2, dtype=np.int64)
+    for b in (range(len(q_cnt)) if clouds is None else clouds):
+        qo, qn, ro, rn = int(q_off[b]), int(q_cnt[b]), int(r_off[b]), int(r_cnt[b])
+        if qn == 0:
+            continue
+        d, i = ball_query(query[None, qo:qo + qn], ref[None, ro:ro + rn], radius, K,
+                          threads=threads)
+        dist2[qo:qo + qn] = d[0]
+        idx[qo:qo + qn] = np.where(i[0] >= 0, i[0] + (ro if global_index else 0), -1)
+    return dist2, idx

@@ -23,6 +23,11 @@ Workloads (sizes follow the five benchmark configurations of the project):
 * ``stress``    B=1, N=1048576 from 16 Gaussian clusters (sigma 0.02) with
                 0.1% exact duplicates; FPS 16384, then Ball Query r=0.03 K=32
                 of the samples against all points.
+
+Ragged batches (``ragged_workload``): 16 clouds, sizes log-uniform in
+[1024, 65536], back to back in one flat array; FPS of ceil(N_b / 8) samples
+per cloud, then kNN k=16 and Ball Query r=0.1 K=32 of each cloud's samples
+against that cloud.
 """
 from __future__ import annotations
 
@@ -238,3 +243,57 @@ def workload(name: str) -> Workload:
 
 
 WORKLOADS = ("unit_square", "tiny", "grouping", "large", "sorted_bq", "stress")
+
+
+# ----------------------------------------------------------------- ragged batches
+
+@dataclasses.dataclass
+class Ragged:
+    """Clouds back to back in one flat (rows, 3) float32 array: cloud b is rows
+    ptr[b] .. ptr[b+1]."""
+    xyz: np.ndarray
+    ptr: np.ndarray
+    fps_counts: np.ndarray = None   # samples per cloud
+    knn_k: int = 0
+    bq_radius: float = 0.0
+    bq_k: int = 0
+    description: str = ""
+
+    @property
+    def off(self) -> np.ndarray:
+        return np.ascontiguousarray(self.ptr[:-1])
+
+    @property
+    def cnt(self) -> np.ndarray:
+        return np.diff(self.ptr)
+
+
+def ragged_sizes(seed: int, B: int, lo: int, hi: int) -> np.ndarray:
+    """B cloud sizes, log-uniform in [lo, hi]."""
+    rng = np.random.default_rng(seed)
+    u = rng.random(B)
+    return np.floor(np.exp(np.log(lo) + u * (np.log(hi + 1) - np.log(lo)))).astype(np.int64)
+
+
+def ragged_batch(seed: int, sizes, maker=None) -> Ragged:
+    """One cloud per size, each drawn by ``maker(seed_b, 1, n)`` (default
+    uniform_cube) with its own seed, concatenated."""
+    maker = maker or uniform_cube
+    sizes = np.asarray(sizes, dtype=np.int64)
+    parts = [maker(seed * 1000 + b, 1, int(n))[0] for b, n in enumerate(sizes)]
+    xyz = np.concatenate(parts, axis=0) if len(parts) else np.zeros((0, 3), np.float32)
+    ptr = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    return Ragged(np.ascontiguousarray(xyz, dtype=np.float32), ptr)
+
+
+def ragged_workload(seed: int = 0) -> Ragged:
+    sizes = ragged_sizes(seed, 16, 1024, 65536)
+    r = ragged_batch(seed, sizes)
+    r.fps_counts = (sizes + 7) // 8
+    r.knn_k = 16
+    r.bq_radius = 0.1
+    r.bq_k = 32
+    r.description = ("16 uniform clouds, sizes log-uniform in [1024, 65536] (seed %d, %d points); "
+                     "FPS ceil(N/8) per cloud, kNN k=16 and Ball Query r=0.1 K=32 of the "
+                     "samples" % (seed, int(sizes.sum())))
+    return r
