@@ -145,6 +145,85 @@ int pointops_ball_query_backward(const float *query, const float *ref, const int
                                  const float *grad_dist2, int64_t B, int64_t Q, int64_t P,
                                  int64_t K, float *grad_query, float *grad_ref, void *stream);
 
+/*
+ * Ragged batches: clouds of different sizes in one call.
+ * Project page, section "Flat torch_cluster subset" (clouds back to back in
+ * one flat point array, delimited by offsets, with separate offsets for the
+ * query and reference sets; indices into the flat input; kNN of a cloud with
+ * fewer than k references yields only the available neighbours) and section
+ * "PyTorch3D-style Ball Query" (padded clouds with per-cloud lengths); its
+ * roadmap, "Phase 1 follow-ups" (multi-workgroup FPS over uneven batches, each
+ * cloud reduced on its own).
+ *
+ * A cloud is a segment of a flat point buffer: cloud b of a buffer of `rows`
+ * rows ((rows, 3) float32, device) is rows [off[b], off[b] + cnt[b]). The
+ * offset form (ptr) is off[b] = ptr[b], cnt[b] = ptr[b+1] - ptr[b]; the padded
+ * form (B, n_max, 3) with lengths is off[b] = b * n_max, cnt[b] = lengths[b].
+ * off and cnt are HOST arrays of B int64, read during the call only. Every
+ * segment must lie inside its buffer; segments that name output rows must not
+ * overlap (INVALID_ARGUMENT otherwise). Each cloud is computed exactly as the
+ * dense entry point computes a batch of one, with its own sizes.
+ *
+ * Indices: with global_index != 0 a returned index is a row of the flat input
+ * buffer (off[b] + local index), otherwise the local index within the cloud.
+ *
+ * workspace: device scratch of the size the matching *_workspace_bytes call
+ * returns; the call writes a small description of the clouds into it (with
+ * kernels on `stream`, no host-to-device copy), so calls that share one must
+ * be ordered on one stream. Output rows outside every segment are not written.
+ */
+
+/* Workspace bytes of pointops_knn_ragged and pointops_ball_query_ragged for B
+ * clouds (8 KiB covers 100 clouds). */
+size_t pointops_ragged_workspace_bytes(int64_t B);
+
+/*
+ * kNN of ragged batches. For each cloud b, the queries are rows q_off[b] ..
+ * of `query` and the references rows r_off[b] .. of `ref`; output row r of
+ * out_dist / out_idx ((q_rows, k), device) belongs to query row r. Where a
+ * cloud has fewer than k references the remaining slots of its rows hold
+ * (+inf, -1). 1 <= k <= POINTOPS_KNN_KMAX.
+ */
+int pointops_knn_ragged(const float *query, int64_t q_rows, const int64_t *q_off,
+                        const int64_t *q_cnt, const float *ref, int64_t r_rows,
+                        const int64_t *r_off, const int64_t *r_cnt, int64_t B, int64_t k,
+                        int global_index, float *out_dist, int64_t *out_idx, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/*
+ * Ball Query of ragged batches: the dense contract (R2 = fl32(radius^2),
+ * first K in increasing reference order, (-1, +0.0f) padding) per cloud;
+ * output row r ((q_rows, K), device) belongs to query row r.
+ */
+int pointops_ball_query_ragged(const float *query, int64_t q_rows, const int64_t *q_off,
+                               const int64_t *q_cnt, const float *ref, int64_t r_rows,
+                               const int64_t *r_off, const int64_t *r_cnt, int64_t B,
+                               float radius, int64_t K, int global_index, float *out_dist2,
+                               int64_t *out_idx, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Workspace bytes of pointops_fps_ragged for these cloud and sample counts
+ * (0 if they are invalid or no launch shape fits). */
+size_t pointops_fps_ragged_workspace_bytes(const int64_t *x_cnt, const int64_t *out_cnt,
+                                           int64_t B);
+
+/*
+ * Farthest point sampling of ragged batches. Cloud b is rows x_off[b] .. of
+ * `xyz`; its out_cnt[b] samples go to rows out_off[b] .. of out_idx
+ * ((out_rows,) int64, device) and, if out_xyz is not NULL, of out_xyz
+ * ((out_rows, 3) float32). start: HOST array of B local start indices, or NULL
+ * for 0. A cloud with out_cnt[b] > 0 needs x_cnt[b] > 0 and
+ * 0 <= start[b] < x_cnt[b]; out_cnt[b] may exceed x_cnt[b] (the repeat-0 rule
+ * of the dense call). Clouds are sampled independently and concurrently; a
+ * large cloud is spread over several workgroups that reduce each step among
+ * themselves only.
+ */
+int pointops_fps_ragged(const float *xyz, int64_t rows, const int64_t *x_off,
+                        const int64_t *x_cnt, const int64_t *start, int64_t B, int64_t *out_idx,
+                        float *out_xyz, int64_t out_rows, const int64_t *out_off,
+                        const int64_t *out_cnt, int global_index, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
 /* POINTOPS_OK if `device` is a gfx950 GPU with 64-wide wavefronts (the kernels
  * assume that width), POINTOPS_UNSUPPORTED_DEVICE otherwise. The entry points
  * above run this check on the current device (cached per device). */

@@ -9,6 +9,9 @@ kernel for gfx950 behind the C ABI declared in ``include/pointops.h``:
   int64 index with -1 padding), (B, Q, K); the squared distances are
   differentiable with respect to both coordinate tensors
 * ``ball_query_backward(query, ref, idx, grad_dist2)`` -> (grad_query, grad_ref)
+* ragged batches: ``fps_ragged``, ``knn_ragged``, ``ball_query_ragged`` over
+  clouds packed back to back in a flat (rows, 3) tensor with ``ptr`` offsets,
+  and ``knn_padded``, ``ball_query_padded`` over padded clouds with lengths
 
 The ops are loaded lazily so that ``workloads`` imports without a GPU; calling
 an op without the built library or a gfx950 device raises, there is no CPU
@@ -16,6 +19,7 @@ fallback.
 """
 
 __all__ = ["furthest_point_sample", "knn", "ball_query", "ball_query_backward",
+           "fps_ragged", "knn_ragged", "ball_query_ragged", "knn_padded", "ball_query_padded",
            "PointopsError"]
 
 

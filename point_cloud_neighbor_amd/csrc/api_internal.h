@@ -1,0 +1,61 @@
+// Internal declarations shared by the C ABI sources: error reporting, the
+// device check, environment knobs and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pointops {
+
+hipError_t launch_ball_query(const float*, const float*, int64_t, int64_t, int64_t, float,
+                             int64_t, float*, int64_t*, int, const int64_t*, int, int64_t,
+                             hipStream_t);
+hipError_t launch_fps(const float*, int64_t, int64_t, int64_t, int64_t, int64_t*, float*, void*,
+                      int, int, int, uint32_t, hipStream_t, const int64_t*, int, int64_t);
+hipError_t launch_fps_clear(void*, size_t, hipStream_t);
+size_t fps_workspace_bytes(int64_t B, int64_t G);
+hipError_t launch_fps_batch(const float*, int64_t, int64_t, int64_t, int64_t, int64_t*, float*,
+                            void*, int, int, int, int, int, uint32_t, hipStream_t,
+                            const int64_t*, int, int64_t, uint64_t*, size_t);
+hipError_t fps_batch_capacity(int ppt, int block, int cpl, size_t lds, int cus, int* out);
+size_t fps_batch_workspace_bytes(int64_t B, int64_t G, int rg);
+size_t fps_batch_lds_bytes(int G, int rg);
+int fps_batch_ppt_round(int ppt);
+int fps_batch_stride(int rg);
+hipError_t launch_knn(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
+                      int64_t*, int, int, const int64_t*, int, int64_t, hipStream_t);
+hipError_t launch_ball_query_backward(const float*, const float*, const int64_t*, const float*,
+                                      int64_t, int64_t, int64_t, int64_t, float*, float*,
+                                      hipStream_t);
+
+namespace api {
+
+constexpr int64_t kMaxPoints = (int64_t)1 << 31;  // indices are int32 internally
+constexpr int64_t kMaxGridY = 65535;
+
+struct DeviceInfo {
+    int checked = 0;  // 0: unknown, 1: supported, -1: unsupported
+    int cus = 0;
+    size_t lds_per_block = 0;
+    char arch[64] = {0};
+};
+
+// Sets the calling thread's error message; returns `status`.
+int fail(int status, const char* fmt, ...);
+int hip_fail(hipError_t e, const char* what);
+void clear_error();
+const char* last_error();
+// POINTOPS_OK if the device is supported (cached per device); *out gets its
+// properties.
+int check_device(int device, DeviceInfo** out);
+int current_device(DeviceInfo** out);
+long env_long(const char* name, long dflt);
+// The largest G' <= G for which slices of ceil(N / G') points are all non-empty.
+int64_t split_even(int64_t N, int64_t G);
+// Knobs shared by the dense and ragged launches.
+int knn_waves(int kcap);
+int bq_queries_per_wave(int64_t rows, int cus);
+
+}  // namespace api
+}  // namespace pointops

@@ -15,20 +15,41 @@
 // here with wave64 ballots and several queries sharing every block of
 // references. A query stops contributing once it has K hits; the wave stops
 // when all of its queries have.
+//
+// Ragged batches (a cloud table, see segments.h): waves are numbered cloud
+// after cloud, QW queries each, and scan their own cloud's references.
 #include "common.h"
+#include "segments.h"
 
 namespace pointops {
 
 template <int QW>
 __global__ __launch_bounds__(kWave) void ball_query_kernel(
     const float* __restrict__ query, const float* __restrict__ ref, int Q, int P, float r2,
-    int K, float* __restrict__ out_d2, int64_t* __restrict__ out_idx) {
-    const int b = blockIdx.y;
-    const int row0 = blockIdx.x * QW;
+    int K, float* __restrict__ out_d2, int64_t* __restrict__ out_idx,
+    const int64_t* __restrict__ seg, int nseg) {
+    // this wave's cloud: its first query row, reference row, sizes
+    int64_t qrow0, rrow0, ibase, unit;
+    if (seg) {
+        const int b = seg_find(seg, nseg, blockIdx.x);
+        const int64_t* rec = seg_record(seg, nseg, b);
+        unit = blockIdx.x - seg[b];
+        qrow0 = rec[kSrQOff];
+        Q = (int)rec[kSrQCnt];
+        rrow0 = rec[kSrROff];
+        P = (int)rec[kSrRCnt];
+        ibase = rec[kSrIdxBase];
+    } else {
+        unit = blockIdx.x;
+        qrow0 = (int64_t)blockIdx.y * Q;
+        rrow0 = (int64_t)blockIdx.y * P;
+        ibase = 0;
+    }
+    const int row0 = (int)unit * QW;
     const int lane = threadIdx.x;
-    const float* qb = query + (size_t)b * Q * 3;
-    const float* xb = ref + (size_t)b * P * 3;
-    const size_t out0 = ((size_t)b * Q + row0) * (size_t)K;
+    const float* qb = query + qrow0 * 3;
+    const float* xb = ref + rrow0 * 3;
+    const size_t out0 = (size_t)(qrow0 + row0) * (size_t)K;
 
     float qx[QW], qy[QW], qz[QW];
     int cnt[QW];
@@ -70,7 +91,7 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
                 if (m) {
                     const int slot = cnt[i] + (int)lanes_below(m);
                     if (((m >> lane) & 1ull) && slot < K) {
-                        out_idx[out0 + (size_t)i * K + slot] = j;
+                        out_idx[out0 + (size_t)i * K + slot] = ibase + j;
                         out_d2[out0 + (size_t)i * K + slot] = s;
                     }
                     cnt[i] += __popcll(m);
@@ -93,17 +114,21 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
     }
 }
 
-// Launch helper used by the C ABI: grid (ceil(Q / QW), B), one wave per group.
+// Launch helper used by the C ABI: grid (ceil(Q / QW), B), one wave per group;
+// ragged (seg != nullptr): grid (waves, 1) with waves = the table's
+// tile_ptr[nseg], Q and P unused.
 hipError_t launch_ball_query(const float* query, const float* ref, int64_t B, int64_t Q,
                              int64_t P, float r2, int64_t K, float* out_d2, int64_t* out_idx,
-                             int qw, hipStream_t stream) {
+                             int qw, const int64_t* seg, int nseg, int64_t waves,
+                             hipStream_t stream) {
     dim3 block(kWave);
     switch (qw) {
 #define POINTOPS_BQ_CASE(W)                                                                  \
     case W: {                                                                                \
-        dim3 grid((unsigned)((Q + W - 1) / W), (unsigned)B);                                 \
+        dim3 grid = seg ? dim3((unsigned)waves, 1)                                           \
+                        : dim3((unsigned)((Q + W - 1) / W), (unsigned)B);                    \
         hipLaunchKernelGGL(ball_query_kernel<W>, grid, block, 0, stream, query, ref, (int)Q, \
-                           (int)P, r2, (int)K, out_d2, out_idx);                             \
+                           (int)P, r2, (int)K, out_d2, out_idx, seg, nseg);                  \
         break;                                                                               \
     }
         POINTOPS_BQ_CASE(1)

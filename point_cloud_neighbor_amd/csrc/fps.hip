@@ -42,12 +42,19 @@
 // Termination: every poll loop is bounded. A workgroup that waits longer than
 // `spin_limit` polls raises the status word and stops; the others then stop on
 // their own bound; output slots not reached are -1.
+//
+// Ragged batches (a cloud table, see segments.h; the project page's flat FPS
+// and its planned multi-workgroup FPS over uneven batches): each cloud gets
+// its own number of workgroups, numbered cloud after cloud, with its own
+// points, outputs, start index and exchange words. Clouds never interact; the
+// argmax of each step is taken over that cloud's workgroups only.
 #include <algorithm>
 #include <tuple>
 #include <type_traits>
 #include <utility>
 
 #include "common.h"
+#include "segments.h"
 
 namespace pointops {
 
@@ -64,19 +71,43 @@ template <int PPT, int BLOCK>
 __global__ __launch_bounds__(BLOCK) void fps_kernel(
     const float* __restrict__ xyz, int N, int M, int start_idx, int G, int slice,
     int64_t* __restrict__ out_idx, float* __restrict__ out_xyz, FpsSlot* __restrict__ slots,
-    uint32_t* __restrict__ status, uint32_t spin_limit) {
+    uint32_t* __restrict__ status, uint32_t spin_limit, const int64_t* __restrict__ seg,
+    int nseg) {
     constexpr int NWAVE = BLOCK / kWave;
     extern __shared__ float lds_xyz[];  // the slice's coordinates, AoS
     __shared__ uint32_t wave_m[2][NWAVE];
     __shared__ uint32_t wave_j[2][NWAVE];
     __shared__ uint32_t result[2][6];    // m, index, x, y, z, abort
 
-    const int b = blockIdx.x / G;
-    const int g = blockIdx.x - b * G;
+    // this workgroup's cloud; ragged launches give every cloud one workgroup
+    int g;
+    int64_t xrow0, orow0, jbase;
+    FpsSlot* cs;
+    if (seg) {
+        const int b = seg_find(seg, nseg, blockIdx.x);
+        const int64_t* rec = seg_record(seg, nseg, b);
+        g = 0;
+        G = 1;
+        N = (int)rec[kFrXCnt];
+        slice = N;
+        M = (int)rec[kFrOCnt];
+        start_idx = (int)rec[kFrStart];
+        xrow0 = rec[kFrXOff];
+        orow0 = rec[kFrOOff];
+        jbase = rec[kFrIdxBase];
+        cs = slots;
+    } else {
+        const int b = blockIdx.x / G;
+        g = blockIdx.x - b * G;
+        xrow0 = (int64_t)b * N;
+        orow0 = (int64_t)b * M;
+        jbase = 0;
+        cs = slots + (size_t)b * 2 * G;
+    }
     const int tid = threadIdx.x;
     const int wave = uniform(tid / kWave);
     const int lane = tid % kWave;
-    const float* xb = xyz + (size_t)b * N * 3;
+    const float* xb = xyz + xrow0 * 3;
     const int lo = g * slice;
     const int cnt = min(N, lo + slice) - lo;  // >= 1: the host never makes empty slices
 
@@ -97,13 +128,12 @@ __global__ __launch_bounds__(BLOCK) void fps_kernel(
 
     int c = start_idx;
     float cx = xb[(size_t)3 * c + 0], cy = xb[(size_t)3 * c + 1], cz = xb[(size_t)3 * c + 2];
-    int64_t* ob = out_idx + (size_t)b * M;
-    float* oxb = out_xyz ? out_xyz + (size_t)b * M * 3 : nullptr;
+    int64_t* ob = out_idx + orow0;
+    float* oxb = out_xyz ? out_xyz + orow0 * 3 : nullptr;
     if (g == 0 && tid == 0) {
-        ob[0] = c;
+        ob[0] = jbase + c;
         if (oxb) { oxb[0] = cx; oxb[1] = cy; oxb[2] = cz; }
     }
-    FpsSlot* cs = slots + (size_t)b * 2 * G;
     __syncthreads();  // lds_xyz is complete
 
     for (int t = 1; t < M; ++t) {
@@ -213,7 +243,7 @@ __global__ __launch_bounds__(BLOCK) void fps_kernel(
         cy = u2f(ry);
         cz = u2f(rz);
         if (g == 0 && tid == 0) {
-            ob[t] = c;
+            ob[t] = jbase + c;
             if (oxb) { oxb[3 * t + 0] = cx; oxb[3 * t + 1] = cy; oxb[3 * t + 2] = cz; }
         }
     }
@@ -285,7 +315,8 @@ template <int PPT, int BLOCK, int CPL>
 __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     const float* __restrict__ xyz, int N, int M, int start_idx, int G, int slice, int RG,
     int64_t* __restrict__ out_idx, float* __restrict__ out_xyz, uint64_t* __restrict__ words,
-    int stride, uint32_t* __restrict__ status, uint32_t spin_limit) {
+    int stride, uint32_t* __restrict__ status, uint32_t spin_limit,
+    const int64_t* __restrict__ seg, int nseg) {
     constexpr int NW = BLOCK / kWave;
     // Waves whose index is a multiple of 4 hold no points, so the certifying
     // wave 0 has its SIMD (waves go round-robin over the 4 SIMDs of a CU) to
@@ -300,12 +331,37 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     __shared__ uint32_t live_c[5][kWave * CPL];  // compacted live candidates
     extern __shared__ uint32_t stage[];  // gathered words, G * (5 * RG + 2)
 
-    const int b = blockIdx.x / G;
-    const int g = blockIdx.x - b * G;
+    // this workgroup's cloud
+    int g;
+    int64_t xrow0, orow0, jbase;
+    uint64_t* cw;  // the cloud's exchange words
+    if (seg) {
+        const int b = seg_find(seg, nseg, blockIdx.x);
+        const int64_t* rec = seg_record(seg, nseg, b);
+        G = (int)(seg[b + 1] - seg[b]);
+        g = (int)(blockIdx.x - seg[b]);
+        N = (int)rec[kFrXCnt];
+        slice = (N + G - 1) / G;
+        M = (int)rec[kFrOCnt];
+        start_idx = (int)rec[kFrStart];
+        RG = (int)rec[kFrRG];
+        stride = 5 * RG + 2;
+        xrow0 = rec[kFrXOff];
+        orow0 = rec[kFrOOff];
+        jbase = rec[kFrIdxBase];
+        cw = words + rec[kFrWOff];
+    } else {
+        const int b = blockIdx.x / G;
+        g = blockIdx.x - b * G;
+        xrow0 = (int64_t)b * N;
+        orow0 = (int64_t)b * M;
+        jbase = 0;
+        cw = words + (size_t)b * 2 * G * stride;
+    }
     const int tid = threadIdx.x;
     const int wave = uniform(tid / kWave);
     const int lane = tid % kWave;
-    const float* xb = xyz + (size_t)b * N * 3;
+    const float* xb = xyz + xrow0 * 3;
     const int lo = g * slice;
     const int cnt = min(N, lo + slice) - lo;  // >= 1
     const bool point_wave = wave % 4 != 0;
@@ -326,9 +382,8 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
         pm[p] = real ? 0x7F800000u : 0u;  // +inf for points, +0 for padding
     }
 
-    int64_t* ob = out_idx + (size_t)b * M;
-    float* oxb = out_xyz ? out_xyz + (size_t)b * M * 3 : nullptr;
-    uint64_t* cw = words + (size_t)b * 2 * G * stride;
+    int64_t* ob = out_idx + orow0;
+    float* oxb = out_xyz ? out_xyz + orow0 * 3 : nullptr;
     if (tid == 0) {
         const float sx = xb[(size_t)3 * start_idx + 0], sy = xb[(size_t)3 * start_idx + 1],
                     sz = xb[(size_t)3 * start_idx + 2];
@@ -338,7 +393,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
         sh_t = 1;
         sh_abort = 0;
         if (g == 0) {
-            ob[0] = start_idx;
+            ob[0] = jbase + start_idx;
             if (oxb) { oxb[0] = sx; oxb[1] = sy; oxb[2] = sz; }
         }
     }
@@ -361,7 +416,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                     // outputs are written here, not by the certifying wave, so that
                     // wave never waits on a global store
                     if (g == 0 && pw == 0 && point_wave && lane == 0 && out_t0 >= 1) {
-                        ob[out_t0 + a] = cen_j[a];
+                        ob[out_t0 + a] = jbase + cen_j[a];
                         if (oxb) {
                             oxb[3 * (out_t0 + a) + 0] = cx;
                             oxb[3 * (out_t0 + a) + 1] = cy;
@@ -640,14 +695,15 @@ size_t fps_workspace_bytes(int64_t B, int64_t G) {
 template <int PPT, int BLOCK>
 static hipError_t launch_fps_t(dim3 grid, size_t lds, hipStream_t stream, const float* xyz, int N,
                                int M, int start_idx, int G, int slice, int64_t* out_idx,
-                               float* out_xyz, FpsSlot* slots, uint32_t* status, uint32_t spin) {
+                               float* out_xyz, FpsSlot* slots, uint32_t* status, uint32_t spin,
+                               const int64_t* seg, int nseg) {
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)fps_kernel<PPT, BLOCK>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((fps_kernel<PPT, BLOCK>), grid, dim3(BLOCK), lds, stream, xyz, N, M,
-                       start_idx, G, slice, out_idx, out_xyz, slots, status, spin);
+                       start_idx, G, slice, out_idx, out_xyz, slots, status, spin, seg, nseg);
     return hipGetLastError();
 }
 
@@ -655,31 +711,37 @@ template <int BLOCK, int... P>
 static hipError_t dispatch_ppt(int ppt, std::integer_sequence<int, P...>, dim3 grid, size_t lds,
                                hipStream_t stream, const float* xyz, int N, int M, int start_idx,
                                int G, int slice, int64_t* out_idx, float* out_xyz, FpsSlot* slots,
-                               uint32_t* status, uint32_t spin) {
+                               uint32_t* status, uint32_t spin, const int64_t* seg, int nseg) {
     hipError_t e = hipErrorInvalidValue;
     ((ppt == P + 1 ? (void)(e = launch_fps_t<P + 1, BLOCK>(grid, lds, stream, xyz, N, M,
                                                             start_idx, G, slice, out_idx,
-                                                            out_xyz, slots, status, spin))
+                                                            out_xyz, slots, status, spin, seg,
+                                                            nseg))
                    : (void)0), ...);
     return e;
 }
 
+// Dense: B * G workgroups. Ragged (seg != nullptr): `units` workgroups, one
+// per cloud, `N` = the largest cloud (it sizes the LDS copy); B, M, start_idx
+// and G are unused.
 hipError_t launch_fps(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t start_idx,
                       int64_t* out_idx, float* out_xyz, void* workspace, int G, int ppt,
-                      int block, uint32_t spin_limit, hipStream_t stream) {
+                      int block, uint32_t spin_limit, hipStream_t stream, const int64_t* seg,
+                      int nseg, int64_t units) {
+    if (seg) G = 1;
     const int slice = (int)((N + G - 1) / G);
     uint32_t* status = (uint32_t*)workspace;
     FpsSlot* slots = (FpsSlot*)((char*)workspace + 256);
     const size_t lds = (size_t)slice * 3 * sizeof(float);
-    dim3 grid((unsigned)(B * G));
+    dim3 grid((unsigned)(seg ? units : B * G));
     if (block == 256)
         return dispatch_ppt<256>(ppt, std::make_integer_sequence<int, 16>{}, grid, lds, stream,
                                  xyz, (int)N, (int)M, (int)start_idx, G, slice, out_idx, out_xyz,
-                                 slots, status, spin_limit);
+                                 slots, status, spin_limit, seg, nseg);
     if (block == 1024)
         return dispatch_ppt<1024>(ppt, std::make_integer_sequence<int, 16>{}, grid, lds, stream,
                                   xyz, (int)N, (int)M, (int)start_idx, G, slice, out_idx, out_xyz,
-                                  slots, status, spin_limit);
+                                  slots, status, spin_limit, seg, nseg);
     return hipErrorInvalidValue;
 }
 
@@ -743,20 +805,27 @@ hipError_t fps_batch_capacity(int ppt, int block, int cpl, size_t lds, int cus, 
     return e;
 }
 
+// Dense: B * G workgroups, exchange words after the 256-byte header. Ragged
+// (seg != nullptr): `units` workgroups, `words` = the exchange words (each
+// cloud's record locates its own), `lds` = the largest stage of any cloud;
+// B, N, M, start_idx, G and rg are unused.
 hipError_t launch_fps_batch(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t start_idx,
                             int64_t* out_idx, float* out_xyz, void* workspace, int G, int ppt,
-                            int block, int rg, int cpl, uint32_t spin_limit, hipStream_t stream) {
-    const int slice = (int)((N + G - 1) / G);
+                            int block, int rg, int cpl, uint32_t spin_limit, hipStream_t stream,
+                            const int64_t* seg, int nseg, int64_t units, uint64_t* seg_words,
+                            size_t seg_lds) {
+    const int slice = seg ? 0 : (int)((N + G - 1) / G);
     uint32_t* status = (uint32_t*)workspace;
-    uint64_t* words = (uint64_t*)((char*)workspace + 256);
-    const size_t lds = fps_batch_lds_bytes(G, rg);
+    uint64_t* words = seg ? seg_words : (uint64_t*)((char*)workspace + 256);
+    const size_t lds = seg ? seg_lds : fps_batch_lds_bytes(G, rg);
+    const unsigned grid = (unsigned)(seg ? units : B * G);
     hipError_t e = hipErrorInvalidValue;
     with_batch_cfg(ppt, block, cpl, [&](auto cfg) {
         using C = decltype(cfg);
-        hipLaunchKernelGGL((fps_batch_kernel<C::PPT, C::BLOCK, C::CPL>), dim3((unsigned)(B * G)),
+        hipLaunchKernelGGL((fps_batch_kernel<C::PPT, C::BLOCK, C::CPL>), dim3(grid),
                            dim3(C::BLOCK), lds, stream, xyz, (int)N, (int)M, (int)start_idx, G,
                            slice, rg, out_idx, out_xyz, words, fps_batch_stride(rg), status,
-                           spin_limit);
+                           spin_limit, seg, nseg);
         e = hipGetLastError();
     });
     return e;

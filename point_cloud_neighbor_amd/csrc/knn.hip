@@ -31,7 +31,14 @@
 // lists of waves 1..NW-1 in order (all their indices are larger than wave 0's
 // and increase with the wave), then writes sqrtf(s) (correctly rounded) and
 // the indices.
+//
+// Ragged batches (a cloud table, see segments.h): workgroups are numbered
+// cloud after cloud, 64 queries each, and a cloud's references are its own
+// segment. A cloud with fewer than k references fills the slots it cannot
+// fill with (+inf, -1): the project page's flat kNN emits only the available
+// neighbours in that case.
 #include "common.h"
+#include "segments.h"
 
 namespace pointops {
 
@@ -74,20 +81,37 @@ struct TopK {
 template <int KCAP, int NW>
 __global__ __launch_bounds__(NW* kWave) void knn_kernel(
     const float* __restrict__ query, const float* __restrict__ ref, int Q, int P, int k,
-    float* __restrict__ out_dist, int64_t* __restrict__ out_idx) {
+    float* __restrict__ out_dist, int64_t* __restrict__ out_idx, const int64_t* __restrict__ seg,
+    int nseg) {
     // LDS: per wave, kKnnBuf candidate rows during the scan, then KCAP list
     // rows for the merge; row e of wave w is uint2[64] (one entry per lane).
     extern __shared__ uint2 lds[];
     constexpr int ROWS = kKnnBuf > KCAP ? kKnnBuf : KCAP;
 
-    const int b = blockIdx.y;
+    // this workgroup's cloud: its first query row, reference row, sizes
+    int64_t qrow0, rrow0, ibase, tile;
+    if (seg) {
+        const int b = seg_find(seg, nseg, blockIdx.x);
+        const int64_t* rec = seg_record(seg, nseg, b);
+        tile = blockIdx.x - seg[b];
+        qrow0 = rec[kSrQOff];
+        Q = (int)rec[kSrQCnt];
+        rrow0 = rec[kSrROff];
+        P = (int)rec[kSrRCnt];
+        ibase = rec[kSrIdxBase];
+    } else {
+        tile = blockIdx.x;
+        qrow0 = (int64_t)blockIdx.y * Q;
+        rrow0 = (int64_t)blockIdx.y * P;
+        ibase = 0;
+    }
     const int lane = threadIdx.x % kWave;
     const int w = uniform((int)(threadIdx.x / kWave));
-    const int qi = blockIdx.x * kWave + lane;
+    const int qi = (int)tile * kWave + lane;
     const bool qvalid = qi < Q;
-    const float* qp = query + ((size_t)b * Q + (qvalid ? qi : Q - 1)) * 3;
+    const float* qp = query + (qrow0 + (qvalid ? qi : Q - 1)) * 3;
     const float qx = qp[0], qy = qp[1], qz = qp[2];
-    const float* xb = ref + (size_t)b * P * 3;
+    const float* xb = ref + rrow0 * 3;
     uint2* buf = lds + (size_t)w * ROWS * kWave;
 
     const int chunk = (P + NW - 1) / NW;
@@ -163,28 +187,32 @@ __global__ __launch_bounds__(NW* kWave) void knn_kernel(
     }
 
     if (!qvalid) return;
-    float* od = out_dist + ((size_t)b * Q + qi) * k;
-    int64_t* oi = out_idx + ((size_t)b * Q + qi) * k;
+    float* od = out_dist + (qrow0 + qi) * k;
+    int64_t* oi = out_idx + (qrow0 + qi) * k;
     const int front = KCAP - k;
 #pragma unroll
     for (int p = 0; p < KCAP; ++p) {
         if (p >= front) {
-            od[p - front] = sqrtf(u2f(top.key[p] - 1u));
-            oi[p - front] = top.id[p];
+            // empty slots remain only when the cloud has fewer than k references
+            const bool empty = top.key[p] == 0xFFFFFFFFu;
+            od[p - front] = empty ? __builtin_inff() : sqrtf(u2f(top.key[p] - 1u));
+            oi[p - front] = empty ? (int64_t)-1 : ibase + top.id[p];
         }
     }
 }
 
+// Dense: grid (ceil(Q / 64), B). Ragged (seg != nullptr): grid (tiles, 1), with
+// tiles = the table's tile_ptr[nseg] and Q, P unused.
 hipError_t launch_knn(const float* query, const float* ref, int64_t B, int64_t Q, int64_t P,
                       int64_t k, float* out_dist, int64_t* out_idx, int kcap, int nw,
-                      hipStream_t stream) {
-    dim3 grid((unsigned)((Q + kWave - 1) / kWave), (unsigned)B);
+                      const int64_t* seg, int nseg, int64_t tiles, hipStream_t stream) {
+    dim3 grid = seg ? dim3((unsigned)tiles, 1) : dim3((unsigned)((Q + kWave - 1) / kWave), (unsigned)B);
 #define POINTOPS_KNN_CASE(KC, W)                                                             \
     if (kcap == KC && nw == W) {                                                             \
         constexpr int rows = kKnnBuf > KC ? kKnnBuf : KC;                                    \
         const size_t lds = (size_t)W * rows * kWave * sizeof(uint2);                         \
         hipLaunchKernelGGL((knn_kernel<KC, W>), grid, dim3(W * kWave), lds, stream, query,  \
-                           ref, (int)Q, (int)P, (int)k, out_dist, out_idx);                  \
+                           ref, (int)Q, (int)P, (int)k, out_dist, out_idx, seg, nseg);       \
         return hipGetLastError();                                                            \
     }
     POINTOPS_KNN_CASE(1, 1) POINTOPS_KNN_CASE(1, 4)

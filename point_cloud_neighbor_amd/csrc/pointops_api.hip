@@ -13,30 +13,16 @@
 #include <utility>
 
 #include "../../include/pointops.h"
+#include "api_internal.h"
+
 
 namespace pointops {
-hipError_t launch_ball_query(const float*, const float*, int64_t, int64_t, int64_t, float,
-                             int64_t, float*, int64_t*, int, hipStream_t);
-hipError_t launch_fps(const float*, int64_t, int64_t, int64_t, int64_t, int64_t*, float*, void*,
-                      int, int, int, uint32_t, hipStream_t);
-hipError_t launch_fps_clear(void*, size_t, hipStream_t);
-size_t fps_workspace_bytes(int64_t B, int64_t G);
-hipError_t launch_fps_batch(const float*, int64_t, int64_t, int64_t, int64_t, int64_t*, float*,
-                            void*, int, int, int, int, int, uint32_t, hipStream_t);
-hipError_t fps_batch_capacity(int ppt, int block, int cpl, size_t lds, int cus, int* out);
-size_t fps_batch_workspace_bytes(int64_t B, int64_t G, int rg);
-size_t fps_batch_lds_bytes(int G, int rg);
-int fps_batch_ppt_round(int ppt);
-hipError_t launch_knn(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
-                      int64_t*, int, int, hipStream_t);
-hipError_t launch_ball_query_backward(const float*, const float*, const int64_t*, const float*,
-                                      int64_t, int64_t, int64_t, int64_t, float*, float*,
-                                      hipStream_t);
-}  // namespace pointops
-
-namespace {
+namespace api {
 
 thread_local char g_err[512];
+
+void clear_error() { g_err[0] = 0; }
+const char* last_error() { return g_err; }
 
 int fail(int status, const char* fmt, ...) {
     va_list ap;
@@ -49,16 +35,6 @@ int fail(int status, const char* fmt, ...) {
 int hip_fail(hipError_t e, const char* what) {
     return fail(POINTOPS_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
 }
-
-constexpr int64_t kMaxPoints = (int64_t)1 << 31;  // indices are int32 internally
-constexpr int64_t kMaxGridY = 65535;
-
-struct DeviceInfo {
-    int checked = 0;  // 0: unknown, 1: supported, -1: unsupported
-    int cus = 0;
-    size_t lds_per_block = 0;
-    char arch[64] = {0};
-};
 
 constexpr int kMaxDevices = 64;
 DeviceInfo g_dev[kMaxDevices];
@@ -102,6 +78,44 @@ long env_long(const char* name, long dflt) {
     return (end && *end == 0) ? x : dflt;
 }
 
+int64_t split_even(int64_t N, int64_t G) {
+    // every slice non-empty: with slice = ceil(N/G) the last slice starts at
+    // (G-1)*slice, which must be < N
+    G = std::max<int64_t>(1, std::min<int64_t>(G, N));
+    while (G > 1 && (G - 1) * ((N + G - 1) / G) >= N) --G;
+    return G;
+}
+
+// kNN: waves per workgroup (each scans a quarter, or half, of the references).
+int knn_waves(int kcap) {
+    int nw = kcap >= 64 ? 2 : 4;
+    const long nw_env = env_long("POINTOPS_KNN_WAVES", 0);
+    if (nw_env == 1 || (nw_env == 2 && kcap >= 16) || (nw_env == 4 && kcap < 64) ||
+        (nw_env == 8 && kcap == 16))
+        nw = (int)nw_env;
+    return nw;
+}
+
+// Ball Query: queries per wave. Fewer queries per wave until the grid is about
+// one device-full of waves; at most 8 (measured faster than 16 on 100k x 100k:
+// the shorter waves balance better).
+int bq_queries_per_wave(int64_t rows, int cus) {
+    const int64_t slots = (int64_t)std::max(1, cus) * 4 * 8;
+    int qw = 8;
+    for (int c : {1, 2, 4, 8})
+        if (rows / c <= slots) { qw = c; break; }
+    const long qw_env = env_long("POINTOPS_BQ_QUERIES_PER_WAVE", 0);
+    if (qw_env == 1 || qw_env == 2 || qw_env == 4 || qw_env == 8 || qw_env == 16) qw = (int)qw_env;
+    return qw;
+}
+
+}  // namespace api
+}  // namespace pointops
+
+namespace {
+
+using namespace pointops::api;
+
 // ------------------------------------------------------------------ FPS geometry
 
 struct FpsPlan {
@@ -114,13 +128,6 @@ struct FpsPlan {
     int err;     // POINTOPS_OK or why no plan fits
 };
 
-int64_t split_even(int64_t N, int64_t G) {
-    // every slice non-empty: with slice = ceil(N/G) the last slice starts at
-    // (G-1)*slice, which must be < N
-    G = std::max<int64_t>(1, std::min<int64_t>(G, N));
-    while (G > 1 && (G - 1) * ((N + G - 1) / G) >= N) --G;
-    return G;
-}
 
 // One exchange per step. One workgroup per cloud avoids the cross-workgroup
 // exchange and is fastest whenever the cloud fits in one workgroup (16 points
@@ -235,6 +242,8 @@ size_t plan_workspace_bytes(int64_t B, const FpsPlan& p) {
 
 }  // namespace
 
+using namespace pointops::api;
+
 extern "C" {
 
 int pointops_abi_version(void) { return 1; }
@@ -296,10 +305,11 @@ int pointops_fps(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t star
     const uint32_t spin = (uint32_t)env_long("POINTOPS_FPS_SPIN_LIMIT", 1L << 22);
     if (p.batch)
         e = pointops::launch_fps_batch(xyz, B, N, M, start_idx, out_idx, out_xyz, workspace, p.G,
-                                       p.ppt, p.block, p.rg, p.cpl, spin, s);
+                                       p.ppt, p.block, p.rg, p.cpl, spin, s, nullptr, 0, 0,
+                                       nullptr, 0);
     else
         e = pointops::launch_fps(xyz, B, N, M, start_idx, out_idx, out_xyz, workspace, p.G, p.ppt,
-                                 p.block, spin, s);
+                                 p.block, spin, s, nullptr, 0, 0);
     if (e != hipSuccess) return hip_fail(e, "fps launch");
     return POINTOPS_OK;
 }
@@ -323,13 +333,8 @@ int pointops_knn(const float* query, const float* ref, int64_t B, int64_t Q, int
     if (st != POINTOPS_OK) return st;
     int kcap = 1;
     while (kcap < k) kcap *= 2;
-    int nw = kcap >= 64 ? 2 : 4;
-    const long nw_env = env_long("POINTOPS_KNN_WAVES", 0);
-    if (nw_env == 1 || (nw_env == 2 && kcap >= 16) || (nw_env == 4 && kcap < 64) ||
-        (nw_env == 8 && kcap == 16))
-        nw = (int)nw_env;
-    hipError_t e = pointops::launch_knn(query, ref, B, Q, P, k, out_dist, out_idx, kcap, nw,
-                                        (hipStream_t)stream);
+    hipError_t e = pointops::launch_knn(query, ref, B, Q, P, k, out_dist, out_idx, kcap,
+                                        knn_waves(kcap), nullptr, 0, 0, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "knn launch");
     return POINTOPS_OK;
 }
@@ -354,18 +359,9 @@ int pointops_ball_query(const float* query, const float* ref, int64_t B, int64_t
     // R2 = fl32(r32 * r32), the project page's dense threshold.
     volatile float r32 = radius;
     const float r2 = r32 * r32;
-    // Queries per wave: fewer queries per wave until the grid is about one
-    // device-full of waves; at most 8 (measured faster than 16 on 100k x 100k:
-    // the shorter waves balance better).
-    const int64_t rows = B * Q;
-    const int64_t slots = (int64_t)std::max(1, dev->cus) * 4 * 8;
-    int qw = 8;
-    for (int c : {1, 2, 4, 8})
-        if (rows / c <= slots) { qw = c; break; }
-    const long qw_env = env_long("POINTOPS_BQ_QUERIES_PER_WAVE", 0);
-    if (qw_env == 1 || qw_env == 2 || qw_env == 4 || qw_env == 8 || qw_env == 16) qw = (int)qw_env;
+    const int qw = bq_queries_per_wave(B * Q, dev->cus);
     hipError_t e = pointops::launch_ball_query(query, ref, B, Q, P, r2, K, out_dist2, out_idx,
-                                               qw, (hipStream_t)stream);
+                                               qw, nullptr, 0, 0, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "ball_query launch");
     return POINTOPS_OK;
 }

@@ -12,6 +12,7 @@ import ctypes
 import os
 import threading
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,6 +57,20 @@ def _load():
         lib.pointops_ball_query_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp,
                                                      vp]
         lib.pointops_ball_query_backward.restype = ctypes.c_int
+        lib.pointops_ragged_workspace_bytes.argtypes = [i64]
+        lib.pointops_ragged_workspace_bytes.restype = ctypes.c_size_t
+        lib.pointops_knn_ragged.argtypes = [vp, i64, vp, vp, vp, i64, vp, vp, i64, i64,
+                                            ctypes.c_int, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.pointops_knn_ragged.restype = ctypes.c_int
+        lib.pointops_ball_query_ragged.argtypes = [vp, i64, vp, vp, vp, i64, vp, vp, i64, f32,
+                                                   i64, ctypes.c_int, vp, vp, vp,
+                                                   ctypes.c_size_t, vp]
+        lib.pointops_ball_query_ragged.restype = ctypes.c_int
+        lib.pointops_fps_ragged_workspace_bytes.argtypes = [vp, vp, i64]
+        lib.pointops_fps_ragged_workspace_bytes.restype = ctypes.c_size_t
+        lib.pointops_fps_ragged.argtypes = [vp, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp,
+                                            ctypes.c_int, vp, ctypes.c_size_t, vp]
+        lib.pointops_fps_ragged.restype = ctypes.c_int
         lib.pointops_device_check.argtypes = [ctypes.c_int]
         lib.pointops_device_check.restype = ctypes.c_int
         lib.pointops_status_string.argtypes = [ctypes.c_int]
@@ -219,3 +234,196 @@ class _BallQueryFn(torch.autograd.Function):
         gq, gx = ball_query_backward(query, ref, idx, grad_d2, ctx.needs_input_grad[0],
                                      ctx.needs_input_grad[1])
         return gq, gx, None, None
+
+
+# ------------------------------------------------------------------ ragged batches
+#
+# A cloud is a segment (offset, count) of a flat (rows, 3) point tensor. The
+# offsets are host arrays in the C ABI; here they may be given as lists, numpy
+# arrays or tensors (a device tensor is copied to the host, which waits for
+# the device).
+
+def _host_i64(a, name) -> np.ndarray:
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().numpy()
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+    if a.ndim != 1:
+        raise PointopsError(1, f"{name} must be one-dimensional")
+    return a
+
+
+def _flat_points(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise PointopsError(3, f"{name} is on {t.device}; pointops runs on the GPU only")
+    if t.dtype != torch.float32:
+        raise PointopsError(1, f"{name} must be float32, got {t.dtype}")
+    if t.dim() != 2 or t.shape[-1] != 3:
+        raise PointopsError(1, f"{name} must have shape (rows, 3), got {tuple(t.shape)}")
+    return t.contiguous()
+
+
+def _ptr_segments(ptr, name):
+    ptr = _host_i64(ptr, name)
+    if len(ptr) < 1:
+        raise PointopsError(1, f"{name} needs at least one entry")
+    return np.ascontiguousarray(ptr[:-1]), np.ascontiguousarray(np.diff(ptr))
+
+
+def _vp(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None and a.size else None
+
+
+def _search_ragged(fn, query, q_off, q_cnt, ref, r_off, r_cnt, width, extra, global_index,
+                   pad_dist, out=None):
+    lib = _load()
+    query = _flat_points(query, "query")
+    ref = _flat_points(ref, "ref")
+    if query.device != ref.device:
+        raise PointopsError(1, "query and ref must share the device")
+    q_off, q_cnt = _host_i64(q_off, "q_off"), _host_i64(q_cnt, "q_cnt")
+    r_off, r_cnt = _host_i64(r_off, "r_off"), _host_i64(r_cnt, "r_cnt")
+    B = len(q_off)
+    if not (len(q_cnt) == len(r_off) == len(r_cnt) == B):
+        raise PointopsError(1, "segment arrays must all have B entries")
+    rows = query.shape[0]
+    with torch.cuda.device(query.device):
+        if out is None:
+            dist = torch.full((rows, width), pad_dist, dtype=torch.float32, device=query.device)
+            idx = torch.full((rows, width), -1, dtype=torch.int64, device=query.device)
+        else:
+            dist, idx = out
+        ws = torch.empty(max(1, int(lib.pointops_ragged_workspace_bytes(B))), dtype=torch.uint8,
+                         device=query.device)
+        rc = fn(query.data_ptr(), rows, _vp(q_off), _vp(q_cnt), ref.data_ptr(), ref.shape[0],
+                _vp(r_off), _vp(r_cnt), B, *extra, int(bool(global_index)), dist.data_ptr(),
+                idx.data_ptr(), ws.data_ptr(), ws.numel(), _stream(query.device))
+        _check(rc)
+    return dist, idx
+
+
+def knn_ragged(query: torch.Tensor, q_ptr, ref: torch.Tensor, r_ptr, k: int,
+               global_index: bool = True):
+    """kNN within each cloud of a flat batch: cloud b has query rows
+    q_ptr[b]..q_ptr[b+1] and reference rows r_ptr[b]..r_ptr[b+1] ->
+    (dist, idx), (query rows, k). Indices are reference rows (or local indices);
+    slots a cloud with fewer than k references cannot fill hold (+inf, -1)."""
+    q_off, q_cnt = _ptr_segments(q_ptr, "q_ptr")
+    r_off, r_cnt = _ptr_segments(r_ptr, "r_ptr")
+    return _search_ragged(_load().pointops_knn_ragged, query, q_off, q_cnt, ref, r_off, r_cnt,
+                          int(k), (int(k),), global_index, float("inf"))
+
+
+def ball_query_ragged(query: torch.Tensor, q_ptr, ref: torch.Tensor, r_ptr, radius: float,
+                      K: int, global_index: bool = True):
+    """First-K Ball Query within each cloud of a flat batch -> (dist2, idx),
+    (query rows, K), indices as reference rows (or local), (-1, 0) padding.
+    Differentiable like ``ball_query`` when an input requires grad and the
+    indices are global."""
+    if torch.is_grad_enabled() and global_index and (
+            getattr(query, "requires_grad", False) or getattr(ref, "requires_grad", False)):
+        return _BallQueryRaggedFn.apply(query, q_ptr, ref, r_ptr, radius, K)
+    return _ball_query_ragged(query, q_ptr, ref, r_ptr, radius, K, global_index)
+
+
+def _ball_query_ragged(query, q_ptr, ref, r_ptr, radius, K, global_index):
+    q_off, q_cnt = _ptr_segments(q_ptr, "q_ptr")
+    r_off, r_cnt = _ptr_segments(r_ptr, "r_ptr")
+    return _search_ragged(_load().pointops_ball_query_ragged, query, q_off, q_cnt, ref, r_off,
+                          r_cnt, int(K), (ctypes.c_float(float(radius)), int(K)), global_index,
+                          0.0)
+
+
+class _BallQueryRaggedFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, query, q_ptr, ref, r_ptr, radius, K):
+        d2, idx = _ball_query_ragged(query, q_ptr, ref, r_ptr, radius, K, True)
+        ctx.save_for_backward(query, ref, idx)
+        ctx.mark_non_differentiable(idx)
+        return d2, idx
+
+    @staticmethod
+    def backward(ctx, grad_d2, grad_idx):
+        query, ref, idx = ctx.saved_tensors
+        if grad_d2 is None:
+            return (None,) * 6
+        # global indices: the flat batch is one cloud for the gradient formulas
+        gq, gx = ball_query_backward(query[None], ref[None], idx[None], grad_d2[None],
+                                     ctx.needs_input_grad[0], ctx.needs_input_grad[2])
+        return (gq[0] if gq is not None else None, None, gx[0] if gx is not None else None,
+                None, None, None)
+
+
+def fps_ragged(xyz: torch.Tensor, ptr, counts, start=None, global_index: bool = True,
+               return_xyz: bool = False):
+    """Farthest point sampling of each cloud of a flat batch (rows ptr[b] ..
+    ptr[b+1]), counts[b] samples each, from local index start[b] (default 0)
+    -> int64 (sum of counts,), cloud after cloud; indices are rows of ``xyz``
+    (or local). With ``return_xyz`` also the sampled coordinates."""
+    lib = _load()
+    xyz = _flat_points(xyz, "xyz")
+    x_off, x_cnt = _ptr_segments(ptr, "ptr")
+    counts = _host_i64(counts, "counts")
+    B = len(x_off)
+    if len(counts) != B:
+        raise PointopsError(1, "counts must have one entry per cloud")
+    o_off = np.ascontiguousarray(np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(np.int64))
+    total = int(counts.sum()) if B else 0
+    st = None if start is None else _host_i64(start, "start")
+    if st is not None and len(st) != B:
+        raise PointopsError(1, "start must have one entry per cloud")
+    with torch.cuda.device(xyz.device):
+        out = torch.empty(total, dtype=torch.int64, device=xyz.device)
+        oxyz = torch.empty((total, 3), dtype=torch.float32, device=xyz.device) if return_xyz else None
+        need = int(lib.pointops_fps_ragged_workspace_bytes(_vp(x_cnt), _vp(counts), B))
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=xyz.device)
+        rc = lib.pointops_fps_ragged(xyz.data_ptr(), xyz.shape[0], _vp(x_off), _vp(x_cnt),
+                                     _vp(st), B, out.data_ptr(),
+                                     oxyz.data_ptr() if oxyz is not None else None, total,
+                                     _vp(o_off), _vp(counts), int(bool(global_index)),
+                                     ws.data_ptr(), ws.numel(), _stream(xyz.device))
+        _check(rc)
+    return (out, oxyz) if return_xyz else out
+
+
+def _lengths(lengths, B, n_max, name):
+    if lengths is None:
+        return np.full(B, n_max, dtype=np.int64)
+    a = _host_i64(lengths, name)
+    if len(a) != B:
+        raise PointopsError(1, f"{name} must have B entries")
+    return a
+
+
+def knn_padded(query: torch.Tensor, ref: torch.Tensor, k: int, lengths1=None, lengths2=None):
+    """kNN of padded clouds (B, n_max, 3) with per-cloud lengths (the
+    PyTorch3D form) -> (dist, idx), (B, Q_max, k), local indices; rows past a
+    cloud's length and slots past its reference count hold (+inf, -1)."""
+    query = _points(query, "query")
+    ref = _points(ref, "ref")
+    B, Qm, _ = query.shape
+    Pm = ref.shape[1]
+    l1, l2 = _lengths(lengths1, B, Qm, "lengths1"), _lengths(lengths2, B, Pm, "lengths2")
+    d, i = _search_ragged(_load().pointops_knn_ragged, query.view(-1, 3),
+                          np.arange(B, dtype=np.int64) * Qm, l1, ref.view(-1, 3),
+                          np.arange(B, dtype=np.int64) * Pm, l2, int(k), (int(k),), False,
+                          float("inf"))
+    return d.view(B, Qm, k), i.view(B, Qm, k)
+
+
+def ball_query_padded(query: torch.Tensor, ref: torch.Tensor, radius: float, K: int,
+                      lengths1=None, lengths2=None):
+    """First-K Ball Query of padded clouds with per-cloud lengths -> (dist2,
+    idx), (B, Q_max, K), local indices; rows past a cloud's length hold
+    (0, -1)."""
+    query = _points(query, "query")
+    ref = _points(ref, "ref")
+    B, Qm, _ = query.shape
+    Pm = ref.shape[1]
+    l1, l2 = _lengths(lengths1, B, Qm, "lengths1"), _lengths(lengths2, B, Pm, "lengths2")
+    d, i = _search_ragged(_load().pointops_ball_query_ragged, query.view(-1, 3),
+                          np.arange(B, dtype=np.int64) * Qm, l1, ref.view(-1, 3),
+                          np.arange(B, dtype=np.int64) * Pm, l2, int(K),
+                          (ctypes.c_float(float(radius)), int(K)), False, 0.0)
+    return d.view(B, Qm, K), i.view(B, Qm, K)
