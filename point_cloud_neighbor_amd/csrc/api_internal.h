@@ -54,8 +54,8 @@ long env_long(const char* name, long dflt);
 // The largest G' <= G for which slices of ceil(N / G') points are all non-empty.
 int64_t split_even(int64_t N, int64_t G);
 // Knobs shared by the dense and ragged launches.
-int knn_waves(int kcap);
-int bq_queries_per_wave(int64_t rows, int cus);
+int knn_waves(int kcap, int64_t tiles, int cus);
+int bq_queries_per_wave(int64_t rows, int cus, int max_qw);
 
 }  // namespace api
 }  // namespace pointops

@@ -167,23 +167,35 @@ __global__ __launch_bounds__(NW* kWave) void knn_kernel(
     }
     flush();
 
-    // Merge the NW lists through LDS (rows reused from the candidate buffers).
+    // Merge the NW lists through LDS (rows reused from the candidate buffers)
+    // as a tree: in the round of distance d, wave w (a multiple of 2d) inserts
+    // the list of wave w + d, whose indices are all larger, so the insertion
+    // keeps the (s, j) order; log2(NW) rounds instead of NW - 1 in a row.
     if (NW > 1) {
 #pragma unroll
         for (int p = 0; p < KCAP; ++p) buf[p * kWave + lane] = make_uint2(top.key[p], (uint32_t)top.id[p]);
-        __syncthreads();
-        if (w != 0) return;
+#pragma unroll
+        for (int d = 1; d < NW; d *= 2) {
+            __syncthreads();
+            if (w % (2 * d) == 0) {
+                const uint2* other = lds + (size_t)(w + d) * ROWS * kWave;
 #pragma unroll 1
-        for (int v = 1; v < NW; ++v) {
-            const uint2* other = lds + (size_t)v * ROWS * kWave;
-#pragma unroll 1
-            for (int p = 0; p < KCAP; ++p) {
-                const uint2 c = other[p * kWave + lane];
-                // front sentinels (key 0) are skipped; empty slots (0xFFFFFFFF)
-                // insert nothing
-                top.insert(c.x != 0u ? c.x : 0xFFFFFFFFu, (int32_t)c.y);
+                for (int p = 0; p < KCAP; ++p) {
+                    const uint2 c = other[p * kWave + lane];
+                    // front sentinels (key 0) are skipped; empty slots
+                    // (0xFFFFFFFF) insert nothing
+                    top.insert(c.x != 0u ? c.x : 0xFFFFFFFFu, (int32_t)c.y);
+                }
+                // the merged list for the next round; nobody reads this
+                // wave's rows in the current one (only rows w + d are read)
+                if (2 * d < NW) {
+#pragma unroll
+                    for (int p = 0; p < KCAP; ++p)
+                        buf[p * kWave + lane] = make_uint2(top.key[p], (uint32_t)top.id[p]);
+                }
             }
         }
+        if (w != 0) return;
     }
 
     if (!qvalid) return;
@@ -211,17 +223,24 @@ hipError_t launch_knn(const float* query, const float* ref, int64_t B, int64_t Q
     if (kcap == KC && nw == W) {                                                             \
         constexpr int rows = kKnnBuf > KC ? kKnnBuf : KC;                                    \
         const size_t lds = (size_t)W * rows * kWave * sizeof(uint2);                         \
+        if (lds > 65536) {                                                                   \
+            hipError_t e = hipFuncSetAttribute((const void*)knn_kernel<KC, W>,               \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,   \
+                                               (int)lds);                                    \
+            if (e != hipSuccess) return e;                                                   \
+        }                                                                                    \
         hipLaunchKernelGGL((knn_kernel<KC, W>), grid, dim3(W * kWave), lds, stream, query,  \
                            ref, (int)Q, (int)P, (int)k, out_dist, out_idx, seg, nseg);       \
         return hipGetLastError();                                                            \
     }
-    POINTOPS_KNN_CASE(1, 1) POINTOPS_KNN_CASE(1, 4)
-    POINTOPS_KNN_CASE(2, 1) POINTOPS_KNN_CASE(2, 4)
-    POINTOPS_KNN_CASE(4, 1) POINTOPS_KNN_CASE(4, 4)
-    POINTOPS_KNN_CASE(8, 1) POINTOPS_KNN_CASE(8, 4)
+    POINTOPS_KNN_CASE(1, 1) POINTOPS_KNN_CASE(1, 4) POINTOPS_KNN_CASE(1, 8)
+    POINTOPS_KNN_CASE(2, 1) POINTOPS_KNN_CASE(2, 4) POINTOPS_KNN_CASE(2, 8)
+    POINTOPS_KNN_CASE(4, 1) POINTOPS_KNN_CASE(4, 4) POINTOPS_KNN_CASE(4, 8)
+    POINTOPS_KNN_CASE(8, 1) POINTOPS_KNN_CASE(8, 4) POINTOPS_KNN_CASE(8, 8)
     POINTOPS_KNN_CASE(16, 1) POINTOPS_KNN_CASE(16, 2) POINTOPS_KNN_CASE(16, 4)
     POINTOPS_KNN_CASE(16, 8)
     POINTOPS_KNN_CASE(32, 1) POINTOPS_KNN_CASE(32, 2) POINTOPS_KNN_CASE(32, 4)
+    POINTOPS_KNN_CASE(32, 8)
     POINTOPS_KNN_CASE(64, 1) POINTOPS_KNN_CASE(64, 2)
 #undef POINTOPS_KNN_CASE
     return hipErrorInvalidValue;

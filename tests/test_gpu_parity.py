@@ -152,11 +152,12 @@ def test_knn_shapes(gpu, oracle_mod, Q, P, k):
     check_knn(gpu, oracle_mod, q, x, k, f"Q={Q} P={P} k={k}")
 
 
-@pytest.mark.parametrize("env", ["1", "4"])
-def test_knn_wave_split_agrees(gpu, oracle_mod, env, monkeypatch):
+@pytest.mark.parametrize("env", ["1", "2", "4", "8"])
+@pytest.mark.parametrize("k", [5, 16, 32])
+def test_knn_wave_split_agrees(gpu, oracle_mod, env, k, monkeypatch):
     monkeypatch.setenv("POINTOPS_KNN_WAVES", env)
     x = W.uniform_cube(9, 1, 3001)
-    check_knn(gpu, oracle_mod, x[:, :97].copy(), x, 16, f"waves={env}")
+    check_knn(gpu, oracle_mod, x[:, :97].copy(), x, k, f"waves={env} k={k}")
 
 
 @pytest.mark.parametrize("Q,P,K,r", [(1, 0, 4, 0.5), (5, 1, 1, 0.5), (63, 64, 31, 0.3),
