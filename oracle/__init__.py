@@ -73,6 +73,8 @@ def _load():
         lib.pco_ball_query_backward.argtypes = [f32p, f32p, i64p, f32p, i64, i64, i64, i64,
                                                 f64p, f64p, f64p, f64p]
         lib.pco_ball_query_backward.restype = ctypes.c_int
+        lib.pco_nearest_rows.argtypes = [f32p, f32p, i64, i64, i64, i64p, f32p, i64p, i64, i64]
+        lib.pco_nearest_rows.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -281,3 +283,107 @@ def ball_query_ragged(query, q_off, q_cnt, ref, r_off, r_cnt, radius, K, global_
         dist2[qo:qo + qn] = d[0]
         idx[qo:qo + qn] = np.where(i[0] >= 0, i[0] + (ro if global_index else 0), -1)
     return dist2, idx
+
+
+
+# ------------------------------------------------------------------ three_nn and Chamfer
+#
+# Project page: the 0.5.0 operators (section "Minimal example" calls them;
+# roadmap "Phase 2" describes three_nn, "Phase 4" the Chamfer distance).
+
+def three_nn(unknown, known, threads=1):
+    """The three nearest known points of every unknown point: Euclidean
+    distances and indices (roadmap, "Phase 2"), i.e. kNN with k = 3."""
+    return knn(unknown, known, 3, threads=threads)
+
+
+def nearest(query, ref, p_len=None, rows=None, threads=1):
+    """Nearest reference (squared distance, index) of every query row; cloud b
+    uses its first p_len[b] references. -> (s (B, Q) float32, idx (B, Q) int64)."""
+    lib = _load()
+    query, pq = _f32(query)
+    ref, pr = _f32(ref)
+    B, Q, _ = query.shape
+    P = ref.shape[1]
+    s = np.full((B, Q), np.nan, dtype=np.float32)
+    idx = np.full((B, Q), -2, dtype=np.int64)
+    pl = None if p_len is None else np.ascontiguousarray(p_len, dtype=np.int64)
+    lo, hi = (0, B * Q) if rows is None else rows
+    ps = s.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+    def run(a, b):
+        _check(lib.pco_nearest_rows(pq, pr, B, Q, P, None if pl is None else _i64(pl), ps,
+                                    _i64(idx), lo + a, lo + b), "nearest")
+
+    if hi > lo:
+        _fan_out(run, hi - lo, threads)
+    return s, idx
+
+
+def _chamfer_weights(B, x_len, y_len, point_reduction, batch_reduction):
+    """Per-cloud factors of the two directions' sums: 1 / length for a point
+    mean (a length of 0 counts as 1), times 1 / B for a batch mean."""
+    wx = np.ones(B) if point_reduction == "sum" else 1.0 / np.maximum(x_len, 1)
+    wy = np.ones(B) if point_reduction == "sum" else 1.0 / np.maximum(y_len, 1)
+    if batch_reduction == "mean":
+        wx, wy = wx / B, wy / B
+    return wx, wy
+
+
+def chamfer(x, y, x_len=None, y_len=None, point_reduction="mean", batch_reduction="mean",
+            single_directional=False, threads=1):
+    """Squared-L2 Chamfer distance of clouds x (B, N, 3) and y (B, M, 3), the
+    first x_len[b] / y_len[b] points of each cloud taking part (roadmap,
+    "Phase 4"): a(i) = the nearest point of y to x_i, b(j) = the nearest of x
+    to y_j; per cloud the sum (or mean) over i of |x_i - y_a(i)|^2 plus, unless
+    single-directional, the same over j of |y_j - x_b(j)|^2; then the sum or
+    mean over the batch, or per cloud (batch_reduction None). float64 sums of
+    the float32 squared distances.
+    -> (loss: float or (B,) float64, s_xy, i_xy, s_yx, i_yx)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    B, N, M = x.shape[0], x.shape[1], y.shape[1]
+    xl = np.full(B, N) if x_len is None else np.asarray(x_len, dtype=np.int64)
+    yl = np.full(B, M) if y_len is None else np.asarray(y_len, dtype=np.int64)
+    s_xy, i_xy = nearest(x, y, yl, threads=threads)
+    s_yx, i_yx = nearest(y, x, xl, threads=threads)
+    mx = np.arange(N)[None, :] < xl[:, None]
+    my = np.arange(M)[None, :] < yl[:, None]
+    wx, wy = _chamfer_weights(B, xl, yl, point_reduction, batch_reduction)
+    per = wx * np.where(mx, s_xy.astype(np.float64), 0.0).sum(axis=1)
+    if not single_directional:
+        per = per + wy * np.where(my, s_yx.astype(np.float64), 0.0).sum(axis=1)
+    loss = per if batch_reduction is None else float(per.sum())
+    return loss, s_xy, i_xy, s_yx, i_yx
+
+
+def chamfer_backward(x, y, i_xy, i_yx, grad_loss, x_len=None, y_len=None,
+                     point_reduction="mean", batch_reduction="mean", single_directional=False):
+    """Gradients of the Chamfer loss with the nearest points held fixed
+    (roadmap, "Phase 4": both directions contribute to both clouds), float64.
+    grad_loss: a float, or (B,) for batch_reduction None.
+    -> (grad_x, grad_y, abs_x, abs_y); abs_* sums the absolute terms."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    y = np.asarray(y, dtype=np.float32).astype(np.float64)
+    B, N, M = x.shape[0], x.shape[1], y.shape[1]
+    xl = np.full(B, N) if x_len is None else np.asarray(x_len, dtype=np.int64)
+    yl = np.full(B, M) if y_len is None else np.asarray(y_len, dtype=np.int64)
+    g = np.broadcast_to(np.asarray(grad_loss, dtype=np.float64), (B,))
+    wx, wy = _chamfer_weights(B, xl, yl, point_reduction, batch_reduction)
+    gx, gy = np.zeros_like(x), np.zeros_like(y)
+    ax, ay = np.zeros_like(x), np.zeros_like(y)
+    dirs = [(x, y, i_xy, xl, g * wx, gx, gy, ax, ay)]
+    if not single_directional:
+        dirs.append((y, x, i_yx, yl, g * wy, gy, gx, ay, ax))
+    for a, o, idx, la, w, ga, go, aa, ao in dirs:
+        for b in range(B):
+            for i in range(int(la[b])):
+                j = int(idx[b, i])
+                if j < 0:
+                    continue
+                t = 2.0 * w[b] * (a[b, i] - o[b, j])
+                ga[b, i] += t
+                go[b, j] -= t
+                aa[b, i] += np.abs(t)
+                ao[b, j] += np.abs(t)
+    return gx, gy, ax, ay

@@ -19,9 +19,11 @@
  *        (r32 = fl32(r), R2 = fl32(r32 * r32), strict s32 < R2, exact ties to
  *        the smaller index, zero distance can be a real match).
  *
- * Arithmetic: float32 for the three selections (the pages fix it), each
+ * Arithmetic: float32 for the selections (the pages fix it), each
  * operation rounded to nearest-even, no fused multiply-add, denormals kept.
- * The Ball Query backward, whose precision the pages leave open, is float64. Build with -O2 -ffp-contract=off and
+ * The Ball Query backward, whose precision the pages leave open, is float64.
+ * The nearest-point selection of the Chamfer distance is here too; its
+ * reductions and gradients are float64 numpy code in oracle/__init__.py. Build with -O2 -ffp-contract=off and
  * never with -ffast-math; the preprocessor checks below refuse builds that
  * would evaluate in a wider type or with fast-math.
  *
@@ -188,6 +190,44 @@ int pco_knn(const float *query, const float *ref, int64_t B, int64_t Q, int64_t 
             float *out_dist, int64_t *out_idx)
 {
     return pco_knn_rows(query, ref, B, Q, P, k, out_dist, out_idx, 0, B * Q);
+}
+
+/* Nearest reference of the query rows [row_begin, row_end), squared distance
+ * kept: [P1] "k nearest neighbors" with k = 1 (the first reference in the
+ * (s, j) order, i.e. the smallest j reaching the minimum s32), which is the
+ * nearest-point selection of [P1]'s Chamfer distance (roadmap, "Phase 4":
+ * a(i) = the nearest point of the other cloud). Cloud b uses only its first
+ * p_len[b] references (all P when p_len is NULL); a row with none gets
+ * (s, j) = (0, -1).
+ * Out: s (B, Q) float32, idx (B, Q) int64, rows outside the range untouched. */
+int pco_nearest_rows(const float *query, const float *ref, int64_t B, int64_t Q, int64_t P,
+                     const int64_t *p_len, float *out_s, int64_t *out_idx, int64_t row_begin,
+                     int64_t row_end)
+{
+    if (B < 0 || Q < 0 || P < 0)
+        return PCO_INVALID_ARGUMENT;
+    if (row_begin < 0 || row_end > B * Q || row_begin > row_end)
+        return PCO_INVALID_ARGUMENT;
+    for (int64_t row = row_begin; row < row_end; ++row) {
+        int64_t b = row / Q;
+        int64_t n = p_len ? p_len[b] : P;
+        if (n < 0 || n > P)
+            return PCO_INVALID_ARGUMENT;
+        const float *q = query + (size_t)row * 3;
+        const float *x = ref + (size_t)b * (size_t)P * 3;
+        float best = 0.0f;
+        int64_t arg = -1;
+        for (int64_t j = 0; j < n; ++j) {
+            float d = pco_s32(q, x + 3 * j);
+            if (arg < 0 || d < best) {  /* strict: an equal distance keeps the smaller j */
+                best = d;
+                arg = j;
+            }
+        }
+        out_s[row] = best;
+        out_idx[row] = arg;
+    }
+    return PCO_OK;
 }
 
 /* First-K Ball Query of the query rows [row_begin, row_end).
