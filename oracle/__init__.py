@@ -349,6 +349,9 @@ def chamfer(x, y, x_len=None, y_len=None, point_reduction="mean", batch_reductio
     s_yx, i_yx = nearest(y, x, xl, threads=threads)
     mx = np.arange(N)[None, :] < xl[:, None]
     my = np.arange(M)[None, :] < yl[:, None]
+    # points past a cloud's length take no part: reported as (0, -1)
+    s_xy[~mx], i_xy[~mx] = 0.0, -1
+    s_yx[~my], i_yx[~my] = 0.0, -1
     wx, wy = _chamfer_weights(B, xl, yl, point_reduction, batch_reduction)
     per = wx * np.where(mx, s_xy.astype(np.float64), 0.0).sum(axis=1)
     if not single_directional:
