@@ -224,6 +224,72 @@ int pointops_fps_ragged(const float *xyz, int64_t rows, const int64_t *x_off,
                         const int64_t *out_cnt, int global_index, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/*
+ * three_nn: the three nearest known points of every unknown point, Euclidean
+ * distances and indices. Project page, "Minimal example" (the 0.5.0 call) and
+ * roadmap, "Phase 2" (PointNet++ feature propagation). It is pointops_knn
+ * with k = 3 (same order and ties): unknown (B, n, 3), known (B, m, 3),
+ * m >= 3; out_dist, out_idx (B, n, 3), device.
+ */
+int pointops_three_nn(const float *unknown, const float *known, int64_t B, int64_t n, int64_t m,
+                      float *out_dist, int64_t *out_idx, void *stream);
+
+/* Reductions of pointops_chamfer. */
+enum pointops_reduction {
+    POINTOPS_REDUCE_NONE = 0, /* batch only: one loss per cloud */
+    POINTOPS_REDUCE_MEAN = 1,
+    POINTOPS_REDUCE_SUM = 2
+};
+
+/* Workspace bytes of pointops_chamfer and pointops_chamfer_backward for B clouds. */
+size_t pointops_chamfer_workspace_bytes(int64_t B);
+
+/*
+ * Squared-L2 Chamfer distance of x (B, N, 3) and y (B, M, 3), device.
+ * Project page, roadmap "Phase 4": a(i) = the nearest point of y to x_i and
+ * b(j) = the nearest point of x to y_j (the kNN order with k = 1: ties to the
+ * smaller index); per cloud, the sum over i of s(x_i, y_a(i)) plus, unless
+ * single_directional, the sum over j of s(y_j, x_b(j)), with s the float32
+ * squared distance s32. x_lengths / y_lengths: HOST arrays of B lengths
+ * (NULL: all points), 0 <= len <= N (M); only the first len points of a cloud
+ * take part. point_reduction MEAN divides each direction's sum by its length
+ * (a length of 0 counts as 1), SUM does not; batch_reduction MEAN / SUM
+ * combine the clouds, NONE keeps one loss per cloud. A point whose other
+ * cloud is empty contributes nothing.
+ *
+ *   loss      device float32: (B,) for batch_reduction NONE, else (1,). Sums
+ *             are taken in float64 in a fixed order (deterministic).
+ *   dist_xy, idx_xy  (B, N) device: s and a(i) per point of x, local indices;
+ *             (0, -1) past x's length or without partner. dist_yx, idx_yx:
+ *             (B, M) likewise for y; not used (may be NULL) when
+ *             single_directional. These are the inputs of the backward.
+ *   workspace pointops_chamfer_workspace_bytes(B) bytes of device scratch.
+ */
+int pointops_chamfer(const float *x, const float *y, int64_t B, int64_t N, int64_t M,
+                     const int64_t *x_lengths, const int64_t *y_lengths, int point_reduction,
+                     int batch_reduction, int single_directional, float *loss, float *dist_xy,
+                     int64_t *idx_xy, float *dist_yx, int64_t *idx_yx, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
+ * Gradients of the Chamfer loss with the nearest points held fixed (project
+ * page, roadmap "Phase 4": the gradient of each selected pair goes to both
+ * points: 2 w (p - o) to the point and its negation to its nearest point).
+ * Same sizes, lengths and reductions as the forward call; idx_xy / idx_yx
+ * its index outputs; grad_loss the upstream gradient, device float32, (B,)
+ * for batch_reduction NONE, else (1,). grad_x (B, N, 3) and grad_y (B, M, 3),
+ * device, are overwritten (either may be NULL). w = fl32(upstream gradient x
+ * reduction factor); terms are added with float atomics in no fixed order,
+ * so the last bits may differ between runs. The workspace is needed only when
+ * lengths are given.
+ */
+int pointops_chamfer_backward(const float *x, const float *y, int64_t B, int64_t N, int64_t M,
+                              const int64_t *x_lengths, const int64_t *y_lengths,
+                              int point_reduction, int batch_reduction, int single_directional,
+                              const int64_t *idx_xy, const int64_t *idx_yx,
+                              const float *grad_loss, float *grad_x, float *grad_y,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
 /* POINTOPS_OK if `device` is a gfx950 GPU with 64-wide wavefronts (the kernels
  * assume that width), POINTOPS_UNSUPPORTED_DEVICE otherwise. The entry points
  * above run this check on the current device (cached per device). */

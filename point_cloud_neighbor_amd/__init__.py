@@ -12,6 +12,9 @@ kernel for gfx950 behind the C ABI declared in ``include/pointops.h``:
 * ragged batches: ``fps_ragged``, ``knn_ragged``, ``ball_query_ragged`` over
   clouds packed back to back in a flat (rows, 3) tensor with ``ptr`` offsets,
   and ``knn_padded``, ``ball_query_padded`` over padded clouds with lengths
+* ``three_nn(unknown, known)`` -> the 3 nearest (distance, index), kNN k=3
+* ``chamfer_distance(x, y, ...)`` -> (squared-L2 Chamfer loss, None),
+  differentiable, with lengths and mean / sum reductions
 
 The ops are loaded lazily so that ``workloads`` imports without a GPU; calling
 an op without the built library or a gfx950 device raises, there is no CPU
@@ -20,7 +23,7 @@ fallback.
 
 __all__ = ["furthest_point_sample", "knn", "ball_query", "ball_query_backward",
            "fps_ragged", "knn_ragged", "ball_query_ragged", "knn_padded", "ball_query_padded",
-           "PointopsError"]
+           "three_nn", "chamfer_distance", "PointopsError"]
 
 
 def __getattr__(name):

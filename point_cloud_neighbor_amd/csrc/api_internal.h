@@ -6,6 +6,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <array>
+#include <vector>
+
 namespace pointops {
 
 hipError_t launch_ball_query(const float*, const float*, int64_t, int64_t, int64_t, float,
@@ -24,7 +27,7 @@ size_t fps_batch_lds_bytes(int G, int rg);
 int fps_batch_ppt_round(int ppt);
 int fps_batch_stride(int rg);
 hipError_t launch_knn(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
-                      int64_t*, int, int, const int64_t*, int, int64_t, hipStream_t);
+                      int64_t*, int, int, const int64_t*, int, int64_t, int, hipStream_t);
 hipError_t launch_ball_query_backward(const float*, const float*, const int64_t*, const float*,
                                       int64_t, int64_t, int64_t, int64_t, float*, float*,
                                       hipStream_t);
@@ -53,6 +56,22 @@ int current_device(DeviceInfo** out);
 long env_long(const char* name, long dflt);
 // The largest G' <= G for which slices of ceil(N / G') points are all non-empty.
 int64_t split_even(int64_t N, int64_t G);
+// The cloud table of a ragged launch (see segments.h): tile_ptr over the
+// clouds in `order` (units per cloud), then their records.
+struct Table {
+    std::vector<int64_t> words;
+    int64_t units = 0;
+    int nseg = 0;
+};
+Table make_table(const std::vector<int64_t>& order, const std::vector<int64_t>& units,
+                 const std::vector<std::array<int64_t, 8>>& recs);
+// kNN / Ball Query table: clouds with queries, `per_unit` queries per
+// workgroup or wave, largest reference sets first.
+Table search_table(const int64_t* q_off, const int64_t* q_cnt, const int64_t* r_off,
+                   const int64_t* r_cnt, int64_t B, int per_unit, bool global_index);
+// Writes the table to the start of the workspace on `stream`.
+int upload(const Table& t, void* workspace, size_t workspace_bytes, hipStream_t s,
+           int64_t** dev_table);
 // Knobs shared by the dense and ragged launches.
 int knn_waves(int kcap, int64_t tiles, int cus);
 int bq_queries_per_wave(int64_t rows, int cus, int max_qw);

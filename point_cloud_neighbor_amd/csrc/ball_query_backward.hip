@@ -86,16 +86,21 @@ __global__ void zero_f32_kernel(float* __restrict__ p, size_t n) {
         p[i] = 0.0f;
 }
 
+// Zeroes n floats with a fill kernel (not a memset node, so callers can be
+// captured into a graph).
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(blocks), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_ball_query_backward(const float* query, const float* ref, const int64_t* idx,
                                       const float* grad, int64_t B, int64_t Q, int64_t P,
                                       int64_t K, float* grad_query, float* grad_ref,
                                       hipStream_t stream) {
     if (grad_ref && B * P > 0) {
-        // a fill kernel rather than a memset node, so the call can be captured
-        const size_t n = (size_t)B * P * 3;
-        const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
-        hipLaunchKernelGGL(zero_f32_kernel, dim3(blocks), dim3(256), 0, stream, grad_ref, n);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_zero_f32(grad_ref, (size_t)B * P * 3, stream);
         if (e != hipSuccess) return e;
     }
     const int64_t rows = B * Q;

@@ -1,0 +1,223 @@
+// C ABI of three_nn and the Chamfer distance. Declarations and contracts are
+// in include/pointops.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "../../include/pointops.h"
+#include "api_internal.h"
+#include "segments.h"
+
+namespace pointops {
+hipError_t launch_chamfer_pad(float*, int64_t*, int64_t, int64_t, const int64_t*, hipStream_t);
+hipError_t launch_chamfer_reduce(const float*, const float*, int64_t, int64_t, int64_t,
+                                 const int64_t*, const int64_t*, int, int, int, double*, float*,
+                                 hipStream_t);
+hipError_t launch_chamfer_backward(const float*, const float*, int64_t, int64_t, int64_t,
+                                   const int64_t*, const int64_t*, int, int, int,
+                                   const int64_t*, const int64_t*, const float*, float*, float*,
+                                   hipStream_t);
+hipError_t launch_zero_f32(float*, size_t, hipStream_t);
+}  // namespace pointops
+
+using namespace pointops::api;
+
+namespace {
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace: both length arrays, the per-cloud partial losses, then the two
+// cloud tables of the nearest-point searches (with lengths).
+struct ChamferLayout {
+    size_t lens, part, table_xy, table_yx, total;
+};
+
+ChamferLayout chamfer_layout(int64_t B) {
+    ChamferLayout l;
+    l.lens = 0;
+    l.part = align256((size_t)2 * B * sizeof(int64_t));
+    l.table_xy = l.part + align256((size_t)B * sizeof(double));
+    const size_t t = align256((size_t)pointops::seg_table_words(B) * sizeof(int64_t));
+    l.table_yx = l.table_xy + t;
+    l.total = std::max<size_t>(l.table_yx + t, 256);
+    return l;
+}
+
+int check_lengths(const char* what, const int64_t* len, int64_t B, int64_t n) {
+    if (!len) return POINTOPS_OK;
+    for (int64_t b = 0; b < B; ++b)
+        if (len[b] < 0 || len[b] > n)
+            return fail(POINTOPS_INVALID_ARGUMENT, "%s[%lld] = %lld not in [0, %lld]", what,
+                        (long long)b, (long long)len[b], (long long)n);
+    return POINTOPS_OK;
+}
+
+int check_chamfer(const float* x, const float* y, int64_t B, int64_t N, int64_t M,
+                  const int64_t* x_lengths, const int64_t* y_lengths, int point_reduction,
+                  int batch_reduction) {
+    if (B < 0 || N < 0 || M < 0) return fail(POINTOPS_INVALID_ARGUMENT, "negative size");
+    if (N >= kMaxPoints || M >= kMaxPoints || B >= kMaxPoints)
+        return fail(POINTOPS_UNSUPPORTED, "sizes >= 2^31");
+    if (point_reduction != POINTOPS_REDUCE_MEAN && point_reduction != POINTOPS_REDUCE_SUM)
+        return fail(POINTOPS_INVALID_ARGUMENT, "point_reduction must be MEAN or SUM");
+    if (batch_reduction != POINTOPS_REDUCE_NONE && batch_reduction != POINTOPS_REDUCE_MEAN &&
+        batch_reduction != POINTOPS_REDUCE_SUM)
+        return fail(POINTOPS_INVALID_ARGUMENT, "batch_reduction must be NONE, MEAN or SUM");
+    int st = check_lengths("x_lengths", x_lengths, B, N);
+    if (st != POINTOPS_OK) return st;
+    st = check_lengths("y_lengths", y_lengths, B, M);
+    if (st != POINTOPS_OK) return st;
+    if ((B * N > 0 && !x) || (B * M > 0 && !y))
+        return fail(POINTOPS_INVALID_ARGUMENT, "null pointer");
+    return POINTOPS_OK;
+}
+
+// Lengths (either may be NULL: the full cloud) to the device, as [lx | ly].
+int upload_lengths(const int64_t* x_lengths, const int64_t* y_lengths, int64_t B, int64_t N,
+                   int64_t M, int64_t* dev, hipStream_t s) {
+    std::vector<int64_t> h((size_t)2 * B);
+    for (int64_t b = 0; b < B; ++b) {
+        h[(size_t)b] = x_lengths ? x_lengths[b] : N;
+        h[(size_t)(B + b)] = y_lengths ? y_lengths[b] : M;
+    }
+    hipError_t e = pointops::upload_words(h.data(), 2 * B, dev, s);
+    return e == hipSuccess ? POINTOPS_OK : hip_fail(e, "length upload");
+}
+
+// Nearest point of every row of `a` (B, n) among the first lb[b] points of
+// `b_` (B, m), squared distance kept; rows past la[b] hold (0, -1).
+int nearest(const float* a, const float* bpts, int64_t B, int64_t n, int64_t m,
+            const int64_t* la, const int64_t* lb, const int64_t* dev_la, float* dist,
+            int64_t* idx, void* table_ws, size_t table_bytes, const DeviceInfo& dev,
+            hipStream_t s) {
+    if (B * n == 0) return POINTOPS_OK;
+    hipError_t e;
+    if (!la && !lb) {
+        const int64_t tiles = B * ((n + 63) / 64);
+        e = pointops::launch_knn(a, bpts, B, n, m, 1, dist, idx, 1, knn_waves(1, tiles, dev.cus),
+                                 nullptr, 0, 0, 1, s);
+        return e == hipSuccess ? POINTOPS_OK : hip_fail(e, "nearest launch");
+    }
+    std::vector<int64_t> qo((size_t)B), qc((size_t)B), ro((size_t)B), rc((size_t)B);
+    for (int64_t b = 0; b < B; ++b) {
+        qo[(size_t)b] = b * n;
+        qc[(size_t)b] = la ? la[b] : n;
+        ro[(size_t)b] = b * m;
+        rc[(size_t)b] = lb ? lb[b] : m;
+    }
+    const Table t = search_table(qo.data(), qc.data(), ro.data(), rc.data(), B, 64, false);
+    e = pointops::launch_chamfer_pad(dist, idx, B, n, dev_la, s);
+    if (e != hipSuccess) return hip_fail(e, "chamfer pad");
+    if (t.units == 0) return POINTOPS_OK;
+    int64_t* table = nullptr;
+    int st = upload(t, table_ws, table_bytes, s, &table);
+    if (st != POINTOPS_OK) return st;
+    e = pointops::launch_knn(a, bpts, 0, 0, 0, 1, dist, idx, 1, knn_waves(1, t.units, dev.cus),
+                             table, t.nseg, t.units, 1, s);
+    return e == hipSuccess ? POINTOPS_OK : hip_fail(e, "nearest launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int pointops_three_nn(const float* unknown, const float* known, int64_t B, int64_t n, int64_t m,
+                      float* out_dist, int64_t* out_idx, void* stream) {
+    clear_error();
+    if (m < 3 && B > 0 && n > 0)
+        return fail(POINTOPS_INVALID_ARGUMENT, "three_nn needs at least 3 known points, got %lld",
+                    (long long)m);
+    return pointops_knn(unknown, known, B, n, m, 3, out_dist, out_idx, stream);
+}
+
+size_t pointops_chamfer_workspace_bytes(int64_t B) {
+    return B < 0 ? 0 : chamfer_layout(B).total;
+}
+
+int pointops_chamfer(const float* x, const float* y, int64_t B, int64_t N, int64_t M,
+                     const int64_t* x_lengths, const int64_t* y_lengths, int point_reduction,
+                     int batch_reduction, int single_directional, float* loss, float* dist_xy,
+                     int64_t* idx_xy, float* dist_yx, int64_t* idx_yx, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    clear_error();
+    int st = check_chamfer(x, y, B, N, M, x_lengths, y_lengths, point_reduction,
+                           batch_reduction);
+    if (st != POINTOPS_OK) return st;
+    if (!loss || (B * N > 0 && (!dist_xy || !idx_xy)) ||
+        (!single_directional && B * M > 0 && (!dist_yx || !idx_yx)))
+        return fail(POINTOPS_INVALID_ARGUMENT, "null output pointer");
+    const ChamferLayout l = chamfer_layout(B);
+    if (!workspace || workspace_bytes < l.total)
+        return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
+                    workspace_bytes, l.total);
+    DeviceInfo* dev = nullptr;
+    st = current_device(&dev);
+    if (st != POINTOPS_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    int64_t* lens = (int64_t*)(ws + l.lens);
+    const bool have_len = x_lengths || y_lengths;
+    if (have_len && B > 0) {
+        st = upload_lengths(x_lengths, y_lengths, B, N, M, lens, s);
+        if (st != POINTOPS_OK) return st;
+    }
+    const int64_t* dlx = have_len ? lens : nullptr;
+    const int64_t* dly = have_len ? lens + B : nullptr;
+    const size_t tb = l.table_yx - l.table_xy;
+    st = nearest(x, y, B, N, M, x_lengths, y_lengths, dlx, dist_xy, idx_xy, ws + l.table_xy, tb,
+                 *dev, s);
+    if (st != POINTOPS_OK) return st;
+    if (!single_directional) {
+        st = nearest(y, x, B, M, N, y_lengths, x_lengths, dly, dist_yx, idx_yx, ws + l.table_yx,
+                     tb, *dev, s);
+        if (st != POINTOPS_OK) return st;
+    }
+    hipError_t e = pointops::launch_chamfer_reduce(
+        dist_xy, dist_yx, B, N, M, dlx, dly, point_reduction == POINTOPS_REDUCE_MEAN,
+        batch_reduction, single_directional != 0, (double*)(ws + l.part), loss, s);
+    if (e != hipSuccess) return hip_fail(e, "chamfer reduce");
+    return POINTOPS_OK;
+}
+
+int pointops_chamfer_backward(const float* x, const float* y, int64_t B, int64_t N, int64_t M,
+                              const int64_t* x_lengths, const int64_t* y_lengths,
+                              int point_reduction, int batch_reduction, int single_directional,
+                              const int64_t* idx_xy, const int64_t* idx_yx,
+                              const float* grad_loss, float* grad_x, float* grad_y,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    clear_error();
+    int st = check_chamfer(x, y, B, N, M, x_lengths, y_lengths, point_reduction,
+                           batch_reduction);
+    if (st != POINTOPS_OK) return st;
+    if (!grad_x && !grad_y) return POINTOPS_OK;
+    if (B > 0 && (!grad_loss || (N > 0 && !idx_xy) ||
+                  (!single_directional && M > 0 && !idx_yx)))
+        return fail(POINTOPS_INVALID_ARGUMENT, "null pointer");
+    const ChamferLayout l = chamfer_layout(B);
+    const bool have_len = x_lengths || y_lengths;
+    if (have_len && (!workspace || workspace_bytes < l.total))
+        return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
+                    workspace_bytes, l.total);
+    st = current_device(nullptr);
+    if (st != POINTOPS_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (grad_x && (e = pointops::launch_zero_f32(grad_x, (size_t)(B * N * 3), s)) != hipSuccess)
+        return hip_fail(e, "gradient clear");
+    if (grad_y && (e = pointops::launch_zero_f32(grad_y, (size_t)(B * M * 3), s)) != hipSuccess)
+        return hip_fail(e, "gradient clear");
+    int64_t* lens = (int64_t*)((char*)workspace + l.lens);
+    if (have_len && B > 0) {
+        st = upload_lengths(x_lengths, y_lengths, B, N, M, lens, s);
+        if (st != POINTOPS_OK) return st;
+    }
+    e = pointops::launch_chamfer_backward(
+        x, y, B, N, M, have_len ? lens : nullptr, have_len ? lens + B : nullptr,
+        point_reduction == POINTOPS_REDUCE_MEAN, batch_reduction, single_directional != 0,
+        idx_xy, idx_yx, grad_loss, grad_x, grad_y, s);
+    if (e != hipSuccess) return hip_fail(e, "chamfer backward");
+    return POINTOPS_OK;
+}
+
+}  // extern "C"

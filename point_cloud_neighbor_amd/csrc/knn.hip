@@ -82,7 +82,7 @@ template <int KCAP, int NW>
 __global__ __launch_bounds__(NW* kWave) void knn_kernel(
     const float* __restrict__ query, const float* __restrict__ ref, int Q, int P, int k,
     float* __restrict__ out_dist, int64_t* __restrict__ out_idx, const int64_t* __restrict__ seg,
-    int nseg) {
+    int nseg, int squared) {
     // LDS: per wave, kKnnBuf candidate rows during the scan, then KCAP list
     // rows for the merge; row e of wave w is uint2[64] (one entry per lane).
     extern __shared__ uint2 lds[];
@@ -207,17 +207,21 @@ __global__ __launch_bounds__(NW* kWave) void knn_kernel(
         if (p >= front) {
             // empty slots remain only when the cloud has fewer than k references
             const bool empty = top.key[p] == 0xFFFFFFFFu;
-            od[p - front] = empty ? __builtin_inff() : sqrtf(u2f(top.key[p] - 1u));
+            const float s = u2f(top.key[p] - 1u);
+            od[p - front] = squared ? (empty ? 0.0f : s) : (empty ? __builtin_inff() : sqrtf(s));
             oi[p - front] = empty ? (int64_t)-1 : ibase + top.id[p];
         }
     }
 }
 
 // Dense: grid (ceil(Q / 64), B). Ragged (seg != nullptr): grid (tiles, 1), with
-// tiles = the table's tile_ptr[nseg] and Q, P unused.
+// tiles = the table's tile_ptr[nseg] and Q, P unused. squared != 0: out_dist
+// holds s itself (the nearest-point distances of the Chamfer distance) and
+// empty slots hold (0, -1).
 hipError_t launch_knn(const float* query, const float* ref, int64_t B, int64_t Q, int64_t P,
                       int64_t k, float* out_dist, int64_t* out_idx, int kcap, int nw,
-                      const int64_t* seg, int nseg, int64_t tiles, hipStream_t stream) {
+                      const int64_t* seg, int nseg, int64_t tiles, int squared,
+                      hipStream_t stream) {
     dim3 grid = seg ? dim3((unsigned)tiles, 1) : dim3((unsigned)((Q + kWave - 1) / kWave), (unsigned)B);
 #define POINTOPS_KNN_CASE(KC, W)                                                             \
     if (kcap == KC && nw == W) {                                                             \
@@ -230,7 +234,8 @@ hipError_t launch_knn(const float* query, const float* ref, int64_t B, int64_t Q
             if (e != hipSuccess) return e;                                                   \
         }                                                                                    \
         hipLaunchKernelGGL((knn_kernel<KC, W>), grid, dim3(W * kWave), lds, stream, query,  \
-                           ref, (int)Q, (int)P, (int)k, out_dist, out_idx, seg, nseg);       \
+                           ref, (int)Q, (int)P, (int)k, out_dist, out_idx, seg, nseg,        \
+                           squared);                                                         \
         return hipGetLastError();                                                            \
     }
     POINTOPS_KNN_CASE(1, 1) POINTOPS_KNN_CASE(1, 4) POINTOPS_KNN_CASE(1, 8)

@@ -341,7 +341,7 @@ int pointops_knn(const float* query, const float* ref, int64_t B, int64_t Q, int
     while (kcap < k) kcap *= 2;
     const int64_t tiles = B * ((Q + 63) / 64);
     hipError_t e = pointops::launch_knn(query, ref, B, Q, P, k, out_dist, out_idx, kcap,
-                                        knn_waves(kcap, tiles, dev->cus), nullptr, 0, 0,
+                                        knn_waves(kcap, tiles, dev->cus), nullptr, 0, 0, 0,
                                         (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "knn launch");
     return POINTOPS_OK;

@@ -19,48 +19,12 @@ using namespace pointops::api;
 using pointops::kSegRecWords;
 using pointops::seg_ptr_words;
 using pointops::seg_table_words;
+static_assert(pointops::kSegRecWords == 8, "api_internal.h declares 8-word records");
 
-namespace {
-
-constexpr size_t kHeader = 256;  // status word of FPS, then the table
-
-size_t align256(size_t n) { return (n + 255) / 256 * 256; }
-
-// Every segment inside [0, rows) with fewer than 2^31 points; with `disjoint`,
-// no two non-empty segments share a row (they are output rows).
-int check_segments(const char* what, const int64_t* off, const int64_t* cnt, int64_t B,
-                   int64_t rows, bool disjoint) {
-    if (B > 0 && (!off || !cnt)) return fail(POINTOPS_INVALID_ARGUMENT, "%s: null segment array", what);
-    for (int64_t b = 0; b < B; ++b) {
-        if (off[b] < 0 || cnt[b] < 0 || off[b] > rows || cnt[b] > rows - off[b])
-            return fail(POINTOPS_INVALID_ARGUMENT,
-                        "%s: segment %lld = [%lld, +%lld) is not inside the %lld rows", what,
-                        (long long)b, (long long)off[b], (long long)cnt[b], (long long)rows);
-        if (cnt[b] >= kMaxPoints)
-            return fail(POINTOPS_UNSUPPORTED, "%s: segment %lld has 2^31 or more points", what,
-                        (long long)b);
-    }
-    if (disjoint) {
-        std::vector<int64_t> order;
-        for (int64_t b = 0; b < B; ++b)
-            if (cnt[b] > 0) order.push_back(b);
-        std::sort(order.begin(), order.end(),
-                  [&](int64_t a, int64_t c) { return off[a] < off[c]; });
-        for (size_t i = 1; i < order.size(); ++i)
-            if (off[order[i - 1]] + cnt[order[i - 1]] > off[order[i]])
-                return fail(POINTOPS_INVALID_ARGUMENT, "%s: segments %lld and %lld overlap", what,
-                            (long long)order[i - 1], (long long)order[i]);
-    }
-    return POINTOPS_OK;
-}
+namespace pointops {
+namespace api {
 
 // The cloud table: tile_ptr over `order` (units per cloud), then the records.
-struct Table {
-    std::vector<int64_t> words;
-    int64_t units = 0;
-    int nseg = 0;
-};
-
 Table make_table(const std::vector<int64_t>& order, const std::vector<int64_t>& units,
                  const std::vector<std::array<int64_t, kSegRecWords>>& recs) {
     Table t;
@@ -97,6 +61,55 @@ Table search_table(const int64_t* q_off, const int64_t* q_cnt, const int64_t* r_
     return make_table(order, units, recs);
 }
 
+int upload(const Table& t, void* workspace, size_t workspace_bytes, hipStream_t s,
+           int64_t** dev_table) {
+    const size_t need = t.words.size() * sizeof(int64_t);
+    if (!workspace || workspace_bytes < need)
+        return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
+                    workspace_bytes, need);
+    *dev_table = (int64_t*)workspace;
+    hipError_t e = pointops::upload_words(t.words.data(), (int64_t)t.words.size(), *dev_table, s);
+    if (e != hipSuccess) return hip_fail(e, "cloud table upload");
+    return POINTOPS_OK;
+}
+
+}  // namespace api
+}  // namespace pointops
+
+namespace {
+
+constexpr size_t kHeader = 256;  // status word of FPS, then the table
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Every segment inside [0, rows) with fewer than 2^31 points; with `disjoint`,
+// no two non-empty segments share a row (they are output rows).
+int check_segments(const char* what, const int64_t* off, const int64_t* cnt, int64_t B,
+                   int64_t rows, bool disjoint) {
+    if (B > 0 && (!off || !cnt)) return fail(POINTOPS_INVALID_ARGUMENT, "%s: null segment array", what);
+    for (int64_t b = 0; b < B; ++b) {
+        if (off[b] < 0 || cnt[b] < 0 || off[b] > rows || cnt[b] > rows - off[b])
+            return fail(POINTOPS_INVALID_ARGUMENT,
+                        "%s: segment %lld = [%lld, +%lld) is not inside the %lld rows", what,
+                        (long long)b, (long long)off[b], (long long)cnt[b], (long long)rows);
+        if (cnt[b] >= kMaxPoints)
+            return fail(POINTOPS_UNSUPPORTED, "%s: segment %lld has 2^31 or more points", what,
+                        (long long)b);
+    }
+    if (disjoint) {
+        std::vector<int64_t> order;
+        for (int64_t b = 0; b < B; ++b)
+            if (cnt[b] > 0) order.push_back(b);
+        std::sort(order.begin(), order.end(),
+                  [&](int64_t a, int64_t c) { return off[a] < off[c]; });
+        for (size_t i = 1; i < order.size(); ++i)
+            if (off[order[i - 1]] + cnt[order[i - 1]] > off[order[i]])
+                return fail(POINTOPS_INVALID_ARGUMENT, "%s: segments %lld and %lld overlap", what,
+                            (long long)order[i - 1], (long long)order[i]);
+    }
+    return POINTOPS_OK;
+}
+
 int check_search(const float* query, int64_t q_rows, const int64_t* q_off, const int64_t* q_cnt,
                  const float* ref, int64_t r_rows, const int64_t* r_off, const int64_t* r_cnt,
                  int64_t B, const void* out_a, const void* out_b) {
@@ -109,18 +122,6 @@ int check_search(const float* query, int64_t q_rows, const int64_t* q_off, const
     if (q_rows > 0 && (!query || !out_a || !out_b))
         return fail(POINTOPS_INVALID_ARGUMENT, "null pointer");
     if (r_rows > 0 && !ref) return fail(POINTOPS_INVALID_ARGUMENT, "null pointer");
-    return POINTOPS_OK;
-}
-
-int upload(const Table& t, void* workspace, size_t workspace_bytes, hipStream_t s,
-           int64_t** dev_table) {
-    const size_t need = t.words.size() * sizeof(int64_t);
-    if (!workspace || workspace_bytes < need)
-        return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
-                    workspace_bytes, need);
-    *dev_table = (int64_t*)workspace;
-    hipError_t e = pointops::upload_words(t.words.data(), (int64_t)t.words.size(), *dev_table, s);
-    if (e != hipSuccess) return hip_fail(e, "cloud table upload");
     return POINTOPS_OK;
 }
 
@@ -304,7 +305,7 @@ int pointops_knn_ragged(const float* query, int64_t q_rows, const int64_t* q_off
     while (kcap < k) kcap *= 2;
     hipError_t e = pointops::launch_knn(query, ref, 0, 0, 0, k, out_dist, out_idx, kcap,
                                         knn_waves(kcap, t.units, dev->cus), table, t.nseg,
-                                        t.units, s);
+                                        t.units, 0, s);
     if (e != hipSuccess) return hip_fail(e, "knn launch");
     return POINTOPS_OK;
 }

@@ -71,6 +71,17 @@ def _load():
         lib.pointops_fps_ragged.argtypes = [vp, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp,
                                             ctypes.c_int, vp, ctypes.c_size_t, vp]
         lib.pointops_fps_ragged.restype = ctypes.c_int
+        lib.pointops_three_nn.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
+        lib.pointops_three_nn.restype = ctypes.c_int
+        lib.pointops_chamfer_workspace_bytes.argtypes = [i64]
+        lib.pointops_chamfer_workspace_bytes.restype = ctypes.c_size_t
+        ci = ctypes.c_int
+        lib.pointops_chamfer.argtypes = [vp, vp, i64, i64, i64, vp, vp, ci, ci, ci, vp, vp, vp,
+                                         vp, vp, vp, ctypes.c_size_t, vp]
+        lib.pointops_chamfer.restype = ctypes.c_int
+        lib.pointops_chamfer_backward.argtypes = [vp, vp, i64, i64, i64, vp, vp, ci, ci, ci, vp,
+                                                  vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.pointops_chamfer_backward.restype = ctypes.c_int
         lib.pointops_device_check.argtypes = [ctypes.c_int]
         lib.pointops_device_check.restype = ctypes.c_int
         lib.pointops_status_string.argtypes = [ctypes.c_int]
@@ -427,3 +438,126 @@ def ball_query_padded(query: torch.Tensor, ref: torch.Tensor, radius: float, K: 
                           np.arange(B, dtype=np.int64) * Pm, l2, int(K),
                           (ctypes.c_float(float(radius)), int(K)), False, 0.0)
     return d.view(B, Qm, K), i.view(B, Qm, K)
+
+
+# ------------------------------------------------------------------ three_nn and Chamfer
+
+def three_nn(unknown: torch.Tensor, known: torch.Tensor):
+    """The three nearest known points of every unknown point -> (Euclidean
+    distance float32, int64 index), (B, n, 3); kNN with k = 3."""
+    lib = _load()
+    unknown = _points(unknown, "unknown")
+    known = _points(known, "known")
+    if unknown.device != known.device or unknown.shape[0] != known.shape[0]:
+        raise PointopsError(1, "unknown and known must share the device and the batch size")
+    B, n, _ = unknown.shape
+    m = known.shape[1]
+    with torch.cuda.device(unknown.device):
+        dist = torch.empty((B, n, 3), dtype=torch.float32, device=unknown.device)
+        idx = torch.empty((B, n, 3), dtype=torch.int64, device=unknown.device)
+        _check(lib.pointops_three_nn(unknown.data_ptr(), known.data_ptr(), B, n, m,
+                                     dist.data_ptr(), idx.data_ptr(), _stream(unknown.device)))
+    return dist, idx
+
+
+_REDUCE = {None: 0, "none": 0, "mean": 1, "sum": 2}
+
+
+def _chamfer_args(x, y, x_lengths, y_lengths, point_reduction, batch_reduction):
+    x = _points(x, "x")
+    y = _points(y, "y")
+    if x.device != y.device or x.shape[0] != y.shape[0]:
+        raise PointopsError(1, "x and y must share the device and the batch size")
+    if point_reduction not in ("mean", "sum"):
+        raise PointopsError(1, "point_reduction must be 'mean' or 'sum'")
+    if batch_reduction not in _REDUCE:
+        raise PointopsError(1, "batch_reduction must be 'mean', 'sum' or None")
+    B = x.shape[0]
+    lx = None if x_lengths is None else _host_i64(x_lengths, "x_lengths")
+    ly = None if y_lengths is None else _host_i64(y_lengths, "y_lengths")
+    for l, name in ((lx, "x_lengths"), (ly, "y_lengths")):
+        if l is not None and len(l) != B:
+            raise PointopsError(1, f"{name} must have B entries")
+    return x, y, lx, ly, _REDUCE[point_reduction], _REDUCE[batch_reduction]
+
+
+def chamfer_nearest(x, y, x_lengths=None, y_lengths=None, point_reduction="mean",
+                    batch_reduction="mean", single_directional=False):
+    """Forward Chamfer call -> (loss, dist_xy, idx_xy, dist_yx, idx_yx): loss
+    (B,) for batch_reduction None else (1,); per point of x (of y) the squared
+    distance to and local index of its nearest point of the other cloud."""
+    lib = _load()
+    x, y, lx, ly, pr, br = _chamfer_args(x, y, x_lengths, y_lengths, point_reduction,
+                                         batch_reduction)
+    B, N, M = x.shape[0], x.shape[1], y.shape[1]
+    dev = x.device
+    with torch.cuda.device(dev):
+        loss = torch.empty((B,) if br == 0 else (1,), dtype=torch.float32, device=dev)
+        d_xy = torch.empty((B, N), dtype=torch.float32, device=dev)
+        i_xy = torch.empty((B, N), dtype=torch.int64, device=dev)
+        d_yx = torch.empty((B, M), dtype=torch.float32, device=dev) if not single_directional else None
+        i_yx = torch.empty((B, M), dtype=torch.int64, device=dev) if not single_directional else None
+        ws = torch.empty(int(lib.pointops_chamfer_workspace_bytes(B)), dtype=torch.uint8,
+                         device=dev)
+        _check(lib.pointops_chamfer(x.data_ptr(), y.data_ptr(), B, N, M, _vp(lx), _vp(ly), pr,
+                                    br, int(bool(single_directional)), loss.data_ptr(),
+                                    d_xy.data_ptr(), i_xy.data_ptr(),
+                                    d_yx.data_ptr() if d_yx is not None else None,
+                                    i_yx.data_ptr() if i_yx is not None else None,
+                                    ws.data_ptr(), ws.numel(), _stream(dev)))
+    return loss, d_xy, i_xy, d_yx, i_yx
+
+
+def chamfer_backward(x, y, idx_xy, idx_yx, grad_loss, x_lengths=None, y_lengths=None,
+                     point_reduction="mean", batch_reduction="mean", single_directional=False,
+                     need_x=True, need_y=True):
+    """Gradients of the Chamfer loss for fixed nearest points -> (grad_x or
+    None, grad_y or None)."""
+    lib = _load()
+    x, y, lx, ly, pr, br = _chamfer_args(x, y, x_lengths, y_lengths, point_reduction,
+                                         batch_reduction)
+    B, N, M = x.shape[0], x.shape[1], y.shape[1]
+    dev = x.device
+    grad_loss = grad_loss.detach().to(device=dev, dtype=torch.float32).reshape(-1).contiguous()
+    if grad_loss.numel() != (B if br == 0 else 1):
+        raise PointopsError(1, "grad_loss has the wrong number of elements")
+    with torch.cuda.device(dev):
+        gx = torch.empty_like(x) if need_x else None
+        gy = torch.empty_like(y) if need_y else None
+        ws = torch.empty(int(lib.pointops_chamfer_workspace_bytes(B)), dtype=torch.uint8,
+                         device=dev)
+        _check(lib.pointops_chamfer_backward(
+            x.data_ptr(), y.data_ptr(), B, N, M, _vp(lx), _vp(ly), pr, br,
+            int(bool(single_directional)), idx_xy.contiguous().data_ptr(),
+            idx_yx.contiguous().data_ptr() if idx_yx is not None else None,
+            grad_loss.data_ptr(), gx.data_ptr() if gx is not None else None,
+            gy.data_ptr() if gy is not None else None, ws.data_ptr(), ws.numel(), _stream(dev)))
+    return gx, gy
+
+
+class _ChamferFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, y, x_lengths, y_lengths, point_reduction, batch_reduction, single):
+        loss, _, i_xy, _, i_yx = chamfer_nearest(x, y, x_lengths, y_lengths, point_reduction,
+                                                 batch_reduction, single)
+        ctx.save_for_backward(x, y, i_xy, i_yx if i_yx is not None else i_xy)
+        ctx.args = (x_lengths, y_lengths, point_reduction, batch_reduction, single)
+        return loss if batch_reduction is None else loss[0]
+
+    @staticmethod
+    def backward(ctx, grad):
+        x, y, i_xy, i_yx = ctx.saved_tensors
+        xl, yl, pr, br, single = ctx.args
+        gx, gy = chamfer_backward(x, y, i_xy, None if single else i_yx, grad, xl, yl, pr, br,
+                                  single, ctx.needs_input_grad[0], ctx.needs_input_grad[1])
+        return gx, gy, None, None, None, None, None
+
+
+def chamfer_distance(x: torch.Tensor, y: torch.Tensor, x_lengths=None, y_lengths=None,
+                     point_reduction: str = "mean", batch_reduction="mean",
+                     single_directional: bool = False):
+    """Squared-L2 Chamfer distance of (B, N, 3) and (B, M, 3) clouds, with
+    optional per-cloud lengths -> (loss, None): a scalar, or (B,) when
+    batch_reduction is None. Differentiable with respect to both clouds."""
+    return _ChamferFn.apply(x, y, x_lengths, y_lengths, point_reduction, batch_reduction,
+                            single_directional), None
