@@ -102,10 +102,21 @@ size_t pointops_fps_workspace_bytes(int64_t B, int64_t N, int64_t M);
 int pointops_knn(const float *query, const float *ref, int64_t B, int64_t Q, int64_t P,
                  int64_t k, float *out_dist, int64_t *out_idx, void *stream);
 
+/* Bytes of device workspace that lets pointops_ball_query skip far blocks of
+ * references (one bounding box per 64 references of each cloud, 32 bytes). */
+size_t pointops_ball_query_workspace_bytes(int64_t B, int64_t P);
+
 /*
  * Dense Ball Query: the first K references within the radius, in input order.
  * Project page, section "The operators in equations", "Ball Query: first K
  * within a radius"; "Numerical contracts" page, section "Selection and output".
+ * With a workspace of pointops_ball_query_workspace_bytes(B, P) bytes the call
+ * first bounds every block of 64 consecutive references by a box and skips,
+ * for each query, the blocks whose lower bound of s32 is >= R2 (the bound is
+ * taken in the same float32 order as s32, so it never exceeds it: results are
+ * identical, bit for bit). This pays when consecutive references are close in
+ * space (sorted clouds); workspace NULL scans every reference. A non-NULL
+ * workspace smaller than needed is INVALID_ARGUMENT.
  *   R2 = fl32(radius * radius) with radius already a float32 (the caller's
  *   fl32(r)); J = the references j with s32(q_i, x_j) < R2, in increasing j;
  *   slot n < min(K, |J|) holds (J[n], s32 of J[n]); the rest hold (-1, +0.0f).
@@ -119,7 +130,7 @@ int pointops_knn(const float *query, const float *ref, int64_t B, int64_t Q, int
  */
 int pointops_ball_query(const float *query, const float *ref, int64_t B, int64_t Q, int64_t P,
                         float radius, int64_t K, float *out_dist2, int64_t *out_idx,
-                        void *stream);
+                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Ball Query backward: gradients of L through the returned squared distances.
@@ -301,7 +312,7 @@ const char *pointops_status_string(int status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char *pointops_last_error(void);
 
-/* Library ABI version: 1. */
+/* Library ABI version: 2. */
 int pointops_abi_version(void);
 
 #ifdef __cplusplus

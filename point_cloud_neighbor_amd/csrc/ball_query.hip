@@ -143,4 +143,218 @@ hipError_t launch_ball_query(const float* query, const float* ref, int64_t B, in
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- culled scan
+//
+// For spatially ordered references (consecutive indices close in space) most
+// 64-reference blocks lie far from a query. A block's bounding box gives a
+// lower bound of s32 over its points that never exceeds the true value:
+// per axis the gap g = max(lo - q, q - hi, 0) is computed with the same
+// float32 subtraction as the distance, and rounding is monotone, so
+// |fl(q - x)| >= fl(gap) for every x of the block; squaring and the two
+// additions, in the order of s32, are monotone too. A block whose bound is
+// >= R2 therefore holds no reference with s32 < R2 and is skipped; the
+// remaining blocks are scanned in increasing order exactly as before, so the
+// first K hits, their order and their bits do not change.
+//
+// The test is made first once per block for the wave's whole group of
+// queries: the gap between the block's box and the box of the group's queries
+// bounds the gap of every (query, point) pair the same way (lo_b - hi_q <=
+// x - q), so a block is skipped for the group when even that bound reaches
+// R2. Only in the runs of 64 blocks where some block survives does each query
+// test the blocks on its own, and a block is then scanned for the queries
+// whose own test it passed.
+
+constexpr int kBoxFloats = 8;  // min x, y, z, max x, y, z, 2 unused
+
+__device__ __forceinline__ float wave_min_f32(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o /= 2) v = fminf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o /= 2) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// One wave per block of 64 references: box[(b * nblk + k) * 8 + 0..5].
+__global__ __launch_bounds__(256) void ball_query_boxes_kernel(const float* __restrict__ ref,
+                                                               int64_t B, int P, int nblk,
+                                                               float* __restrict__ box) {
+    const int64_t w = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (w >= B * nblk) return;  // whole waves leave together
+    const int64_t b = w / nblk;
+    const int k = (int)(w - b * nblk);
+    const int j = k * kWave + lane;
+    const float inf = __builtin_inff();
+    float x = inf, y = inf, z = inf, X = -inf, Y = -inf, Z = -inf;
+    if (j < P) {
+        const float* p = ref + ((size_t)b * P + j) * 3;
+        x = X = p[0];
+        y = Y = p[1];
+        z = Z = p[2];
+    }
+    x = wave_min_f32(x); y = wave_min_f32(y); z = wave_min_f32(z);
+    X = wave_max_f32(X); Y = wave_max_f32(Y); Z = wave_max_f32(Z);
+    if (lane == 0) {
+        float* o = box + (size_t)w * kBoxFloats;
+        o[0] = x; o[1] = y; o[2] = z; o[3] = X; o[4] = Y; o[5] = Z;
+    }
+}
+
+template <int QW>
+__global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
+    const float* __restrict__ query, const float* __restrict__ ref, int Q, int P, float r2,
+    int K, float* __restrict__ out_d2, int64_t* __restrict__ out_idx,
+    const float* __restrict__ box, int nblk) {
+    const int b = blockIdx.y;
+    const int row0 = blockIdx.x * QW;
+    const int lane = threadIdx.x;
+    const float* qb = query + (size_t)b * Q * 3;
+    const float* xb = ref + (size_t)b * P * 3;
+    const float* bb = box + (size_t)b * nblk * kBoxFloats;
+    const size_t out0 = ((size_t)b * Q + row0) * (size_t)K;
+
+    float qx[QW], qy[QW], qz[QW];
+    int cnt[QW];
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+        const int row = row0 + i < Q ? row0 + i : Q - 1;
+        qx[i] = qb[(size_t)3 * row + 0];
+        qy[i] = qb[(size_t)3 * row + 1];
+        qz[i] = qb[(size_t)3 * row + 2];
+        cnt[i] = row0 + i < Q ? 0 : K;
+    }
+    const float nan = __builtin_nanf("");
+    const float inf = __builtin_inff();
+    // the box of the group's queries (rows past Q repeat row Q - 1)
+    float gqx = qx[0], gqy = qy[0], gqz = qz[0], gQx = qx[0], gQy = qy[0], gQz = qz[0];
+#pragma unroll
+    for (int i = 1; i < QW; ++i) {
+        gqx = fminf(gqx, qx[i]); gqy = fminf(gqy, qy[i]); gqz = fminf(gqz, qz[i]);
+        gQx = fmaxf(gQx, qx[i]); gQy = fmaxf(gQy, qy[i]); gQz = fmaxf(gQz, qz[i]);
+    }
+
+    for (int c0 = 0; c0 < nblk; c0 += kWave) {
+        // lane l: block c0 + l; blocks past the end have an empty box (bound +inf)
+        const int k = c0 + lane;
+        float lx = inf, ly = inf, lz = inf, hx = -inf, hy = -inf, hz = -inf;
+        if (k < nblk) {
+            const float* o = bb + (size_t)k * kBoxFloats;
+            lx = o[0]; ly = o[1]; lz = o[2]; hx = o[3]; hy = o[4]; hz = o[5];
+        }
+        const float gx = fmaxf(fmaxf(lx - gQx, gqx - hx), 0.0f);
+        const float gy = fmaxf(fmaxf(ly - gQy, gqy - hy), 0.0f);
+        const float gz = fmaxf(fmaxf(lz - gQz, gqz - hz), 0.0f);
+        const float lb = (gx * gx + gy * gy) + gz * gz;
+        if (ballot(lb < r2) == 0) continue;
+        uint64_t want[QW];
+        uint64_t any = 0;
+#pragma unroll
+        for (int i = 0; i < QW; ++i) {
+            want[i] = 0;
+            if (cnt[i] < K) {
+                const float ex = fmaxf(fmaxf(lx - qx[i], qx[i] - hx), 0.0f);
+                const float ey = fmaxf(fmaxf(ly - qy[i], qy[i] - hy), 0.0f);
+                const float ez = fmaxf(fmaxf(lz - qz[i], qz[i] - hz), 0.0f);
+                want[i] = ballot((ex * ex + ey * ey) + ez * ez < r2);
+                any |= want[i];
+            }
+        }
+        if (any == 0) continue;
+        // candidate blocks in increasing order, the next one's load in flight
+        int cur = __builtin_ctzll(any);
+        float nx = nan, ny = nan, nz = nan;
+        {
+            const int j = (c0 + cur) * kWave + lane;
+            if (j < P) { nx = xb[(size_t)3 * j + 0]; ny = xb[(size_t)3 * j + 1]; nz = xb[(size_t)3 * j + 2]; }
+        }
+        uint64_t rest = any & (any - 1);
+        bool live = true;
+        while (true) {
+            const float x = nx, y = ny, z = nz;
+            const int blk = cur;
+            if (rest) {
+                cur = __builtin_ctzll(rest);
+                rest &= rest - 1;
+                const int j = (c0 + cur) * kWave + lane;
+                nx = ny = nz = nan;
+                if (j < P) { nx = xb[(size_t)3 * j + 0]; ny = xb[(size_t)3 * j + 1]; nz = xb[(size_t)3 * j + 2]; }
+            } else {
+                cur = -1;
+            }
+            const int j = (c0 + blk) * kWave + lane;
+            live = false;
+#pragma unroll
+            for (int i = 0; i < QW; ++i) {
+                if (cnt[i] < K && ((want[i] >> blk) & 1ull)) {
+                    const float s = s32(qx[i], qy[i], qz[i], x, y, z);
+                    const uint64_t m = ballot(s < r2);
+                    if (m) {
+                        const int slot = cnt[i] + (int)lanes_below(m);
+                        if (((m >> lane) & 1ull) && slot < K) {
+                            out_idx[out0 + (size_t)i * K + slot] = j;
+                            out_d2[out0 + (size_t)i * K + slot] = s;
+                        }
+                        cnt[i] += __popcll(m);
+                    }
+                }
+                live |= cnt[i] < K;
+            }
+            if (!live || cur < 0) break;
+        }
+        if (!live) break;
+    }
+
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+        if (row0 + i < Q) {
+            for (int slot = cnt[i] + lane; slot < K; slot += kWave) {
+                out_idx[out0 + (size_t)i * K + slot] = -1;
+                out_d2[out0 + (size_t)i * K + slot] = 0.0f;
+            }
+        }
+    }
+}
+
+size_t ball_query_box_bytes(int64_t B, int64_t P) {
+    return (size_t)B * (size_t)((P + kWave - 1) / kWave) * kBoxFloats * sizeof(float);
+}
+
+// Boxes of every 64-reference block into `box`, then the culled scan: grid
+// (ceil(Q / QW), B), one wave per group of QW queries.
+hipError_t launch_ball_query_culled(const float* query, const float* ref, int64_t B, int64_t Q,
+                                    int64_t P, float r2, int64_t K, float* out_d2,
+                                    int64_t* out_idx, int qw, float* box, hipStream_t stream) {
+    const int nblk = (int)((P + kWave - 1) / kWave);
+    if (B * nblk > 0) {
+        const int64_t waves = B * nblk;
+        hipLaunchKernelGGL(ball_query_boxes_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256),
+                           0, stream, ref, B, (int)P, nblk, box);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    dim3 block(kWave);
+    switch (qw) {
+#define POINTOPS_BQC_CASE(W)                                                                  \
+    case W: {                                                                                 \
+        dim3 grid((unsigned)((Q + W - 1) / W), (unsigned)B);                                  \
+        hipLaunchKernelGGL(ball_query_cull_kernel<W>, grid, block, 0, stream, query, ref,     \
+                           (int)Q, (int)P, r2, (int)K, out_d2, out_idx, box, nblk);           \
+        break;                                                                                \
+    }
+        POINTOPS_BQC_CASE(1)
+        POINTOPS_BQC_CASE(2)
+        POINTOPS_BQC_CASE(4)
+        POINTOPS_BQC_CASE(8)
+        POINTOPS_BQC_CASE(16)
+#undef POINTOPS_BQC_CASE
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace pointops

@@ -251,7 +251,7 @@ using namespace pointops::api;
 
 extern "C" {
 
-int pointops_abi_version(void) { return 1; }
+int pointops_abi_version(void) { return 2; }
 
 const char* pointops_status_string(int status) {
     switch (status) {
@@ -347,9 +347,13 @@ int pointops_knn(const float* query, const float* ref, int64_t B, int64_t Q, int
     return POINTOPS_OK;
 }
 
+size_t pointops_ball_query_workspace_bytes(int64_t B, int64_t P) {
+    return B <= 0 || P <= 0 ? 0 : pointops::ball_query_box_bytes(B, P);
+}
+
 int pointops_ball_query(const float* query, const float* ref, int64_t B, int64_t Q, int64_t P,
                         float radius, int64_t K, float* out_dist2, int64_t* out_idx,
-                        void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     if (B < 0 || Q < 0 || P < 0) return fail(POINTOPS_INVALID_ARGUMENT, "negative size");
     if (!(radius > 0.0f) || std::isinf(radius))
@@ -368,8 +372,15 @@ int pointops_ball_query(const float* query, const float* ref, int64_t B, int64_t
     volatile float r32 = radius;
     const float r2 = r32 * r32;
     const int qw = bq_queries_per_wave(B * Q, dev->cus, 8);
-    hipError_t e = pointops::launch_ball_query(query, ref, B, Q, P, r2, K, out_dist2, out_idx,
-                                               qw, nullptr, 0, 0, (hipStream_t)stream);
+    const size_t need = pointops::ball_query_box_bytes(B, P);
+    if (workspace && workspace_bytes < need)
+        return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
+                    workspace_bytes, need);
+    hipError_t e = workspace && P > 0
+        ? pointops::launch_ball_query_culled(query, ref, B, Q, P, r2, K, out_dist2, out_idx, qw,
+                                             (float*)workspace, (hipStream_t)stream)
+        : pointops::launch_ball_query(query, ref, B, Q, P, r2, K, out_dist2, out_idx, qw, nullptr,
+                                      0, 0, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "ball_query launch");
     return POINTOPS_OK;
 }

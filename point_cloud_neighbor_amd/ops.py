@@ -52,7 +52,10 @@ def _load():
         lib.pointops_fps_workspace_bytes.restype = ctypes.c_size_t
         lib.pointops_knn.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp]
         lib.pointops_knn.restype = ctypes.c_int
-        lib.pointops_ball_query.argtypes = [vp, vp, i64, i64, i64, f32, i64, vp, vp, vp]
+        lib.pointops_ball_query.argtypes = [vp, vp, i64, i64, i64, f32, i64, vp, vp, vp,
+                                            ctypes.c_size_t, vp]
+        lib.pointops_ball_query_workspace_bytes.argtypes = [i64, i64]
+        lib.pointops_ball_query_workspace_bytes.restype = ctypes.c_size_t
         lib.pointops_ball_query.restype = ctypes.c_int
         lib.pointops_ball_query_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp,
                                                      vp]
@@ -162,21 +165,24 @@ def knn(query: torch.Tensor, ref: torch.Tensor, k: int):
     return dist, idx
 
 
-def ball_query(query: torch.Tensor, ref: torch.Tensor, radius: float, K: int):
+def ball_query(query: torch.Tensor, ref: torch.Tensor, radius: float, K: int,
+               cull: bool = True):
     """First K references within ``radius`` in input order -> (squared distance
     float32, int64 index with -1 padding), (B, Q, K). ``radius`` is rounded to
     float32 first (the threshold is fl32(fl32(r) * fl32(r))).
 
     When grad mode is on and ``query`` or ``ref`` requires grad, the squared
     distances are differentiable with respect to both coordinate tensors (the
-    backward runs ``ball_query_backward``); the indices are not."""
+    backward runs ``ball_query_backward``); the indices are not. ``cull`` lets
+    the call skip reference blocks whose bounding box is out of reach (same
+    results; faster on spatially sorted references)."""
     if torch.is_grad_enabled() and (getattr(query, "requires_grad", False)
                                     or getattr(ref, "requires_grad", False)):
-        return _BallQueryFn.apply(query, ref, radius, K)
-    return _ball_query(query, ref, radius, K)
+        return _BallQueryFn.apply(query, ref, radius, K, cull)
+    return _ball_query(query, ref, radius, K, cull)
 
 
-def _ball_query(query: torch.Tensor, ref: torch.Tensor, radius: float, K: int):
+def _ball_query(query: torch.Tensor, ref: torch.Tensor, radius: float, K: int, cull: bool):
     lib = _load()
     query = _points(query, "query")
     ref = _points(ref, "ref")
@@ -187,9 +193,12 @@ def _ball_query(query: torch.Tensor, ref: torch.Tensor, radius: float, K: int):
     with torch.cuda.device(query.device):
         d2 = torch.empty((B, Q, K), dtype=torch.float32, device=query.device)
         idx = torch.empty((B, Q, K), dtype=torch.int64, device=query.device)
+        nbytes = int(lib.pointops_ball_query_workspace_bytes(B, P)) if cull else 0
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=query.device) if nbytes else None
         rc = lib.pointops_ball_query(query.data_ptr(), ref.data_ptr(), B, Q, P,
                                      ctypes.c_float(float(radius)), int(K), d2.data_ptr(),
-                                     idx.data_ptr(), _stream(query.device))
+                                     idx.data_ptr(), ws.data_ptr() if ws is not None else None,
+                                     nbytes, _stream(query.device))
         _check(rc)
     return d2, idx
 
@@ -231,8 +240,8 @@ def ball_query_backward(query: torch.Tensor, ref: torch.Tensor, idx: torch.Tenso
 
 class _BallQueryFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, query, ref, radius, K):
-        d2, idx = _ball_query(query, ref, radius, K)
+    def forward(ctx, query, ref, radius, K, cull):
+        d2, idx = _ball_query(query, ref, radius, K, cull)
         ctx.save_for_backward(query, ref, idx)
         ctx.mark_non_differentiable(idx)
         return d2, idx
@@ -244,7 +253,7 @@ class _BallQueryFn(torch.autograd.Function):
             return None, None, None, None
         gq, gx = ball_query_backward(query, ref, idx, grad_d2, ctx.needs_input_grad[0],
                                      ctx.needs_input_grad[1])
-        return gq, gx, None, None
+        return gq, gx, None, None, None
 
 
 # ------------------------------------------------------------------ ragged batches

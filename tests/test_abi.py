@@ -31,7 +31,8 @@ def lib():
     i64, vp, f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
     lib.pointops_fps.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, ctypes.c_size_t, vp]
     lib.pointops_knn.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp]
-    lib.pointops_ball_query.argtypes = [vp, vp, i64, i64, i64, f32, i64, vp, vp, vp]
+    lib.pointops_ball_query.argtypes = [vp, vp, i64, i64, i64, f32, i64, vp, vp, vp,
+                                        ctypes.c_size_t, vp]
     lib.pointops_status_string.restype = ctypes.c_char_p
     lib.pointops_last_error.restype = ctypes.c_char_p
     return lib
@@ -51,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pointops_abi_version() == 1
+    assert lib.pointops_abi_version() == 2
     for code in range(5):
         assert lib.pointops_status_string(code)
     assert lib.pointops_status_string(99) == b"unknown status"
@@ -87,10 +88,12 @@ def test_knn_argument_checks(lib):
 
 def test_ball_query_argument_checks(lib):
     for r in (0.0, -1.0, float("nan"), float("inf")):
-        assert lib.pointops_ball_query(FAKE, FAKE, 1, 4, 10, r, 3, FAKE, FAKE, None) == INVALID
-    assert lib.pointops_ball_query(FAKE, FAKE, 1, 4, 10, 0.5, 0, FAKE, FAKE, None) == INVALID
-    assert lib.pointops_ball_query(None, None, 0, 4, 10, 0.5, 3, None, None, None) == OK
-    assert lib.pointops_ball_query(None, None, 3, 0, 10, 0.5, 3, None, None, None) == OK
+        assert lib.pointops_ball_query(FAKE, FAKE, 1, 4, 10, r, 3, FAKE, FAKE, None, 0,
+                                       None) == INVALID
+    assert lib.pointops_ball_query(FAKE, FAKE, 1, 4, 10, 0.5, 0, FAKE, FAKE, None, 0,
+                                   None) == INVALID
+    assert lib.pointops_ball_query(None, None, 0, 4, 10, 0.5, 3, None, None, None, 0, None) == OK
+    assert lib.pointops_ball_query(None, None, 3, 0, 10, 0.5, 3, None, None, None, 0, None) == OK
 
 
 def test_no_gpu_means_an_error_not_a_fallback(lib):

@@ -35,10 +35,12 @@ def check_knn(gpu, oracle_mod, q, x, k, what=""):
 
 
 def check_bq(gpu, oracle_mod, q, x, r, K, what=""):
-    d2, i = gpu.ball_query(dev(q), dev(x), r, K)
+    """Both scans: with the bounding-box culling (the default) and without."""
     wd, wi = oracle_mod.ball_query(q, x, r, K, threads=8)
-    assert_idx_equal(host(i), wi, f"bq idx {what}")
-    assert_dist_close(host(d2), wd, f"bq dist2 {what}")
+    for cull in (True, False):
+        d2, i = gpu.ball_query(dev(q), dev(x), r, K, cull=cull)
+        assert_idx_equal(host(i), wi, f"bq idx {what} cull={cull}")
+        assert_dist_close(host(d2), wd, f"bq dist2 {what} cull={cull}")
 
 
 # ------------------------------------------------------------------ the pages' example
@@ -177,6 +179,29 @@ def test_ball_query_queries_per_wave(gpu, oracle_mod, qw, monkeypatch):
     check_bq(gpu, oracle_mod, x[:, :77].copy(), x, 0.12, 40, f"qw={qw}")
 
 
+@pytest.mark.parametrize("case", ["dyadic", "planted", "uniform"])
+def test_ball_query_culling_on_sorted_clouds(gpu, oracle_mod, case):
+    """Morton-sorted clouds, where the bounding-box test skips most blocks:
+    dyadic coordinates put many block bounds and distances exactly on R2, the
+    planted cloud has pairs at prev(R2), R2 and next(R2)."""
+    if case == "dyadic":
+        raw = W.integer_cloud(31, 1, 6000, 0, 8)[0] / np.float32(8)
+        x = raw[W.morton_order(raw)][None].copy()
+        r = 0.25                                  # R2 = 1/16 exactly
+        q = np.concatenate([x[:, ::7], x[:, 5:400]], axis=1)
+    elif case == "planted":
+        x = W.sorted_bq_cloud(32, N=8000, n_anchor=40)
+        r = 0.05
+        q = x.copy()
+    else:
+        raw = W.uniform_cube(33, 1, 20000)[0]
+        x = raw[W.morton_order(raw)][None].copy()
+        r = 0.03
+        q = W.uniform_cube(34, 1, 700)
+    for K in (1, 16, 64, 200):
+        check_bq(gpu, oracle_mod, q, x, r, K, f"sorted {case} K={K}")
+
+
 def test_ball_query_planted_boundary(gpu, oracle_mod):
     rng = np.random.default_rng(3)
     xyz = (np.round(rng.random((400, 3)) * 64) / 64).astype(np.float32)
@@ -229,12 +254,20 @@ def test_every_output_slot_written(gpu):
     x = dev(W.uniform_cube(21, 2, 3000))
     q = x[:, :150].contiguous()
     s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    wsb = torch.empty(lib.pointops_ball_query_workspace_bytes(2, 3000), dtype=torch.uint8,
+                      device="cuda")
     for K in (1, 33, 100):
-        d2 = torch.full((2, 150, K), float("nan"), device="cuda")
-        ix = torch.full((2, 150, K), -2, dtype=torch.int64, device="cuda")
-        assert lib.pointops_ball_query(q.data_ptr(), x.data_ptr(), 2, 150, 3000,
-                                       ctypes.c_float(0.1), K, d2.data_ptr(), ix.data_ptr(), s) == 0
-        assert not torch.isnan(d2).any() and not (ix == -2).any()
+        for ws in (None, wsb):
+            d2 = torch.full((2, 150, K), float("nan"), device="cuda")
+            ix = torch.full((2, 150, K), -2, dtype=torch.int64, device="cuda")
+            assert lib.pointops_ball_query(q.data_ptr(), x.data_ptr(), 2, 150, 3000,
+                                           ctypes.c_float(0.1), K, d2.data_ptr(), ix.data_ptr(),
+                                           None if ws is None else ws.data_ptr(),
+                                           0 if ws is None else ws.numel(), s) == 0
+            assert not torch.isnan(d2).any() and not (ix == -2).any()
+    # a workspace that is too small is an error, not a silent fallback
+    assert lib.pointops_ball_query(q.data_ptr(), x.data_ptr(), 2, 150, 3000, ctypes.c_float(0.1),
+                                   4, d2.data_ptr(), ix.data_ptr(), wsb.data_ptr(), 16, s) == 1
     d = torch.full((2, 150, 20), float("nan"), device="cuda")
     ix = torch.full((2, 150, 20), -2, dtype=torch.int64, device="cuda")
     assert lib.pointops_knn(q.data_ptr(), x.data_ptr(), 2, 150, 3000, 20, d.data_ptr(),
