@@ -92,6 +92,13 @@ size_t pointops_fps_workspace_bytes(int64_t B, int64_t N, int64_t M);
  * "Numerical contracts" page, section "Selection and output".
  *   For every query i of cloud b: sort the references j by (s32(q_i, x_j), j),
  *   keep the first k; out_idx = j, out_dist = sqrtf(s32) correctly rounded.
+ * With a workspace of pointops_knn_workspace_bytes(B, Q, P) bytes (when that
+ * is not 0) the call counting-sorts references and queries into a uniform
+ * grid, bounds every 64 sorted references by a box, and visits near boxes
+ * first, skipping a box when the lower bound of s32 over it (taken in the
+ * float32 order of s32, so never above it) exceeds a query's current k-th
+ * distance. Results are identical, bit for bit; workspace NULL scans every
+ * reference. A non-NULL workspace smaller than needed is INVALID_ARGUMENT.
  *
  *   query     (B, Q, 3) float32, device.      ref (B, P, 3) float32, device.
  *   k         1 <= k <= P (INVALID_ARGUMENT otherwise) and
@@ -100,7 +107,12 @@ size_t pointops_fps_workspace_bytes(int64_t B, int64_t N, int64_t M);
  *   B == 0 or Q == 0 is a no-op.
  */
 int pointops_knn(const float *query, const float *ref, int64_t B, int64_t Q, int64_t P,
-                 int64_t k, float *out_dist, int64_t *out_idx, void *stream);
+                 int64_t k, float *out_dist, int64_t *out_idx, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace that lets pointops_knn sort the clouds into a grid
+ * and skip far references (0 when that path is not used for this shape). */
+size_t pointops_knn_workspace_bytes(int64_t B, int64_t Q, int64_t P);
 
 /* Bytes of device workspace that lets pointops_ball_query skip far blocks of
  * references (one bounding box per 64 references of each cloud, 32 bytes). */

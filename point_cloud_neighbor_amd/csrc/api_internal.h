@@ -17,6 +17,9 @@ hipError_t launch_ball_query(const float*, const float*, int64_t, int64_t, int64
 hipError_t launch_ball_query_culled(const float*, const float*, int64_t, int64_t, int64_t,
                                     float, int64_t, float*, int64_t*, int, float*, hipStream_t);
 size_t ball_query_box_bytes(int64_t B, int64_t P);
+hipError_t launch_knn_grid(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
+                           int64_t*, int, int, void*, hipStream_t);
+size_t knn_grid_workspace_bytes(int64_t B, int64_t Q, int64_t P);
 hipError_t launch_fps(const float*, int64_t, int64_t, int64_t, int64_t, int64_t*, float*, void*,
                       int, int, int, uint32_t, hipStream_t, const int64_t*, int, int64_t);
 hipError_t launch_fps_clear(void*, size_t, hipStream_t);

@@ -128,7 +128,7 @@ int pointops_three_nn(const float* unknown, const float* known, int64_t B, int64
     if (m < 3 && B > 0 && n > 0)
         return fail(POINTOPS_INVALID_ARGUMENT, "three_nn needs at least 3 known points, got %lld",
                     (long long)m);
-    return pointops_knn(unknown, known, B, n, m, 3, out_dist, out_idx, stream);
+    return pointops_knn(unknown, known, B, n, m, 3, out_dist, out_idx, nullptr, 0, stream);
 }
 
 size_t pointops_chamfer_workspace_bytes(int64_t B) {

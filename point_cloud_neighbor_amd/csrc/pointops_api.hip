@@ -319,8 +319,23 @@ int pointops_fps(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t star
     return POINTOPS_OK;
 }
 
+// kNN takes the grid path (sort, boxes, culled search) when the references
+// are many enough for the sort to pay: at least 8192 per cloud and 2^27
+// query-reference pairs in all. POINTOPS_KNN_GRID=0 / 1 forces either path.
+static bool knn_use_grid(int64_t B, int64_t Q, int64_t P) {
+    const long env = env_long("POINTOPS_KNN_GRID", -1);
+    if (env == 0 || env == 1) return env == 1 && P >= 1;
+    return P >= 8192 && B * Q * P >= ((int64_t)1 << 27);
+}
+
+size_t pointops_knn_workspace_bytes(int64_t B, int64_t Q, int64_t P) {
+    if (B <= 0 || Q <= 0 || P <= 0 || !knn_use_grid(B, Q, P)) return 0;
+    return pointops::knn_grid_workspace_bytes(B, Q, P);
+}
+
 int pointops_knn(const float* query, const float* ref, int64_t B, int64_t Q, int64_t P,
-                 int64_t k, float* out_dist, int64_t* out_idx, void* stream) {
+                 int64_t k, float* out_dist, int64_t* out_idx, void* workspace,
+                 size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     if (B < 0 || Q < 0 || P < 0) return fail(POINTOPS_INVALID_ARGUMENT, "negative size");
     if (k < 1 || k > P)
@@ -339,6 +354,17 @@ int pointops_knn(const float* query, const float* ref, int64_t B, int64_t Q, int
     if (st != POINTOPS_OK) return st;
     int kcap = 1;
     while (kcap < k) kcap *= 2;
+    if (workspace && knn_use_grid(B, Q, P)) {
+        const size_t need = pointops::knn_grid_workspace_bytes(B, Q, P);
+        if (workspace_bytes < need)
+            return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
+                        workspace_bytes, need);
+        hipError_t e = pointops::launch_knn_grid(query, ref, B, Q, P, k, out_dist, out_idx, kcap,
+                                                 kcap >= 64 ? 2 : 4, workspace,
+                                                 (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "knn launch");
+        return POINTOPS_OK;
+    }
     const int64_t tiles = B * ((Q + 63) / 64);
     hipError_t e = pointops::launch_knn(query, ref, B, Q, P, k, out_dist, out_idx, kcap,
                                         knn_waves(kcap, tiles, dev->cus), nullptr, 0, 0, 0,

@@ -50,7 +50,10 @@ def _load():
         lib.pointops_fps.restype = ctypes.c_int
         lib.pointops_fps_workspace_bytes.argtypes = [i64, i64, i64]
         lib.pointops_fps_workspace_bytes.restype = ctypes.c_size_t
-        lib.pointops_knn.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp]
+        lib.pointops_knn.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp, ctypes.c_size_t,
+                                     vp]
+        lib.pointops_knn_workspace_bytes.argtypes = [i64, i64, i64]
+        lib.pointops_knn_workspace_bytes.restype = ctypes.c_size_t
         lib.pointops_knn.restype = ctypes.c_int
         lib.pointops_ball_query.argtypes = [vp, vp, i64, i64, i64, f32, i64, vp, vp, vp,
                                             ctypes.c_size_t, vp]
@@ -147,8 +150,10 @@ def furthest_point_sample(xyz: torch.Tensor, npoint: int, start_idx: int = 0,
     return (out, oxyz) if return_xyz else out
 
 
-def knn(query: torch.Tensor, ref: torch.Tensor, k: int):
-    """k nearest neighbours -> (Euclidean distance float32, int64 index), (B, Q, k)."""
+def knn(query: torch.Tensor, ref: torch.Tensor, k: int, grid: bool = True):
+    """k nearest neighbours -> (Euclidean distance float32, int64 index), (B, Q, k).
+    ``grid`` lets large calls sort the clouds into a grid and skip far
+    references (same results)."""
     lib = _load()
     query = _points(query, "query")
     ref = _points(ref, "ref")
@@ -159,8 +164,11 @@ def knn(query: torch.Tensor, ref: torch.Tensor, k: int):
     with torch.cuda.device(query.device):
         dist = torch.empty((B, Q, k), dtype=torch.float32, device=query.device)
         idx = torch.empty((B, Q, k), dtype=torch.int64, device=query.device)
+        nbytes = int(lib.pointops_knn_workspace_bytes(B, Q, P)) if grid else 0
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=query.device) if nbytes else None
         rc = lib.pointops_knn(query.data_ptr(), ref.data_ptr(), B, Q, P, int(k), dist.data_ptr(),
-                              idx.data_ptr(), _stream(query.device))
+                              idx.data_ptr(), ws.data_ptr() if ws is not None else None, nbytes,
+                              _stream(query.device))
         _check(rc)
     return dist, idx
 

@@ -30,7 +30,7 @@ def lib():
     lib = ctypes.CDLL(LIB)
     i64, vp, f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
     lib.pointops_fps.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, ctypes.c_size_t, vp]
-    lib.pointops_knn.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp]
+    lib.pointops_knn.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp, ctypes.c_size_t, vp]
     lib.pointops_ball_query.argtypes = [vp, vp, i64, i64, i64, f32, i64, vp, vp, vp,
                                         ctypes.c_size_t, vp]
     lib.pointops_status_string.restype = ctypes.c_char_p
@@ -77,13 +77,13 @@ def test_fps_argument_checks(lib):
 
 
 def test_knn_argument_checks(lib):
-    assert lib.pointops_knn(FAKE, FAKE, 1, 4, 10, 11, FAKE, FAKE, None) == INVALID  # k > P
-    assert lib.pointops_knn(FAKE, FAKE, 1, 4, 10, 0, FAKE, FAKE, None) == INVALID   # k < 1
-    assert lib.pointops_knn(FAKE, FAKE, 1, 4, 100, 65, FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.pointops_knn(FAKE, FAKE, 1, 4, 10, 11, FAKE, FAKE, None, 0, None) == INVALID  # k > P
+    assert lib.pointops_knn(FAKE, FAKE, 1, 4, 10, 0, FAKE, FAKE, None, 0, None) == INVALID   # k < 1
+    assert lib.pointops_knn(FAKE, FAKE, 1, 4, 100, 65, FAKE, FAKE, None, 0, None) == UNSUPPORTED
     assert b"KMAX" in lib.pointops_last_error()
-    assert lib.pointops_knn(None, None, 0, 4, 10, 3, None, None, None) == OK        # B == 0
-    assert lib.pointops_knn(None, None, 2, 0, 10, 3, None, None, None) == OK        # Q == 0
-    assert lib.pointops_knn(FAKE, FAKE, 70000, 4, 10, 3, FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.pointops_knn(None, None, 0, 4, 10, 3, None, None, None, 0, None) == OK        # B == 0
+    assert lib.pointops_knn(None, None, 2, 0, 10, 3, None, None, None, 0, None) == OK        # Q == 0
+    assert lib.pointops_knn(FAKE, FAKE, 70000, 4, 10, 3, FAKE, FAKE, None, 0, None) == UNSUPPORTED
 
 
 def test_ball_query_argument_checks(lib):
@@ -103,7 +103,7 @@ def test_no_gpu_means_an_error_not_a_fallback(lib):
         pytest.skip("a GPU is visible; covered by the GPU tests")
     st = lib.pointops_device_check(0)
     assert st in (UNSUPPORTED_DEVICE, HIP_ERROR)
-    st = lib.pointops_knn(FAKE, FAKE, 1, 4, 10, 3, FAKE, FAKE, None)
+    st = lib.pointops_knn(FAKE, FAKE, 1, 4, 10, 3, FAKE, FAKE, None, 0, None)
     assert st in (UNSUPPORTED_DEVICE, HIP_ERROR)
 
 

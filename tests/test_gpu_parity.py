@@ -28,10 +28,21 @@ def check_fps(gpu, oracle_mod, xyz, M, start=0, what=""):
 
 
 def check_knn(gpu, oracle_mod, q, x, k, what=""):
-    d, i = gpu.knn(dev(q), dev(x), k)
+    """Both searches: the full scan and the grid search (forced on, whatever
+    the size)."""
     wd, wi = oracle_mod.knn(q, x, k, threads=8)
-    assert_idx_equal(host(i), wi, f"knn idx {what}")
-    assert_dist_close(host(d), wd, f"knn dist {what}")
+    for grid in (False, True):
+        old = os.environ.get("POINTOPS_KNN_GRID")
+        os.environ["POINTOPS_KNN_GRID"] = "1" if grid else "0"
+        try:
+            d, i = gpu.knn(dev(q), dev(x), k)
+        finally:
+            if old is None:
+                del os.environ["POINTOPS_KNN_GRID"]
+            else:
+                os.environ["POINTOPS_KNN_GRID"] = old
+        assert_idx_equal(host(i), wi, f"knn idx {what} grid={grid}")
+        assert_dist_close(host(d), wd, f"knn dist {what} grid={grid}")
 
 
 def check_bq(gpu, oracle_mod, q, x, r, K, what=""):
@@ -154,6 +165,34 @@ def test_knn_shapes(gpu, oracle_mod, Q, P, k):
     check_knn(gpu, oracle_mod, q, x, k, f"Q={Q} P={P} k={k}")
 
 
+@pytest.mark.parametrize("case", ["clustered", "outside", "identical", "sorted", "lines"])
+def test_knn_grid_search_cases(gpu, oracle_mod, case):
+    """Clouds that stress the grid search: dense clusters with exact
+    duplicates, queries far outside the references' box (clamped cells), a
+    cloud of identical points (one cell, all ties), references already in
+    grid order, and points on a few lines (many equal distances)."""
+    if case == "clustered":
+        x = W.clustered_cloud(41, N=20000, n_clusters=5, sigma=0.01, dup_frac=0.05)
+        q = np.concatenate([x[:, :300], W.uniform_cube(42, 1, 200)], axis=1)
+    elif case == "outside":
+        x = W.uniform_cube(43, 2, 9000)
+        q = (W.uniform_cube(44, 2, 400) * np.float32(5.0) - np.float32(2.0)).astype(np.float32)
+    elif case == "identical":
+        x = np.full((1, 5000, 3), 0.25, dtype=np.float32)
+        q = np.concatenate([x[:, :10], W.uniform_cube(45, 1, 60)], axis=1)
+    elif case == "sorted":
+        raw = W.uniform_cube(46, 1, 30000)[0]
+        x = raw[W.morton_order(raw)][None].copy()
+        q = x[:, ::37].copy()
+    else:
+        t = W.integer_cloud(47, 1, 12000, 0, 64).astype(np.float32)
+        t[..., 1:] = np.floor(t[..., 1:] / 32) * 32      # 4 lines per axis pair
+        x = t
+        q = x[:, ::29].copy()
+    for k in (1, 16, 33, 64):
+        check_knn(gpu, oracle_mod, q, x, k, f"{case} k={k}")
+
+
 @pytest.mark.parametrize("env", ["1", "2", "4", "8"])
 @pytest.mark.parametrize("k", [5, 16, 32])
 def test_knn_wave_split_agrees(gpu, oracle_mod, env, k, monkeypatch):
@@ -271,7 +310,7 @@ def test_every_output_slot_written(gpu):
     d = torch.full((2, 150, 20), float("nan"), device="cuda")
     ix = torch.full((2, 150, 20), -2, dtype=torch.int64, device="cuda")
     assert lib.pointops_knn(q.data_ptr(), x.data_ptr(), 2, 150, 3000, 20, d.data_ptr(),
-                            ix.data_ptr(), s) == 0
+                            ix.data_ptr(), None, 0, s) == 0
     assert not torch.isnan(d).any() and not (ix < 0).any()
     ws = torch.empty(lib.pointops_fps_workspace_bytes(2, 3000, 64), dtype=torch.uint8, device="cuda")
     o = torch.full((2, 64), -2, dtype=torch.int64, device="cuda")
