@@ -13,14 +13,16 @@
 //    Morton code of a uniform grid cell (2^L cells per axis over the
 //    references' bounding box). The cell formula only decides the order; no
 //    result depends on it.
-// 2. Boxes. Every 64 consecutive sorted references form a block with its
+// 2. Boxes. Every 16 consecutive sorted references form a block with its
 //    bounding box, every 64 blocks a superblock with the union box.
 // 3. Search. A workgroup holds 64 sorted queries (one per lane) and NW waves.
-//    The waves first scan the blocks around the group's own grid position
-//    (seeding each lane's list with near neighbours), then test every
-//    superblock and, inside a surviving one, every block: a lane needs a box
-//    only if the box's lower bound of s32 does not exceed the lane's current
-//    k-th distance. The bound is computed from the per-axis gaps with the
+//    Wave 0 first inserts, for every lane, the 64 references around the
+//    lane's own grid position in sorted order (most of its k nearest are
+//    there), so each lane's limit is tight before any box is tested. The
+//    waves then test every superblock and,
+//    inside a surviving one, every block: a lane needs a box only if the
+//    box's lower bound of s32 does not exceed the lane's current k-th
+//    distance. The bound is computed from the per-axis gaps with the
 //    float32 operations of s32; rounding is monotone, so it never exceeds the
 //    s32 of any point in the box, and a box is skipped only when no point in
 //    it could enter the final list. Keys are 64-bit, (bits(s) + 1) << 32 |
@@ -33,7 +35,9 @@
 
 namespace pointops {
 
-constexpr int kGridBuf = 16;  // candidate slots per lane (>= 8 + 1)
+constexpr int kGridBuf = 16;    // candidate slots per lane; at most 8 in use between groups of 8
+constexpr int kGridBlk = 16;    // references per block (per box)
+constexpr int kGridLocal = 64;  // references around each query's own position, scanned first
 
 // ------------------------------------------------------------------ grid build
 
@@ -63,46 +67,61 @@ __device__ __forceinline__ uint32_t cell_code(const GridParams& g, float x, floa
     return spread3((uint32_t)cx) | (spread3((uint32_t)cy) << 1) | (spread3((uint32_t)cz) << 2);
 }
 
-// One workgroup per cloud: the references' bounding box -> cell mapping.
-__global__ __launch_bounds__(256) void grid_bounds_kernel(const float* __restrict__ ref, int P,
-                                                          int L, GridParams* __restrict__ gp) {
-    __shared__ float sh[6][256];
-    const int b = blockIdx.x;
+// The references' bounding box, in three launches: slots set to the empty box,
+// many workgroups folding their points in with integer atomics on an order-
+// preserving encoding of the floats, then the cell mapping per cloud.
+__device__ __forceinline__ uint32_t ord_enc(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // unsigned order = float order
+}
+
+__device__ __forceinline__ float ord_dec(uint32_t e) {
+    return __uint_as_float((e & 0x80000000u) ? (e & 0x7FFFFFFFu) : ~e);
+}
+
+__global__ void grid_bounds_init_kernel(uint32_t* __restrict__ enc, int64_t B) {
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i < B * 6) enc[i] = (i % 6) < 3 ? 0xFFFFFFFFu : 0u;  // min slots high, max slots low
+}
+
+__global__ __launch_bounds__(256) void grid_bounds_kernel(const float* __restrict__ ref, int64_t B,
+                                                          int P, uint32_t* __restrict__ enc) {
+    __shared__ uint32_t sh[6];
+    const int b = blockIdx.y;
     const float* xb = ref + (size_t)b * P * 3;
-    const float inf = __builtin_inff();
-    float mn[3] = {inf, inf, inf}, mx[3] = {-inf, -inf, -inf};
-    for (int j = threadIdx.x; j < P; j += 256)
+    if (threadIdx.x < 6) sh[threadIdx.x] = threadIdx.x < 3 ? 0xFFFFFFFFu : 0u;
+    __syncthreads();
+    uint32_t mn[3] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu}, mx[3] = {0u, 0u, 0u};
+    for (int j = blockIdx.x * 256 + threadIdx.x; j < P; j += gridDim.x * 256)
 #pragma unroll
         for (int d = 0; d < 3; ++d) {
-            const float v = xb[(size_t)3 * j + d];
-            mn[d] = fminf(mn[d], v);
-            mx[d] = fmaxf(mx[d], v);
+            const uint32_t v = ord_enc(xb[(size_t)3 * j + d]);
+            mn[d] = min(mn[d], v);
+            mx[d] = max(mx[d], v);
         }
 #pragma unroll
     for (int d = 0; d < 3; ++d) {
-        sh[d][threadIdx.x] = mn[d];
-        sh[3 + d][threadIdx.x] = mx[d];
+        atomicMin(&sh[d], mn[d]);
+        atomicMax(&sh[3 + d], mx[d]);
     }
     __syncthreads();
-    for (int s = 128; s >= 1; s /= 2) {
-        if ((int)threadIdx.x < s)
+    if (threadIdx.x < 3) atomicMin(&enc[b * 6 + threadIdx.x], sh[threadIdx.x]);
+    else if (threadIdx.x < 6) atomicMax(&enc[b * 6 + threadIdx.x], sh[threadIdx.x]);
+}
+
+__global__ void grid_params_kernel(const uint32_t* __restrict__ enc, int64_t B, int L,
+                                   GridParams* __restrict__ gp) {
+    const int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    GridParams g{};
 #pragma unroll
-            for (int d = 0; d < 3; ++d) {
-                sh[d][threadIdx.x] = fminf(sh[d][threadIdx.x], sh[d][threadIdx.x + s]);
-                sh[3 + d][threadIdx.x] = fmaxf(sh[3 + d][threadIdx.x], sh[3 + d][threadIdx.x + s]);
-            }
-        __syncthreads();
+    for (int d = 0; d < 3; ++d) {
+        const float lo = ord_dec(enc[b * 6 + d]), hi = ord_dec(enc[b * 6 + 3 + d]);
+        const float ext = hi - lo;
+        g.lo[d] = lo;
+        g.inv[d] = ext > 0.0f ? (float)(1 << L) / ext : 0.0f;
     }
-    if (threadIdx.x == 0) {
-        GridParams g{};
-#pragma unroll
-        for (int d = 0; d < 3; ++d) {
-            const float ext = sh[3 + d][0] - sh[d][0];
-            g.lo[d] = sh[d][0];
-            g.inv[d] = ext > 0.0f ? (float)(1 << L) / ext : 0.0f;
-        }
-        gp[b] = g;
-    }
+    gp[b] = g;
 }
 
 __global__ void grid_zero_kernel(uint32_t* __restrict__ p, size_t n) {
@@ -123,33 +142,71 @@ __global__ void grid_count_kernel(const float* __restrict__ pts, int64_t B, int 
     }
 }
 
-// One workgroup per cloud: exclusive scan of its C counts in place; `fill`
-// (the scatter cursors) is cleared.
-__global__ __launch_bounds__(1024) void grid_scan_kernel(uint32_t* __restrict__ cnt,
-                                                         uint32_t* __restrict__ fill, int L) {
-    __shared__ uint32_t part[1024];
+// Exclusive scan of each cloud's C counts in place, in chunks of 1024 bins:
+// first the sum of every chunk, then each chunk adds the sums before it to
+// its own scan. `fill` (the scatter cursors) is cleared on the way.
+constexpr int kScanChunk = 1024;
+
+__global__ __launch_bounds__(256) void grid_chunk_sums_kernel(const uint32_t* __restrict__ cnt,
+                                                              int L, uint32_t* __restrict__ sums) {
+    __shared__ uint32_t sh[256];
     const int64_t C = (int64_t)1 << (3 * L);
-    uint32_t* c = cnt + (int64_t)blockIdx.x * C;
-    uint32_t* f = fill + (int64_t)blockIdx.x * C;
-    const int64_t per = (C + 1023) / 1024;
-    const int64_t a = threadIdx.x * per, e = min(C, a + per);
-    uint32_t s = 0;
-    for (int64_t i = a; i < e; ++i) s += c[i];
-    part[threadIdx.x] = s;
+    const int64_t base = (int64_t)blockIdx.y * C + (int64_t)blockIdx.x * kScanChunk;
+    uint32_t v = 0;
+    for (int i = threadIdx.x; i < kScanChunk && blockIdx.x * (int64_t)kScanChunk + i < C; i += 256)
+        v += cnt[base + i];
+    sh[threadIdx.x] = v;
     __syncthreads();
-    // Hillis-Steele inclusive scan of the 1024 partial sums
-    for (int o = 1; o < 1024; o *= 2) {
-        const uint32_t v = (int)threadIdx.x >= o ? part[threadIdx.x - o] : 0u;
-        __syncthreads();
-        part[threadIdx.x] += v;
+    for (int o = 128; o >= 1; o /= 2) {
+        if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
         __syncthreads();
     }
-    uint32_t run = threadIdx.x ? part[threadIdx.x - 1] : 0u;
-    for (int64_t i = a; i < e; ++i) {
-        const uint32_t v = c[i];
-        c[i] = run;
-        f[i] = 0;
-        run += v;
+    if (threadIdx.x == 0) sums[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = sh[0];
+}
+
+__global__ __launch_bounds__(256) void grid_chunk_scan_kernel(uint32_t* __restrict__ cnt,
+                                                              uint32_t* __restrict__ fill, int L,
+                                                              const uint32_t* __restrict__ sums) {
+    __shared__ uint32_t sh[256];
+    const int64_t C = (int64_t)1 << (3 * L);
+    const int64_t base = (int64_t)blockIdx.y * C + (int64_t)blockIdx.x * kScanChunk;
+    // offset of this chunk: the sum of the chunks before it
+    uint32_t off = 0;
+    for (int i = threadIdx.x; i < (int)blockIdx.x; i += 256)
+        off += sums[(int64_t)blockIdx.y * gridDim.x + i];
+    sh[threadIdx.x] = off;
+    __syncthreads();
+    for (int o = 128; o >= 1; o /= 2) {
+        if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+        __syncthreads();
+    }
+    off = sh[0];
+    __syncthreads();
+    // four consecutive bins per thread
+    const int i0 = threadIdx.x * 4;
+    uint32_t v[4], t = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const bool in = blockIdx.x * (int64_t)kScanChunk + i0 + r < C;
+        v[r] = in ? cnt[base + i0 + r] : 0u;
+        t += v[r];
+    }
+    sh[threadIdx.x] = t;
+    __syncthreads();
+    for (int o = 1; o < 256; o *= 2) {  // inclusive scan of the thread sums
+        const uint32_t a = (int)threadIdx.x >= o ? sh[threadIdx.x - o] : 0u;
+        __syncthreads();
+        sh[threadIdx.x] += a;
+        __syncthreads();
+    }
+    uint32_t run = off + sh[threadIdx.x] - t;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (blockIdx.x * (int64_t)kScanChunk + i0 + r < C) {
+            cnt[base + i0 + r] = run;
+            fill[base + i0 + r] = 0;
+            run += v[r];
+        }
     }
 }
 
@@ -170,16 +227,17 @@ __global__ void grid_scatter_kernel(const float* __restrict__ pts, int64_t B, in
     }
 }
 
-// One wave per block of 64 sorted references: box[(b * nblk + k) * 8 + 0..5].
+// One wave per 64 sorted references, four blocks of 16: box[(b * nblk + k) * 8 + 0..5].
 __global__ __launch_bounds__(256) void grid_boxes_kernel(const float4* __restrict__ sr, int64_t B,
                                                          int P, int nblk,
                                                          float* __restrict__ box) {
+    const int64_t nw = ((int64_t)nblk + 3) / 4;  // waves per cloud
     const int64_t w = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
-    if (w >= B * nblk) return;
-    const int64_t b = w / nblk;
-    const int k = (int)(w - b * nblk);
-    const int j = k * kWave + lane;
+    if (w >= B * nw) return;
+    const int64_t b = w / nw;
+    const int k = (int)(w - b * nw) * 4 + lane / kGridBlk;  // this lane's block
+    const int j = (int)(w - b * nw) * kWave + lane;
     const float inf = __builtin_inff();
     float v[6] = {inf, inf, inf, -inf, -inf, -inf};
     if (j < P) {
@@ -189,14 +247,14 @@ __global__ __launch_bounds__(256) void grid_boxes_kernel(const float4* __restric
         v[2] = v[5] = p.z;
     }
 #pragma unroll
-    for (int o = kWave / 2; o >= 1; o /= 2)
+    for (int o = kGridBlk / 2; o >= 1; o /= 2)
 #pragma unroll
         for (int d = 0; d < 3; ++d) {
             v[d] = fminf(v[d], __shfl_xor(v[d], o));
             v[3 + d] = fmaxf(v[3 + d], __shfl_xor(v[3 + d], o));
         }
-    if (lane == 0) {
-        float* o = box + (size_t)w * 8;
+    if (lane % kGridBlk == 0 && k < nblk) {
+        float* o = box + ((size_t)b * nblk + k) * 8;
 #pragma unroll
         for (int d = 0; d < 6; ++d) o[d] = v[d];
     }
@@ -244,6 +302,14 @@ struct TopK64 {
         for (int p = 0; p < KCAP; ++p) key[p] = p < KCAP - k ? 0ull : ~0ull;
     }
 
+    // True if kk is already in the list.
+    __device__ __forceinline__ bool contains(uint64_t kk) const {
+        bool f = false;
+#pragma unroll
+        for (int p = 0; p < KCAP; ++p) f |= key[p] == kk;
+        return f;
+    }
+
     // Insert kk (~0 inserts nothing); the largest key drops out.
     __device__ __forceinline__ void insert(uint64_t kk) {
 #pragma unroll
@@ -289,10 +355,20 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
 
     TopK64<KCAP> top;
     top.init(k);
-    // a lane without a query takes nothing
-    uint32_t lim = qvalid ? 0xFFFFFFFFu : 0u;  // accept key high half u <= lim
+    uint32_t lim = qvalid ? 0xFFFFFFFFu : 0u;  // accept key high half u <= lim; none without a query
     thr[w][lane] = lim;
     int cnt = 0;
+
+    // Each lane's own neighbourhood in sorted order: the kGridLocal references
+    // around the first reference of its grid cell.
+    const int nloc = min(P, kGridLocal);
+    int loc0;
+    {
+        const int64_t C = (int64_t)1 << (3 * L);
+        const uint32_t code = cell_code(gp[b], q.x, q.y, q.z, L);
+        const int pos = (int)ref_start[(int64_t)b * C + code];
+        loc0 = max(0, min(pos - nloc / 2, P - nloc));
+    }
 
     auto flush = [&]() {
         const int rounds = wave_max_i32(cnt);
@@ -313,71 +389,131 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
             lim = min(lim, __hip_atomic_load(&thr[v][lane], __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_WORKGROUP));
     };
+    // Candidates of 8 keys u[] at sorted positions j..j+7 (per lane `jl` when
+    // the positions differ between lanes).
+    auto take8 = [&](const uint32_t (&u)[8], const int (&jl)[8]) {
+        uint32_t mn = u[0];
+#pragma unroll
+        for (int r = 1; r < 8; ++r) mn = min(mn, u[r]);
+        if (ballot(mn <= lim)) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                if (u[r] <= lim) {
+                    buf[cnt * kWave + lane] =
+                        make_uint2(u[r], (uint32_t)__float_as_int(rb[jl[r]].w));
+                    ++cnt;
+                }
+            }
+            if (ballot(cnt > kGridBuf - 8)) flush();
+        }
+    };
+    // Wave 0 skips, in later blocks, the references of the local pass (they
+    // are in its list already).
+    const bool skip_local = w == 0;
     auto scan_block = [&](int blk) {
-        const int j0 = blk * kWave, j1 = min(P, j0 + kWave);
+        const int j0 = blk * kGridBlk, j1 = min(P, j0 + kGridBlk);
         int j = j0;
         for (; j + 8 <= j1; j += 8) {
             uint32_t u[8];
+            int jl[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const float4 p = rb[j + r];
                 u[r] = f2u(s32(q.x, q.y, q.z, p.x, p.y, p.z)) + 1u;
+                if (skip_local && (uint32_t)(j + r - loc0) < (uint32_t)nloc) u[r] = 0xFFFFFFFFu;
+                jl[r] = j + r;
             }
-            uint32_t mn = u[0];
-#pragma unroll
-            for (int r = 1; r < 8; ++r) mn = min(mn, u[r]);
-            if (ballot(mn <= lim)) {
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    if (u[r] <= lim) {
-                        buf[cnt * kWave + lane] =
-                            make_uint2(u[r], (uint32_t)__float_as_int(rb[j + r].w));
-                        ++cnt;
-                    }
-                }
-                if (ballot(cnt > kGridBuf - 8)) flush();
-            }
+            take8(u, jl);
         }
         for (; j < j1; ++j) {
             const float4 p = rb[j];
+            uint32_t u = f2u(s32(q.x, q.y, q.z, p.x, p.y, p.z)) + 1u;
+            if (skip_local && (uint32_t)(j - loc0) < (uint32_t)nloc) u = 0xFFFFFFFFu;
+            if (u <= lim) {
+                buf[cnt * kWave + lane] = make_uint2(u, (uint32_t)__float_as_int(p.w));
+                ++cnt;
+            }
+            if (ballot(cnt > kGridBuf - 8)) flush();  // keep room for 8
+        }
+        // no flush here: candidates are rare once the limits are tight, and a
+        // flush costs as many insertions as the fullest lane's buffer
+    };
+
+    // 1. Local pass (wave 0): every lane's own kGridLocal references, which
+    //    hold most of its k nearest, so the limits are tight from the start.
+    if (w == 0) {
+        int r = 0;
+        for (; r + 8 <= nloc; r += 8) {
+            uint32_t u[8];
+            int jl[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                jl[t] = loc0 + r + t;
+                const float4 p = rb[jl[t]];
+                u[t] = f2u(s32(q.x, q.y, q.z, p.x, p.y, p.z)) + 1u;
+            }
+            take8(u, jl);
+        }
+        for (; r < nloc; ++r) {
+            const float4 p = rb[loc0 + r];
             const uint32_t u = f2u(s32(q.x, q.y, q.z, p.x, p.y, p.z)) + 1u;
             if (u <= lim) {
                 buf[cnt * kWave + lane] = make_uint2(u, (uint32_t)__float_as_int(p.w));
                 ++cnt;
             }
-            if (ballot(cnt >= kGridBuf)) flush();
+            if (ballot(cnt > kGridBuf - 8)) flush();  // keep room for 8
         }
         flush();
-    };
-
-    // 1. Seed: the NW blocks around the grid position of the group's first query.
-    int s0 = 0;
-    {
-        const float4 q0 = sq[(size_t)b * Q + (size_t)blockIdx.x * kWave];
-        const uint32_t code = cell_code(gp[b], q0.x, q0.y, q0.z, L);
-        const int64_t C = (int64_t)1 << (3 * L);
-        const int home = (int)min<int64_t>(ref_start[(int64_t)b * C + code] / kWave, nblk - 1);
-        s0 = max(0, min(home - NW / 2, nblk - NW));
     }
-    const int seed_end = min(nblk, s0 + NW);
-    if (s0 + w < seed_end) scan_block(s0 + w);
-    __syncthreads();
+    __syncthreads();  // every wave's limits, wave 0's local ones included, are in LDS
     refresh();
 
-    // 2. Every superblock whose box some lane still needs; inside it, the
-    //    blocks of this wave (block % NW == w) whose box some lane needs.
-    for (int s = 0; s < nsb; ++s) {
-        const float* so = sbx + (size_t)s * 8;
-        if (ballot(f2u(box_bound(so, q.x, q.y, q.z)) + 1u <= lim) == 0) continue;
-        const int first = s * kWave, end = min(nblk, first + kWave);
-        for (int blk = first + (w - first % NW + NW) % NW; blk < end; blk += NW) {
-            if (blk >= s0 && blk < seed_end) continue;
-            const float* o = bx + (size_t)blk * 8;
-            if (ballot(f2u(box_bound(o, q.x, q.y, q.z)) + 1u <= lim) == 0) continue;
-            scan_block(blk);
-            refresh();
+    // 2. Candidates first for the whole group at once, one box per lane: the
+    //    bound between a box and the box of the group's queries (no larger than
+    //    any query's bound) against the largest limit of the lanes; then each
+    //    candidate per lane. Superblocks, then the blocks of a surviving
+    //    superblock that belong to this wave (block % NW == w).
+    float gl[3] = {q.x, q.y, q.z}, gh[3] = {q.x, q.y, q.z};
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o /= 2)
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+            gl[d] = fminf(gl[d], __shfl_xor(gl[d], o));
+            gh[d] = fmaxf(gh[d], __shfl_xor(gh[d], o));
+        }
+    auto group_bound = [&](const float* __restrict__ o) {
+        const float gx = fmaxf(fmaxf(o[0] - gh[0], gl[0] - o[3]), 0.0f);
+        const float gy = fmaxf(fmaxf(o[1] - gh[1], gl[1] - o[4]), 0.0f);
+        const float gz = fmaxf(fmaxf(o[2] - gh[2], gl[2] - o[5]), 0.0f);
+        return (gx * gx + gy * gy) + gz * gz;
+    };
+    for (int sb0 = 0; sb0 < nsb; sb0 += kWave) {
+        uint32_t mlim = wave_max_u32(lim);
+        const int my_sb = sb0 + lane;
+        uint64_t cs = ballot(my_sb < nsb &&
+                             f2u(group_bound(sbx + (size_t)min(my_sb, nsb - 1) * 8)) + 1u <= mlim);
+        while (cs) {
+            const int s = sb0 + __builtin_ctzll(cs);
+            cs &= cs - 1;
+            if (ballot(f2u(box_bound(sbx + (size_t)s * 8, q.x, q.y, q.z)) + 1u <= lim) == 0)
+                continue;
+            mlim = wave_max_u32(lim);
+            const int my_blk = s * kWave + lane;
+            const bool mine = my_blk < nblk && my_blk % NW == w;
+            uint64_t cb = ballot(mine && f2u(group_bound(bx + (size_t)min(my_blk, nblk - 1) * 8)) +
+                                             1u <= mlim);
+            while (cb) {
+                const int blk = s * kWave + __builtin_ctzll(cb);
+                cb &= cb - 1;
+                if (ballot(f2u(box_bound(bx + (size_t)blk * 8, q.x, q.y, q.z)) + 1u <= lim) == 0)
+                    continue;
+                scan_block(blk);
+                refresh();
+            }
         }
     }
+
+    flush();
 
     // 3. Merge the NW lists (tree over LDS rows), then write rows in query order.
     if (NW > 1) {
@@ -393,7 +529,9 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
                 for (int p = 0; p < KCAP; ++p) {
                     const uint2 c = other[p * kWave + lane];
                     const uint64_t kk = ((uint64_t)c.y << 32) | c.x;
-                    top.insert(kk != 0ull ? kk : ~0ull);  // front sentinels insert nothing
+                    // front sentinels insert nothing, nor does a reference that
+                    // two waves both hold (the local pass and a later block)
+                    top.insert(kk != 0ull && !top.contains(kk) ? kk : ~0ull);
                 }
                 if (2 * d < NW) {
 #pragma unroll
@@ -422,14 +560,15 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
 // ------------------------------------------------------------------ host side
 
 int knn_grid_level(int64_t P) {
-    // about four references per cell, 2..7 bits per axis
+    // two to sixteen references per cell, 2..7 bits per axis (a CPU model of
+    // the scanned references at 100k uniform points favoured about 3 per cell)
     int L = 2;
-    while (L < 7 && ((int64_t)1 << (3 * (L + 1))) * 4 <= P) ++L;
+    while (L < 7 && ((int64_t)1 << (3 * (L + 1))) * 2 <= P) ++L;
     return L;
 }
 
 struct GridLayout {
-    size_t params, ref_cnt, ref_fill, q_cnt, q_fill, sref, squery, box, sbox, total;
+    size_t params, enc, sums, ref_cnt, ref_fill, q_cnt, q_fill, sref, squery, box, sbox, total;
 };
 
 static size_t al(size_t n) { return (n + 255) / 256 * 256; }
@@ -437,10 +576,12 @@ static size_t al(size_t n) { return (n + 255) / 256 * 256; }
 static GridLayout grid_layout(int64_t B, int64_t Q, int64_t P) {
     const int L = knn_grid_level(P);
     const size_t C = (size_t)1 << (3 * L);
-    const int64_t nblk = (P + kWave - 1) / kWave, nsb = (nblk + kWave - 1) / kWave;
+    const int64_t nblk = (P + kGridBlk - 1) / kGridBlk, nsb = (nblk + kWave - 1) / kWave;
     GridLayout g;
     size_t o = 0;
     g.params = o; o += al(B * sizeof(GridParams));
+    g.enc = o; o += al(B * 6 * sizeof(uint32_t));
+    g.sums = o; o += al(B * ((C + 1023) / 1024) * sizeof(uint32_t));
     g.ref_cnt = o; o += al(B * C * 4);
     g.ref_fill = o; o += al(B * C * 4);
     g.q_cnt = o; o += al(B * C * 4);
@@ -466,7 +607,7 @@ hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int6
                            void* workspace, hipStream_t stream) {
     const int L = knn_grid_level(P);
     const int64_t C = (int64_t)1 << (3 * L);
-    const int nblk = (int)((P + kWave - 1) / kWave), nsb = (nblk + kWave - 1) / kWave;
+    const int nblk = (int)((P + kGridBlk - 1) / kGridBlk), nsb = (nblk + kWave - 1) / kWave;
     const GridLayout g = grid_layout(B, Q, P);
     char* ws = (char*)workspace;
     GridParams* gp = (GridParams*)(ws + g.params);
@@ -485,8 +626,15 @@ hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int6
         e = hipGetLastError(); \
         if (e != hipSuccess) return e; \
     } while (0)
-    POINTOPS_CHECK(hipLaunchKernelGGL(grid_bounds_kernel, dim3((unsigned)B), dim3(256), 0, stream,
-                                      ref, (int)P, L, gp));
+    uint32_t* enc = (uint32_t*)(ws + g.enc);
+    POINTOPS_CHECK(hipLaunchKernelGGL(grid_bounds_init_kernel, dim3(grid_blocks(B * 6)), dim3(256),
+                                      0, stream, enc, B));
+    POINTOPS_CHECK(hipLaunchKernelGGL(grid_bounds_kernel,
+                                      dim3((unsigned)std::min<int64_t>((P + 1023) / 1024, 256),
+                                           (unsigned)B),
+                                      dim3(256), 0, stream, ref, B, (int)P, enc));
+    POINTOPS_CHECK(hipLaunchKernelGGL(grid_params_kernel, dim3(grid_blocks(B)), dim3(256), 0,
+                                      stream, enc, B, L, gp));
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_zero_kernel, dim3(grid_blocks(B * C)), dim3(256), 0,
                                       stream, rcnt, (size_t)(B * C)));
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_zero_kernel, dim3(grid_blocks(B * C)), dim3(256), 0,
@@ -495,15 +643,22 @@ hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int6
                                       stream, ref, B, (int)P, L, gp, rcnt));
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_count_kernel, dim3(grid_blocks(B * Q)), dim3(256), 0,
                                       stream, query, B, (int)Q, L, gp, qcnt));
-    POINTOPS_CHECK(hipLaunchKernelGGL(grid_scan_kernel, dim3((unsigned)B), dim3(1024), 0, stream,
-                                      rcnt, rfill, L));
-    POINTOPS_CHECK(hipLaunchKernelGGL(grid_scan_kernel, dim3((unsigned)B), dim3(1024), 0, stream,
-                                      qcnt, qfill, L));
+    const unsigned nchunk = (unsigned)((C + kScanChunk - 1) / kScanChunk);
+    uint32_t* sums = (uint32_t*)(ws + g.sums);
+    for (int side = 0; side < 2; ++side) {
+        uint32_t* c = side ? qcnt : rcnt;
+        uint32_t* f = side ? qfill : rfill;
+        POINTOPS_CHECK(hipLaunchKernelGGL(grid_chunk_sums_kernel, dim3(nchunk, (unsigned)B),
+                                          dim3(256), 0, stream, c, L, sums));
+        POINTOPS_CHECK(hipLaunchKernelGGL(grid_chunk_scan_kernel, dim3(nchunk, (unsigned)B),
+                                          dim3(256), 0, stream, c, f, L, sums));
+    }
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_scatter_kernel, dim3(grid_blocks(B * P)), dim3(256), 0,
                                       stream, ref, B, (int)P, L, gp, rcnt, rfill, sref));
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_scatter_kernel, dim3(grid_blocks(B * Q)), dim3(256), 0,
                                       stream, query, B, (int)Q, L, gp, qcnt, qfill, squery));
-    POINTOPS_CHECK(hipLaunchKernelGGL(grid_boxes_kernel, dim3((unsigned)((B * nblk + 3) / 4)),
+    const int64_t box_waves = B * ((nblk + 3) / 4);
+    POINTOPS_CHECK(hipLaunchKernelGGL(grid_boxes_kernel, dim3((unsigned)((box_waves + 3) / 4)),
                                       dim3(256), 0, stream, sref, B, (int)P, nblk, box));
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_superboxes_kernel, dim3((unsigned)((B * nsb + 3) / 4)),
                                       dim3(256), 0, stream, box, B, nblk, nsb, sbox));
@@ -522,9 +677,10 @@ hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int6
                                           sbox, nblk, nsb, rcnt, gp, L, out_dist, out_idx));   \
         return hipSuccess;                                                                     \
     }
-    POINTOPS_GRID_CASE(1, 4) POINTOPS_GRID_CASE(2, 4) POINTOPS_GRID_CASE(4, 4)
-    POINTOPS_GRID_CASE(8, 4) POINTOPS_GRID_CASE(16, 4) POINTOPS_GRID_CASE(32, 4)
+    POINTOPS_GRID_CASE(1, 2) POINTOPS_GRID_CASE(2, 2) POINTOPS_GRID_CASE(4, 2)
+    POINTOPS_GRID_CASE(8, 2) POINTOPS_GRID_CASE(16, 2) POINTOPS_GRID_CASE(32, 2)
     POINTOPS_GRID_CASE(64, 2)
+    POINTOPS_GRID_CASE(16, 1) POINTOPS_GRID_CASE(16, 4) POINTOPS_GRID_CASE(16, 8)
 #undef POINTOPS_GRID_CASE
 #undef POINTOPS_CHECK
     return hipErrorInvalidValue;

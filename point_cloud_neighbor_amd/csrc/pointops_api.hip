@@ -359,9 +359,14 @@ int pointops_knn(const float* query, const float* ref, int64_t B, int64_t Q, int
         if (workspace_bytes < need)
             return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
                         workspace_bytes, need);
+        // two waves per 64 queries: each wave keeps its own list, so more waves
+        // mean more insertions; fewer leave too few waves to hide latency
+        // (100k uniform, k=16: 0.44 / 0.33 / 0.37 / 0.49 ms for 1 / 2 / 4 / 8)
+        int gw = 2;
+        const long gw_env = env_long("POINTOPS_KNN_GRID_WAVES", 0);
+        if (kcap == 16 && (gw_env == 1 || gw_env == 2 || gw_env == 4 || gw_env == 8)) gw = (int)gw_env;
         hipError_t e = pointops::launch_knn_grid(query, ref, B, Q, P, k, out_dist, out_idx, kcap,
-                                                 kcap >= 64 ? 2 : 4, workspace,
-                                                 (hipStream_t)stream);
+                                                 gw, workspace, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, "knn launch");
         return POINTOPS_OK;
     }

@@ -193,6 +193,13 @@ def test_knn_grid_search_cases(gpu, oracle_mod, case):
         check_knn(gpu, oracle_mod, q, x, k, f"{case} k={k}")
 
 
+@pytest.mark.parametrize("waves", ["1", "2", "4", "8"])
+def test_knn_grid_waves_agree(gpu, oracle_mod, waves, monkeypatch):
+    monkeypatch.setenv("POINTOPS_KNN_GRID_WAVES", waves)
+    x = W.uniform_cube(10, 1, 20000)
+    check_knn(gpu, oracle_mod, x[:, ::41].copy(), x, 16, f"grid waves={waves}")
+
+
 @pytest.mark.parametrize("env", ["1", "2", "4", "8"])
 @pytest.mark.parametrize("k", [5, 16, 32])
 def test_knn_wave_split_agrees(gpu, oracle_mod, env, k, monkeypatch):
