@@ -67,9 +67,11 @@ __device__ __forceinline__ uint32_t cell_code(const GridParams& g, float x, floa
     return spread3((uint32_t)cx) | (spread3((uint32_t)cy) << 1) | (spread3((uint32_t)cz) << 2);
 }
 
-// The references' bounding box, in three launches: slots set to the empty box,
-// many workgroups folding their points in with integer atomics on an order-
-// preserving encoding of the floats, then the cell mapping per cloud.
+// The references' bounding box: many workgroups fold their points in with
+// integer atomics on an order-preserving encoding of the floats; the last
+// workgroup of a cloud to finish turns the box into the cell mapping.
+constexpr int kEncWords = 8;  // per cloud: 3 minima, 3 maxima, a finish counter, unused
+
 __device__ __forceinline__ uint32_t ord_enc(float f) {
     const uint32_t u = __float_as_uint(f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // unsigned order = float order
@@ -79,16 +81,26 @@ __device__ __forceinline__ float ord_dec(uint32_t e) {
     return __uint_as_float((e & 0x80000000u) ? (e & 0x7FFFFFFFu) : ~e);
 }
 
-__global__ void grid_bounds_init_kernel(uint32_t* __restrict__ enc, int64_t B) {
-    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (i < B * 6) enc[i] = (i % 6) < 3 ? 0xFFFFFFFFu : 0u;  // min slots high, max slots low
+// Clears the histograms (n words from `zero`) and sets every cloud's box
+// slots to the empty box and its counter to 0.
+__global__ void grid_init_kernel(uint32_t* __restrict__ enc, int64_t B,
+                                 uint32_t* __restrict__ zero, size_t n) {
+    const size_t i0 = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+    if (i0 < (size_t)B * kEncWords) {
+        const int r = (int)(i0 % kEncWords);
+        enc[i0] = r < 3 ? 0xFFFFFFFFu : 0u;  // min slots high, max slots and counter 0
+    }
+    for (size_t i = i0; i < n; i += (size_t)gridDim.x * blockDim.x) zero[i] = 0;
 }
 
 __global__ __launch_bounds__(256) void grid_bounds_kernel(const float* __restrict__ ref, int64_t B,
-                                                          int P, uint32_t* __restrict__ enc) {
+                                                          int P, int L, uint32_t* __restrict__ enc,
+                                                          GridParams* __restrict__ gp) {
     __shared__ uint32_t sh[6];
+    __shared__ bool last;
     const int b = blockIdx.y;
     const float* xb = ref + (size_t)b * P * 3;
+    uint32_t* e = enc + (size_t)b * kEncWords;
     if (threadIdx.x < 6) sh[threadIdx.x] = threadIdx.x < 3 ? 0xFFFFFFFFu : 0u;
     __syncthreads();
     uint32_t mn[3] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu}, mx[3] = {0u, 0u, 0u};
@@ -105,40 +117,44 @@ __global__ __launch_bounds__(256) void grid_bounds_kernel(const float* __restric
         atomicMax(&sh[3 + d], mx[d]);
     }
     __syncthreads();
-    if (threadIdx.x < 3) atomicMin(&enc[b * 6 + threadIdx.x], sh[threadIdx.x]);
-    else if (threadIdx.x < 6) atomicMax(&enc[b * 6 + threadIdx.x], sh[threadIdx.x]);
-}
-
-__global__ void grid_params_kernel(const uint32_t* __restrict__ enc, int64_t B, int L,
-                                   GridParams* __restrict__ gp) {
-    const int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (b >= B) return;
-    GridParams g{};
-#pragma unroll
-    for (int d = 0; d < 3; ++d) {
-        const float lo = ord_dec(enc[b * 6 + d]), hi = ord_dec(enc[b * 6 + 3 + d]);
-        const float ext = hi - lo;
-        g.lo[d] = lo;
-        g.inv[d] = ext > 0.0f ? (float)(1 << L) / ext : 0.0f;
+    if (threadIdx.x < 3) atomicMin(&e[threadIdx.x], sh[threadIdx.x]);
+    else if (threadIdx.x < 6) atomicMax(&e[threadIdx.x], sh[threadIdx.x]);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();  // this workgroup's box atomics before its count
+        last = atomicAdd(&e[6], 1u) == gridDim.x - 1;
     }
-    gp[b] = g;
+    __syncthreads();
+    if (last && threadIdx.x == 0) {
+        __threadfence();
+        GridParams g{};
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+            // atomic reads: the other workgroups' updates are in the device-scope values
+            const float lo = ord_dec(atomicOr(&e[d], 0u));
+            const float hi = ord_dec(atomicOr(&e[3 + d], 0u));
+            const float ext = hi - lo;
+            g.lo[d] = lo;
+            g.inv[d] = ext > 0.0f ? (float)(1 << L) / ext : 0.0f;
+        }
+        gp[b] = g;
+    }
 }
 
-__global__ void grid_zero_kernel(uint32_t* __restrict__ p, size_t n) {
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
-         i += (size_t)gridDim.x * blockDim.x)
-        p[i] = 0;
-}
-
-// Histogram of cell codes: cnt[b * C + code]++.
-__global__ void grid_count_kernel(const float* __restrict__ pts, int64_t B, int n, int L,
-                                  const GridParams* __restrict__ gp, uint32_t* __restrict__ cnt) {
+// Histograms of cell codes, references then queries: cnt[b * C + code]++.
+__global__ void grid_count_kernel(const float* __restrict__ ref, const float* __restrict__ query,
+                                  int64_t B, int P, int Q, int L,
+                                  const GridParams* __restrict__ gp, uint32_t* __restrict__ rcnt,
+                                  uint32_t* __restrict__ qcnt) {
     const int64_t C = (int64_t)1 << (3 * L);
-    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < B * n;
+    const int64_t nr = B * P;
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < nr + B * Q;
          e += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t b = e / n;
-        const float* p = pts + e * 3;
-        atomicAdd(&cnt[b * C + cell_code(gp[b], p[0], p[1], p[2], L)], 1u);
+        const bool is_ref = e < nr;
+        const int64_t i = is_ref ? e : e - nr;
+        const int64_t b = i / (is_ref ? P : Q);
+        const float* p = (is_ref ? ref : query) + i * 3;
+        atomicAdd(&(is_ref ? rcnt : qcnt)[b * C + cell_code(gp[b], p[0], p[1], p[2], L)], 1u);
     }
 }
 
@@ -147,10 +163,14 @@ __global__ void grid_count_kernel(const float* __restrict__ pts, int64_t B, int 
 // its own scan. `fill` (the scatter cursors) is cleared on the way.
 constexpr int kScanChunk = 1024;
 
-__global__ __launch_bounds__(256) void grid_chunk_sums_kernel(const uint32_t* __restrict__ cnt,
-                                                              int L, uint32_t* __restrict__ sums) {
+// blockIdx.z: 0 references, 1 queries (each side its own counts and sums).
+__global__ __launch_bounds__(256) void grid_chunk_sums_kernel(const uint32_t* __restrict__ rcnt,
+                                                              const uint32_t* __restrict__ qcnt,
+                                                              int L, uint32_t* __restrict__ sums2) {
     __shared__ uint32_t sh[256];
     const int64_t C = (int64_t)1 << (3 * L);
+    const uint32_t* cnt = blockIdx.z ? qcnt : rcnt;
+    uint32_t* sums = sums2 + (size_t)blockIdx.z * gridDim.y * gridDim.x;
     const int64_t base = (int64_t)blockIdx.y * C + (int64_t)blockIdx.x * kScanChunk;
     uint32_t v = 0;
     for (int i = threadIdx.x; i < kScanChunk && blockIdx.x * (int64_t)kScanChunk + i < C; i += 256)
@@ -164,11 +184,14 @@ __global__ __launch_bounds__(256) void grid_chunk_sums_kernel(const uint32_t* __
     if (threadIdx.x == 0) sums[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = sh[0];
 }
 
-__global__ __launch_bounds__(256) void grid_chunk_scan_kernel(uint32_t* __restrict__ cnt,
-                                                              uint32_t* __restrict__ fill, int L,
-                                                              const uint32_t* __restrict__ sums) {
+__global__ __launch_bounds__(256) void grid_chunk_scan_kernel(
+    uint32_t* __restrict__ rcnt, uint32_t* __restrict__ rfill, uint32_t* __restrict__ qcnt,
+    uint32_t* __restrict__ qfill, int L, const uint32_t* __restrict__ sums2) {
     __shared__ uint32_t sh[256];
     const int64_t C = (int64_t)1 << (3 * L);
+    uint32_t* cnt = blockIdx.z ? qcnt : rcnt;
+    uint32_t* fill = blockIdx.z ? qfill : rfill;
+    const uint32_t* sums = sums2 + (size_t)blockIdx.z * gridDim.y * gridDim.x;
     const int64_t base = (int64_t)blockIdx.y * C + (int64_t)blockIdx.x * kScanChunk;
     // offset of this chunk: the sum of the chunks before it
     uint32_t off = 0;
@@ -210,34 +233,44 @@ __global__ __launch_bounds__(256) void grid_chunk_scan_kernel(uint32_t* __restri
     }
 }
 
-// Sorted copy: out[b * n + start[code] + k] = (x, y, z, original index).
-__global__ void grid_scatter_kernel(const float* __restrict__ pts, int64_t B, int n, int L,
+// Sorted copies, references then queries:
+// out[b * n + start[code] + k] = (x, y, z, original index).
+__global__ void grid_scatter_kernel(const float* __restrict__ ref, const float* __restrict__ query,
+                                    int64_t B, int P, int Q, int L,
                                     const GridParams* __restrict__ gp,
-                                    const uint32_t* __restrict__ start, uint32_t* __restrict__ fill,
-                                    float4* __restrict__ out) {
+                                    const uint32_t* __restrict__ rstart, uint32_t* __restrict__ rfill,
+                                    const uint32_t* __restrict__ qstart, uint32_t* __restrict__ qfill,
+                                    float4* __restrict__ rout, float4* __restrict__ qout) {
     const int64_t C = (int64_t)1 << (3 * L);
-    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < B * n;
+    const int64_t nr = B * P;
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < nr + B * Q;
          e += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t b = e / n;
-        const int j = (int)(e - b * n);
-        const float* p = pts + e * 3;
+        const bool is_ref = e < nr;
+        const int64_t i = is_ref ? e : e - nr;
+        const int n = is_ref ? P : Q;
+        const int64_t b = i / n;
+        const int j = (int)(i - b * n);
+        const float* p = (is_ref ? ref : query) + i * 3;
         const uint32_t code = cell_code(gp[b], p[0], p[1], p[2], L);
-        const uint32_t pos = start[b * C + code] + atomicAdd(&fill[b * C + code], 1u);
-        out[b * n + pos] = make_float4(p[0], p[1], p[2], __int_as_float(j));
+        const uint32_t pos = (is_ref ? rstart : qstart)[b * C + code] +
+                             atomicAdd(&(is_ref ? rfill : qfill)[b * C + code], 1u);
+        (is_ref ? rout : qout)[b * n + pos] = make_float4(p[0], p[1], p[2], __int_as_float(j));
     }
 }
 
-// One wave per 64 sorted references, four blocks of 16: box[(b * nblk + k) * 8 + 0..5].
-__global__ __launch_bounds__(256) void grid_boxes_kernel(const float4* __restrict__ sr, int64_t B,
-                                                         int P, int nblk,
-                                                         float* __restrict__ box) {
-    const int64_t nw = ((int64_t)nblk + 3) / 4;  // waves per cloud
-    const int64_t w = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
-    if (w >= B * nw) return;
-    const int64_t b = w / nw;
-    const int k = (int)(w - b * nw) * 4 + lane / kGridBlk;  // this lane's block
-    const int j = (int)(w - b * nw) * kWave + lane;
+// One 1024-thread workgroup per superblock (64 blocks of 16 sorted
+// references): every block's box, box[(b * nblk + k) * 8 + 0..5], then the
+// superblock's, sbox[(b * nsb + s) * 8 + 0..5].
+__global__ __launch_bounds__(1024) void grid_boxes_kernel(const float4* __restrict__ sr,
+                                                          int64_t B, int P, int nblk, int nsb,
+                                                          float* __restrict__ box,
+                                                          float* __restrict__ sbox) {
+    __shared__ float sh[kWave][6];
+    const int64_t b = blockIdx.y;
+    const int sb = blockIdx.x;
+    const int t = threadIdx.x;
+    const int j = sb * kWave * kGridBlk + t;
+    const int k = sb * kWave + t / kGridBlk;  // this thread's block
     const float inf = __builtin_inff();
     float v[6] = {inf, inf, inf, -inf, -inf, -inf};
     if (j < P) {
@@ -253,41 +286,31 @@ __global__ __launch_bounds__(256) void grid_boxes_kernel(const float4* __restric
             v[d] = fminf(v[d], __shfl_xor(v[d], o));
             v[3 + d] = fmaxf(v[3 + d], __shfl_xor(v[3 + d], o));
         }
-    if (lane % kGridBlk == 0 && k < nblk) {
-        float* o = box + ((size_t)b * nblk + k) * 8;
+    if (t % kGridBlk == 0) {
 #pragma unroll
-        for (int d = 0; d < 6; ++d) o[d] = v[d];
-    }
-}
-
-// One wave per superblock (64 blocks): the union of its blocks' boxes.
-__global__ __launch_bounds__(256) void grid_superboxes_kernel(const float* __restrict__ box,
-                                                              int64_t B, int nblk, int nsb,
-                                                              float* __restrict__ sbox) {
-    const int64_t w = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
-    if (w >= B * nsb) return;
-    const int64_t b = w / nsb;
-    const int s = (int)(w - b * nsb);
-    const int k = s * kWave + lane;
-    const float inf = __builtin_inff();
-    float v[6] = {inf, inf, inf, -inf, -inf, -inf};
-    if (k < nblk) {
-        const float* o = box + ((size_t)b * nblk + k) * 8;
+        for (int d = 0; d < 6; ++d) sh[t / kGridBlk][d] = v[d];
+        if (k < nblk) {
+            float* o = box + ((size_t)b * nblk + k) * 8;
 #pragma unroll
-        for (int d = 0; d < 6; ++d) v[d] = o[d];
-    }
-#pragma unroll
-    for (int o = kWave / 2; o >= 1; o /= 2)
-#pragma unroll
-        for (int d = 0; d < 3; ++d) {
-            v[d] = fminf(v[d], __shfl_xor(v[d], o));
-            v[3 + d] = fmaxf(v[3 + d], __shfl_xor(v[3 + d], o));
+            for (int d = 0; d < 6; ++d) o[d] = v[d];
         }
-    if (lane == 0) {
-        float* o = sbox + (size_t)w * 8;
+    }
+    __syncthreads();
+    if (t < kWave) {
 #pragma unroll
-        for (int d = 0; d < 6; ++d) o[d] = v[d];
+        for (int d = 0; d < 6; ++d) v[d] = sh[t][d];  // empty boxes past the end
+#pragma unroll
+        for (int o = kWave / 2; o >= 1; o /= 2)
+#pragma unroll
+            for (int d = 0; d < 3; ++d) {
+                v[d] = fminf(v[d], __shfl_xor(v[d], o));
+                v[3 + d] = fmaxf(v[3 + d], __shfl_xor(v[3 + d], o));
+            }
+        if (t == 0) {
+            float* o = sbox + ((size_t)b * nsb + sb) * 8;
+#pragma unroll
+            for (int d = 0; d < 6; ++d) o[d] = v[d];
+        }
     }
 }
 
@@ -580,8 +603,8 @@ static GridLayout grid_layout(int64_t B, int64_t Q, int64_t P) {
     GridLayout g;
     size_t o = 0;
     g.params = o; o += al(B * sizeof(GridParams));
-    g.enc = o; o += al(B * 6 * sizeof(uint32_t));
-    g.sums = o; o += al(B * ((C + 1023) / 1024) * sizeof(uint32_t));
+    g.enc = o; o += al(B * kEncWords * sizeof(uint32_t));
+    g.sums = o; o += al(2 * B * ((C + 1023) / 1024) * sizeof(uint32_t));
     g.ref_cnt = o; o += al(B * C * 4);
     g.ref_fill = o; o += al(B * C * 4);
     g.q_cnt = o; o += al(B * C * 4);
@@ -627,41 +650,30 @@ hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int6
         if (e != hipSuccess) return e; \
     } while (0)
     uint32_t* enc = (uint32_t*)(ws + g.enc);
-    POINTOPS_CHECK(hipLaunchKernelGGL(grid_bounds_init_kernel, dim3(grid_blocks(B * 6)), dim3(256),
-                                      0, stream, enc, B));
+    // the four histogram arrays are contiguous: cleared together
+    const size_t nzero = (g.sref - g.ref_cnt) / sizeof(uint32_t);
+    POINTOPS_CHECK(hipLaunchKernelGGL(grid_init_kernel,
+                                      dim3(std::max(grid_blocks((int64_t)nzero),
+                                                    grid_blocks(B * kEncWords))),
+                                      dim3(256), 0, stream, enc, B, rcnt, nzero));
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_bounds_kernel,
                                       dim3((unsigned)std::min<int64_t>((P + 1023) / 1024, 256),
                                            (unsigned)B),
-                                      dim3(256), 0, stream, ref, B, (int)P, enc));
-    POINTOPS_CHECK(hipLaunchKernelGGL(grid_params_kernel, dim3(grid_blocks(B)), dim3(256), 0,
-                                      stream, enc, B, L, gp));
-    POINTOPS_CHECK(hipLaunchKernelGGL(grid_zero_kernel, dim3(grid_blocks(B * C)), dim3(256), 0,
-                                      stream, rcnt, (size_t)(B * C)));
-    POINTOPS_CHECK(hipLaunchKernelGGL(grid_zero_kernel, dim3(grid_blocks(B * C)), dim3(256), 0,
-                                      stream, qcnt, (size_t)(B * C)));
-    POINTOPS_CHECK(hipLaunchKernelGGL(grid_count_kernel, dim3(grid_blocks(B * P)), dim3(256), 0,
-                                      stream, ref, B, (int)P, L, gp, rcnt));
-    POINTOPS_CHECK(hipLaunchKernelGGL(grid_count_kernel, dim3(grid_blocks(B * Q)), dim3(256), 0,
-                                      stream, query, B, (int)Q, L, gp, qcnt));
+                                      dim3(256), 0, stream, ref, B, (int)P, L, enc, gp));
+    POINTOPS_CHECK(hipLaunchKernelGGL(grid_count_kernel, dim3(grid_blocks(B * (P + Q))), dim3(256),
+                                      0, stream, ref, query, B, (int)P, (int)Q, L, gp, rcnt, qcnt));
     const unsigned nchunk = (unsigned)((C + kScanChunk - 1) / kScanChunk);
     uint32_t* sums = (uint32_t*)(ws + g.sums);
-    for (int side = 0; side < 2; ++side) {
-        uint32_t* c = side ? qcnt : rcnt;
-        uint32_t* f = side ? qfill : rfill;
-        POINTOPS_CHECK(hipLaunchKernelGGL(grid_chunk_sums_kernel, dim3(nchunk, (unsigned)B),
-                                          dim3(256), 0, stream, c, L, sums));
-        POINTOPS_CHECK(hipLaunchKernelGGL(grid_chunk_scan_kernel, dim3(nchunk, (unsigned)B),
-                                          dim3(256), 0, stream, c, f, L, sums));
-    }
-    POINTOPS_CHECK(hipLaunchKernelGGL(grid_scatter_kernel, dim3(grid_blocks(B * P)), dim3(256), 0,
-                                      stream, ref, B, (int)P, L, gp, rcnt, rfill, sref));
-    POINTOPS_CHECK(hipLaunchKernelGGL(grid_scatter_kernel, dim3(grid_blocks(B * Q)), dim3(256), 0,
-                                      stream, query, B, (int)Q, L, gp, qcnt, qfill, squery));
-    const int64_t box_waves = B * ((nblk + 3) / 4);
-    POINTOPS_CHECK(hipLaunchKernelGGL(grid_boxes_kernel, dim3((unsigned)((box_waves + 3) / 4)),
-                                      dim3(256), 0, stream, sref, B, (int)P, nblk, box));
-    POINTOPS_CHECK(hipLaunchKernelGGL(grid_superboxes_kernel, dim3((unsigned)((B * nsb + 3) / 4)),
-                                      dim3(256), 0, stream, box, B, nblk, nsb, sbox));
+    POINTOPS_CHECK(hipLaunchKernelGGL(grid_chunk_sums_kernel, dim3(nchunk, (unsigned)B, 2),
+                                      dim3(256), 0, stream, rcnt, qcnt, L, sums));
+    POINTOPS_CHECK(hipLaunchKernelGGL(grid_chunk_scan_kernel, dim3(nchunk, (unsigned)B, 2),
+                                      dim3(256), 0, stream, rcnt, rfill, qcnt, qfill, L, sums));
+    POINTOPS_CHECK(hipLaunchKernelGGL(grid_scatter_kernel, dim3(grid_blocks(B * (P + Q))),
+                                      dim3(256), 0, stream, ref, query, B, (int)P, (int)Q, L, gp,
+                                      rcnt, rfill, qcnt, qfill, sref, squery));
+    POINTOPS_CHECK(hipLaunchKernelGGL(grid_boxes_kernel, dim3((unsigned)nsb, (unsigned)B),
+                                      dim3(1024), 0, stream, sref, B, (int)P, nblk, nsb, box,
+                                      sbox));
     dim3 grid((unsigned)((Q + kWave - 1) / kWave), (unsigned)B);
 #define POINTOPS_GRID_CASE(KC, W)                                                              \
     if (kcap == KC && nw == W) {                                                               \
