@@ -430,9 +430,8 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
             if (ballot(cnt > kGridBuf - 8)) flush();
         }
     };
-    // Wave 0 skips, in later blocks, the references of the local pass (they
-    // are in its list already).
-    const bool skip_local = w == 0;
+    // Every wave skips, in later blocks, the references of its lane's local
+    // pass: they are in wave 0's list already.
     auto scan_block = [&](int blk) {
         const int j0 = blk * kGridBlk, j1 = min(P, j0 + kGridBlk);
         int j = j0;
@@ -443,7 +442,7 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
             for (int r = 0; r < 8; ++r) {
                 const float4 p = rb[j + r];
                 u[r] = f2u(s32(q.x, q.y, q.z, p.x, p.y, p.z)) + 1u;
-                if (skip_local && (uint32_t)(j + r - loc0) < (uint32_t)nloc) u[r] = 0xFFFFFFFFu;
+                if ((uint32_t)(j + r - loc0) < (uint32_t)nloc) u[r] = 0xFFFFFFFFu;
                 jl[r] = j + r;
             }
             take8(u, jl);
@@ -451,7 +450,7 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
         for (; j < j1; ++j) {
             const float4 p = rb[j];
             uint32_t u = f2u(s32(q.x, q.y, q.z, p.x, p.y, p.z)) + 1u;
-            if (skip_local && (uint32_t)(j - loc0) < (uint32_t)nloc) u = 0xFFFFFFFFu;
+            if ((uint32_t)(j - loc0) < (uint32_t)nloc) u = 0xFFFFFFFFu;
             if (u <= lim) {
                 buf[cnt * kWave + lane] = make_uint2(u, (uint32_t)__float_as_int(p.w));
                 ++cnt;
