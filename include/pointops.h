@@ -252,10 +252,15 @@ int pointops_fps_ragged(const float *xyz, int64_t rows, const int64_t *x_off,
  * distances and indices. Project page, "Minimal example" (the 0.5.0 call) and
  * roadmap, "Phase 2" (PointNet++ feature propagation). It is pointops_knn
  * with k = 3 (same order and ties): unknown (B, n, 3), known (B, m, 3),
- * m >= 3; out_dist, out_idx (B, n, 3), device.
+ * m >= 3; out_dist, out_idx (B, n, 3), device; workspace as for pointops_knn
+ * (NULL: full scan).
  */
 int pointops_three_nn(const float *unknown, const float *known, int64_t B, int64_t n, int64_t m,
-                      float *out_dist, int64_t *out_idx, void *stream);
+                      float *out_dist, int64_t *out_idx, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Workspace bytes for pointops_three_nn's grid search (as pointops_knn's). */
+size_t pointops_three_nn_workspace_bytes(int64_t B, int64_t n, int64_t m);
 
 /* Reductions of pointops_chamfer. */
 enum pointops_reduction {
@@ -264,8 +269,10 @@ enum pointops_reduction {
     POINTOPS_REDUCE_SUM = 2
 };
 
-/* Workspace bytes of pointops_chamfer and pointops_chamfer_backward for B clouds. */
-size_t pointops_chamfer_workspace_bytes(int64_t B);
+/* Workspace bytes of pointops_chamfer (and enough for pointops_chamfer_backward)
+ * for B clouds of N and M points; large clouds without lengths get the kNN
+ * grid search's workspace too. */
+size_t pointops_chamfer_workspace_bytes(int64_t B, int64_t N, int64_t M);
 
 /*
  * Squared-L2 Chamfer distance of x (B, N, 3) and y (B, M, 3), device.
@@ -286,7 +293,9 @@ size_t pointops_chamfer_workspace_bytes(int64_t B);
  *             (0, -1) past x's length or without partner. dist_yx, idx_yx:
  *             (B, M) likewise for y; not used (may be NULL) when
  *             single_directional. These are the inputs of the backward.
- *   workspace pointops_chamfer_workspace_bytes(B) bytes of device scratch.
+ *   workspace pointops_chamfer_workspace_bytes(B, N, M) bytes of device scratch.
+ *   Without lengths, large clouds find their nearest points with the kNN
+ *   grid search (same results, bit for bit).
  */
 int pointops_chamfer(const float *x, const float *y, int64_t B, int64_t N, int64_t M,
                      const int64_t *x_lengths, const int64_t *y_lengths, int point_reduction,
@@ -304,7 +313,7 @@ int pointops_chamfer(const float *x, const float *y, int64_t B, int64_t N, int64
  * device, are overwritten (either may be NULL). w = fl32(upstream gradient x
  * reduction factor); terms are added with float atomics in no fixed order,
  * so the last bits may differ between runs. The workspace is needed only when
- * lengths are given.
+ * lengths are given (then 16 * B bytes suffice).
  */
 int pointops_chamfer_backward(const float *x, const float *y, int64_t B, int64_t N, int64_t M,
                               const int64_t *x_lengths, const int64_t *y_lengths,

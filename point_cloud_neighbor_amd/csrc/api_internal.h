@@ -18,7 +18,7 @@ hipError_t launch_ball_query_culled(const float*, const float*, int64_t, int64_t
                                     float, int64_t, float*, int64_t*, int, float*, hipStream_t);
 size_t ball_query_box_bytes(int64_t B, int64_t P);
 hipError_t launch_knn_grid(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
-                           int64_t*, int, int, void*, hipStream_t);
+                           int64_t*, int, int, void*, int, hipStream_t);
 size_t knn_grid_workspace_bytes(int64_t B, int64_t Q, int64_t P);
 hipError_t launch_fps(const float*, int64_t, int64_t, int64_t, int64_t, int64_t*, float*, void*,
                       int, int, int, uint32_t, hipStream_t, const int64_t*, int, int64_t);
@@ -80,6 +80,10 @@ int upload(const Table& t, void* workspace, size_t workspace_bytes, hipStream_t 
            int64_t** dev_table);
 // Knobs shared by the dense and ragged launches.
 int knn_waves(int kcap, int64_t tiles, int cus);
+// kNN takes the grid search for this shape (when given a workspace).
+bool knn_use_grid(int64_t B, int64_t Q, int64_t P);
+// Waves per workgroup of the grid search.
+int knn_grid_waves(int kcap);
 int bq_queries_per_wave(int64_t rows, int cus, int max_qw);
 
 }  // namespace api

@@ -27,20 +27,30 @@ namespace {
 
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
-// Workspace: both length arrays, the per-cloud partial losses, then the two
-// cloud tables of the nearest-point searches (with lengths).
+// Workspace: both length arrays, the per-cloud partial losses, the two cloud
+// tables of the nearest-point searches (with lengths), then the grid of the
+// kNN grid search (without lengths, for large clouds; both directions use it
+// in turn).
 struct ChamferLayout {
-    size_t lens, part, table_xy, table_yx, total;
+    size_t lens, part, table_xy, table_yx, grid, grid_bytes, total;
 };
 
-ChamferLayout chamfer_layout(int64_t B) {
+ChamferLayout chamfer_layout(int64_t B, int64_t N, int64_t M) {
     ChamferLayout l;
     l.lens = 0;
     l.part = align256((size_t)2 * B * sizeof(int64_t));
     l.table_xy = l.part + align256((size_t)B * sizeof(double));
     const size_t t = align256((size_t)pointops::seg_table_words(B) * sizeof(int64_t));
     l.table_yx = l.table_xy + t;
-    l.total = std::max<size_t>(l.table_yx + t, 256);
+    l.grid = l.table_yx + t;
+    l.grid_bytes = 0;
+    if (B > 0 && N > 0 && M > 0) {
+        if (knn_use_grid(B, N, M))
+            l.grid_bytes = std::max(l.grid_bytes, pointops::knn_grid_workspace_bytes(B, N, M));
+        if (knn_use_grid(B, M, N))
+            l.grid_bytes = std::max(l.grid_bytes, pointops::knn_grid_workspace_bytes(B, M, N));
+    }
+    l.total = std::max<size_t>(l.grid + align256(l.grid_bytes), 256);
     return l;
 }
 
@@ -89,10 +99,16 @@ int upload_lengths(const int64_t* x_lengths, const int64_t* y_lengths, int64_t B
 // `b_` (B, m), squared distance kept; rows past la[b] hold (0, -1).
 int nearest(const float* a, const float* bpts, int64_t B, int64_t n, int64_t m,
             const int64_t* la, const int64_t* lb, const int64_t* dev_la, float* dist,
-            int64_t* idx, void* table_ws, size_t table_bytes, const DeviceInfo& dev,
-            hipStream_t s) {
+            int64_t* idx, void* table_ws, size_t table_bytes, void* grid_ws, size_t grid_bytes,
+            const DeviceInfo& dev, hipStream_t s) {
     if (B * n == 0) return POINTOPS_OK;
     hipError_t e;
+    if (!la && !lb && m > 0 && knn_use_grid(B, n, m) &&
+        grid_bytes >= pointops::knn_grid_workspace_bytes(B, n, m)) {
+        e = pointops::launch_knn_grid(a, bpts, B, n, m, 1, dist, idx, 1, knn_grid_waves(1),
+                                      grid_ws, 1, s);
+        return e == hipSuccess ? POINTOPS_OK : hip_fail(e, "nearest launch");
+    }
     if (!la && !lb) {
         const int64_t tiles = B * ((n + 63) / 64);
         e = pointops::launch_knn(a, bpts, B, n, m, 1, dist, idx, 1, knn_waves(1, tiles, dev.cus),
@@ -123,16 +139,22 @@ int nearest(const float* a, const float* bpts, int64_t B, int64_t n, int64_t m,
 extern "C" {
 
 int pointops_three_nn(const float* unknown, const float* known, int64_t B, int64_t n, int64_t m,
-                      float* out_dist, int64_t* out_idx, void* stream) {
+                      float* out_dist, int64_t* out_idx, void* workspace, size_t workspace_bytes,
+                      void* stream) {
     clear_error();
     if (m < 3 && B > 0 && n > 0)
         return fail(POINTOPS_INVALID_ARGUMENT, "three_nn needs at least 3 known points, got %lld",
                     (long long)m);
-    return pointops_knn(unknown, known, B, n, m, 3, out_dist, out_idx, nullptr, 0, stream);
+    return pointops_knn(unknown, known, B, n, m, 3, out_dist, out_idx, workspace,
+                        workspace_bytes, stream);
 }
 
-size_t pointops_chamfer_workspace_bytes(int64_t B) {
-    return B < 0 ? 0 : chamfer_layout(B).total;
+size_t pointops_three_nn_workspace_bytes(int64_t B, int64_t n, int64_t m) {
+    return pointops_knn_workspace_bytes(B, n, m);
+}
+
+size_t pointops_chamfer_workspace_bytes(int64_t B, int64_t N, int64_t M) {
+    return B < 0 || N < 0 || M < 0 ? 0 : chamfer_layout(B, N, M).total;
 }
 
 int pointops_chamfer(const float* x, const float* y, int64_t B, int64_t N, int64_t M,
@@ -147,7 +169,7 @@ int pointops_chamfer(const float* x, const float* y, int64_t B, int64_t N, int64
     if (!loss || (B * N > 0 && (!dist_xy || !idx_xy)) ||
         (!single_directional && B * M > 0 && (!dist_yx || !idx_yx)))
         return fail(POINTOPS_INVALID_ARGUMENT, "null output pointer");
-    const ChamferLayout l = chamfer_layout(B);
+    const ChamferLayout l = chamfer_layout(B, N, M);
     if (!workspace || workspace_bytes < l.total)
         return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
                     workspace_bytes, l.total);
@@ -166,11 +188,11 @@ int pointops_chamfer(const float* x, const float* y, int64_t B, int64_t N, int64
     const int64_t* dly = have_len ? lens + B : nullptr;
     const size_t tb = l.table_yx - l.table_xy;
     st = nearest(x, y, B, N, M, x_lengths, y_lengths, dlx, dist_xy, idx_xy, ws + l.table_xy, tb,
-                 *dev, s);
+                 ws + l.grid, l.grid_bytes, *dev, s);
     if (st != POINTOPS_OK) return st;
     if (!single_directional) {
         st = nearest(y, x, B, M, N, y_lengths, x_lengths, dly, dist_yx, idx_yx, ws + l.table_yx,
-                     tb, *dev, s);
+                     tb, ws + l.grid, l.grid_bytes, *dev, s);
         if (st != POINTOPS_OK) return st;
     }
     hipError_t e = pointops::launch_chamfer_reduce(
@@ -194,11 +216,12 @@ int pointops_chamfer_backward(const float* x, const float* y, int64_t B, int64_t
     if (B > 0 && (!grad_loss || (N > 0 && !idx_xy) ||
                   (!single_directional && M > 0 && !idx_yx)))
         return fail(POINTOPS_INVALID_ARGUMENT, "null pointer");
-    const ChamferLayout l = chamfer_layout(B);
+    // only the length arrays are used here
+    const ChamferLayout l = chamfer_layout(B, 0, 0);
     const bool have_len = x_lengths || y_lengths;
-    if (have_len && (!workspace || workspace_bytes < l.total))
+    if (have_len && (!workspace || workspace_bytes < l.part))
         return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
-                    workspace_bytes, l.total);
+                    workspace_bytes, l.part);
     st = current_device(nullptr);
     if (st != POINTOPS_OK) return st;
     hipStream_t s = (hipStream_t)stream;

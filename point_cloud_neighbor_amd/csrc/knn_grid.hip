@@ -360,7 +360,7 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
     const float4* __restrict__ sq, const float4* __restrict__ sr, int Q, int P, int k,
     const float* __restrict__ box, const float* __restrict__ sbox, int nblk, int nsb,
     const uint32_t* __restrict__ ref_start, const GridParams* __restrict__ gp, int L,
-    float* __restrict__ out_dist, int64_t* __restrict__ out_idx) {
+    float* __restrict__ out_dist, int64_t* __restrict__ out_idx, int squared) {
     constexpr int ROWS = kGridBuf > KCAP ? kGridBuf : KCAP;
     extern __shared__ uint2 lds[];             // per wave ROWS x 64 entries
     __shared__ uint32_t thr[NW][kWave];        // each wave's lanes' k-th key (high half)
@@ -573,7 +573,8 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
 #pragma unroll
     for (int p = 0; p < KCAP; ++p) {
         if (p >= front) {
-            od[p - front] = sqrtf(u2f((uint32_t)(top.key[p] >> 32) - 1u));
+            const float sv = u2f((uint32_t)(top.key[p] >> 32) - 1u);
+            od[p - front] = squared ? sv : sqrtf(sv);
             oi[p - front] = (int64_t)(uint32_t)top.key[p];
         }
     }
@@ -624,9 +625,10 @@ static unsigned grid_blocks(int64_t n) {
     return (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 8192));
 }
 
+// squared != 0: out_dist holds s itself (the Chamfer distance's nearest points).
 hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int64_t Q, int64_t P,
                            int64_t k, float* out_dist, int64_t* out_idx, int kcap, int nw,
-                           void* workspace, hipStream_t stream) {
+                           void* workspace, int squared, hipStream_t stream) {
     const int L = knn_grid_level(P);
     const int64_t C = (int64_t)1 << (3 * L);
     const int nblk = (int)((P + kGridBlk - 1) / kGridBlk), nsb = (nblk + kWave - 1) / kWave;
@@ -685,7 +687,8 @@ hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int6
         }                                                                                      \
         POINTOPS_CHECK(hipLaunchKernelGGL((knn_grid_kernel<KC, W>), grid, dim3(W * kWave), lds, \
                                           stream, squery, sref, (int)Q, (int)P, (int)k, box,   \
-                                          sbox, nblk, nsb, rcnt, gp, L, out_dist, out_idx));   \
+                                          sbox, nblk, nsb, rcnt, gp, L, out_dist, out_idx,     \
+                                          squared));                                           \
         return hipSuccess;                                                                     \
     }
     POINTOPS_GRID_CASE(1, 2) POINTOPS_GRID_CASE(2, 2) POINTOPS_GRID_CASE(4, 2)

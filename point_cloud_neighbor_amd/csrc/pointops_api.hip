@@ -101,6 +101,24 @@ int knn_waves(int kcap, int64_t tiles, int cus) {
     return nw;
 }
 
+// kNN takes the grid path (sort, boxes, culled search) when the references
+// are many enough for the sort to pay: at least 8192 per cloud and 2^27
+// query-reference pairs in all. POINTOPS_KNN_GRID=0 / 1 forces either path.
+bool knn_use_grid(int64_t B, int64_t Q, int64_t P) {
+    const long env = env_long("POINTOPS_KNN_GRID", -1);
+    if (env == 0 || env == 1) return env == 1 && P >= 1;
+    return P >= 8192 && B * Q * P >= ((int64_t)1 << 27);
+}
+
+// Two waves per 64 queries: each wave keeps its own list, so more waves mean
+// more insertions; fewer leave too few waves to hide latency (100k uniform,
+// k=16: 0.44 / 0.33 / 0.37 / 0.49 ms for 1 / 2 / 4 / 8).
+int knn_grid_waves(int kcap) {
+    const long env = env_long("POINTOPS_KNN_GRID_WAVES", 0);
+    if (kcap == 16 && (env == 1 || env == 2 || env == 4 || env == 8)) return (int)env;
+    return 2;
+}
+
 // Ball Query: queries per wave. Fewer queries per wave until the grid is about
 // one device-full of waves; at most 8 (measured faster than 16 on 100k x 100k:
 // the shorter waves balance better).
@@ -319,14 +337,6 @@ int pointops_fps(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t star
     return POINTOPS_OK;
 }
 
-// kNN takes the grid path (sort, boxes, culled search) when the references
-// are many enough for the sort to pay: at least 8192 per cloud and 2^27
-// query-reference pairs in all. POINTOPS_KNN_GRID=0 / 1 forces either path.
-static bool knn_use_grid(int64_t B, int64_t Q, int64_t P) {
-    const long env = env_long("POINTOPS_KNN_GRID", -1);
-    if (env == 0 || env == 1) return env == 1 && P >= 1;
-    return P >= 8192 && B * Q * P >= ((int64_t)1 << 27);
-}
 
 size_t pointops_knn_workspace_bytes(int64_t B, int64_t Q, int64_t P) {
     if (B <= 0 || Q <= 0 || P <= 0 || !knn_use_grid(B, Q, P)) return 0;
@@ -359,14 +369,9 @@ int pointops_knn(const float* query, const float* ref, int64_t B, int64_t Q, int
         if (workspace_bytes < need)
             return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
                         workspace_bytes, need);
-        // two waves per 64 queries: each wave keeps its own list, so more waves
-        // mean more insertions; fewer leave too few waves to hide latency
-        // (100k uniform, k=16: 0.44 / 0.33 / 0.37 / 0.49 ms for 1 / 2 / 4 / 8)
-        int gw = 2;
-        const long gw_env = env_long("POINTOPS_KNN_GRID_WAVES", 0);
-        if (kcap == 16 && (gw_env == 1 || gw_env == 2 || gw_env == 4 || gw_env == 8)) gw = (int)gw_env;
         hipError_t e = pointops::launch_knn_grid(query, ref, B, Q, P, k, out_dist, out_idx, kcap,
-                                                 gw, workspace, (hipStream_t)stream);
+                                                 knn_grid_waves(kcap), workspace, 0,
+                                                 (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, "knn launch");
         return POINTOPS_OK;
     }

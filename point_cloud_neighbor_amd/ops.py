@@ -77,9 +77,11 @@ def _load():
         lib.pointops_fps_ragged.argtypes = [vp, i64, vp, vp, vp, i64, vp, vp, i64, vp, vp,
                                             ctypes.c_int, vp, ctypes.c_size_t, vp]
         lib.pointops_fps_ragged.restype = ctypes.c_int
-        lib.pointops_three_nn.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
+        lib.pointops_three_nn.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, ctypes.c_size_t, vp]
         lib.pointops_three_nn.restype = ctypes.c_int
-        lib.pointops_chamfer_workspace_bytes.argtypes = [i64]
+        lib.pointops_three_nn_workspace_bytes.argtypes = [i64, i64, i64]
+        lib.pointops_three_nn_workspace_bytes.restype = ctypes.c_size_t
+        lib.pointops_chamfer_workspace_bytes.argtypes = [i64, i64, i64]
         lib.pointops_chamfer_workspace_bytes.restype = ctypes.c_size_t
         ci = ctypes.c_int
         lib.pointops_chamfer.argtypes = [vp, vp, i64, i64, i64, vp, vp, ci, ci, ci, vp, vp, vp,
@@ -472,8 +474,12 @@ def three_nn(unknown: torch.Tensor, known: torch.Tensor):
     with torch.cuda.device(unknown.device):
         dist = torch.empty((B, n, 3), dtype=torch.float32, device=unknown.device)
         idx = torch.empty((B, n, 3), dtype=torch.int64, device=unknown.device)
+        nbytes = int(lib.pointops_three_nn_workspace_bytes(B, n, m))
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=unknown.device) if nbytes else None
         _check(lib.pointops_three_nn(unknown.data_ptr(), known.data_ptr(), B, n, m,
-                                     dist.data_ptr(), idx.data_ptr(), _stream(unknown.device)))
+                                     dist.data_ptr(), idx.data_ptr(),
+                                     ws.data_ptr() if ws is not None else None, nbytes,
+                                     _stream(unknown.device)))
     return dist, idx
 
 
@@ -514,7 +520,7 @@ def chamfer_nearest(x, y, x_lengths=None, y_lengths=None, point_reduction="mean"
         i_xy = torch.empty((B, N), dtype=torch.int64, device=dev)
         d_yx = torch.empty((B, M), dtype=torch.float32, device=dev) if not single_directional else None
         i_yx = torch.empty((B, M), dtype=torch.int64, device=dev) if not single_directional else None
-        ws = torch.empty(int(lib.pointops_chamfer_workspace_bytes(B)), dtype=torch.uint8,
+        ws = torch.empty(int(lib.pointops_chamfer_workspace_bytes(B, N, M)), dtype=torch.uint8,
                          device=dev)
         _check(lib.pointops_chamfer(x.data_ptr(), y.data_ptr(), B, N, M, _vp(lx), _vp(ly), pr,
                                     br, int(bool(single_directional)), loss.data_ptr(),
@@ -541,8 +547,7 @@ def chamfer_backward(x, y, idx_xy, idx_yx, grad_loss, x_lengths=None, y_lengths=
     with torch.cuda.device(dev):
         gx = torch.empty_like(x) if need_x else None
         gy = torch.empty_like(y) if need_y else None
-        ws = torch.empty(int(lib.pointops_chamfer_workspace_bytes(B)), dtype=torch.uint8,
-                         device=dev)
+        ws = torch.empty(16 * B + 256, dtype=torch.uint8, device=dev)
         _check(lib.pointops_chamfer_backward(
             x.data_ptr(), y.data_ptr(), B, N, M, _vp(lx), _vp(ly), pr, br,
             int(bool(single_directional)), idx_xy.contiguous().data_ptr(),

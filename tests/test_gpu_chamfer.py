@@ -159,3 +159,20 @@ def test_chamfer_invalid_arguments(gpu):
         gpu.chamfer_nearest(x, x, point_reduction="max")
     with pytest.raises(gpu.PointopsError):
         gpu.three_nn(x, x[:, :2].contiguous())
+
+
+@pytest.mark.parametrize("case", ["uniform", "integer"])
+def test_chamfer_and_three_nn_grid_search_forced(gpu, oracle_mod, case, monkeypatch):
+    """The nearest points of the Chamfer distance and three_nn through the
+    kNN grid search (forced on at small sizes), against the oracle."""
+    monkeypatch.setenv("POINTOPS_KNN_GRID", "1")
+    if case == "uniform":
+        x, y = W.uniform_cube(21, 2, 700), W.uniform_cube(22, 2, 1300)
+    else:
+        x, y = W.integer_cloud(23, 2, 900, 0, 5), W.integer_cloud(24, 2, 600, 0, 5)
+    for single in (False, True):
+        check_chamfer(gpu, oracle_mod, x, y, single=single, what=f"grid {case}")
+    d, i = gpu.three_nn(dev(x), dev(y))
+    wd, wi = oracle_mod.three_nn(x, y, threads=8)
+    assert_idx_equal(host(i), wi, "three_nn grid idx")
+    assert_dist_close(host(d), wd, "three_nn grid dist")
