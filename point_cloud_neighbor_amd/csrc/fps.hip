@@ -639,39 +639,52 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
         }
         int t = t0;
         if (!abort) {
-            int nc = 0;
-            while (true) {
-                // largest key among the valid candidates (lane-major = index order)
-                uint32_t lm = 0;
-                int ls = -1;
+            // The loop for U candidate slots per lane (U = `used`, after the
+            // compaction above; usually 1), so no step touches empty slots.
+            auto certify = [&](auto u_) {
+                constexpr int U = decltype(u_)::value;
+                int nc = 0;
+                while (true) {
+                    // largest key among the valid candidates (lane-major = index order)
+                    uint32_t lm = 0;
+                    int ls = -1;
 #pragma unroll
-                for (int s = 0; s < CPL; ++s)
-                    if (cj[s] != kNone && (ls < 0 || cm[s] > lm)) { lm = cm[s]; ls = s; }
-                uint32_t km, kj;
-                int kl;
-                wave_max_key(lm, select_u32(cj, ls < 0 ? 0 : ls), ls >= 0, km, kj, kl);
-                if (nc > 0 && !key_gt(km, kj, beta_m, beta_j)) break;  // not certified
-                const int s_sel = ls < 0 ? 0 : ls;
-                const float X = u2f(lane_value(select_u32(cxv, s_sel), kl));
-                const float Y = u2f(lane_value(select_u32(cyv, s_sel), kl));
-                const float Z = u2f(lane_value(select_u32(czv, s_sel), kl));
-                if (lane == 0) {
-                    cen[0][nc] = X; cen[1][nc] = Y; cen[2][nc] = Z;
-                    cen_j[nc] = kj;
-                    // LDS performs one wave's operations in issue order, so a
-                    // reader that sees the new count also sees the entry; only
-                    // the compiler must keep the order (no wait for completion)
-                    __asm__ __volatile__("" ::: "memory");
-                    __hip_atomic_store(&cen_count, nc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                }
-                ++nc;
-                ++t;
+                    for (int s = 0; s < U; ++s)
+                        if (cj[s] != kNone && (ls < 0 || cm[s] > lm)) { lm = cm[s]; ls = s; }
+                    uint32_t km, kj;
+                    int kl;
+                    if (U == 1)
+                        wave_max_key(cm[0], cj[0], cj[0] != kNone, km, kj, kl);
+                    else
+                        wave_max_key(lm, select_u32(cj, ls < 0 ? 0 : ls), ls >= 0, km, kj, kl);
+                    if (nc > 0 && !key_gt(km, kj, beta_m, beta_j)) break;  // not certified
+                    const int s_sel = U == 1 ? 0 : (ls < 0 ? 0 : ls);
+                    const float X = u2f(lane_value(U == 1 ? cxv[0] : select_u32(cxv, s_sel), kl));
+                    const float Y = u2f(lane_value(U == 1 ? cyv[0] : select_u32(cyv, s_sel), kl));
+                    const float Z = u2f(lane_value(U == 1 ? czv[0] : select_u32(czv, s_sel), kl));
+                    if (lane == 0) {
+                        cen[0][nc] = X; cen[1][nc] = Y; cen[2][nc] = Z;
+                        cen_j[nc] = kj;
+                        // LDS performs one wave's operations in issue order, so a
+                        // reader that sees the new count also sees the entry; only
+                        // the compiler must keep the order (no wait for completion)
+                        __asm__ __volatile__("" ::: "memory");
+                        __hip_atomic_store(&cen_count, nc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    }
+                    ++nc;
+                    ++t;
 #pragma unroll
-                for (int s = 0; s < CPL; ++s)
-                    if (s < used)
+                    for (int s = 0; s < U; ++s)
                         cm[s] = min(cm[s], f2u(s32(X, Y, Z, u2f(cxv[s]), u2f(cyv[s]), u2f(czv[s]))));
-                if (t >= M || nc == kFpsMaxBatch) break;
-            }
+                    if (t >= M || nc == kFpsMaxBatch) break;
+                }
+            };
+            if (used <= 1)
+                certify(std::integral_constant<int, 1>{});
+            else if (used <= 2 && CPL >= 2)
+                certify(std::integral_constant<int, (CPL >= 2 ? 2 : 1)>{});
+            else
+                certify(std::integral_constant<int, CPL>{});
         }
         if (lane == 0) {
             sh_t = t;
