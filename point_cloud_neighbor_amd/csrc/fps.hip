@@ -323,8 +323,10 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     // itself; the other waves are the point waves.
     constexpr int NPW = NW - NW / 4;
     static_assert(NW % 4 == 0 && NPW >= 1 && NPW <= kWave, "wave count");
-    __shared__ float cen[3][kFpsMaxBatch];
-    __shared__ uint32_t cen_j[kFpsMaxBatch];  // index of each certified centre
+    // certified centres of the batch: x, y, z bits and the point's index
+    __shared__ uint4 cen[kFpsMaxBatch];
+    __shared__ uint4 sink_rec[kWave];  // stores of the certifying wave's other lanes
+    __shared__ int sink_cnt[kWave];
     __shared__ int cen_count, cen_done, sh_t, sh_abort;
     __shared__ uint32_t wt[5][NPW];  // each point wave's top: m, index, x, y, z
     __shared__ uint32_t wb[2][NPW];  // each point wave's bound: m, index
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     if (tid == 0) {
         const float sx = xb[(size_t)3 * start_idx + 0], sy = xb[(size_t)3 * start_idx + 1],
                     sz = xb[(size_t)3 * start_idx + 2];
-        cen[0][0] = sx; cen[1][0] = sy; cen[2][0] = sz;
+        cen[0] = make_uint4(f2u(sx), f2u(sy), f2u(sz), (uint32_t)start_idx);
         cen_count = 1;
         cen_done = 1;
         sh_t = 1;
@@ -412,11 +414,12 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 const int n = __hip_atomic_load(&cen_count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 __asm__ __volatile__("" ::: "memory");
                 for (; a < n; ++a) {
-                    const float cx = cen[0][a], cy = cen[1][a], cz = cen[2][a];
+                    const uint4 c = cen[a];
+                    const float cx = u2f(c.x), cy = u2f(c.y), cz = u2f(c.z);
                     // outputs are written here, not by the certifying wave, so that
                     // wave never waits on a global store
                     if (g == 0 && pw == 0 && point_wave && lane == 0 && out_t0 >= 1) {
-                        ob[out_t0 + a] = jbase + cen_j[a];
+                        ob[out_t0 + a] = jbase + c.w;
                         if (oxb) {
                             oxb[3 * (out_t0 + a) + 0] = cx;
                             oxb[3 * (out_t0 + a) + 1] = cy;
@@ -663,8 +666,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                     const float Y = u2f(lane_value(U == 1 ? cyv[0] : select_u32(cyv, s_sel), kl));
                     const float Z = u2f(lane_value(U == 1 ? czv[0] : select_u32(czv, s_sel), kl));
                     if (lane == 0) {
-                        cen[0][nc] = X; cen[1][nc] = Y; cen[2][nc] = Z;
-                        cen_j[nc] = kj;
+                        cen[nc] = make_uint4(f2u(X), f2u(Y), f2u(Z), kj);
                         // LDS performs one wave's operations in issue order, so a
                         // reader that sees the new count also sees the entry; only
                         // the compiler must keep the order (no wait for completion)
@@ -679,8 +681,49 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                     if (t >= M || nc == kFpsMaxBatch) break;
                 }
             };
+            // One slot per lane (the usual case). The live candidates fill
+            // lanes 0..total-1; the other lanes hold key 0, which the min
+            // update keeps at 0, so they can win only when every live key is 0,
+            // and then lane 0 (live) is the first lane holding the maximum. So
+            // no lane needs a validity mask, the index is read only when the
+            // key ties the bound, and the winning lane publishes its own record.
+            auto certify1 = [&]() {
+                uint32_t m = cm[0];
+                const uint32_t x = cxv[0], y = cyv[0], z = czv[0], j = cj[0];
+                const int limit = min(M - t0, kFpsMaxBatch);
+                int nc = 0;
+                uint32_t floor_m = 0;  // the first centre is certified whatever its key
+                // the candidates' LDS loads are complete here, so the loop's
+                // only LDS operations are its own stores, which need no wait
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                while (true) {
+                    const uint32_t mx = wave_max_u32(m);
+                    const int kl = (int)__builtin_ctzll(ballot(m == mx));
+                    if (mx <= floor_m) {
+                        // certified only while the key exceeds the bound
+                        const uint32_t kj = lane_value(j, kl);
+                        if (nc > 0 && (mx < beta_m || kj >= beta_j)) break;
+                    }
+                    {
+                        // every lane stores; all but the winner into its own sink
+                        // slot, so no branch splits the wave
+                        const bool win = lane == kl;
+                        *(win ? &cen[nc] : &sink_rec[lane]) = make_uint4(x, y, z, j);
+                        __asm__ __volatile__("" ::: "memory");  // entry before count
+                        __hip_atomic_store(win ? &cen_count : &sink_cnt[lane], nc + 1,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    }
+                    const float X = u2f(lane_value(x, kl)), Y = u2f(lane_value(y, kl)),
+                                Z = u2f(lane_value(z, kl));
+                    ++nc;
+                    floor_m = beta_m;
+                    m = min(m, f2u(s32(X, Y, Z, u2f(x), u2f(y), u2f(z))));
+                    if (nc >= limit) break;
+                }
+                t = t0 + nc;
+            };
             if (used <= 1)
-                certify(std::integral_constant<int, 1>{});
+                certify1();
             else if (used <= 2 && CPL >= 2)
                 certify(std::integral_constant<int, (CPL >= 2 ? 2 : 1)>{});
             else
