@@ -85,6 +85,9 @@ bool knn_use_grid(int64_t B, int64_t Q, int64_t P);
 // Waves per workgroup of the grid search.
 int knn_grid_waves(int kcap);
 int bq_queries_per_wave(int64_t rows, int cus, int max_qw);
+// Candidates a workgroup publishes per exchange of the batched FPS when its
+// cloud spans G > 1 workgroups of `npw` point waves (each wave reports two).
+int fps_batch_rg(int64_t G, int npw);
 
 }  // namespace api
 }  // namespace pointops

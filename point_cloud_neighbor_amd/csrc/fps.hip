@@ -271,25 +271,38 @@ __global__ __launch_bounds__(BLOCK) void fps_kernel(
 constexpr int kFpsMaxBatch = 256;  // centres certified per batch at most
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 
-template <int N_>
-__device__ __forceinline__ uint32_t select_u32(const uint32_t (&v)[N_], int i) {
-    uint32_t r = v[0];
-#pragma unroll
-    for (int s = 1; s < N_; ++s) r = i == s ? v[s] : r;
-    return r;
-}
-
-template <int N_>
-__device__ __forceinline__ float select_f32(const float (&v)[N_], int i) {
-    float r = v[0];
-#pragma unroll
-    for (int s = 1; s < N_; ++s) r = i == s ? v[s] : r;
-    return r;
-}
-
 // Key order: larger m first, then smaller index.
 __device__ __forceinline__ bool key_gt(uint32_t ma, uint32_t ja, uint32_t mb, uint32_t jb) {
     return ma > mb || (ma == mb && ja < jb);
+}
+
+// Exchange words of the batched kernel: an 8-bit batch tag in the low byte and
+// 56 payload bits above it. A candidate's five 32-bit fields (m, index, x, y,
+// z: 160 bits) travel in three words; a bound's m and index in two.
+__device__ __forceinline__ uint64_t tag8(uint64_t payload, uint32_t tag) {
+    return (payload << 8) | (tag & 0xFFu);
+}
+
+__device__ __forceinline__ void pack_candidate(uint32_t m, uint32_t j, uint32_t x, uint32_t y,
+                                               uint32_t z, uint64_t& w0, uint64_t& w1,
+                                               uint64_t& w2) {
+    const uint64_t a = (uint64_t)m | ((uint64_t)j << 32);
+    const uint64_t b = (uint64_t)x | ((uint64_t)y << 32);
+    w0 = a & ((1ull << 56) - 1);                       // a bits 0..55
+    w1 = ((a >> 56) | (b << 8)) & ((1ull << 56) - 1);  // a bits 56..63, b bits 0..47
+    w2 = (b >> 48) | ((uint64_t)z << 16);              // b bits 48..63, z
+}
+
+__device__ __forceinline__ void unpack_candidate(uint64_t w0, uint64_t w1, uint64_t w2,
+                                                 uint32_t& m, uint32_t& j, uint32_t& x,
+                                                 uint32_t& y, uint32_t& z) {
+    const uint64_t a = w0 | (w1 << 56);
+    const uint64_t b = (w1 >> 8) | (w2 << 48);
+    m = (uint32_t)a;
+    j = (uint32_t)(a >> 32);
+    x = (uint32_t)b;
+    y = (uint32_t)(b >> 32);
+    z = (uint32_t)(w2 >> 16);
 }
 
 // Largest key over the lanes of a wave whose `use` flag is set. Lanes must be
@@ -328,10 +341,12 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     __shared__ uint4 sink_rec[kWave];  // stores of the certifying wave's other lanes
     __shared__ int sink_cnt[kWave];
     __shared__ int cen_count, cen_done, sh_t, sh_abort;
-    __shared__ uint32_t wt[5][NPW];  // each point wave's top: m, index, x, y, z
-    __shared__ uint32_t wb[2][NPW];  // each point wave's bound: m, index
+    __shared__ uint4 rep[2 * NPW];       // reports of the point waves: m, index, x, y
+    __shared__ uint32_t rep_z[2 * NPW];  // and z
+    __shared__ uint2 bnd[NPW];           // each point wave's bound: m, index
     __shared__ uint32_t live_c[5][kWave * CPL];  // compacted live candidates
-    extern __shared__ uint32_t stage[];  // gathered words, G * (5 * RG + 2)
+    extern __shared__ uint64_t stage[];  // gathered payloads, G * (3 * RG + 2)
+    constexpr int kPoll = 16;  // loads per lane in flight per poll
 
     // this workgroup's cloud
     int g;
@@ -347,7 +362,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
         M = (int)rec[kFrOCnt];
         start_idx = (int)rec[kFrStart];
         RG = (int)rec[kFrRG];
-        stride = 5 * RG + 2;
+        stride = 3 * RG + 2;
         xrow0 = rec[kFrXOff];
         orow0 = rec[kFrOOff];
         jbase = rec[kFrIdxBase];
@@ -445,123 +460,172 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 cen_done = 0;
             }
         } else if (point_wave) {
-            // ---- point waves: top and bound of this wave
-            uint32_t m1 = pm[0], m2 = 0;
-            int p1 = 0, p2 = -1;
+            // ---- point waves: the two largest keys of this wave (its reports)
+            // and a bound, the third largest. Per thread first: its three
+            // largest keys in position order (strict > keeps the earlier,
+            // smaller-index point first on ties), with the coordinates of the
+            // first two.
+            uint32_t m1 = pm[0], m2 = 0, m3 = 0;
+            int p1 = 0, p2 = -1, p3 = -1;
+            float x1 = px[0], y1 = py[0], z1 = pz[0], x2 = 0.f, y2 = 0.f, z2 = 0.f;
 #pragma unroll
             for (int p = 1; p < PPT; ++p) {
-                if (pm[p] > m1) {
-                    m2 = m1; p2 = p1; m1 = pm[p]; p1 = p;
-                } else if (p2 < 0 || pm[p] > m2) {
-                    m2 = pm[p]; p2 = p;
-                }
+                const uint32_t v = pm[p];
+                const bool a1 = v > m1, a2 = !a1 && (p2 < 0 || v > m2),
+                           a3 = !a1 && !a2 && (p3 < 0 || v > m3);
+                // shift down the entries the new key displaces
+                m3 = a1 || a2 ? m2 : (a3 ? v : m3);
+                p3 = a1 || a2 ? p2 : (a3 ? p : p3);
+                m2 = a1 ? m1 : (a2 ? v : m2);
+                p2 = a1 ? p1 : (a2 ? p : p2);
+                x2 = a1 ? x1 : (a2 ? px[p] : x2);
+                y2 = a1 ? y1 : (a2 ? py[p] : y2);
+                z2 = a1 ? z1 : (a2 ? pz[p] : z2);
+                m1 = a1 ? v : m1;
+                p1 = a1 ? p : p1;
+                x1 = a1 ? px[p] : x1;
+                y1 = a1 ? py[p] : y1;
+                z1 = a1 ? pz[p] : z1;
             }
-            const bool valid = wbase < cnt;  // the wave holds real points
-            uint32_t tm, tj, bm, bj;
-            int tl;
-            wave_max_key(m1, (uint32_t)(lo + wbase + lane * PPT + p1), true, tm, tj, tl);
-            const float sx = select_f32(px, p1), sy = select_f32(py, p1), sz = select_f32(pz, p1);
-            const uint32_t tx = lane_value(f2u(sx), tl), ty = lane_value(f2u(sy), tl),
-                           tz = lane_value(f2u(sz), tl);
-            const uint32_t vm = lane == tl ? m2 : m1;
-            const int vp = lane == tl ? p2 : p1;
-            int bl;
-            wave_max_key(vm, (uint32_t)(lo + wbase + lane * PPT + vp), vp >= 0, bm, bj, bl);
+            const int pos = lo + wbase + lane * PPT;  // index of this thread's first point
+            // the k-th report is a real point only if the wave holds more than
+            // k real points (real positions come first and win ties)
+            const int reals = cnt - wbase;
+            uint32_t am, aj, bm, bj, cm_, cj_;
+            int al, bl, cl;
+            wave_max_key(m1, (uint32_t)(pos + p1), true, am, aj, al);
+            const uint32_t ax = lane_value(f2u(x1), al), ay = lane_value(f2u(y1), al),
+                           az = lane_value(f2u(z1), al);
+            const bool in1 = lane == al;
+            // second: lane al offers its second key, the others their first
+            wave_max_key(in1 ? m2 : m1, (uint32_t)(pos + (in1 ? p2 : p1)), !in1 || p2 >= 0, bm, bj,
+                         bl);
+            const uint32_t bx = lane_value(f2u(in1 ? x2 : x1), bl < 0 ? 0 : bl),
+                           by = lane_value(f2u(in1 ? y2 : y1), bl < 0 ? 0 : bl),
+                           bz = lane_value(f2u(in1 ? z2 : z1), bl < 0 ? 0 : bl);
+            // bound: the largest key not reported
+            const bool in2 = lane == bl;
+            const int taken = (int)in1 + (int)in2;
+            const uint32_t nm = taken == 0 ? m1 : (taken == 1 ? m2 : m3);
+            const int np = taken == 0 ? p1 : (taken == 1 ? p2 : p3);
+            wave_max_key(nm, (uint32_t)(pos + np), np >= 0, cm_, cj_, cl);
             if (lane == 0) {
-                const int w = pw;
-                wt[0][w] = tm; wt[1][w] = valid ? tj : kNone; wt[2][w] = tx; wt[3][w] = ty;
-                wt[4][w] = tz;
-                wb[0][w] = valid ? bm : 0u; wb[1][w] = valid ? bj : kNone;
+                rep[2 * pw + 0] = make_uint4(am, reals > 0 ? aj : kNone, ax, ay);
+                rep_z[2 * pw + 0] = az;
+                rep[2 * pw + 1] = make_uint4(bm, reals > 1 && bl >= 0 ? bj : kNone, bx, by);
+                rep_z[2 * pw + 1] = bz;
+                const bool bv = reals > 2 && cl >= 0;
+                bnd[pw] = make_uint2(bv ? cm_ : 0u, bv ? cj_ : kNone);
             }
         }
         __syncthreads();
         if (wave != 0) continue;
 
         // ---- wave 0: exchange, then certify centres ----------------------------
+        // Reports r = 2 * wave + k (k = 0, 1) are in index order, as are the
+        // waves: lane order is index order in every reduction below.
+        constexpr int NR = 2 * NPW;
         uint32_t cm[CPL], cj[CPL], cxv[CPL], cyv[CPL], czv[CPL];
         uint32_t beta_m = 0, beta_j = kNone;
         uint32_t abort = 0;
         {
-            const bool own = lane < NPW;
-            const uint32_t tm = own ? wt[0][lane] : 0u, tj = own ? wt[1][lane] : kNone;
-            const uint32_t bm = own ? wb[0][lane] : 0u, bj = own ? wb[1][lane] : kNone;
-            const bool tv = tj != kNone;
+            const bool own = lane < NR;
+            const uint4 r = own ? rep[lane] : make_uint4(0u, kNone, 0u, 0u);
+            const uint32_t rz = own ? rep_z[lane] : 0u;
+            // lane w < NPW: wave w's bound and its two reports' keys
+            const bool wl = lane < NPW;
+            const uint2 wbd = wl ? bnd[lane] : make_uint2(0u, kNone);
+            const uint4 r0 = wl ? rep[2 * lane] : make_uint4(0u, kNone, 0u, 0u);
+            const uint4 r1 = wl ? rep[2 * lane + 1] : make_uint4(0u, kNone, 0u, 0u);
+            const bool rv = r.y != kNone;
             if (G == 1) {
-                // candidates: every wave's top, lane = wave (index order)
+                // candidates: every report, lane = report
 #pragma unroll
                 for (int s = 0; s < CPL; ++s) {
-                    cm[s] = s == 0 ? tm : 0u;
-                    cj[s] = s == 0 ? tj : kNone;
-                    cxv[s] = s == 0 && own ? wt[2][lane] : 0u;
-                    cyv[s] = s == 0 && own ? wt[3][lane] : 0u;
-                    czv[s] = s == 0 && own ? wt[4][lane] : 0u;
+                    cm[s] = s == 0 ? r.x : 0u;
+                    cj[s] = s == 0 ? r.y : kNone;
+                    cxv[s] = s == 0 ? r.z : 0u;
+                    cyv[s] = s == 0 ? r.w : 0u;
+                    czv[s] = s == 0 ? rz : 0u;
                 }
                 int l;
-                wave_max_key(bm, bj, bj != kNone, beta_m, beta_j, l);
+                wave_max_key(wbd.x, wbd.y, wbd.y != kNone, beta_m, beta_j, l);
             } else {
-                // publish this workgroup's RG best wave tops (in index order) and
-                // its bound: the best of the wave bounds and the unpublished tops
+                // publish this workgroup's RG best reports (in index order) and
+                // its bound: the best of the wave bounds and unpublished reports
                 uint64_t sel = 0;
-                for (int r = 0; r < RG; ++r) {
+                for (int k = 0; k < RG; ++k) {
                     uint32_t om, oj;
                     int ol;
-                    wave_max_key(tm, tj, tv && !((sel >> lane) & 1ull), om, oj, ol);
+                    wave_max_key(r.x, r.y, rv && !((sel >> lane) & 1ull), om, oj, ol);
                     if (ol >= 0) sel |= 1ull << ol;
                 }
-                const bool mine = (sel >> lane) & 1ull;
-                const bool unpub = tv && !mine;
+                uint32_t um = wbd.x, uj = wbd.y;  // this wave's largest unpublished key
+                if (wl) {
+                    const bool s0 = (sel >> (2 * lane)) & 1ull, s1 = (sel >> (2 * lane + 1)) & 1ull;
+                    if (!s0 && r0.y != kNone && (uj == kNone || key_gt(r0.x, r0.y, um, uj))) {
+                        um = r0.x;
+                        uj = r0.y;
+                    }
+                    if (!s1 && r1.y != kNone && (uj == kNone || key_gt(r1.x, r1.y, um, uj))) {
+                        um = r1.x;
+                        uj = r1.y;
+                    }
+                }
                 uint32_t gm, gj;
                 int gl;
-                wave_max_key(unpub && key_gt(tm, tj, bm, bj) ? tm : bm,
-                             unpub && key_gt(tm, tj, bm, bj) ? tj : bj,
-                             unpub || bj != kNone, gm, gj, gl);
+                wave_max_key(um, uj, uj != kNone, gm, gj, gl);
+                // this batch's word set: G * RG candidates of 3 words, then G
+                // bounds of 2 words
                 const uint32_t tag = batch;
                 uint64_t* set = cw + (size_t)(batch & 1) * G * stride;
-                uint64_t* my = set + (size_t)g * stride;
+                const bool mine = (sel >> lane) & 1ull;
                 const int rank = (int)lanes_below(sel);
                 const int nsel = __popcll(sel);
                 if (mine) {
-                    __hip_atomic_store(&my[rank * 5 + 0], tagged(tm, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&my[rank * 5 + 1], tagged(tj, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&my[rank * 5 + 2], tagged(wt[2][lane], tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&my[rank * 5 + 3], tagged(wt[3][lane], tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&my[rank * 5 + 4], tagged(wt[4][lane], tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    uint64_t w0, w1, w2;
+                    pack_candidate(r.x, r.y, r.z, r.w, rz, w0, w1, w2);
+                    uint64_t* w = set + (size_t)(g * RG + rank) * 3;
+                    __hip_atomic_store(&w[0], tag8(w0, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&w[1], tag8(w1, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&w[2], tag8(w2, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                // unused candidate ranks are published as empty, and the bound
-                for (int r = nsel + lane; r < RG; r += kWave) {
-                    __hip_atomic_store(&my[r * 5 + 0], tagged(0u, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&my[r * 5 + 1], tagged(kNone, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&my[r * 5 + 2], tagged(0u, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&my[r * 5 + 3], tagged(0u, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&my[r * 5 + 4], tagged(0u, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                // unused candidate ranks are published as empty
+                for (int k = nsel + lane; k < RG; k += kWave) {
+                    uint64_t w0, w1, w2;
+                    pack_candidate(0u, kNone, 0u, 0u, 0u, w0, w1, w2);
+                    uint64_t* w = set + (size_t)(g * RG + k) * 3;
+                    __hip_atomic_store(&w[0], tag8(w0, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&w[1], tag8(w1, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&w[2], tag8(w2, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
                 if (lane == 0) {
-                    __hip_atomic_store(&my[RG * 5 + 0], tagged(gm, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&my[RG * 5 + 1], tagged(gj, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    uint64_t* w = set + (size_t)G * RG * 3 + (size_t)g * 2;
+                    __hip_atomic_store(&w[0], tag8(gm, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&w[1], tag8(gj, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                // gather every workgroup's words of this batch into LDS: up to 16
-                // loads per lane in flight per poll, so a poll costs one round trip
-                const int per = RG * 5 + 2;
-                const int total = G * per;  // slots are contiguous: word w of the set
-                for (int w0 = 0; w0 < total && !abort; w0 += 16 * kWave) {
+                // gather the whole set into LDS: up to kPoll loads per lane in
+                // flight per poll, so a poll costs one round trip
+                const int total = G * stride;
+                for (int w0 = 0; w0 < total && !abort; w0 += kPoll * kWave) {
                     uint32_t spins = 0;
                     while (true) {
-                        uint64_t v[16];
+                        uint64_t v[kPoll];
 #pragma unroll
-                        for (int k = 0; k < 16; ++k) {
+                        for (int k = 0; k < kPoll; ++k) {
                             const int w = w0 + k * kWave + lane;
                             v[k] = w < total ? __hip_atomic_load(&set[w], __ATOMIC_RELAXED,
                                                                  __HIP_MEMORY_SCOPE_AGENT)
-                                             : (uint64_t)tag;
+                                             : tag8(0, tag);
                         }
                         bool ready = true;
 #pragma unroll
-                        for (int k = 0; k < 16; ++k) ready &= (uint32_t)v[k] == tag;
+                        for (int k = 0; k < kPoll; ++k) ready &= (uint32_t)(v[k] & 0xFFu) == (tag & 0xFFu);
                         if (ballot(!ready) == 0) {
 #pragma unroll
-                            for (int k = 0; k < 16; ++k) {
+                            for (int k = 0; k < kPoll; ++k) {
                                 const int w = w0 + k * kWave + lane;
-                                if (w < total) stage[w] = (uint32_t)(v[k] >> 32);
+                                if (w < total) stage[w] = v[k] >> 8;
                             }
                             break;
                         }
@@ -571,26 +635,30 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 }
                 __builtin_amdgcn_s_waitcnt(0);  // LDS writes of this wave complete
                 __builtin_amdgcn_wave_barrier();
-                // candidates: q = wg * RG + r, lane-major (lane q / CPL, slot q % CPL)
+                // candidates: q = wg * RG + r (index order), lane-major (lane q / CPL,
+                // slot q % CPL), three words each
 #pragma unroll
                 for (int s = 0; s < CPL; ++s) {
                     const int q = lane * CPL + s;
                     const bool in = q < G * RG;
-                    const int off = in ? (q / RG) * per + (q % RG) * 5 : 0;
-                    cm[s] = in ? stage[off + 0] : 0u;
-                    cj[s] = in ? stage[off + 1] : kNone;
-                    cxv[s] = in ? stage[off + 2] : 0u;
-                    cyv[s] = in ? stage[off + 3] : 0u;
-                    czv[s] = in ? stage[off + 4] : 0u;
+                    const uint64_t* c = stage + (in ? q : 0) * 3;
+                    uint32_t m, j, x, y, z;
+                    unpack_candidate(c[0], c[1], c[2], m, j, x, y, z);
+                    cm[s] = in ? m : 0u;
+                    cj[s] = in ? j : kNone;
+                    cxv[s] = in ? x : 0u;
+                    cyv[s] = in ? y : 0u;
+                    czv[s] = in ? z : 0u;
                 }
                 // beta: the largest bound over the workgroups (lane order = index order)
                 beta_m = 0;
                 beta_j = kNone;
+                const uint64_t* bw = stage + G * RG * 3;
                 for (int base = 0; base < G; base += kWave) {
                     const int wg = base + lane;
                     const bool in = wg < G;
-                    const uint32_t m = in ? stage[wg * per + RG * 5 + 0] : 0u;
-                    const uint32_t j = in ? stage[wg * per + RG * 5 + 1] : kNone;
+                    const uint32_t m = in ? (uint32_t)bw[wg * 2 + 0] : 0u;
+                    const uint32_t j = in ? (uint32_t)bw[wg * 2 + 1] : kNone;
                     uint32_t om, oj;
                     int ol;
                     wave_max_key(m, j, in && j != kNone, om, oj, ol);
@@ -649,22 +717,23 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 int nc = 0;
                 while (true) {
                     // largest key among the valid candidates (lane-major = index order)
-                    uint32_t lm = 0;
-                    int ls = -1;
+                    uint32_t lm = 0, lj = kNone, lx = 0, ly = 0, lz = 0;
 #pragma unroll
-                    for (int s = 0; s < U; ++s)
-                        if (cj[s] != kNone && (ls < 0 || cm[s] > lm)) { lm = cm[s]; ls = s; }
+                    for (int s = 0; s < U; ++s) {
+                        const bool b = cj[s] != kNone && (lj == kNone || cm[s] > lm);
+                        lm = b ? cm[s] : lm;
+                        lj = b ? cj[s] : lj;
+                        lx = b ? cxv[s] : lx;
+                        ly = b ? cyv[s] : ly;
+                        lz = b ? czv[s] : lz;
+                    }
                     uint32_t km, kj;
                     int kl;
-                    if (U == 1)
-                        wave_max_key(cm[0], cj[0], cj[0] != kNone, km, kj, kl);
-                    else
-                        wave_max_key(lm, select_u32(cj, ls < 0 ? 0 : ls), ls >= 0, km, kj, kl);
+                    wave_max_key(lm, lj, lj != kNone, km, kj, kl);
                     if (nc > 0 && !key_gt(km, kj, beta_m, beta_j)) break;  // not certified
-                    const int s_sel = U == 1 ? 0 : (ls < 0 ? 0 : ls);
-                    const float X = u2f(lane_value(U == 1 ? cxv[0] : select_u32(cxv, s_sel), kl));
-                    const float Y = u2f(lane_value(U == 1 ? cyv[0] : select_u32(cyv, s_sel), kl));
-                    const float Z = u2f(lane_value(U == 1 ? czv[0] : select_u32(czv, s_sel), kl));
+                    const float X = u2f(lane_value(lx, kl));
+                    const float Y = u2f(lane_value(ly, kl));
+                    const float Z = u2f(lane_value(lz, kl));
                     if (lane == 0) {
                         cen[nc] = make_uint4(f2u(X), f2u(Y), f2u(Z), kj);
                         // LDS performs one wave's operations in issue order, so a
@@ -722,10 +791,50 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 }
                 t = t0 + nc;
             };
+            // Two slots per lane: the same with each lane's better slot first
+            // (ties keep slot 0, the smaller index); padding entries again
+            // hold key 0 and come after the live ones.
+            auto certify2 = [&](auto c_) {
+                constexpr int C = decltype(c_)::value;  // >= 2 where called
+                uint32_t m0 = cm[0], m1 = cm[C - 1];
+                const uint32_t x0 = cxv[0], y0 = cyv[0], z0 = czv[0], j0 = cj[0];
+                const uint32_t x1 = cxv[C - 1], y1 = cyv[C - 1], z1 = czv[C - 1], j1 = cj[C - 1];
+                const int limit = min(M - t0, kFpsMaxBatch);
+                int nc = 0;
+                uint32_t floor_m = 0;
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), as above
+                while (true) {
+                    const bool second = m1 > m0;
+                    const uint32_t lm = second ? m1 : m0;
+                    const uint32_t mx = wave_max_u32(lm);
+                    const int kl = (int)__builtin_ctzll(ballot(lm == mx));
+                    const uint32_t wx = second ? x1 : x0, wy = second ? y1 : y0,
+                                   wz = second ? z1 : z0, wj = second ? j1 : j0;
+                    if (mx <= floor_m) {
+                        const uint32_t kj = lane_value(wj, kl);
+                        if (nc > 0 && (mx < beta_m || kj >= beta_j)) break;
+                    }
+                    {
+                        const bool win = lane == kl;
+                        *(win ? &cen[nc] : &sink_rec[lane]) = make_uint4(wx, wy, wz, wj);
+                        __asm__ __volatile__("" ::: "memory");  // entry before count
+                        __hip_atomic_store(win ? &cen_count : &sink_cnt[lane], nc + 1,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    }
+                    const float X = u2f(lane_value(wx, kl)), Y = u2f(lane_value(wy, kl)),
+                                Z = u2f(lane_value(wz, kl));
+                    ++nc;
+                    floor_m = beta_m;
+                    m0 = min(m0, f2u(s32(X, Y, Z, u2f(x0), u2f(y0), u2f(z0))));
+                    m1 = min(m1, f2u(s32(X, Y, Z, u2f(x1), u2f(y1), u2f(z1))));
+                    if (nc >= limit) break;
+                }
+                t = t0 + nc;
+            };
             if (used <= 1)
                 certify1();
-            else if (used <= 2 && CPL >= 2)
-                certify(std::integral_constant<int, (CPL >= 2 ? 2 : 1)>{});
+            else if (CPL >= 2 && used <= 2)
+                certify2(std::integral_constant<int, (CPL >= 2 ? 2 : 1)>{});
             else
                 certify(std::integral_constant<int, CPL>{});
         }
@@ -812,13 +921,13 @@ int fps_batch_ppt_round(int ppt) {
     return -1;
 }
 
-int fps_batch_stride(int rg) { return 5 * rg + 2; }  // words per workgroup, contiguous
+int fps_batch_stride(int rg) { return 3 * rg + 2; }  // words per workgroup
 
 size_t fps_batch_workspace_bytes(int64_t B, int64_t G, int rg) {
     return G > 1 ? 256 + (size_t)B * 2 * (size_t)G * fps_batch_stride(rg) * sizeof(uint64_t) : 256;
 }
 
-size_t fps_batch_lds_bytes(int G, int rg) { return G > 1 ? (size_t)G * (5 * rg + 2) * 4 : 0; }
+size_t fps_batch_lds_bytes(int G, int rg) { return G > 1 ? (size_t)G * (3 * rg + 2) * 8 : 0; }
 
 // The (points per thread, block, candidates per lane) triples that are built.
 template <int PPT_, int BLOCK_, int CPL_>

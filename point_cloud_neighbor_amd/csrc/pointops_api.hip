@@ -122,6 +122,14 @@ int knn_grid_waves(int kcap) {
 // Ball Query: queries per wave. Fewer queries per wave until the grid is about
 // one device-full of waves; at most 8 (measured faster than 16 on 100k x 100k:
 // the shorter waves balance better).
+// Up to 256 candidates per cloud (four slots per lane of the certifying wave),
+// at most the workgroup's 2 * npw reports.
+int fps_batch_rg(int64_t G, int npw) {
+    const long env = env_long("POINTOPS_FPS_RG", 0);
+    const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(2 * npw, 256 / std::max<int64_t>(G, 1)));
+    return (int)(env > 0 ? std::min<int64_t>(env, cap) : cap);
+}
+
 int bq_queries_per_wave(int64_t rows, int cus, int max_qw) {
     const int64_t slots = (int64_t)std::max(1, cus) * 4 * 8;
     int qw = max_qw;
@@ -192,12 +200,11 @@ FpsPlan fps_plan_step(int64_t B, int64_t N, const DeviceInfo& dev) {
 // exchange of candidates slower than the update they save; measured on 100k
 // and 1M points) and, when a cloud spans several workgroups, no more
 // workgroups than the device holds at once (they wait on each other). Each workgroup publishes
-// up to 128 / G of its wave tops per exchange; the certifying wave holds at most
+// up to 256 / G of its waves' reports per exchange; the certifying wave holds at most
 // 256 candidates.
 FpsPlan fps_plan_batch(int64_t B, int64_t N, const DeviceInfo& dev) {
     const int cus = std::max(1, dev.cus);
     const long g_env = env_long("POINTOPS_FPS_WG_PER_CLOUD", 0);
-    const long rg_env = env_long("POINTOPS_FPS_RG", 0);
     const long block_env = env_long("POINTOPS_FPS_BLOCK", 0);
     int64_t want = g_env > 0 ? g_env : (N <= 2048 ? 1 : std::min<int64_t>((N + 1599) / 1600, 128));
     int block = block_env == 256 || block_env == 1024 ? (int)block_env : 0;
@@ -221,10 +228,8 @@ FpsPlan fps_plan_batch(int64_t B, int64_t N, const DeviceInfo& dev) {
             p.cpl = 1;
         } else {
             if (G > 256) break;
-            int rg = (int)std::max<long>(1, std::min<long>(npw, rg_env > 0 ? rg_env : 128 / G));
-            while (G * rg > 256) --rg;
-            p.rg = rg;
-            const int64_t cand = G * rg;
+            p.rg = fps_batch_rg(G, npw);
+            const int64_t cand = G * p.rg;
             p.cpl = cand <= 64 ? 1 : cand <= 128 ? 2 : 4;
             if (p.block == 256 && p.cpl > 1) { block = 1024; continue; }
         }

@@ -204,8 +204,7 @@ RaggedFps plan_fps_ragged(const int64_t* x_off, const int64_t* x_cnt, const int6
         for (int64_t b : active) {
             const int64_t g = G[(size_t)b];
             if (g == 1) { rg[(size_t)b] = npw; continue; }
-            int64_t r = std::max<int64_t>(1, std::min<int64_t>(npw, 128 / g));
-            while (g * r > 256) --r;
+            const int64_t r = fps_batch_rg(g, npw);
             rg[(size_t)b] = r;
             cand = std::max(cand, g * r);
             multi += g;
