@@ -336,7 +336,9 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     // itself; the other waves are the point waves.
     constexpr int NPW = NW - NW / 4;
     static_assert(NW % 4 == 0 && NPW >= 1 && NPW <= kWave, "wave count");
-    // certified centres of the batch: x, y, z bits and the point's index
+    // Certified centres of the batch: x, y, z bits and the point's index. An
+    // entry is written before the count that includes it (LDS performs one
+    // wave's operations in issue order), and readers load the count first.
     __shared__ uint4 cen[kFpsMaxBatch];
     __shared__ uint4 sink_rec[kWave];  // stores of the certifying wave's other lanes
     __shared__ int sink_cnt[kWave];
@@ -422,6 +424,9 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     while (true) {
         // ---- point waves: fold in the centres of the current batch as they come
         if (point_wave) {
+            // outputs are written here, not by the certifying wave, so that
+            // wave never waits on a global store
+            const bool writer = g == 0 && pw == 0 && out_t0 >= 1;
             int a = 0;
             while (true) {
                 const int d = __hip_atomic_load(&cen_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -431,14 +436,14 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 for (; a < n; ++a) {
                     const uint4 c = cen[a];
                     const float cx = u2f(c.x), cy = u2f(c.y), cz = u2f(c.z);
-                    // outputs are written here, not by the certifying wave, so that
-                    // wave never waits on a global store
-                    if (g == 0 && pw == 0 && point_wave && lane == 0 && out_t0 >= 1) {
-                        ob[out_t0 + a] = jbase + c.w;
-                        if (oxb) {
-                            oxb[3 * (out_t0 + a) + 0] = cx;
-                            oxb[3 * (out_t0 + a) + 1] = cy;
-                            oxb[3 * (out_t0 + a) + 2] = cz;
+                    if (writer) {
+                        if (lane == 0) {
+                            ob[out_t0 + a] = jbase + c.w;
+                            if (oxb) {
+                                oxb[3 * (out_t0 + a) + 0] = cx;
+                                oxb[3 * (out_t0 + a) + 1] = cy;
+                                oxb[3 * (out_t0 + a) + 2] = cz;
+                            }
                         }
                     }
 #pragma unroll
@@ -736,10 +741,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                     const float Z = u2f(lane_value(lz, kl));
                     if (lane == 0) {
                         cen[nc] = make_uint4(f2u(X), f2u(Y), f2u(Z), kj);
-                        // LDS performs one wave's operations in issue order, so a
-                        // reader that sees the new count also sees the entry; only
-                        // the compiler must keep the order (no wait for completion)
-                        __asm__ __volatile__("" ::: "memory");
+                        __asm__ __volatile__("" ::: "memory");  // entry before count
                         __hip_atomic_store(&cen_count, nc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                     }
                     ++nc;
@@ -750,67 +752,40 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                     if (t >= M || nc == kFpsMaxBatch) break;
                 }
             };
-            // One slot per lane (the usual case). The live candidates fill
-            // lanes 0..total-1; the other lanes hold key 0, which the min
-            // update keeps at 0, so they can win only when every live key is 0,
-            // and then lane 0 (live) is the first lane holding the maximum. So
-            // no lane needs a validity mask, the index is read only when the
-            // key ties the bound, and the winning lane publishes its own record.
-            auto certify1 = [&]() {
-                uint32_t m = cm[0];
-                const uint32_t x = cxv[0], y = cyv[0], z = czv[0], j = cj[0];
+            // One or two slots per lane (the usual cases). The live candidates
+            // come first in lane-major order; the other slots hold key 0,
+            // which the min update keeps at 0, so they can win only when every
+            // live key is 0, and then lane 0, slot 0 (live) is the first entry
+            // holding the maximum. So no slot needs a validity mask, the index
+            // is read only when the key reaches the bound, and the winning lane
+            // publishes its own entry and the count (the others write their
+            // sink slots, so no branch splits the wave). With two slots each lane offers its
+            // better one, slot 0 on ties (the smaller index).
+            auto certify_fast = [&](auto c_) {
+                constexpr int C = decltype(c_)::value;
+                constexpr int S1 = CPL > 1 ? 1 : 0;
+                uint32_t m0 = cm[0], m1 = C == 2 ? cm[S1] : 0u;
+                const uint32_t x0 = cxv[0], y0 = cyv[0], z0 = czv[0], j0 = cj[0];
+                const uint32_t x1 = cxv[S1], y1 = cyv[S1], z1 = czv[S1], j1 = cj[S1];
                 const int limit = min(M - t0, kFpsMaxBatch);
                 int nc = 0;
-                uint32_t floor_m = 0;  // the first centre is certified whatever its key
+                // keys at or below floor_m take the slow path: the bound check,
+                // or the exit once the batch is full (the first centre is
+                // certified whatever its key)
+                uint32_t floor_m = 0;
                 // the candidates' LDS loads are complete here, so the loop's
                 // only LDS operations are its own stores, which need no wait
                 __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
                 while (true) {
-                    const uint32_t mx = wave_max_u32(m);
-                    const int kl = (int)__builtin_ctzll(ballot(m == mx));
-                    if (mx <= floor_m) {
-                        // certified only while the key exceeds the bound
-                        const uint32_t kj = lane_value(j, kl);
-                        if (nc > 0 && (mx < beta_m || kj >= beta_j)) break;
-                    }
-                    {
-                        // every lane stores; all but the winner into its own sink
-                        // slot, so no branch splits the wave
-                        const bool win = lane == kl;
-                        *(win ? &cen[nc] : &sink_rec[lane]) = make_uint4(x, y, z, j);
-                        __asm__ __volatile__("" ::: "memory");  // entry before count
-                        __hip_atomic_store(win ? &cen_count : &sink_cnt[lane], nc + 1,
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                    }
-                    const float X = u2f(lane_value(x, kl)), Y = u2f(lane_value(y, kl)),
-                                Z = u2f(lane_value(z, kl));
-                    ++nc;
-                    floor_m = beta_m;
-                    m = min(m, f2u(s32(X, Y, Z, u2f(x), u2f(y), u2f(z))));
-                    if (nc >= limit) break;
-                }
-                t = t0 + nc;
-            };
-            // Two slots per lane: the same with each lane's better slot first
-            // (ties keep slot 0, the smaller index); padding entries again
-            // hold key 0 and come after the live ones.
-            auto certify2 = [&](auto c_) {
-                constexpr int C = decltype(c_)::value;  // >= 2 where called
-                uint32_t m0 = cm[0], m1 = cm[C - 1];
-                const uint32_t x0 = cxv[0], y0 = cyv[0], z0 = czv[0], j0 = cj[0];
-                const uint32_t x1 = cxv[C - 1], y1 = cyv[C - 1], z1 = czv[C - 1], j1 = cj[C - 1];
-                const int limit = min(M - t0, kFpsMaxBatch);
-                int nc = 0;
-                uint32_t floor_m = 0;
-                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), as above
-                while (true) {
-                    const bool second = m1 > m0;
+                    const bool second = C == 2 && m1 > m0;
                     const uint32_t lm = second ? m1 : m0;
-                    const uint32_t mx = wave_max_u32(lm);
-                    const int kl = (int)__builtin_ctzll(ballot(lm == mx));
                     const uint32_t wx = second ? x1 : x0, wy = second ? y1 : y0,
                                    wz = second ? z1 : z0, wj = second ? j1 : j0;
+                    const uint32_t mx = wave_max_u32(lm);
+                    const int kl = (int)__builtin_ctzll(ballot(lm == mx));
                     if (mx <= floor_m) {
+                        if (nc >= limit) break;
+                        // certified only while the key exceeds the bound
                         const uint32_t kj = lane_value(wj, kl);
                         if (nc > 0 && (mx < beta_m || kj >= beta_j)) break;
                     }
@@ -824,17 +799,16 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                     const float X = u2f(lane_value(wx, kl)), Y = u2f(lane_value(wy, kl)),
                                 Z = u2f(lane_value(wz, kl));
                     ++nc;
-                    floor_m = beta_m;
+                    floor_m = nc >= limit ? 0xFFFFFFFFu : beta_m;
                     m0 = min(m0, f2u(s32(X, Y, Z, u2f(x0), u2f(y0), u2f(z0))));
-                    m1 = min(m1, f2u(s32(X, Y, Z, u2f(x1), u2f(y1), u2f(z1))));
-                    if (nc >= limit) break;
+                    if (C == 2) m1 = min(m1, f2u(s32(X, Y, Z, u2f(x1), u2f(y1), u2f(z1))));
                 }
                 t = t0 + nc;
             };
             if (used <= 1)
-                certify1();
+                certify_fast(std::integral_constant<int, 1>{});
             else if (CPL >= 2 && used <= 2)
-                certify2(std::integral_constant<int, (CPL >= 2 ? 2 : 1)>{});
+                certify_fast(std::integral_constant<int, (CPL >= 2 ? 2 : 1)>{});
             else
                 certify(std::integral_constant<int, CPL>{});
         }
