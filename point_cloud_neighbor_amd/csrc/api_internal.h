@@ -32,6 +32,7 @@ size_t fps_batch_workspace_bytes(int64_t B, int64_t G, int rg);
 size_t fps_batch_lds_bytes(int G, int rg);
 int fps_batch_ppt_round(int ppt);
 int fps_batch_stride(int rg);
+int fps_batch_point_waves(int block);  // waves of a workgroup that hold points
 hipError_t launch_knn(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
                       int64_t*, int, int, const int64_t*, int, int64_t, int, hipStream_t);
 hipError_t launch_ball_query_backward(const float*, const float*, const int64_t*, const float*,

@@ -331,11 +331,12 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     int stride, uint32_t* __restrict__ status, uint32_t spin_limit,
     const int64_t* __restrict__ seg, int nseg) {
     constexpr int NW = BLOCK / kWave;
-    // Waves whose index is a multiple of 4 hold no points, so the certifying
-    // wave 0 has its SIMD (waves go round-robin over the 4 SIMDs of a CU) to
-    // itself; the other waves are the point waves.
-    constexpr int NPW = NW - NW / 4;
-    static_assert(NW % 4 == 0 && NPW >= 1 && NPW <= kWave, "wave count");
+    // Every wave but the certifying wave 0 holds points. Waves go round-robin
+    // over the 4 SIMDs of a CU, so wave 0 shares its SIMD with the point waves
+    // 4, 8, 12; it runs at a higher priority, so they take the issue cycles it
+    // leaves idle.
+    constexpr int NPW = NW - 1;
+    static_assert(NW % 4 == 0 && NPW >= 1 && 2 * NPW <= kWave, "wave count");
     // Certified centres of the batch: x, y, z bits and the point's index. An
     // entry is written before the count that includes it (LDS performs one
     // wave's operations in issue order), and readers load the count first.
@@ -383,8 +384,8 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     const float* xb = xyz + xrow0 * 3;
     const int lo = g * slice;
     const int cnt = min(N, lo + slice) - lo;  // >= 1
-    const bool point_wave = wave % 4 != 0;
-    const int pw = wave - 1 - wave / 4;       // index among the point waves
+    const bool point_wave = wave != 0;
+    const int pw = wave - 1;                  // index among the point waves
     const int u = pw * kWave + lane;          // point-thread id
     const int wbase = pw * kWave * PPT;       // first slice position of this wave
 
@@ -896,6 +897,8 @@ int fps_batch_ppt_round(int ppt) {
 }
 
 int fps_batch_stride(int rg) { return 3 * rg + 2; }  // words per workgroup
+
+int fps_batch_point_waves(int block) { return block / kWave - 1; }
 
 size_t fps_batch_workspace_bytes(int64_t B, int64_t G, int rg) {
     return G > 1 ? 256 + (size_t)B * 2 * (size_t)G * fps_batch_stride(rg) * sizeof(uint64_t) : 256;

@@ -215,7 +215,7 @@ FpsPlan fps_plan_batch(int64_t B, int64_t N, const DeviceInfo& dev) {
         const int64_t slice = (N + G - 1) / G;
         p.G = (int)G;
         p.block = block ? block : (slice <= 768 ? 256 : 1024);
-        const int npw = p.block / 64 - p.block / 256;  // point waves (every 4th holds none)
+        const int npw = pointops::fps_batch_point_waves(p.block);
         p.ppt = pointops::fps_batch_ppt_round((int)((slice + npw * 64 - 1) / (npw * 64)));
         if (p.ppt < 0) {  // more than 16 points per thread
             if (p.block == 256) { block = 1024; continue; }

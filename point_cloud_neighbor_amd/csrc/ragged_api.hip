@@ -191,7 +191,7 @@ RaggedFps plan_fps_ragged(const int64_t* x_off, const int64_t* x_cnt, const int6
             slice_max = std::max(slice_max, (x_cnt[b] + G[(size_t)b] - 1) / G[(size_t)b]);
         }
         p.block = block ? block : (slice_max <= 768 ? 256 : 1024);
-        const int npw = p.block / 64 - p.block / 256;
+        const int npw = pointops::fps_batch_point_waves(p.block);
         p.ppt = pointops::fps_batch_ppt_round((int)((slice_max + npw * 64 - 1) / (npw * 64)));
         if (p.ppt < 0) {  // more than 16 points per thread somewhere
             if (p.block == 256) { block = 1024; continue; }
