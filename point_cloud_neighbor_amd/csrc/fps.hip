@@ -344,10 +344,14 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     __shared__ uint4 sink_rec[kWave];  // stores of the certifying wave's other lanes
     __shared__ int sink_cnt[kWave];
     __shared__ int cen_count, cen_done, sh_t, sh_abort;
-    __shared__ uint4 rep[2 * NPW];       // reports of the point waves: m, index, x, y
-    __shared__ uint32_t rep_z[2 * NPW];  // and z
-    __shared__ uint2 bnd[NPW];           // each point wave's bound: m, index
-    __shared__ uint32_t live_c[5][kWave * CPL];  // compacted live candidates
+    // reports of the point waves (m, index, x, y; z) and each wave's bound
+    // (m, index), one entry per lane of the reading wave: the entries past the
+    // last report or wave stay empty
+    __shared__ uint4 rep[kWave];
+    __shared__ uint32_t rep_z[kWave];
+    __shared__ uint2 bnd[kWave];
+    __shared__ uint4 live_a[kWave * CPL];  // compacted live candidates: m, index, x, y
+    __shared__ uint32_t live_z[kWave * CPL];  // and z
     extern __shared__ uint64_t stage[];  // gathered payloads, G * (3 * RG + 2)
     constexpr int kPoll = 16;  // loads per lane in flight per poll
 
@@ -417,7 +421,12 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
             if (oxb) { oxb[0] = sx; oxb[1] = sy; oxb[2] = sz; }
         }
     }
-    if (wave == 0) __builtin_amdgcn_s_setprio(3);
+    if (wave == 0) {
+        rep[lane] = make_uint4(0u, kNone, 0u, 0u);
+        rep_z[lane] = 0u;
+        bnd[lane] = make_uint2(0u, kNone);
+        __builtin_amdgcn_s_setprio(3);
+    }
     __syncthreads();
 
     uint32_t batch = 0;
@@ -530,54 +539,51 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
         // ---- wave 0: exchange, then certify centres ----------------------------
         // Reports r = 2 * wave + k (k = 0, 1) are in index order, as are the
         // waves: lane order is index order in every reduction below.
-        constexpr int NR = 2 * NPW;
-        uint32_t cm[CPL], cj[CPL], cxv[CPL], cyv[CPL], czv[CPL];
         uint32_t beta_m = 0, beta_j = kNone;
         uint32_t abort = 0;
+        uint32_t total = 0;  // live candidates, compacted into live_a / live_z
+        // A candidate stays only if it can still be certified in this batch
+        // (key > beta; keys only decrease): in index order into the list. The
+        // best candidate is always kept: its key is the largest of the cloud.
+        auto keep = [&](bool in, uint32_t m, uint32_t j, uint32_t x, uint32_t y, uint32_t z) {
+            const bool live = in && j != kNone && key_gt(m, j, beta_m, beta_j);
+            const uint64_t mk = ballot(live);
+            if (live) {
+                const uint32_t q = total + lanes_below(mk);
+                live_a[q] = make_uint4(m, j, x, y);
+                live_z[q] = z;
+            }
+            total += (uint32_t)__popcll(mk);
+        };
         {
-            const bool own = lane < NR;
-            const uint4 r = own ? rep[lane] : make_uint4(0u, kNone, 0u, 0u);
-            const uint32_t rz = own ? rep_z[lane] : 0u;
-            // lane w < NPW: wave w's bound and its two reports' keys
-            const bool wl = lane < NPW;
-            const uint2 wbd = wl ? bnd[lane] : make_uint2(0u, kNone);
-            const uint4 r0 = wl ? rep[2 * lane] : make_uint4(0u, kNone, 0u, 0u);
-            const uint4 r1 = wl ? rep[2 * lane + 1] : make_uint4(0u, kNone, 0u, 0u);
-            const bool rv = r.y != kNone;
+            const uint4 r = rep[lane];  // lane = report (empty past the last)
+            const uint32_t rz = rep_z[lane];
+            const uint2 wbd = bnd[lane];  // lane = wave (empty past the last)
             if (G == 1) {
-                // candidates: every report, lane = report
-#pragma unroll
-                for (int s = 0; s < CPL; ++s) {
-                    cm[s] = s == 0 ? r.x : 0u;
-                    cj[s] = s == 0 ? r.y : kNone;
-                    cxv[s] = s == 0 ? r.z : 0u;
-                    cyv[s] = s == 0 ? r.w : 0u;
-                    czv[s] = s == 0 ? rz : 0u;
-                }
                 int l;
                 wave_max_key(wbd.x, wbd.y, wbd.y != kNone, beta_m, beta_j, l);
+                keep(true, r.x, r.y, r.z, r.w, rz);
             } else {
                 // publish this workgroup's RG best reports (in index order) and
                 // its bound: the best of the wave bounds and unpublished reports
+                uint64_t alive = ballot(r.y != kNone);  // reports not yet taken
                 uint64_t sel = 0;
-                for (int k = 0; k < RG; ++k) {
-                    uint32_t om, oj;
-                    int ol;
-                    wave_max_key(r.x, r.y, rv && !((sel >> lane) & 1ull), om, oj, ol);
-                    if (ol >= 0) sel |= 1ull << ol;
+                for (int k = 0; k < RG && alive != 0; ++k) {
+                    const bool a = __builtin_amdgcn_inverse_ballot_w64(alive);
+                    const uint32_t mx = wave_max_u32(a ? r.x : 0u);
+                    const int l = (int)__builtin_ctzll(alive & ballot(r.x == mx));
+                    sel |= 1ull << l;
+                    alive &= ~(1ull << l);
                 }
-                uint32_t um = wbd.x, uj = wbd.y;  // this wave's largest unpublished key
-                if (wl) {
-                    const bool s0 = (sel >> (2 * lane)) & 1ull, s1 = (sel >> (2 * lane + 1)) & 1ull;
-                    if (!s0 && r0.y != kNone && (uj == kNone || key_gt(r0.x, r0.y, um, uj))) {
-                        um = r0.x;
-                        uj = r0.y;
-                    }
-                    if (!s1 && r1.y != kNone && (uj == kNone || key_gt(r1.x, r1.y, um, uj))) {
-                        um = r1.x;
-                        uj = r1.y;
-                    }
-                }
+                // a wave's keys are ordered: report 0 >= report 1 >= bound, so
+                // its best unpublished key is the first of them not published
+                const uint4 r0 = rep[(2 * lane) & (kWave - 1)];
+                const uint4 r1 = rep[(2 * lane + 1) & (kWave - 1)];
+                const bool p0 = (sel >> ((2 * lane) & 63)) & 1ull,
+                           p1 = (sel >> ((2 * lane + 1) & 63)) & 1ull;
+                const bool wl = lane < NPW;
+                const uint32_t um = !p0 ? r0.x : (!p1 ? r1.x : wbd.x);
+                const uint32_t uj = !wl ? kNone : (!p0 ? r0.y : (!p1 ? r1.y : wbd.y));
                 uint32_t gm, gj;
                 int gl;
                 wave_max_key(um, uj, uj != kNone, gm, gj, gl);
@@ -585,25 +591,25 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 // bounds of 2 words
                 const uint32_t tag = batch;
                 uint64_t* set = cw + (size_t)(batch & 1) * G * stride;
-                const bool mine = (sel >> lane) & 1ull;
-                const int rank = (int)lanes_below(sel);
                 const int nsel = __popcll(sel);
-                if (mine) {
+                if ((sel >> lane) & 1ull) {
                     uint64_t w0, w1, w2;
                     pack_candidate(r.x, r.y, r.z, r.w, rz, w0, w1, w2);
-                    uint64_t* w = set + (size_t)(g * RG + rank) * 3;
+                    uint64_t* w = set + (size_t)(g * RG + (int)lanes_below(sel)) * 3;
                     __hip_atomic_store(&w[0], tag8(w0, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     __hip_atomic_store(&w[1], tag8(w1, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     __hip_atomic_store(&w[2], tag8(w2, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                // unused candidate ranks are published as empty
-                for (int k = nsel + lane; k < RG; k += kWave) {
-                    uint64_t w0, w1, w2;
-                    pack_candidate(0u, kNone, 0u, 0u, 0u, w0, w1, w2);
-                    uint64_t* w = set + (size_t)(g * RG + k) * 3;
-                    __hip_atomic_store(&w[0], tag8(w0, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&w[1], tag8(w1, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&w[2], tag8(w2, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (nsel < RG) {
+                    // unused candidate ranks are published as empty
+                    for (int k = nsel + lane; k < RG; k += kWave) {
+                        uint64_t w0, w1, w2;
+                        pack_candidate(0u, kNone, 0u, 0u, 0u, w0, w1, w2);
+                        uint64_t* w = set + (size_t)(g * RG + k) * 3;
+                        __hip_atomic_store(&w[0], tag8(w0, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(&w[1], tag8(w1, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(&w[2], tag8(w2, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
                 }
                 if (lane == 0) {
                     uint64_t* w = set + (size_t)G * RG * 3 + (size_t)g * 2;
@@ -612,17 +618,17 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 }
                 // gather the whole set into LDS: up to kPoll loads per lane in
                 // flight per poll, so a poll costs one round trip
-                const int total = G * stride;
-                for (int w0 = 0; w0 < total && !abort; w0 += kPoll * kWave) {
+                const int words_total = G * stride;
+                for (int w0 = 0; w0 < words_total && !abort; w0 += kPoll * kWave) {
                     uint32_t spins = 0;
                     while (true) {
                         uint64_t v[kPoll];
 #pragma unroll
                         for (int k = 0; k < kPoll; ++k) {
                             const int w = w0 + k * kWave + lane;
-                            v[k] = w < total ? __hip_atomic_load(&set[w], __ATOMIC_RELAXED,
-                                                                 __HIP_MEMORY_SCOPE_AGENT)
-                                             : tag8(0, tag);
+                            v[k] = w < words_total ? __hip_atomic_load(&set[w], __ATOMIC_RELAXED,
+                                                                       __HIP_MEMORY_SCOPE_AGENT)
+                                                   : tag8(0, tag);
                         }
                         bool ready = true;
 #pragma unroll
@@ -631,7 +637,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
 #pragma unroll
                             for (int k = 0; k < kPoll; ++k) {
                                 const int w = w0 + k * kWave + lane;
-                                if (w < total) stage[w] = v[k] >> 8;
+                                if (w < words_total) stage[w] = v[k] >> 8;
                             }
                             break;
                         }
@@ -641,77 +647,53 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 }
                 __builtin_amdgcn_s_waitcnt(0);  // LDS writes of this wave complete
                 __builtin_amdgcn_wave_barrier();
-                // candidates: q = wg * RG + r (index order), lane-major (lane q / CPL,
-                // slot q % CPL), three words each
-#pragma unroll
-                for (int s = 0; s < CPL; ++s) {
-                    const int q = lane * CPL + s;
-                    const bool in = q < G * RG;
-                    const uint64_t* c = stage + (in ? q : 0) * 3;
-                    uint32_t m, j, x, y, z;
-                    unpack_candidate(c[0], c[1], c[2], m, j, x, y, z);
-                    cm[s] = in ? m : 0u;
-                    cj[s] = in ? j : kNone;
-                    cxv[s] = in ? x : 0u;
-                    cyv[s] = in ? y : 0u;
-                    czv[s] = in ? z : 0u;
-                }
-                // beta: the largest bound over the workgroups (lane order = index order)
-                beta_m = 0;
-                beta_j = kNone;
-                const uint64_t* bw = stage + G * RG * 3;
-                for (int base = 0; base < G; base += kWave) {
-                    const int wg = base + lane;
-                    const bool in = wg < G;
-                    const uint32_t m = in ? (uint32_t)bw[wg * 2 + 0] : 0u;
-                    const uint32_t j = in ? (uint32_t)bw[wg * 2 + 1] : kNone;
-                    uint32_t om, oj;
-                    int ol;
-                    wave_max_key(m, j, in && j != kNone, om, oj, ol);
-                    if (ol >= 0 && (beta_j == kNone || key_gt(om, oj, beta_m, beta_j))) {
-                        beta_m = om;
-                        beta_j = oj;
+                if (!abort) {
+                    // beta: the largest bound over the workgroups (lane order =
+                    // index order)
+                    const uint64_t* bw = stage + G * RG * 3;
+                    for (int base = 0; base < G; base += kWave) {
+                        const int wg = base + lane;
+                        const bool in = wg < G;
+                        const uint32_t m = in ? (uint32_t)bw[wg * 2 + 0] : 0u;
+                        const uint32_t j = in ? (uint32_t)bw[wg * 2 + 1] : kNone;
+                        uint32_t om, oj;
+                        int ol;
+                        wave_max_key(m, j, in && j != kNone, om, oj, ol);
+                        if (ol >= 0 && (beta_j == kNone || key_gt(om, oj, beta_m, beta_j))) {
+                            beta_m = om;
+                            beta_j = oj;
+                        }
+                    }
+                    // candidates q = wg * RG + r (index order), three words each,
+                    // 64 at a time
+                    for (int q0 = 0; q0 < G * RG; q0 += kWave) {
+                        const int q = q0 + lane;
+                        const bool in = q < G * RG;
+                        const uint64_t* c = stage + (in ? q : 0) * 3;
+                        uint32_t m, j, x, y, z;
+                        unpack_candidate(c[0], c[1], c[2], m, j, x, y, z);
+                        keep(in, m, j, x, y, z);
                     }
                 }
             }
         }
-        // Keep only the candidates that can still be certified in this batch
-        // (key > beta; keys only decrease), compacted in index order into the
-        // first `used` slots of each lane (lane-major). The best candidate is
-        // always among them: its key is the largest of the cloud.
+        // the live candidates, lane-major: `used` slots per lane
+        uint32_t cm[CPL], cj[CPL], cxv[CPL], cyv[CPL], czv[CPL];
         int used = CPL;
         if (!abort) {
-            bool live[CPL];
-            uint32_t below = 0, total = 0;
-#pragma unroll
-            for (int s = 0; s < CPL; ++s) {
-                live[s] = cj[s] != kNone && key_gt(cm[s], cj[s], beta_m, beta_j);
-                const uint64_t mk = ballot(live[s]);
-                below += lanes_below(mk);
-                total += (uint32_t)__popcll(mk);
-            }
-            // lane-major order of the live entries: all entries of lower lanes
-            // come first, then this lane's in slot order
-            uint32_t q = below;
-#pragma unroll
-            for (int s = 0; s < CPL; ++s) {
-                if (live[s]) {
-                    live_c[0][q] = cm[s]; live_c[1][q] = cj[s]; live_c[2][q] = cxv[s];
-                    live_c[3][q] = cyv[s]; live_c[4][q] = czv[s];
-                    ++q;
-                }
-            }
             used = (int)((total + kWave - 1) / kWave);  // >= 1: the best is live
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int s = 0; s < CPL; ++s) {
                 const int qq = lane * used + s;
                 const bool in = s < used && qq < (int)total;
-                cm[s] = in ? live_c[0][qq] : 0u;
-                cj[s] = in ? live_c[1][qq] : kNone;
-                cxv[s] = in ? live_c[2][qq] : 0u;
-                cyv[s] = in ? live_c[3][qq] : 0u;
-                czv[s] = in ? live_c[4][qq] : 0u;
+                const uint4 e = live_a[in ? qq : 0];
+                const uint32_t ez = live_z[in ? qq : 0];
+                cm[s] = in ? e.x : 0u;
+                cj[s] = in ? e.y : kNone;
+                cxv[s] = in ? e.z : 0u;
+                cyv[s] = in ? e.w : 0u;
+                czv[s] = in ? ez : 0u;
             }
         }
         int t = t0;
