@@ -648,6 +648,17 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 __builtin_amdgcn_s_waitcnt(0);  // LDS writes of this wave complete
                 __builtin_amdgcn_wave_barrier();
                 if (!abort) {
+                    // candidates q = wg * RG + r (index order), three words each,
+                    // 64 at a time (at most CPL rounds); all loads first
+                    uint64_t cw0[CPL], cw1[CPL], cw2[CPL];
+#pragma unroll
+                    for (int k = 0; k < CPL; ++k) {
+                        const int q = k * kWave + lane;
+                        const uint64_t* c = stage + (q < G * RG ? q : 0) * 3;
+                        cw0[k] = c[0];
+                        cw1[k] = c[1];
+                        cw2[k] = c[2];
+                    }
                     // beta: the largest bound over the workgroups (lane order =
                     // index order)
                     const uint64_t* bw = stage + G * RG * 3;
@@ -664,15 +675,12 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                             beta_j = oj;
                         }
                     }
-                    // candidates q = wg * RG + r (index order), three words each,
-                    // 64 at a time
-                    for (int q0 = 0; q0 < G * RG; q0 += kWave) {
-                        const int q = q0 + lane;
-                        const bool in = q < G * RG;
-                        const uint64_t* c = stage + (in ? q : 0) * 3;
+#pragma unroll
+                    for (int k = 0; k < CPL; ++k) {
+                        const int q = k * kWave + lane;
                         uint32_t m, j, x, y, z;
-                        unpack_candidate(c[0], c[1], c[2], m, j, x, y, z);
-                        keep(in, m, j, x, y, z);
+                        unpack_candidate(cw0[k], cw1[k], cw2[k], m, j, x, y, z);
+                        keep(q < G * RG, m, j, x, y, z);
                     }
                 }
             }
