@@ -133,11 +133,13 @@ def test_fps_ties_and_duplicates(gpu, oracle_mod, mode, monkeypatch):
 
 
 @pytest.mark.parametrize("G,rg,block", [(1, 0, 256), (1, 0, 1024), (4, 1, 1024), (4, 15, 1024),
-                                        (9, 3, 1024), (40, 2, 1024), (70, 1, 1024),
-                                        (130, 1, 1024), (3, 1, 256)])
+                                        (4, 30, 1024), (9, 3, 1024), (40, 2, 1024),
+                                        (63, 4, 1024), (70, 1, 1024), (130, 1, 1024),
+                                        (3, 1, 256), (3, 6, 256)])
 def test_fps_batch_shapes(gpu, oracle_mod, G, rg, block, monkeypatch):
     """Certified-batch kernel over workgroup counts, published candidates per
-    workgroup (1..15) and block sizes, including more candidates than lanes."""
+    workgroup (1 .. all 2 * point-wave reports) and block sizes, including more
+    candidates than lanes."""
     monkeypatch.setenv("POINTOPS_FPS_MODE", "batch")
     monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", str(G))
     monkeypatch.setenv("POINTOPS_FPS_BLOCK", str(block))
@@ -148,6 +150,26 @@ def test_fps_batch_shapes(gpu, oracle_mod, G, rg, block, monkeypatch):
     check_fps(gpu, oracle_mod, xyz, 600, 3, f"batch G={G} rg={rg} block={block}")
     xi = W.integer_cloud(G, 1, N, 0, 5)
     check_fps(gpu, oracle_mod, xi, 200, 0, f"batch ints G={G} rg={rg} block={block}")
+
+
+@pytest.mark.parametrize("G,rg", [(4, 30), (64, 4), (33, 7)])
+def test_fps_batch_many_live_candidates(gpu, oracle_mod, G, rg, monkeypatch):
+    """Every workgroup's slice (1920 points: 15 point waves of 128) is a tiny
+    cluster plus `rg` far outliers, one or two per point wave, so each
+    workgroup publishes outliers only and its bound is a cluster point: the
+    first batches keep all G * rg candidates live (up to four slots per lane,
+    the general certification loop), later ones one or two."""
+    monkeypatch.setenv("POINTOPS_FPS_MODE", "batch")
+    monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", str(G))
+    monkeypatch.setenv("POINTOPS_FPS_BLOCK", "1024")
+    monkeypatch.setenv("POINTOPS_FPS_RG", str(rg))
+    per = 1920
+    xyz = W.uniform_cube(500 + G, 1, G * per) * np.float32(0.01)
+    far = W.sphere_shell(600 + G, 1, G * rg, sigma=0.0) * np.float32(10.0)
+    pos = [(k % 15) * 128 + k // 15 for k in range(rg)]
+    for g in range(G):
+        xyz[0, [g * per + p for p in pos]] = far[0, g * rg:(g + 1) * rg]
+    check_fps(gpu, oracle_mod, xyz, 700, per // 2, f"many live G={G} rg={rg}")
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 5, 8, 15, 16, 17, 31, 32, 33, 63, 64])
