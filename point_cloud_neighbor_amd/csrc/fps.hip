@@ -436,6 +436,8 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
         if (point_wave) {
             // outputs are written here, not by the certifying wave, so that
             // wave never waits on a global store
+            // outputs are written here, not by the certifying wave, so that
+            // wave never waits on a global store
             const bool writer = g == 0 && pw == 0 && out_t0 >= 1;
             int a = 0;
             while (true) {
@@ -443,22 +445,22 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 __asm__ __volatile__("" ::: "memory");
                 const int n = __hip_atomic_load(&cen_count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 __asm__ __volatile__("" ::: "memory");
-                for (; a < n; ++a) {
-                    const uint4 c = cen[a];
-                    const float cx = u2f(c.x), cy = u2f(c.y), cz = u2f(c.z);
-                    if (writer) {
-                        if (lane == 0) {
-                            ob[out_t0 + a] = jbase + c.w;
-                            if (oxb) {
-                                oxb[3 * (out_t0 + a) + 0] = cx;
-                                oxb[3 * (out_t0 + a) + 1] = cy;
-                                oxb[3 * (out_t0 + a) + 2] = cz;
-                            }
+                if (writer) {
+                    for (int i = a + lane; i < n; i += kWave) {
+                        const uint4 c = cen[i];
+                        ob[out_t0 + i] = jbase + c.w;
+                        if (oxb) {
+                            oxb[3 * (out_t0 + i) + 0] = u2f(c.x);
+                            oxb[3 * (out_t0 + i) + 1] = u2f(c.y);
+                            oxb[3 * (out_t0 + i) + 2] = u2f(c.z);
                         }
                     }
+                }
+                for (; a < n; ++a) {
+                    const uint4 c = cen[a];
 #pragma unroll
                     for (int p = 0; p < PPT; ++p)
-                        pm[p] = min(pm[p], f2u(s32(cx, cy, cz, px[p], py[p], pz[p])));
+                        pm[p] = min(pm[p], f2u(s32(u2f(c.x), u2f(c.y), u2f(c.z), px[p], py[p], pz[p])));
                 }
                 if (d) break;  // done was set after the last count: n is final
                 __builtin_amdgcn_s_sleep(1);
