@@ -98,7 +98,9 @@ size_t pointops_fps_workspace_bytes(int64_t B, int64_t N, int64_t M);
  * first, skipping a box when the lower bound of s32 over it (taken in the
  * float32 order of s32, so never above it) exceeds a query's current k-th
  * distance. Results are identical, bit for bit; workspace NULL scans every
- * reference. A non-NULL workspace smaller than needed is INVALID_ARGUMENT.
+ * reference, and so does a call with k > 16 on clouds of fewer than 32768
+ * references, where the grid does not pay. A non-NULL workspace smaller than
+ * needed is INVALID_ARGUMENT.
  *
  *   query     (B, Q, 3) float32, device.      ref (B, P, 3) float32, device.
  *   k         1 <= k <= P (INVALID_ARGUMENT otherwise) and

@@ -83,6 +83,8 @@ int upload(const Table& t, void* workspace, size_t workspace_bytes, hipStream_t 
 int knn_waves(int kcap, int64_t tiles, int cus);
 // kNN takes the grid search for this shape (when given a workspace).
 bool knn_use_grid(int64_t B, int64_t Q, int64_t P);
+// ... and the grid search beats the full scan for this k (capacity) and cloud size.
+bool knn_grid_pays(int kcap, int64_t P);
 // Waves per workgroup of the grid search.
 int knn_grid_waves(int kcap);
 int bq_queries_per_wave(int64_t rows, int cus, int max_qw);

@@ -93,7 +93,9 @@ int64_t split_even(int64_t N, int64_t G) {
 // four).
 int knn_waves(int kcap, int64_t tiles, int cus) {
     int nw = kcap >= 64 ? 2 : 4;
-    if (kcap <= 32 && tiles * 4 < (int64_t)std::max(1, cus) * 16) nw = 8;
+    // few workgroups: more waves each (k = 32 is best at 4: the merge of the
+    // waves' lists grows with k)
+    if (kcap <= 16 && tiles * 4 < (int64_t)std::max(1, cus) * 16) nw = 8;
     const long nw_env = env_long("POINTOPS_KNN_WAVES", 0);
     if (nw_env == 1 || (nw_env == 2 && kcap >= 16) || (nw_env == 4 && kcap < 64) ||
         (nw_env == 8 && kcap < 64))
@@ -108,6 +110,16 @@ bool knn_use_grid(int64_t B, int64_t Q, int64_t P) {
     const long env = env_long("POINTOPS_KNN_GRID", -1);
     if (env == 0 || env == 1) return env == 1 && P >= 1;
     return P >= 8192 && B * Q * P >= ((int64_t)1 << 27);
+}
+
+// With k above 16 every reference that enters a list costs a long insertion,
+// and a grid visit touches many of them: below 32768 references per cloud the
+// full scan is faster (32 clouds of 8192 points near a sphere, 512 queries,
+// k = 32: 0.30 ms scanning, 0.65 ms through the grid). POINTOPS_KNN_GRID=1
+// forces the grid.
+bool knn_grid_pays(int kcap, int64_t P) {
+    if (env_long("POINTOPS_KNN_GRID", -1) == 1) return true;
+    return kcap <= 16 || P >= 32768;
 }
 
 // Two waves per 64 queries: each wave keeps its own list, so more waves mean
@@ -374,6 +386,8 @@ int pointops_knn(const float* query, const float* ref, int64_t B, int64_t Q, int
         if (workspace_bytes < need)
             return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
                         workspace_bytes, need);
+    }
+    if (workspace && knn_use_grid(B, Q, P) && knn_grid_pays(kcap, P)) {
         hipError_t e = pointops::launch_knn_grid(query, ref, B, Q, P, k, out_dist, out_idx, kcap,
                                                  knn_grid_waves(kcap), workspace, 0,
                                                  (hipStream_t)stream);
