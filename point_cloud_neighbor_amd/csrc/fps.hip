@@ -252,21 +252,23 @@ __global__ __launch_bounds__(BLOCK) void fps_kernel(
 // ---------------------------------------------------------------- batched FPS
 //
 // The same selection, with far fewer cross-workgroup exchanges. Wave 0 of every
-// workgroup holds no points; the other waves hold the slice. At an exchange
-// each point wave reports its top point (largest key (m, -index)) and a bound:
-// the largest key among its other points. Every workgroup receives the same
-// candidate set C (the reported tops, with coordinates and m) and the largest
-// bound beta over all reports, and wave 0 of each workgroup then runs FPS steps
-// on C alone: it takes the largest key K* in C and folds the new centre into
-// the m of every candidate. Every point outside C has a key below beta, and
+// workgroup certifies; the other waves hold the slice. At an exchange each
+// point wave reports its two largest keys (m, -index) with their coordinates,
+// and a bound: its third largest key. Each workgroup publishes its RG best
+// reports and its own bound, the largest of its wave bounds and unpublished
+// reports. Every workgroup of the cloud receives the same candidate set C and
+// the largest bound beta, and wave 0 of each workgroup then runs FPS steps on
+// C alone: it takes the largest key K* in C and folds the new centre into the
+// m of every candidate. Every point outside C has a key at most beta, and
 // keys only decrease as centres are added, so whenever K* > beta the candidate
 // is the true next centre of the whole cloud; the first step after an
-// exchange always qualifies (every report's top is in C). When a step does not
-// qualify, or the batch is full, the batch ends. While wave 0 certifies
-// centres, the point waves fold each new centre (read from an LDS list) into
-// their points' m; at the end of the batch every point is up to date and the
-// next exchange starts. All decisions are the ones the plain definition makes,
-// in the same order; only the communication is batched.
+// exchange always qualifies (the cloud's largest key is a report that its
+// workgroup publishes). When a step does not qualify, or the batch is full,
+// the batch ends. While wave 0 certifies centres, the point waves fold each
+// new centre (read from an LDS list) into their points' m; at the end of the
+// batch every point is up to date and the next exchange starts. All decisions
+// are the ones the plain definition makes, in the same order; only the
+// communication is batched.
 
 constexpr int kFpsMaxBatch = 256;  // centres certified per batch at most
 constexpr uint32_t kNone = 0xFFFFFFFFu;
