@@ -23,6 +23,7 @@
 namespace pointops {
 
 constexpr int kChamferThreads = 256;
+constexpr int kChamferChunk = 1024;  // rows per workgroup of the loss's first stage
 
 // Rows i >= len[b] of a (B, n) nearest-point output are set to (0, -1).
 __global__ void chamfer_pad_kernel(float* __restrict__ d, int64_t* __restrict__ idx, int64_t B,
@@ -51,41 +52,58 @@ __device__ __forceinline__ double block_sum_f64(double v, double* sh) {
     return r;
 }
 
-// part[b] = fx_b * sum_{i < lx_b} d_xy[b, i] + fy_b * sum_{j < ly_b} d_yx[b, j]
-// (the second term unless single-directional), f = 1 / max(len, 1) for a
-// point mean, 1 for a sum, and / B for a batch mean.
+// Stage 1: workgroup b * nchunk + c sums rows [c * chunk, (c + 1) * chunk) of
+// cloud b below the lengths, in float64, for both directions:
+// part[(b * nchunk + c) * 2 + {0, 1}].
 __global__ __launch_bounds__(kChamferThreads) void chamfer_reduce_kernel(
-    const float* __restrict__ d_xy, const float* __restrict__ d_yx, int64_t B, int64_t N,
-    int64_t M, const int64_t* __restrict__ lx, const int64_t* __restrict__ ly, int point_mean,
-    int batch_mean, int single, double* __restrict__ part) {
+    const float* __restrict__ d_xy, const float* __restrict__ d_yx, int64_t N, int64_t M,
+    const int64_t* __restrict__ lx, const int64_t* __restrict__ ly, int single, int64_t nchunk,
+    int64_t chunk, double* __restrict__ part) {
     __shared__ double sh[kChamferThreads];
-    const int64_t b = blockIdx.x;
+    const int64_t b = blockIdx.x / nchunk, c = blockIdx.x - b * nchunk;
     const int64_t nx = lx ? lx[b] : N, ny = ly ? ly[b] : M;
+    const int64_t i0 = c * chunk, i1x = std::min(nx, i0 + chunk), i1y = std::min(ny, i0 + chunk);
     double sx = 0.0, sy = 0.0;
-    for (int64_t i = threadIdx.x; i < nx; i += kChamferThreads) sx += (double)d_xy[b * N + i];
+    for (int64_t i = i0 + threadIdx.x; i < i1x; i += kChamferThreads) sx += (double)d_xy[b * N + i];
     if (!single)
-        for (int64_t j = threadIdx.x; j < ny; j += kChamferThreads) sy += (double)d_yx[b * M + j];
+        for (int64_t j = i0 + threadIdx.x; j < i1y; j += kChamferThreads) sy += (double)d_yx[b * M + j];
     sx = block_sum_f64(sx, sh);
     sy = block_sum_f64(sy, sh);
     if (threadIdx.x == 0) {
+        part[(b * nchunk + c) * 2 + 0] = sx;
+        part[(b * nchunk + c) * 2 + 1] = sy;
+    }
+}
+
+// Stage 2, one workgroup, every order fixed (the same bits on every call):
+// cloud b's value is fx_b * sum_{i < lx_b} d_xy[b, i] + fy_b * sum_{j < ly_b}
+// d_yx[b, j] (the second term unless single-directional), its chunk sums added
+// in chunk order, f = 1 / max(len, 1) for a point mean, 1 for a sum, and / B for
+// a batch mean; loss[b] = that value (no batch reduction) or loss[0] = the sum
+// over the clouds.
+__global__ __launch_bounds__(kChamferThreads) void chamfer_finish_kernel(
+    const double* __restrict__ part, int64_t B, int64_t N, int64_t M,
+    const int64_t* __restrict__ lx, const int64_t* __restrict__ ly, int point_mean,
+    int batch_mean, int single, int reduce_batch, int64_t nchunk, float* __restrict__ loss) {
+    __shared__ double sh[kChamferThreads];
+    double s = 0.0;
+    for (int64_t b = threadIdx.x; b < B; b += kChamferThreads) {
+        double sx = 0.0, sy = 0.0;
+        for (int64_t c = 0; c < nchunk; ++c) {
+            sx += part[(b * nchunk + c) * 2 + 0];
+            sy += part[(b * nchunk + c) * 2 + 1];
+        }
+        const int64_t nx = lx ? lx[b] : N, ny = ly ? ly[b] : M;
         const double fx = point_mean ? 1.0 / (double)std::max<int64_t>(nx, 1) : 1.0;
         const double fy = point_mean ? 1.0 / (double)std::max<int64_t>(ny, 1) : 1.0;
         double v = fx * sx + (single ? 0.0 : fy * sy);
         if (batch_mean) v /= (double)B;
-        part[b] = v;
+        if (reduce_batch)
+            s += v;
+        else
+            loss[b] = (float)v;
     }
-}
-
-// loss[b] = part[b] (no batch reduction) or loss[0] = sum of part (fixed order).
-__global__ __launch_bounds__(kChamferThreads) void chamfer_finish_kernel(
-    const double* __restrict__ part, int64_t B, int reduce_batch, float* __restrict__ loss) {
-    __shared__ double sh[kChamferThreads];
-    if (!reduce_batch) {
-        for (int64_t b = threadIdx.x; b < B; b += kChamferThreads) loss[b] = (float)part[b];
-        return;
-    }
-    double s = 0.0;
-    for (int64_t b = threadIdx.x; b < B; b += kChamferThreads) s += part[b];
+    if (!reduce_batch) return;
     s = block_sum_f64(s, sh);
     if (threadIdx.x == 0) loss[0] = (float)s;
 }
@@ -134,19 +152,31 @@ hipError_t launch_chamfer_pad(float* d, int64_t* idx, int64_t B, int64_t n, cons
     return hipGetLastError();
 }
 
+// Chunks of the loss's first stage: about kChamferChunk rows each, at most 2^30
+// workgroups in all.
+int64_t chamfer_chunks(int64_t B, int64_t N, int64_t M) {
+    const int64_t rows = std::max<int64_t>(std::max(N, M), 1);
+    const int64_t cap = std::max<int64_t>(1, ((int64_t)1 << 30) / std::max<int64_t>(B, 1));
+    return std::min((rows + kChamferChunk - 1) / kChamferChunk, cap);
+}
+
 hipError_t launch_chamfer_reduce(const float* d_xy, const float* d_yx, int64_t B, int64_t N,
                                  int64_t M, const int64_t* lx, const int64_t* ly, int point_mean,
                                  int batch_reduction, int single, double* part, float* loss,
                                  hipStream_t stream) {
+    const int64_t nchunk = chamfer_chunks(B, N, M);
+    const int64_t rows = std::max<int64_t>(std::max(N, M), 1);
+    const int64_t chunk = (rows + nchunk - 1) / nchunk;
     if (B > 0) {
-        hipLaunchKernelGGL(chamfer_reduce_kernel, dim3((unsigned)B), dim3(kChamferThreads), 0,
-                           stream, d_xy, d_yx, B, N, M, lx, ly, point_mean,
-                           batch_reduction == 1 ? 1 : 0, single, part);
+        hipLaunchKernelGGL(chamfer_reduce_kernel, dim3((unsigned)(B * nchunk)),
+                           dim3(kChamferThreads), 0, stream, d_xy, d_yx, N, M, lx, ly, single,
+                           nchunk, chunk, part);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(chamfer_finish_kernel, dim3(1), dim3(kChamferThreads), 0, stream, part, B,
-                       batch_reduction != 0 ? 1 : 0, loss);
+                       N, M, lx, ly, point_mean, batch_reduction == 1 ? 1 : 0, single,
+                       batch_reduction != 0 ? 1 : 0, nchunk, loss);
     return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@
 
 namespace pointops {
 hipError_t launch_chamfer_pad(float*, int64_t*, int64_t, int64_t, const int64_t*, hipStream_t);
+int64_t chamfer_chunks(int64_t B, int64_t N, int64_t M);
 hipError_t launch_chamfer_reduce(const float*, const float*, int64_t, int64_t, int64_t,
                                  const int64_t*, const int64_t*, int, int, int, double*, float*,
                                  hipStream_t);
@@ -39,7 +40,9 @@ ChamferLayout chamfer_layout(int64_t B, int64_t N, int64_t M) {
     ChamferLayout l;
     l.lens = 0;
     l.part = align256((size_t)2 * B * sizeof(int64_t));
-    l.table_xy = l.part + align256((size_t)B * sizeof(double));
+    // two float64 sums per (cloud, chunk of the loss reduction)
+    l.table_xy = l.part + align256((size_t)B * (size_t)pointops::chamfer_chunks(B, N, M) * 2 *
+                                   sizeof(double));
     const size_t t = align256((size_t)pointops::seg_table_words(B) * sizeof(int64_t));
     l.table_yx = l.table_xy + t;
     l.grid = l.table_yx + t;
