@@ -111,10 +111,18 @@ __global__ __launch_bounds__(256) void grid_bounds_kernel(const float* __restric
             mn[d] = min(mn[d], v);
             mx[d] = max(mx[d], v);
         }
+    // wave reductions first (DPP), then one LDS atomic per wave and value
 #pragma unroll
     for (int d = 0; d < 3; ++d) {
-        atomicMin(&sh[d], mn[d]);
-        atomicMax(&sh[3 + d], mx[d]);
+        mn[d] = ~wave_max_u32(~mn[d]);
+        mx[d] = wave_max_u32(mx[d]);
+    }
+    if (threadIdx.x % kWave == 0) {
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+            atomicMin(&sh[d], mn[d]);
+            atomicMax(&sh[3 + d], mx[d]);
+        }
     }
     __syncthreads();
     if (threadIdx.x < 3) atomicMin(&e[threadIdx.x], sh[threadIdx.x]);
