@@ -91,6 +91,9 @@ int bq_queries_per_wave(int64_t rows, int cus, int max_qw);
 // Candidates a workgroup publishes per exchange of the batched FPS when its
 // cloud spans G > 1 workgroups of `npw` point waves (each wave reports two).
 int fps_batch_rg(int64_t G, int npw);
+// Largest cloud for which FPS takes the one-exchange-per-step kernel (one
+// workgroup per cloud); larger clouds take certified batches.
+constexpr int64_t kFpsStepMaxPoints = 4096;
 
 }  // namespace api
 }  // namespace pointops

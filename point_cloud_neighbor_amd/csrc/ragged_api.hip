@@ -166,7 +166,9 @@ RaggedFps plan_fps_ragged(const int64_t* x_off, const int64_t* x_cnt, const int6
     const char* mode = getenv("POINTOPS_FPS_MODE");
     const int64_t max_slice =
         std::min<int64_t>(16 * 1024, ((int64_t)dev.lds_per_block - 1024) / 12);
-    if (!(mode && strcmp(mode, "batch") == 0) && p.max_n <= max_slice) {
+    const bool step = mode && strcmp(mode, "step") == 0 ? p.max_n <= max_slice
+                                                         : p.max_n <= kFpsStepMaxPoints;
+    if (!(mode && strcmp(mode, "batch") == 0) && step) {
         p.batch = false;
         p.block = p.max_n > 1024 ? 1024 : 256;
         p.ppt = (int)((p.max_n + p.block - 1) / p.block);
