@@ -93,14 +93,17 @@ size_t pointops_fps_workspace_bytes(int64_t B, int64_t N, int64_t M);
  *   For every query i of cloud b: sort the references j by (s32(q_i, x_j), j),
  *   keep the first k; out_idx = j, out_dist = sqrtf(s32) correctly rounded.
  * With a workspace of pointops_knn_workspace_bytes(B, Q, P) bytes (when that
- * is not 0) the call counting-sorts references and queries into a uniform
- * grid, bounds every 64 sorted references by a box, and visits near boxes
+ * is not 0) the call may counting-sort references and queries into a uniform
+ * grid, bound every 64 sorted references by a box, and visit near boxes
  * first, skipping a box when the lower bound of s32 over it (taken in the
  * float32 order of s32, so never above it) exceeds a query's current k-th
- * distance. Results are identical, bit for bit; workspace NULL scans every
- * reference, and so does a call with k > 16 on clouds of fewer than 32768
- * references, where the grid does not pay. A non-NULL workspace smaller than
- * needed is INVALID_ARGUMENT.
+ * distance; it does so when the full scan would be long enough to hide the
+ * sort (pointops_knn_search tells which search a shape takes). Otherwise, and
+ * with workspace NULL, every reference is scanned: for k <= 32 one query per
+ * wave with a merged top-32 list, else (and for k <= 8 with many queries on
+ * small clouds) one query per lane. Results are identical, bit for bit,
+ * whatever the search. A non-NULL workspace smaller than needed is
+ * INVALID_ARGUMENT.
  *
  *   query     (B, Q, 3) float32, device.      ref (B, P, 3) float32, device.
  *   k         1 <= k <= P (INVALID_ARGUMENT otherwise) and
@@ -115,6 +118,18 @@ int pointops_knn(const float *query, const float *ref, int64_t B, int64_t Q, int
 /* Bytes of device workspace that lets pointops_knn sort the clouds into a grid
  * and skip far references (0 when that path is not used for this shape). */
 size_t pointops_knn_workspace_bytes(int64_t B, int64_t Q, int64_t P);
+
+/* The searches pointops_knn chooses from (same results, different speed). */
+#define POINTOPS_KNN_SEARCH_LANES 0 /* full scan, one query per lane */
+#define POINTOPS_KNN_SEARCH_WAVES 1 /* full scan, one or two queries per wave */
+#define POINTOPS_KNN_SEARCH_GRID 2  /* grid sort and culled search */
+
+/* Which search pointops_knn takes on the current device for this shape, with
+ * (with_workspace != 0) or without its workspace: one of the
+ * POINTOPS_KNN_SEARCH_* values above, or minus a status code
+ * (INVALID_ARGUMENT for a shape pointops_knn rejects, the device errors).
+ * Reads the same environment overrides as pointops_knn. */
+int pointops_knn_search(int64_t B, int64_t Q, int64_t P, int64_t k, int with_workspace);
 
 /* Bytes of device workspace that lets pointops_ball_query skip far blocks of
  * references (one bounding box per 64 references of each cloud, 32 bytes). */

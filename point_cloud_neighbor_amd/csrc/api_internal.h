@@ -35,6 +35,8 @@ int fps_batch_stride(int rg);
 int fps_batch_point_waves(int block);  // waves of a workgroup that hold points
 hipError_t launch_knn(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
                       int64_t*, int, int, const int64_t*, int, int64_t, int, hipStream_t);
+hipError_t launch_knn_wave(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
+                           int64_t*, int, int, const int64_t*, int, int64_t, int, hipStream_t);
 hipError_t launch_ball_query_backward(const float*, const float*, const int64_t*, const float*,
                                       int64_t, int64_t, int64_t, int64_t, float*, float*,
                                       hipStream_t);
@@ -83,14 +85,20 @@ int upload(const Table& t, void* workspace, size_t workspace_bytes, hipStream_t 
 int knn_waves(int kcap, int64_t tiles, int cus);
 // kNN takes the grid search for this shape (when given a workspace).
 bool knn_use_grid(int64_t B, int64_t Q, int64_t P);
-// ... and the grid search beats the full scan for this k (capacity) and cloud size.
-bool knn_grid_pays(int kcap, int64_t P);
+// ... and the grid search beats the full scans for this k and shape.
+bool knn_grid_pays(int64_t k, int64_t B, int64_t Q, int64_t P);
 // Waves per workgroup of the grid search.
 int knn_grid_waves(int kcap);
 int bq_queries_per_wave(int64_t rows, int cus, int max_qw);
 // Candidates a workgroup publishes per exchange of the batched FPS when its
 // cloud spans G > 1 workgroups of `npw` point waves (each wave reports two).
 int fps_batch_rg(int64_t G, int npw);
+// One-query-per-wave kNN: waves per workgroup and queries per wave; nw == 0
+// selects the lane-per-query kernel.
+struct KnnWavePlan {
+    int nw = 0, qw = 1;
+};
+KnnWavePlan knn_wave_plan(int64_t k, int64_t queries, int64_t max_refs, int cus);
 // Largest cloud for which FPS takes the one-exchange-per-step kernel (one
 // workgroup per cloud); larger clouds take certified batches.
 constexpr int64_t kFpsStepMaxPoints = 4096;

@@ -106,34 +106,48 @@ int nearest(const float* a, const float* bpts, int64_t B, int64_t n, int64_t m,
             const DeviceInfo& dev, hipStream_t s) {
     if (B * n == 0) return POINTOPS_OK;
     hipError_t e;
-    if (!la && !lb && m > 0 && knn_use_grid(B, n, m) &&
+    if (!la && !lb && m > 0 && knn_use_grid(B, n, m) && knn_grid_pays(1, B, n, m) &&
         grid_bytes >= pointops::knn_grid_workspace_bytes(B, n, m)) {
         e = pointops::launch_knn_grid(a, bpts, B, n, m, 1, dist, idx, 1, knn_grid_waves(1),
                                       grid_ws, 1, s);
         return e == hipSuccess ? POINTOPS_OK : hip_fail(e, "nearest launch");
     }
     if (!la && !lb) {
-        const int64_t tiles = B * ((n + 63) / 64);
-        e = pointops::launch_knn(a, bpts, B, n, m, 1, dist, idx, 1, knn_waves(1, tiles, dev.cus),
-                                 nullptr, 0, 0, 1, s);
+        const KnnWavePlan wp = knn_wave_plan(1, B * n, m, dev.cus);
+        if (wp.nw)
+            e = pointops::launch_knn_wave(a, bpts, B, n, m, 1, dist, idx, wp.nw, wp.qw, nullptr,
+                                          0, 0, 1, s);
+        else
+            e = pointops::launch_knn(a, bpts, B, n, m, 1, dist, idx, 1,
+                                     knn_waves(1, B * ((n + 63) / 64), dev.cus), nullptr, 0, 0,
+                                     1, s);
         return e == hipSuccess ? POINTOPS_OK : hip_fail(e, "nearest launch");
     }
     std::vector<int64_t> qo((size_t)B), qc((size_t)B), ro((size_t)B), rc((size_t)B);
+    int64_t queries = 0, max_refs = 0;
     for (int64_t b = 0; b < B; ++b) {
         qo[(size_t)b] = b * n;
         qc[(size_t)b] = la ? la[b] : n;
         ro[(size_t)b] = b * m;
         rc[(size_t)b] = lb ? lb[b] : m;
+        queries += qc[(size_t)b];
+        if (qc[(size_t)b] > 0) max_refs = std::max(max_refs, rc[(size_t)b]);
     }
-    const Table t = search_table(qo.data(), qc.data(), ro.data(), rc.data(), B, 64, false);
+    const KnnWavePlan wp = knn_wave_plan(1, queries, max_refs, dev.cus);
+    const Table t = search_table(qo.data(), qc.data(), ro.data(), rc.data(), B,
+                                 wp.nw ? wp.nw * wp.qw : 64, false);
     e = pointops::launch_chamfer_pad(dist, idx, B, n, dev_la, s);
     if (e != hipSuccess) return hip_fail(e, "chamfer pad");
     if (t.units == 0) return POINTOPS_OK;
     int64_t* table = nullptr;
     int st = upload(t, table_ws, table_bytes, s, &table);
     if (st != POINTOPS_OK) return st;
-    e = pointops::launch_knn(a, bpts, 0, 0, 0, 1, dist, idx, 1, knn_waves(1, t.units, dev.cus),
-                             table, t.nseg, t.units, 1, s);
+    if (wp.nw)
+        e = pointops::launch_knn_wave(a, bpts, 0, 0, 0, 1, dist, idx, wp.nw, wp.qw, table, t.nseg,
+                                      t.units, 1, s);
+    else
+        e = pointops::launch_knn(a, bpts, 0, 0, 0, 1, dist, idx, 1,
+                                 knn_waves(1, t.units, dev.cus), table, t.nseg, t.units, 1, s);
     return e == hipSuccess ? POINTOPS_OK : hip_fail(e, "nearest launch");
 }
 

@@ -112,14 +112,50 @@ bool knn_use_grid(int64_t B, int64_t Q, int64_t P) {
     return P >= 8192 && B * Q * P >= ((int64_t)1 << 27);
 }
 
-// With k above 16 every reference that enters a list costs a long insertion,
-// and a grid visit touches many of them: below 32768 references per cloud the
-// full scan is faster (32 clouds of 8192 points near a sphere, 512 queries,
-// k = 32: 0.30 ms scanning, 0.65 ms through the grid). POINTOPS_KNN_GRID=1
-// forces the grid.
-bool knn_grid_pays(int kcap, int64_t P) {
+// The grid pays once a full scan would be long enough to hide its sort and
+// launches: from 2^28 query-reference pairs for k <= 4, 2^30 for k <= 16 and
+// 2^31 for k <= 32 (uniform clouds, best full scan / grid: 8192 queries on
+// 100k references, k = 16: 0.32 / 0.43 ms; 16384 on 100k: 0.47 / 0.36 ms;
+// 16384 on 100k, k = 32: 0.53 / 0.73 ms; 32768 on 100k: 0.99 / 0.71 ms;
+// 4 clouds of 8192 queries on 16384 references, k = 1: 0.15 / 0.13 ms). Points
+// on a surface fill few cells and favour the scan further (32 clouds of 8192
+// points near a sphere, 512 queries, k = 16: 0.10 / 0.31 ms). Above k = 32
+// only the lane-per-query scan remains, and the grid pays from 32768
+// references. POINTOPS_KNN_GRID=1 forces the grid.
+bool knn_grid_pays(int64_t k, int64_t B, int64_t Q, int64_t P) {
     if (env_long("POINTOPS_KNN_GRID", -1) == 1) return true;
-    return kcap <= 16 || P >= 32768;
+    if (k > 32) return P >= 32768;
+    const int64_t need = k <= 4 ? (int64_t)1 << 28 : k <= 16 ? (int64_t)1 << 30 : (int64_t)1 << 31;
+    return B * Q * P >= need;
+}
+
+// Full scans with k <= 32 take one query per wave (knn_wave.hip): its lists
+// merge candidates 32 at a time, where the lane-per-query kernel pays a
+// k-long insertion per candidate and needs many queries to fill the chip.
+// Measured on uniform clouds (lane-per-query / one / two queries per wave):
+// 1024 queries, 100k references, k = 16: 0.75 / 0.19 / 0.26 ms; 32 clouds of
+// 512 queries and 8192 references, k = 32: 0.31 / 0.11 / 0.11 ms; 100k x
+// 100k, k = 16: 2.81 / 2.94 / 2.27 ms. Two queries per wave share each
+// reference read and pay from 64 queries per CU on. The lane-per-query kernel
+// stays for k <= 8 with many queries on small clouds (16 clouds of 8192
+// queries and 2048 references, k = 3: 0.12 / 0.20 / 0.18 ms; 16 clouds of 4096
+// queries and 8192 references, k = 8: 0.21 / - / 0.26 ms), where the wave's
+// fixed cost per query (the first sort, the merges) outweighs its short
+// scan. POINTOPS_KNN_WAVE=0 / 1 forces either kernel; POINTOPS_KNN_WAVE_NW
+// picks 4, 8 or 16 waves per workgroup and POINTOPS_KNN_WAVE_QW 1 or 2
+// queries per wave.
+KnnWavePlan knn_wave_plan(int64_t k, int64_t queries, int64_t max_refs, int cus) {
+    KnnWavePlan p;
+    if (k > 32) return p;
+    const long env = env_long("POINTOPS_KNN_WAVE", -1);
+    if (env == 0) return p;
+    const int64_t c = std::max(1, cus);
+    if (env != 1 && k <= 8 && queries >= 256 * c && max_refs <= 16384) return p;
+    const long nw = env_long("POINTOPS_KNN_WAVE_NW", 8);
+    p.nw = nw == 4 || nw == 16 ? (int)nw : 8;
+    const long qw = env_long("POINTOPS_KNN_WAVE_QW", 0);
+    p.qw = qw == 1 || qw == 2 ? (int)qw : (queries >= 64 * c ? 2 : 1);
+    return p;
 }
 
 // Two waves per 64 queries: each wave keeps its own list, so more waves mean
@@ -362,6 +398,19 @@ size_t pointops_knn_workspace_bytes(int64_t B, int64_t Q, int64_t P) {
     return pointops::knn_grid_workspace_bytes(B, Q, P);
 }
 
+int pointops_knn_search(int64_t B, int64_t Q, int64_t P, int64_t k, int with_workspace) {
+    g_err[0] = 0;
+    if (B < 0 || Q < 0 || P < 0 || k < 1 || k > P || k > POINTOPS_KNN_KMAX)
+        return -fail(POINTOPS_INVALID_ARGUMENT, "no kNN search for this shape");
+    DeviceInfo* dev = nullptr;
+    const int st = current_device(&dev);
+    if (st != POINTOPS_OK) return -st;
+    if (with_workspace && knn_use_grid(B, Q, P) && knn_grid_pays(k, B, Q, P))
+        return POINTOPS_KNN_SEARCH_GRID;
+    return knn_wave_plan(k, B * Q, P, dev->cus).nw ? POINTOPS_KNN_SEARCH_WAVES
+                                                   : POINTOPS_KNN_SEARCH_LANES;
+}
+
 int pointops_knn(const float* query, const float* ref, int64_t B, int64_t Q, int64_t P,
                  int64_t k, float* out_dist, int64_t* out_idx, void* workspace,
                  size_t workspace_bytes, void* stream) {
@@ -389,10 +438,17 @@ int pointops_knn(const float* query, const float* ref, int64_t B, int64_t Q, int
             return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
                         workspace_bytes, need);
     }
-    if (workspace && knn_use_grid(B, Q, P) && knn_grid_pays(kcap, P)) {
+    if (workspace && knn_use_grid(B, Q, P) && knn_grid_pays(k, B, Q, P)) {
         hipError_t e = pointops::launch_knn_grid(query, ref, B, Q, P, k, out_dist, out_idx, kcap,
                                                  knn_grid_waves(kcap), workspace, 0,
                                                  (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "knn launch");
+        return POINTOPS_OK;
+    }
+    const KnnWavePlan wp = knn_wave_plan(k, B * Q, P, dev->cus);
+    if (wp.nw) {
+        hipError_t e = pointops::launch_knn_wave(query, ref, B, Q, P, k, out_dist, out_idx, wp.nw,
+                                                 wp.qw, nullptr, 0, 0, 0, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, "knn launch");
         return POINTOPS_OK;
     }

@@ -295,13 +295,26 @@ int pointops_knn_ragged(const float* query, int64_t q_rows, const int64_t* q_off
     DeviceInfo* dev = nullptr;
     st = current_device(&dev);
     if (st != POINTOPS_OK) return st;
-    const Table t = search_table(q_off, q_cnt, r_off, r_cnt, B, 64, global_index != 0);
+    int64_t queries = 0, max_refs = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        queries += q_cnt[b];
+        if (q_cnt[b] > 0) max_refs = std::max(max_refs, r_cnt[b]);
+    }
+    const KnnWavePlan wp = knn_wave_plan(k, queries, max_refs, dev->cus);
+    const Table t = search_table(q_off, q_cnt, r_off, r_cnt, B, wp.nw ? wp.nw * wp.qw : 64,
+                                 global_index != 0);
     if (t.units == 0) return POINTOPS_OK;
     if (t.units >= kMaxPoints) return fail(POINTOPS_UNSUPPORTED, "too many workgroups");
     hipStream_t s = (hipStream_t)stream;
     int64_t* table = nullptr;
     st = upload(t, workspace, workspace_bytes, s, &table);
     if (st != POINTOPS_OK) return st;
+    if (wp.nw) {
+        hipError_t e = pointops::launch_knn_wave(query, ref, 0, 0, 0, k, out_dist, out_idx, wp.nw,
+                                                 wp.qw, table, t.nseg, t.units, 0, s);
+        if (e != hipSuccess) return hip_fail(e, "knn launch");
+        return POINTOPS_OK;
+    }
     int kcap = 1;
     while (kcap < k) kcap *= 2;
     hipError_t e = pointops::launch_knn(query, ref, 0, 0, 0, k, out_dist, out_idx, kcap,

@@ -55,6 +55,8 @@ def _load():
         lib.pointops_knn_workspace_bytes.argtypes = [i64, i64, i64]
         lib.pointops_knn_workspace_bytes.restype = ctypes.c_size_t
         lib.pointops_knn.restype = ctypes.c_int
+        lib.pointops_knn_search.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+        lib.pointops_knn_search.restype = ctypes.c_int
         lib.pointops_ball_query.argtypes = [vp, vp, i64, i64, i64, f32, i64, vp, vp, vp,
                                             ctypes.c_size_t, vp]
         lib.pointops_ball_query_workspace_bytes.argtypes = [i64, i64]
@@ -173,6 +175,19 @@ def knn(query: torch.Tensor, ref: torch.Tensor, k: int, grid: bool = True):
                               _stream(query.device))
         _check(rc)
     return dist, idx
+
+
+KNN_SEARCHES = {0: "full scan, one query per lane", 1: "full scan, queries per wave",
+                2: "grid"}
+
+
+def knn_search(B: int, Q: int, P: int, k: int, grid: bool = True) -> str:
+    """Which search ``knn`` takes for this shape on the current device (a key
+    of the library's choice; every search gives the same results)."""
+    rc = int(_load().pointops_knn_search(B, Q, P, int(k), 1 if grid else 0))
+    if rc < 0:
+        _check(-rc)
+    return KNN_SEARCHES[rc]
 
 
 def ball_query(query: torch.Tensor, ref: torch.Tensor, radius: float, K: int,

@@ -176,3 +176,21 @@ def test_chamfer_and_three_nn_grid_search_forced(gpu, oracle_mod, case, monkeypa
     wd, wi = oracle_mod.three_nn(x, y, threads=8)
     assert_idx_equal(host(i), wi, "three_nn grid idx")
     assert_dist_close(host(d), wd, "three_nn grid dist")
+
+
+@pytest.mark.parametrize("wave", ["0", "1"])
+@pytest.mark.parametrize("lengths", [False, True])
+def test_chamfer_and_three_nn_both_scans(gpu, oracle_mod, wave, lengths, monkeypatch):
+    """The nearest points (and three_nn) through either full scan: one query
+    per lane, or one per wave (squared distances kept), dense and with
+    lengths, against the oracle."""
+    monkeypatch.setenv("POINTOPS_KNN_GRID", "0")
+    monkeypatch.setenv("POINTOPS_KNN_WAVE", wave)
+    x, y = W.uniform_cube(25, 3, 1100), W.integer_cloud(26, 3, 700, 0, 6)
+    xl, yl = ([1100, 5, 0], [700, 0, 64]) if lengths else (None, None)
+    for single in (False, True):
+        check_chamfer(gpu, oracle_mod, x, y, xl, yl, single=single, what=f"wave={wave}")
+    d, i = gpu.three_nn(dev(x), dev(y))
+    wd, wi = oracle_mod.three_nn(x, y, threads=8)
+    assert_idx_equal(host(i), wi, f"three_nn wave={wave} idx")
+    assert_dist_close(host(d), wd, f"three_nn wave={wave} dist")
