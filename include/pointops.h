@@ -132,20 +132,38 @@ size_t pointops_knn_workspace_bytes(int64_t B, int64_t Q, int64_t P);
 int pointops_knn_search(int64_t B, int64_t Q, int64_t P, int64_t k, int with_workspace);
 
 /* Bytes of device workspace that lets pointops_ball_query skip far blocks of
- * references (one bounding box per 64 references of each cloud, 32 bytes). */
-size_t pointops_ball_query_workspace_bytes(int64_t B, int64_t P);
+ * references: one bounding box per 64 references of each cloud (32 bytes),
+ * and for clouds of more than 32768 references also room for the grid pass
+ * (8 bytes per query, the sorted copies of references and queries, 16 bytes
+ * each, their boxes and the cell histograms). */
+size_t pointops_ball_query_workspace_bytes(int64_t B, int64_t Q, int64_t P);
+
+/* The searches pointops_ball_query chooses from (same results). */
+#define POINTOPS_BQ_SEARCH_SCAN 0   /* every reference, in index order */
+#define POINTOPS_BQ_SEARCH_CULLED 1 /* index order, skipping blocks whose box is too far */
+#define POINTOPS_BQ_SEARCH_GRID 2   /* the culled scan with a budget, then the grid pass */
+
+/* Which search pointops_ball_query takes for this shape, with
+ * (with_workspace != 0) or without its workspace: one of the
+ * POINTOPS_BQ_SEARCH_* values above, or minus INVALID_ARGUMENT for a shape it
+ * rejects. Reads the same environment overrides as pointops_ball_query. */
+int pointops_ball_query_search(int64_t B, int64_t Q, int64_t P, int64_t K, int with_workspace);
 
 /*
  * Dense Ball Query: the first K references within the radius, in input order.
  * Project page, section "The operators in equations", "Ball Query: first K
  * within a radius"; "Numerical contracts" page, section "Selection and output".
- * With a workspace of pointops_ball_query_workspace_bytes(B, P) bytes the call
- * first bounds every block of 64 consecutive references by a box and skips,
- * for each query, the blocks whose lower bound of s32 is >= R2 (the bound is
- * taken in the same float32 order as s32, so it never exceeds it: results are
- * identical, bit for bit). This pays when consecutive references are close in
- * space (sorted clouds); workspace NULL scans every reference. A non-NULL
- * workspace smaller than needed is INVALID_ARGUMENT.
+ * With a workspace of pointops_ball_query_workspace_bytes(B, Q, P) bytes the
+ * call first bounds every block of 64 consecutive references by a box and
+ * skips, for each query, the blocks whose lower bound of s32 is >= R2 (the
+ * bound is taken in the same float32 order as s32, so it never exceeds it:
+ * results are identical, bit for bit). This pays when consecutive references
+ * are close in space (sorted clouds). On clouds of more than 32768 references
+ * (and K <= 32) that scan stops after 128 blocks per wave, and the queries it
+ * leaves short of K (sparse regions of clouds in random order) find the rest
+ * of their first K hits through a uniform grid of the references, built on
+ * the device only when some query is left. Workspace NULL scans every
+ * reference. A non-NULL workspace smaller than needed is INVALID_ARGUMENT.
  *   R2 = fl32(radius * radius) with radius already a float32 (the caller's
  *   fl32(r)); J = the references j with s32(q_i, x_j) < R2, in increasing j;
  *   slot n < min(K, |J|) holds (J[n], s32 of J[n]); the rest hold (-1, +0.0f).
@@ -350,7 +368,7 @@ const char *pointops_status_string(int status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char *pointops_last_error(void);
 
-/* Library ABI version: 2. */
+/* Library ABI version: 3. */
 int pointops_abi_version(void);
 
 #ifdef __cplusplus

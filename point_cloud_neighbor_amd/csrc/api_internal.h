@@ -15,8 +15,13 @@ hipError_t launch_ball_query(const float*, const float*, int64_t, int64_t, int64
                              int64_t, float*, int64_t*, int, const int64_t*, int, int64_t,
                              hipStream_t);
 hipError_t launch_ball_query_culled(const float*, const float*, int64_t, int64_t, int64_t,
-                                    float, int64_t, float*, int64_t*, int, float*, hipStream_t);
+                                    float, int64_t, float*, int64_t*, int, float*, int, uint2*,
+                                    uint32_t*, hipStream_t);
 size_t ball_query_box_bytes(int64_t B, int64_t P);
+hipError_t launch_ball_query_grid(const float*, const float*, int64_t, int64_t, int64_t, float,
+                                  int64_t, float*, int64_t*, int, int, int, void*, hipStream_t);
+int knn_grid_level(int64_t P);
+size_t ball_query_grid_bytes(int64_t B, int64_t Q, int64_t P);
 hipError_t launch_knn_grid(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
                            int64_t*, int, int, void*, int, hipStream_t);
 size_t knn_grid_workspace_bytes(int64_t B, int64_t Q, int64_t P);
@@ -90,6 +95,9 @@ bool knn_grid_pays(int64_t k, int64_t B, int64_t Q, int64_t P);
 // Waves per workgroup of the grid search.
 int knn_grid_waves(int kcap);
 int bq_queries_per_wave(int64_t rows, int cus, int max_qw);
+bool bq_grid_possible(int64_t P);
+int bq_scan_budget();
+int bq_grid_level(int64_t P);
 // Candidates a workgroup publishes per exchange of the batched FPS when its
 // cloud spans G > 1 workgroups of `npw` point waves (each wave reports two).
 int fps_batch_rg(int64_t G, int npw);

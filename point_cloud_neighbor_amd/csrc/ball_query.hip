@@ -179,9 +179,13 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 }
 
 // One wave per block of 64 references: box[(b * nblk + k) * 8 + 0..5].
+// `flag` (nullable): cleared here, set by the culled scan when a query is left
+// for the grid pass.
 __global__ __launch_bounds__(256) void ball_query_boxes_kernel(const float* __restrict__ ref,
                                                                int64_t B, int P, int nblk,
-                                                               float* __restrict__ box) {
+                                                               float* __restrict__ box,
+                                                               uint32_t* __restrict__ flag) {
+    if (flag && blockIdx.x == 0 && threadIdx.x == 0) *flag = 0u;
     const int64_t w = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
     const int lane = threadIdx.x % kWave;
     if (w >= B * nblk) return;  // whole waves leave together
@@ -204,11 +208,20 @@ __global__ __launch_bounds__(256) void ball_query_boxes_kernel(const float* __re
     }
 }
 
+// Budget (state != nullptr): a wave scans at most `budget` blocks. Where it
+// stops early, each of its queries still short of K records (hits so far,
+// first reference index not examined) in state[b * Q + row], and the wave
+// sets *flag; every other query records (count, kBqDone). The grid pass then
+// looks only at references from that index on, so the hits it adds come
+// after these in index order.
+constexpr uint32_t kBqDone = 0xFFFFFFFFu;
+
 template <int QW>
 __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
     const float* __restrict__ query, const float* __restrict__ ref, int Q, int P, float r2,
     int K, float* __restrict__ out_d2, int64_t* __restrict__ out_idx,
-    const float* __restrict__ box, int nblk) {
+    const float* __restrict__ box, int nblk, int budget, uint2* __restrict__ state,
+    uint32_t* __restrict__ flag) {
     const int b = blockIdx.y;
     const int row0 = blockIdx.x * QW;
     const int lane = threadIdx.x;
@@ -237,6 +250,8 @@ __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
         gQx = fmaxf(gQx, qx[i]); gQy = fmaxf(gQy, qy[i]); gQz = fmaxf(gQz, qz[i]);
     }
 
+    int scanned = 0;    // blocks this wave has scanned
+    int stop_blk = -1;  // first block not examined when the budget ran out
     for (int c0 = 0; c0 < nblk; c0 += kWave) {
         // lane l: block c0 + l; blocks past the end have an empty box (bound +inf)
         const int k = c0 + lane;
@@ -276,6 +291,11 @@ __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
         while (true) {
             const float x = nx, y = ny, z = nz;
             const int blk = cur;
+            if (scanned == budget) {  // budget spent: block c0 + blk is left to the grid pass
+                stop_blk = c0 + blk;
+                break;
+            }
+            ++scanned;
             if (rest) {
                 cur = __builtin_ctzll(rest);
                 rest &= rest - 1;
@@ -305,9 +325,10 @@ __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
             }
             if (!live || cur < 0) break;
         }
-        if (!live) break;
+        if (!live || stop_blk >= 0) break;
     }
 
+    bool left = false;
 #pragma unroll
     for (int i = 0; i < QW; ++i) {
         if (row0 + i < Q) {
@@ -315,8 +336,15 @@ __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
                 out_idx[out0 + (size_t)i * K + slot] = -1;
                 out_d2[out0 + (size_t)i * K + slot] = 0.0f;
             }
+            if (state && lane == 0) {
+                const bool open = stop_blk >= 0 && cnt[i] < K;
+                state[(size_t)b * Q + row0 + i] =
+                    make_uint2((uint32_t)min(cnt[i], K), open ? (uint32_t)stop_blk * kWave : kBqDone);
+                left |= open;
+            }
         }
     }
+    if (left) atomicOr(flag, 1u);  // lane 0 only
 }
 
 size_t ball_query_box_bytes(int64_t B, int64_t P) {
@@ -325,14 +353,18 @@ size_t ball_query_box_bytes(int64_t B, int64_t P) {
 
 // Boxes of every 64-reference block into `box`, then the culled scan: grid
 // (ceil(Q / QW), B), one wave per group of QW queries.
+// With `state` non-null, the scan keeps to `budget` blocks per wave and leaves
+// the rest to the grid pass (see ball_query_cull_kernel).
 hipError_t launch_ball_query_culled(const float* query, const float* ref, int64_t B, int64_t Q,
                                     int64_t P, float r2, int64_t K, float* out_d2,
-                                    int64_t* out_idx, int qw, float* box, hipStream_t stream) {
+                                    int64_t* out_idx, int qw, float* box, int budget,
+                                    uint2* state, uint32_t* flag, hipStream_t stream) {
     const int nblk = (int)((P + kWave - 1) / kWave);
+    if (!state) budget = -1;  // never reached
     if (B * nblk > 0) {
         const int64_t waves = B * nblk;
         hipLaunchKernelGGL(ball_query_boxes_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256),
-                           0, stream, ref, B, (int)P, nblk, box);
+                           0, stream, ref, B, (int)P, nblk, box, flag);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -342,7 +374,8 @@ hipError_t launch_ball_query_culled(const float* query, const float* ref, int64_
     case W: {                                                                                 \
         dim3 grid((unsigned)((Q + W - 1) / W), (unsigned)B);                                  \
         hipLaunchKernelGGL(ball_query_cull_kernel<W>, grid, block, 0, stream, query, ref,     \
-                           (int)Q, (int)P, r2, (int)K, out_d2, out_idx, box, nblk);           \
+                           (int)Q, (int)P, r2, (int)K, out_d2, out_idx, box, nblk, budget,    \
+                           state, flag);                                                      \
         break;                                                                                \
     }
         POINTOPS_BQC_CASE(1)

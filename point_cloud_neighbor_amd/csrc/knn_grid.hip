@@ -15,6 +15,8 @@
 //    result depends on it.
 // 2. Boxes. Every 16 consecutive sorted references form a block with its
 //    bounding box, every 64 blocks a superblock with the union box.
+//    (Steps 1 and 2 are launch_grid_build, shared with the Ball Query grid
+//    pass; grid.h holds the helpers both searches use.)
 // 3. Search. A workgroup holds 64 sorted queries (one per lane) and NW waves.
 //    Wave 0 first inserts, for every lane, the 64 references around the
 //    lane's own grid position in sorted order (most of its k nearest are
@@ -32,40 +34,14 @@
 #include <algorithm>
 
 #include "common.h"
+#include "grid.h"
 
 namespace pointops {
 
 constexpr int kGridBuf = 16;    // candidate slots per lane; at most 8 in use between groups of 8
-constexpr int kGridBlk = 16;    // references per block (per box)
 constexpr int kGridLocal = 64;  // references around each query's own position, scanned first
 
 // ------------------------------------------------------------------ grid build
-
-struct GridParams {
-    float lo[3];
-    float inv[3];  // cells per unit length
-    float pad[2];
-};
-
-__device__ __forceinline__ uint32_t spread3(uint32_t v) {
-    // bit b of v -> bit 3b
-    v &= 0x3FF;
-    v = (v | (v << 16)) & 0x030000FF;
-    v = (v | (v << 8)) & 0x0300F00F;
-    v = (v | (v << 4)) & 0x030C30C3;
-    v = (v | (v << 2)) & 0x09249249;
-    return v;
-}
-
-__device__ __forceinline__ uint32_t cell_code(const GridParams& g, float x, float y, float z,
-                                              int L) {
-    // clamped in float first, so points outside the box (queries) convert safely
-    const float top = (float)((1 << L) - 1);
-    const int cx = (int)fminf(fmaxf((x - g.lo[0]) * g.inv[0], 0.0f), top);
-    const int cy = (int)fminf(fmaxf((y - g.lo[1]) * g.inv[1], 0.0f), top);
-    const int cz = (int)fminf(fmaxf((z - g.lo[2]) * g.inv[2], 0.0f), top);
-    return spread3((uint32_t)cx) | (spread3((uint32_t)cy) << 1) | (spread3((uint32_t)cz) << 2);
-}
 
 // The references' bounding box: many workgroups fold their points in with
 // integer atomics on an order-preserving encoding of the floats; the last
@@ -84,7 +60,9 @@ __device__ __forceinline__ float ord_dec(uint32_t e) {
 // Clears the histograms (n words from `zero`) and sets every cloud's box
 // slots to the empty box and its counter to 0.
 __global__ void grid_init_kernel(uint32_t* __restrict__ enc, int64_t B,
-                                 uint32_t* __restrict__ zero, size_t n) {
+                                 uint32_t* __restrict__ zero, size_t n,
+                                 const uint32_t* __restrict__ gate) {
+    if (gate && *gate == 0) return;  // the grid is not needed
     const size_t i0 = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
     if (i0 < (size_t)B * kEncWords) {
         const int r = (int)(i0 % kEncWords);
@@ -95,7 +73,9 @@ __global__ void grid_init_kernel(uint32_t* __restrict__ enc, int64_t B,
 
 __global__ __launch_bounds__(256) void grid_bounds_kernel(const float* __restrict__ ref, int64_t B,
                                                           int P, int L, uint32_t* __restrict__ enc,
-                                                          GridParams* __restrict__ gp) {
+                                                          GridParams* __restrict__ gp,
+                                                          const uint32_t* __restrict__ gate) {
+    if (gate && *gate == 0) return;  // the grid is not needed
     __shared__ uint32_t sh[6];
     __shared__ bool last;
     const int b = blockIdx.y;
@@ -153,7 +133,8 @@ __global__ __launch_bounds__(256) void grid_bounds_kernel(const float* __restric
 __global__ void grid_count_kernel(const float* __restrict__ ref, const float* __restrict__ query,
                                   int64_t B, int P, int Q, int L,
                                   const GridParams* __restrict__ gp, uint32_t* __restrict__ rcnt,
-                                  uint32_t* __restrict__ qcnt) {
+                                  uint32_t* __restrict__ qcnt, const uint32_t* __restrict__ gate) {
+    if (gate && *gate == 0) return;  // the grid is not needed
     const int64_t C = (int64_t)1 << (3 * L);
     const int64_t nr = B * P;
     for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < nr + B * Q;
@@ -174,7 +155,9 @@ constexpr int kScanChunk = 1024;
 // blockIdx.z: 0 references, 1 queries (each side its own counts and sums).
 __global__ __launch_bounds__(256) void grid_chunk_sums_kernel(const uint32_t* __restrict__ rcnt,
                                                               const uint32_t* __restrict__ qcnt,
-                                                              int L, uint32_t* __restrict__ sums2) {
+                                                              int L, uint32_t* __restrict__ sums2,
+                                                              const uint32_t* __restrict__ gate) {
+    if (gate && *gate == 0) return;  // the grid is not needed
     __shared__ uint32_t sh[256];
     const int64_t C = (int64_t)1 << (3 * L);
     const uint32_t* cnt = blockIdx.z ? qcnt : rcnt;
@@ -194,7 +177,9 @@ __global__ __launch_bounds__(256) void grid_chunk_sums_kernel(const uint32_t* __
 
 __global__ __launch_bounds__(256) void grid_chunk_scan_kernel(
     uint32_t* __restrict__ rcnt, uint32_t* __restrict__ rfill, uint32_t* __restrict__ qcnt,
-    uint32_t* __restrict__ qfill, int L, const uint32_t* __restrict__ sums2) {
+    uint32_t* __restrict__ qfill, int L, const uint32_t* __restrict__ sums2,
+    const uint32_t* __restrict__ gate) {
+    if (gate && *gate == 0) return;  // the grid is not needed
     __shared__ uint32_t sh[256];
     const int64_t C = (int64_t)1 << (3 * L);
     uint32_t* cnt = blockIdx.z ? qcnt : rcnt;
@@ -248,7 +233,9 @@ __global__ void grid_scatter_kernel(const float* __restrict__ ref, const float* 
                                     const GridParams* __restrict__ gp,
                                     const uint32_t* __restrict__ rstart, uint32_t* __restrict__ rfill,
                                     const uint32_t* __restrict__ qstart, uint32_t* __restrict__ qfill,
-                                    float4* __restrict__ rout, float4* __restrict__ qout) {
+                                    float4* __restrict__ rout, float4* __restrict__ qout,
+                                    const uint32_t* __restrict__ gate) {
+    if (gate && *gate == 0) return;  // the grid is not needed
     const int64_t C = (int64_t)1 << (3 * L);
     const int64_t nr = B * P;
     for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < nr + B * Q;
@@ -272,7 +259,9 @@ __global__ void grid_scatter_kernel(const float* __restrict__ ref, const float* 
 __global__ __launch_bounds__(1024) void grid_boxes_kernel(const float4* __restrict__ sr,
                                                           int64_t B, int P, int nblk, int nsb,
                                                           float* __restrict__ box,
-                                                          float* __restrict__ sbox) {
+                                                          float* __restrict__ sbox,
+                                                          const uint32_t* __restrict__ gate) {
+    if (gate && *gate == 0) return;  // the grid is not needed
     __shared__ float sh[kWave][6];
     const int64_t b = blockIdx.y;
     const int sb = blockIdx.x;
@@ -323,45 +312,6 @@ __global__ __launch_bounds__(1024) void grid_boxes_kernel(const float4* __restri
 }
 
 // ------------------------------------------------------------------ search
-
-template <int KCAP>
-struct TopK64 {
-    uint64_t key[KCAP];  // ascending; front sentinels 0, empty slots ~0
-
-    __device__ __forceinline__ void init(int k) {
-#pragma unroll
-        for (int p = 0; p < KCAP; ++p) key[p] = p < KCAP - k ? 0ull : ~0ull;
-    }
-
-    // True if kk is already in the list.
-    __device__ __forceinline__ bool contains(uint64_t kk) const {
-        bool f = false;
-#pragma unroll
-        for (int p = 0; p < KCAP; ++p) f |= key[p] == kk;
-        return f;
-    }
-
-    // Insert kk (~0 inserts nothing); the largest key drops out.
-    __device__ __forceinline__ void insert(uint64_t kk) {
-#pragma unroll
-        for (int p = KCAP - 1; p >= 1; --p) {
-            const uint64_t hi = key[p - 1] > kk ? key[p - 1] : kk;
-            key[p] = hi < key[p] ? hi : key[p];
-        }
-        key[0] = kk < key[0] ? kk : key[0];
-    }
-
-    __device__ __forceinline__ uint32_t last_hi() const { return (uint32_t)(key[KCAP - 1] >> 32); }
-};
-
-// Lower bound of s32 between a point and a box (see the file comment).
-__device__ __forceinline__ float box_bound(const float* __restrict__ o, float qx, float qy,
-                                           float qz) {
-    const float gx = fmaxf(fmaxf(o[0] - qx, qx - o[3]), 0.0f);
-    const float gy = fmaxf(fmaxf(o[1] - qy, qy - o[4]), 0.0f);
-    const float gz = fmaxf(fmaxf(o[2] - qz, qz - o[5]), 0.0f);
-    return (gx * gx + gy * gy) + gz * gz;
-}
 
 template <int KCAP, int NW>
 __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
@@ -604,8 +554,7 @@ struct GridLayout {
 
 static size_t al(size_t n) { return (n + 255) / 256 * 256; }
 
-static GridLayout grid_layout(int64_t B, int64_t Q, int64_t P) {
-    const int L = knn_grid_level(P);
+static GridLayout grid_layout(int64_t B, int64_t Q, int64_t P, int L) {
     const size_t C = (size_t)1 << (3 * L);
     const int64_t nblk = (P + kGridBlk - 1) / kGridBlk, nsb = (nblk + kWave - 1) / kWave;
     GridLayout g;
@@ -625,22 +574,24 @@ static GridLayout grid_layout(int64_t B, int64_t Q, int64_t P) {
     return g;
 }
 
+size_t grid_workspace_bytes(int64_t B, int64_t Q, int64_t P, int L) {
+    return grid_layout(B, Q, P, L).total;
+}
+
 size_t knn_grid_workspace_bytes(int64_t B, int64_t Q, int64_t P) {
-    return grid_layout(B, Q, P).total;
+    return grid_workspace_bytes(B, Q, P, knn_grid_level(P));
 }
 
 static unsigned grid_blocks(int64_t n) {
     return (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 8192));
 }
 
-// squared != 0: out_dist holds s itself (the Chamfer distance's nearest points).
-hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int64_t Q, int64_t P,
-                           int64_t k, float* out_dist, int64_t* out_idx, int kcap, int nw,
-                           void* workspace, int squared, hipStream_t stream) {
-    const int L = knn_grid_level(P);
+hipError_t launch_grid_build(const float* query, const float* ref, int64_t B, int64_t Q,
+                             int64_t P, int L, void* workspace, const uint32_t* gate,
+                             hipStream_t stream, GridView* view) {
     const int64_t C = (int64_t)1 << (3 * L);
     const int nblk = (int)((P + kGridBlk - 1) / kGridBlk), nsb = (nblk + kWave - 1) / kWave;
-    const GridLayout g = grid_layout(B, Q, P);
+    const GridLayout g = grid_layout(B, Q, P, L);
     char* ws = (char*)workspace;
     GridParams* gp = (GridParams*)(ws + g.params);
     uint32_t* rcnt = (uint32_t*)(ws + g.ref_cnt);
@@ -651,6 +602,7 @@ hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int6
     float4* squery = (float4*)(ws + g.squery);
     float* box = (float*)(ws + g.box);
     float* sbox = (float*)(ws + g.sbox);
+    *view = GridView{gp, rcnt, sref, squery, box, sbox, L, nblk, nsb};
     hipError_t e;
 #define POINTOPS_CHECK(x) \
     do {                   \
@@ -664,25 +616,45 @@ hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int6
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_init_kernel,
                                       dim3(std::max(grid_blocks((int64_t)nzero),
                                                     grid_blocks(B * kEncWords))),
-                                      dim3(256), 0, stream, enc, B, rcnt, nzero));
+                                      dim3(256), 0, stream, enc, B, rcnt, nzero, gate));
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_bounds_kernel,
                                       dim3((unsigned)std::min<int64_t>((P + 1023) / 1024, 256),
                                            (unsigned)B),
-                                      dim3(256), 0, stream, ref, B, (int)P, L, enc, gp));
+                                      dim3(256), 0, stream, ref, B, (int)P, L, enc, gp, gate));
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_count_kernel, dim3(grid_blocks(B * (P + Q))), dim3(256),
-                                      0, stream, ref, query, B, (int)P, (int)Q, L, gp, rcnt, qcnt));
+                                      0, stream, ref, query, B, (int)P, (int)Q, L, gp, rcnt, qcnt,
+                                      gate));
     const unsigned nchunk = (unsigned)((C + kScanChunk - 1) / kScanChunk);
     uint32_t* sums = (uint32_t*)(ws + g.sums);
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_chunk_sums_kernel, dim3(nchunk, (unsigned)B, 2),
-                                      dim3(256), 0, stream, rcnt, qcnt, L, sums));
+                                      dim3(256), 0, stream, rcnt, qcnt, L, sums, gate));
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_chunk_scan_kernel, dim3(nchunk, (unsigned)B, 2),
-                                      dim3(256), 0, stream, rcnt, rfill, qcnt, qfill, L, sums));
+                                      dim3(256), 0, stream, rcnt, rfill, qcnt, qfill, L, sums,
+                                      gate));
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_scatter_kernel, dim3(grid_blocks(B * (P + Q))),
                                       dim3(256), 0, stream, ref, query, B, (int)P, (int)Q, L, gp,
-                                      rcnt, rfill, qcnt, qfill, sref, squery));
+                                      rcnt, rfill, qcnt, qfill, sref, squery, gate));
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_boxes_kernel, dim3((unsigned)nsb, (unsigned)B),
                                       dim3(1024), 0, stream, sref, B, (int)P, nblk, nsb, box,
-                                      sbox));
+                                      sbox, gate));
+#undef POINTOPS_CHECK
+    return hipSuccess;
+}
+
+// squared != 0: out_dist holds s itself (the Chamfer distance's nearest points).
+hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int64_t Q, int64_t P,
+                           int64_t k, float* out_dist, int64_t* out_idx, int kcap, int nw,
+                           void* workspace, int squared, hipStream_t stream) {
+    GridView v;
+    hipError_t e = launch_grid_build(query, ref, B, Q, P, knn_grid_level(P), workspace, nullptr,
+                                     stream, &v);
+    if (e != hipSuccess) return e;
+#define POINTOPS_CHECK(x) \
+    do {                   \
+        x;                 \
+        e = hipGetLastError(); \
+        if (e != hipSuccess) return e; \
+    } while (0)
     dim3 grid((unsigned)((Q + kWave - 1) / kWave), (unsigned)B);
 #define POINTOPS_GRID_CASE(KC, W)                                                              \
     if (kcap == KC && nw == W) {                                                               \
@@ -694,9 +666,9 @@ hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int6
             if (e != hipSuccess) return e;                                                     \
         }                                                                                      \
         POINTOPS_CHECK(hipLaunchKernelGGL((knn_grid_kernel<KC, W>), grid, dim3(W * kWave), lds, \
-                                          stream, squery, sref, (int)Q, (int)P, (int)k, box,   \
-                                          sbox, nblk, nsb, rcnt, gp, L, out_dist, out_idx,     \
-                                          squared));                                           \
+                                          stream, v.squery, v.sref, (int)Q, (int)P, (int)k,    \
+                                          v.box, v.sbox, v.nblk, v.nsb, v.ref_start, v.gp, v.L,\
+                                          out_dist, out_idx, squared));                        \
         return hipSuccess;                                                                     \
     }
     POINTOPS_GRID_CASE(1, 2) POINTOPS_GRID_CASE(2, 2) POINTOPS_GRID_CASE(4, 2)

@@ -178,6 +178,33 @@ int fps_batch_rg(int64_t G, int npw) {
     return (int)(env > 0 ? std::min<int64_t>(env, cap) : cap);
 }
 
+// Ball Query with a workspace: the culled index-order scan, and for clouds of
+// more than 32768 references a budget of 128 scanned blocks (8192 references)
+// per wave, after which the queries still short of K go to the grid pass
+// (clouds in random order; sorted clouds finish within the budget, and the
+// grid kernels then return at once). POINTOPS_BQ_GRID=0 / 1 forbids or allows
+// it at any size; POINTOPS_BQ_BUDGET sets the budget in blocks.
+bool bq_grid_possible(int64_t P) {
+    const long env = env_long("POINTOPS_BQ_GRID", -1);
+    if (env == 0 || env == 1) return env == 1;
+    return P > 32768;
+}
+
+int bq_scan_budget() {
+    const long env = env_long("POINTOPS_BQ_BUDGET", 0);
+    return env > 0 && env < (1L << 30) ? (int)env : 128;
+}
+
+// Cells per axis of the Ball Query's grid: one level finer than the kNN
+// search's, so the counting sort's atomics spread over more cells where points
+// cluster (the cells decide only the order of the sorted copies, so no result
+// depends on them). POINTOPS_BQ_GRID_LEVEL overrides (2..7).
+int bq_grid_level(int64_t P) {
+    const long env = env_long("POINTOPS_BQ_GRID_LEVEL", 0);
+    if (env >= 2 && env <= 7) return (int)env;
+    return std::min(7, pointops::knn_grid_level(P) + 1);
+}
+
 int bq_queries_per_wave(int64_t rows, int cus, int max_qw) {
     const int64_t slots = (int64_t)std::max(1, cus) * 4 * 8;
     int qw = max_qw;
@@ -324,7 +351,7 @@ using namespace pointops::api;
 
 extern "C" {
 
-int pointops_abi_version(void) { return 2; }
+int pointops_abi_version(void) { return 3; }
 
 const char* pointops_status_string(int status) {
     switch (status) {
@@ -460,8 +487,18 @@ int pointops_knn(const float* query, const float* ref, int64_t B, int64_t Q, int
     return POINTOPS_OK;
 }
 
-size_t pointops_ball_query_workspace_bytes(int64_t B, int64_t P) {
-    return B <= 0 || P <= 0 ? 0 : pointops::ball_query_box_bytes(B, P);
+size_t pointops_ball_query_workspace_bytes(int64_t B, int64_t Q, int64_t P) {
+    if (B <= 0 || Q <= 0 || P <= 0) return 0;
+    return bq_grid_possible(P) ? pointops::ball_query_grid_bytes(B, Q, P)
+                               : pointops::ball_query_box_bytes(B, P);
+}
+
+int pointops_ball_query_search(int64_t B, int64_t Q, int64_t P, int64_t K, int with_workspace) {
+    g_err[0] = 0;
+    if (B < 0 || Q < 0 || P < 0 || K < 1)
+        return -fail(POINTOPS_INVALID_ARGUMENT, "no Ball Query for this shape");
+    if (!with_workspace || P == 0) return POINTOPS_BQ_SEARCH_SCAN;
+    return bq_grid_possible(P) && K <= 32 ? POINTOPS_BQ_SEARCH_GRID : POINTOPS_BQ_SEARCH_CULLED;
 }
 
 int pointops_ball_query(const float* query, const float* ref, int64_t B, int64_t Q, int64_t P,
@@ -485,15 +522,22 @@ int pointops_ball_query(const float* query, const float* ref, int64_t B, int64_t
     volatile float r32 = radius;
     const float r2 = r32 * r32;
     const int qw = bq_queries_per_wave(B * Q, dev->cus, 8);
-    const size_t need = pointops::ball_query_box_bytes(B, P);
+    const size_t need = pointops_ball_query_workspace_bytes(B, Q, P);
     if (workspace && workspace_bytes < need)
         return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
                     workspace_bytes, need);
-    hipError_t e = workspace && P > 0
-        ? pointops::launch_ball_query_culled(query, ref, B, Q, P, r2, K, out_dist2, out_idx, qw,
-                                             (float*)workspace, (hipStream_t)stream)
-        : pointops::launch_ball_query(query, ref, B, Q, P, r2, K, out_dist2, out_idx, qw, nullptr,
-                                      0, 0, (hipStream_t)stream);
+    hipError_t e;
+    if (workspace && P > 0 && bq_grid_possible(P) && K <= 32)
+        e = pointops::launch_ball_query_grid(query, ref, B, Q, P, r2, K, out_dist2, out_idx, qw,
+                                             bq_scan_budget(), bq_grid_level(P), workspace,
+                                             (hipStream_t)stream);
+    else if (workspace && P > 0)  // the boxes come first in either layout
+        e = pointops::launch_ball_query_culled(query, ref, B, Q, P, r2, K, out_dist2, out_idx,
+                                               qw, (float*)workspace, -1, nullptr, nullptr,
+                                               (hipStream_t)stream);
+    else
+        e = pointops::launch_ball_query(query, ref, B, Q, P, r2, K, out_dist2, out_idx, qw,
+                                        nullptr, 0, 0, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "ball_query launch");
     return POINTOPS_OK;
 }

@@ -57,9 +57,11 @@ def _load():
         lib.pointops_knn.restype = ctypes.c_int
         lib.pointops_knn_search.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         lib.pointops_knn_search.restype = ctypes.c_int
+        lib.pointops_ball_query_search.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+        lib.pointops_ball_query_search.restype = ctypes.c_int
         lib.pointops_ball_query.argtypes = [vp, vp, i64, i64, i64, f32, i64, vp, vp, vp,
                                             ctypes.c_size_t, vp]
-        lib.pointops_ball_query_workspace_bytes.argtypes = [i64, i64]
+        lib.pointops_ball_query_workspace_bytes.argtypes = [i64, i64, i64]
         lib.pointops_ball_query_workspace_bytes.restype = ctypes.c_size_t
         lib.pointops_ball_query.restype = ctypes.c_int
         lib.pointops_ball_query_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp,
@@ -190,6 +192,18 @@ def knn_search(B: int, Q: int, P: int, k: int, grid: bool = True) -> str:
     return KNN_SEARCHES[rc]
 
 
+BQ_SEARCHES = {0: "scan", 1: "culled scan", 2: "culled scan, then grid pass"}
+
+
+def ball_query_search(B: int, Q: int, P: int, K: int, cull: bool = True) -> str:
+    """Which search ``ball_query`` takes for this shape (a key of the
+    library's choice; every search gives the same results)."""
+    rc = int(_load().pointops_ball_query_search(B, Q, P, int(K), 1 if cull else 0))
+    if rc < 0:
+        _check(-rc)
+    return BQ_SEARCHES[rc]
+
+
 def ball_query(query: torch.Tensor, ref: torch.Tensor, radius: float, K: int,
                cull: bool = True):
     """First K references within ``radius`` in input order -> (squared distance
@@ -218,7 +232,7 @@ def _ball_query(query: torch.Tensor, ref: torch.Tensor, radius: float, K: int, c
     with torch.cuda.device(query.device):
         d2 = torch.empty((B, Q, K), dtype=torch.float32, device=query.device)
         idx = torch.empty((B, Q, K), dtype=torch.int64, device=query.device)
-        nbytes = int(lib.pointops_ball_query_workspace_bytes(B, P)) if cull else 0
+        nbytes = int(lib.pointops_ball_query_workspace_bytes(B, Q, P)) if cull else 0
         ws = torch.empty(nbytes, dtype=torch.uint8, device=query.device) if nbytes else None
         rc = lib.pointops_ball_query(query.data_ptr(), ref.data_ptr(), B, Q, P,
                                      ctypes.c_float(float(radius)), int(K), d2.data_ptr(),

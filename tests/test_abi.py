@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pointops_abi_version() == 2
+    assert lib.pointops_abi_version() == 3
     for code in range(5):
         assert lib.pointops_status_string(code)
     assert lib.pointops_status_string(99) == b"unknown status"

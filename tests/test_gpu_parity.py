@@ -322,7 +322,7 @@ def test_every_output_slot_written(gpu):
     x = dev(W.uniform_cube(21, 2, 3000))
     q = x[:, :150].contiguous()
     s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    wsb = torch.empty(lib.pointops_ball_query_workspace_bytes(2, 3000), dtype=torch.uint8,
+    wsb = torch.empty(lib.pointops_ball_query_workspace_bytes(2, 150, 3000), dtype=torch.uint8,
                       device="cuda")
     for K in (1, 33, 100):
         for ws in (None, wsb):

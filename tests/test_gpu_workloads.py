@@ -118,8 +118,11 @@ def test_stress(gpu, oracle_mod):
     d2, i = gpu.ball_query(cx, dev(x), w.bq_radius, w.bq_k)
     d2, i = host(d2), host(i)
     bq_properties(d2, i, w.bq_k, W.bits_to_f32(W.R2_BITS[0.03]))
-    centres = gather(x, c)
-    for lo, hi in row_blocks(w.fps_m, 128):
+    # rows of the full launch whose queries the oracle fixed: its own FPS
+    # prefix (asserted equal to the GPU's above); these, the farthest points,
+    # lie in the sparse regions where the grid pass takes over
+    centres = gather(x, wc)
+    for lo, hi in row_blocks(prefix, 128, 5):
         wd2, wi = oracle_mod.ball_query(centres, x, w.bq_radius, w.bq_k, rows=(lo, hi),
                                         threads=THREADS)
         assert_idx_equal(i[:, lo:hi], wi[:, lo:hi], f"stress bq rows {lo}:{hi}")
