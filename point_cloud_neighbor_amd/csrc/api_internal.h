@@ -99,7 +99,8 @@ bool bq_grid_possible(int64_t P);
 int bq_scan_budget();
 int bq_grid_level(int64_t P);
 // Candidates a workgroup publishes per exchange of the batched FPS when its
-// cloud spans G > 1 workgroups of `npw` point waves (each wave reports two).
+// cloud spans G > 1 workgroups of `npw` point waves (each wave reports two):
+// at most 256 in all, 512 when G > 128.
 int fps_batch_rg(int64_t G, int npw);
 // One-query-per-wave kNN: waves per workgroup and queries per wave; nw == 0
 // selects the lane-per-query kernel.

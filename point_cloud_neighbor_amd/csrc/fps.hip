@@ -908,7 +908,7 @@ struct BatchCfg {
 
 template <int P>
 using BatchCfgsFor = std::tuple<BatchCfg<P, 1024, 1>, BatchCfg<P, 1024, 2>, BatchCfg<P, 1024, 4>,
-                                BatchCfg<P, 256, 1>>;
+                                BatchCfg<P, 1024, 8>, BatchCfg<P, 256, 1>>;
 
 using BatchCfgs = decltype(std::tuple_cat(BatchCfgsFor<1>{}, BatchCfgsFor<2>{}, BatchCfgsFor<3>{},
                                           BatchCfgsFor<4>{}, BatchCfgsFor<5>{}, BatchCfgsFor<6>{},

@@ -174,7 +174,8 @@ int knn_grid_waves(int kcap) {
 // at most the workgroup's 2 * npw reports.
 int fps_batch_rg(int64_t G, int npw) {
     const long env = env_long("POINTOPS_FPS_RG", 0);
-    const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(2 * npw, 256 / std::max<int64_t>(G, 1)));
+    const int64_t total = G > 128 ? 512 : 256;  // candidates per exchange in all
+    const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(2 * npw, total / std::max<int64_t>(G, 1)));
     return (int)(env > 0 ? std::min<int64_t>(env, cap) : cap);
 }
 
@@ -271,17 +272,25 @@ FpsPlan fps_plan_step(int64_t B, int64_t N, const DeviceInfo& dev) {
 }
 
 // Certified batches. About 1600 points per workgroup keeps the per-centre
-// update short; at most 128 workgroups per cloud by default (more make the
-// exchange of candidates slower than the update they save; measured on 100k
-// and 1M points) and, when a cloud spans several workgroups, no more
-// workgroups than the device holds at once (they wait on each other). Each workgroup publishes
-// up to 256 / G of its waves' reports per exchange; the certifying wave holds at most
-// 256 candidates.
+// update short; at most 128 workgroups per cloud (more make the exchange of
+// candidates slower than the update they save, measured on 100k points) up to
+// kFpsWideMin points, and 256 from there on, each publishing two reports (512
+// candidates, eight per lane of the certifying wave): at that size the update
+// of a centre outweighs the longer certification (uniform clouds, 4096
+// samples, 128 workgroups / 256: 400k points 1.62 / 1.56 ms, 786k 2.36 /
+// 1.74 ms; 2^20 clustered points, 16384 samples, 9.07 / 6.10 ms; 200k points
+// 1.42 / 1.60 ms). A cloud spanning several workgroups gets no more of them
+// than the device holds at once (they wait on each other).
+constexpr int64_t kFpsWideMin = 393216;
+
 FpsPlan fps_plan_batch(int64_t B, int64_t N, const DeviceInfo& dev) {
     const int cus = std::max(1, dev.cus);
     const long g_env = env_long("POINTOPS_FPS_WG_PER_CLOUD", 0);
     const long block_env = env_long("POINTOPS_FPS_BLOCK", 0);
-    int64_t want = g_env > 0 ? g_env : (N <= 2048 ? 1 : std::min<int64_t>((N + 1599) / 1600, 128));
+    int64_t want = g_env > 0          ? g_env
+                   : N <= 2048        ? 1
+                   : N >= kFpsWideMin ? 256
+                                      : std::min<int64_t>((N + 1599) / 1600, 128);
     int block = block_env == 256 || block_env == 1024 ? (int)block_env : 0;
     FpsPlan p{};
     p.batch = true;
@@ -305,7 +314,7 @@ FpsPlan fps_plan_batch(int64_t B, int64_t N, const DeviceInfo& dev) {
             if (G > 256) break;
             p.rg = fps_batch_rg(G, npw);
             const int64_t cand = G * p.rg;
-            p.cpl = cand <= 64 ? 1 : cand <= 128 ? 2 : 4;
+            p.cpl = cand <= 64 ? 1 : cand <= 128 ? 2 : cand <= 256 ? 4 : 8;
             if (p.block == 256 && p.cpl > 1) { block = 1024; continue; }
         }
         int cap = 0;

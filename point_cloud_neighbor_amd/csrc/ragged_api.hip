@@ -212,8 +212,8 @@ RaggedFps plan_fps_ragged(const int64_t* x_off, const int64_t* x_cnt, const int6
             multi += g;
             p.lds = std::max(p.lds, pointops::fps_batch_lds_bytes((int)g, (int)r));
         }
-        if (cand > 256) break;
-        p.cpl = cand <= 64 ? 1 : cand <= 128 ? 2 : 4;
+        if (cand > 512) break;
+        p.cpl = cand <= 64 ? 1 : cand <= 128 ? 2 : cand <= 256 ? 4 : 8;
         if (p.block == 256 && p.cpl > 1) { block = 1024; continue; }
         int cap = 0;
         hipError_t e = pointops::fps_batch_capacity(p.ppt, p.block, p.cpl, p.lds, dev.cus, &cap);

@@ -135,6 +135,7 @@ def test_fps_ties_and_duplicates(gpu, oracle_mod, mode, monkeypatch):
 @pytest.mark.parametrize("G,rg,block", [(1, 0, 256), (1, 0, 1024), (4, 1, 1024), (4, 15, 1024),
                                         (4, 30, 1024), (9, 3, 1024), (40, 2, 1024),
                                         (63, 4, 1024), (70, 1, 1024), (130, 1, 1024),
+                                        (130, 3, 1024), (200, 2, 1024), (256, 2, 1024),
                                         (3, 1, 256), (3, 6, 256)])
 def test_fps_batch_shapes(gpu, oracle_mod, G, rg, block, monkeypatch):
     """Certified-batch kernel over workgroup counts, published candidates per
@@ -152,13 +153,14 @@ def test_fps_batch_shapes(gpu, oracle_mod, G, rg, block, monkeypatch):
     check_fps(gpu, oracle_mod, xi, 200, 0, f"batch ints G={G} rg={rg} block={block}")
 
 
-@pytest.mark.parametrize("G,rg", [(4, 30), (64, 4), (33, 7)])
+@pytest.mark.parametrize("G,rg", [(4, 30), (64, 4), (33, 7), (130, 3)])
 def test_fps_batch_many_live_candidates(gpu, oracle_mod, G, rg, monkeypatch):
     """Every workgroup's slice (1920 points: 15 point waves of 128) is a tiny
     cluster plus `rg` far outliers, one or two per point wave, so each
     workgroup publishes outliers only and its bound is a cluster point: the
-    first batches keep all G * rg candidates live (up to four slots per lane,
-    the general certification loop), later ones one or two."""
+    first batches keep all G * rg candidates live (up to eight slots per lane
+    above 128 workgroups, the general certification loop), later ones one or
+    two."""
     monkeypatch.setenv("POINTOPS_FPS_MODE", "batch")
     monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", str(G))
     monkeypatch.setenv("POINTOPS_FPS_BLOCK", "1024")
