@@ -162,7 +162,9 @@ hipError_t launch_ball_query(const float* query, const float* ref, int64_t B, in
 // x - q), so a block is skipped for the group when even that bound reaches
 // R2. Only in the runs of 64 blocks where some block survives does each query
 // test the blocks on its own, and a block is then scanned for the queries
-// whose own test it passed.
+// whose own test it passed. One level up, the union box of every 64 blocks
+// lets a wave find the runs worth loading with one load per lane, instead of
+// loading every run's 64 boxes in turn.
 
 constexpr int kBoxFloats = 8;  // min x, y, z, max x, y, z, 2 unused
 
@@ -216,18 +218,42 @@ __global__ __launch_bounds__(256) void ball_query_boxes_kernel(const float* __re
 // after these in index order.
 constexpr uint32_t kBqDone = 0xFFFFFFFFu;
 
+// One wave per 64 blocks: their union box, sbox[(b * nsb + s) * 8 + 0..5].
+__global__ __launch_bounds__(256) void ball_query_superboxes_kernel(const float* __restrict__ box,
+                                                                    int64_t B, int nblk, int nsb,
+                                                                    float* __restrict__ sbox) {
+    const int64_t w = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (w >= B * nsb) return;  // whole waves leave together
+    const int64_t b = w / nsb;
+    const int k = (int)(w - b * nsb) * kWave + lane;
+    const float inf = __builtin_inff();
+    float x = inf, y = inf, z = inf, X = -inf, Y = -inf, Z = -inf;
+    if (k < nblk) {
+        const float* o = box + ((size_t)b * nblk + k) * kBoxFloats;
+        x = o[0]; y = o[1]; z = o[2]; X = o[3]; Y = o[4]; Z = o[5];
+    }
+    x = wave_min_f32(x); y = wave_min_f32(y); z = wave_min_f32(z);
+    X = wave_max_f32(X); Y = wave_max_f32(Y); Z = wave_max_f32(Z);
+    if (lane == 0) {
+        float* o = sbox + (size_t)w * kBoxFloats;
+        o[0] = x; o[1] = y; o[2] = z; o[3] = X; o[4] = Y; o[5] = Z;
+    }
+}
+
 template <int QW>
 __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
     const float* __restrict__ query, const float* __restrict__ ref, int Q, int P, float r2,
     int K, float* __restrict__ out_d2, int64_t* __restrict__ out_idx,
-    const float* __restrict__ box, int nblk, int budget, uint2* __restrict__ state,
-    uint32_t* __restrict__ flag) {
+    const float* __restrict__ box, int nblk, const float* __restrict__ sbox, int nsb, int budget,
+    uint2* __restrict__ state, uint32_t* __restrict__ flag) {
     const int b = blockIdx.y;
     const int row0 = blockIdx.x * QW;
     const int lane = threadIdx.x;
     const float* qb = query + (size_t)b * Q * 3;
     const float* xb = ref + (size_t)b * P * 3;
     const float* bb = box + (size_t)b * nblk * kBoxFloats;
+    const float* sbb = sbox + (size_t)b * nsb * kBoxFloats;
     const size_t out0 = ((size_t)b * Q + row0) * (size_t)K;
 
     float qx[QW], qy[QW], qz[QW];
@@ -252,7 +278,26 @@ __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
 
     int scanned = 0;    // blocks this wave has scanned
     int stop_blk = -1;  // first block not examined when the budget ran out
-    for (int c0 = 0; c0 < nblk; c0 += kWave) {
+    bool finished = false;
+    // Runs of 64 blocks in increasing order, only those whose union box the
+    // group's box can reach (the same bound, one level up)
+    for (int s0 = 0; s0 < nsb && !finished; s0 += kWave) {
+      uint64_t ms;
+      {
+        const int sl = s0 + lane;
+        float lx = inf, ly = inf, lz = inf, hx = -inf, hy = -inf, hz = -inf;
+        if (sl < nsb) {
+            const float* o = sbb + (size_t)sl * kBoxFloats;
+            lx = o[0]; ly = o[1]; lz = o[2]; hx = o[3]; hy = o[4]; hz = o[5];
+        }
+        const float gx = fmaxf(fmaxf(lx - gQx, gqx - hx), 0.0f);
+        const float gy = fmaxf(fmaxf(ly - gQy, gqy - hy), 0.0f);
+        const float gz = fmaxf(fmaxf(lz - gQz, gqz - hz), 0.0f);
+        ms = ballot((gx * gx + gy * gy) + gz * gz < r2);
+      }
+      while (ms) {
+        const int c0 = (s0 + __builtin_ctzll(ms)) * kWave;
+        ms &= ms - 1;
         // lane l: block c0 + l; blocks past the end have an empty box (bound +inf)
         const int k = c0 + lane;
         float lx = inf, ly = inf, lz = inf, hx = -inf, hy = -inf, hz = -inf;
@@ -325,7 +370,11 @@ __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
             }
             if (!live || cur < 0) break;
         }
-        if (!live || stop_blk >= 0) break;
+        if (!live || stop_blk >= 0) {
+            finished = true;
+            break;
+        }
+      }
     }
 
     bool left = false;
@@ -347,8 +396,10 @@ __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
     if (left) atomicOr(flag, 1u);  // lane 0 only
 }
 
+// Boxes of the 64-reference blocks, then of every 64 blocks.
 size_t ball_query_box_bytes(int64_t B, int64_t P) {
-    return (size_t)B * (size_t)((P + kWave - 1) / kWave) * kBoxFloats * sizeof(float);
+    const int64_t nblk = (P + kWave - 1) / kWave, nsb = (nblk + kWave - 1) / kWave;
+    return (size_t)B * (size_t)(nblk + nsb) * kBoxFloats * sizeof(float);
 }
 
 // Boxes of every 64-reference block into `box`, then the culled scan: grid
@@ -359,13 +410,19 @@ hipError_t launch_ball_query_culled(const float* query, const float* ref, int64_
                                     int64_t P, float r2, int64_t K, float* out_d2,
                                     int64_t* out_idx, int qw, float* box, int budget,
                                     uint2* state, uint32_t* flag, hipStream_t stream) {
-    const int nblk = (int)((P + kWave - 1) / kWave);
+    const int nblk = (int)((P + kWave - 1) / kWave), nsb = (nblk + kWave - 1) / kWave;
+    float* sbox = box + (size_t)B * nblk * kBoxFloats;
     if (!state) budget = -1;  // never reached
     if (B * nblk > 0) {
         const int64_t waves = B * nblk;
         hipLaunchKernelGGL(ball_query_boxes_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256),
                            0, stream, ref, B, (int)P, nblk, box, flag);
         hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(ball_query_superboxes_kernel,
+                           dim3((unsigned)((B * nsb + 3) / 4)), dim3(256), 0, stream, box, B,
+                           nblk, nsb, sbox);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     dim3 block(kWave);
@@ -374,8 +431,8 @@ hipError_t launch_ball_query_culled(const float* query, const float* ref, int64_
     case W: {                                                                                 \
         dim3 grid((unsigned)((Q + W - 1) / W), (unsigned)B);                                  \
         hipLaunchKernelGGL(ball_query_cull_kernel<W>, grid, block, 0, stream, query, ref,     \
-                           (int)Q, (int)P, r2, (int)K, out_d2, out_idx, box, nblk, budget,    \
-                           state, flag);                                                      \
+                           (int)Q, (int)P, r2, (int)K, out_d2, out_idx, box, nblk, sbox, nsb, \
+                           budget, state, flag);                                              \
         break;                                                                                \
     }
         POINTOPS_BQC_CASE(1)
