@@ -117,3 +117,25 @@ def test_python_binding_refuses_cpu_tensors():
         ops.ball_query(x, x, 0.5, 2)
     with pytest.raises(ops.PointopsError):
         ops.furthest_point_sample(x, 2)
+
+
+def test_workspace_sizes(lib):
+    """Host-only size queries: the Ball Query's workspace grows by the grid
+    pass's room (per query, sorted copies, histograms) above 32768 references
+    and is zero for empty shapes; kNN's grid workspace starts at 8192
+    references and 2^27 pairs."""
+    i64 = ctypes.c_int64
+    lib.pointops_ball_query_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.pointops_ball_query_workspace_bytes.restype = ctypes.c_size_t
+    lib.pointops_knn_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.pointops_knn_workspace_bytes.restype = ctypes.c_size_t
+    bq = lib.pointops_ball_query_workspace_bytes
+    # boxes only: (blocks of 64 + runs of 64 blocks) x 32 bytes per cloud
+    nblk = (30000 + 63) // 64
+    assert bq(2, 10, 30000) == 2 * (nblk + (nblk + 63) // 64) * 32
+    assert bq(1, 10, 32769) > bq(1, 10, 32768) + 16 * 32769   # the sorted copies alone
+    assert bq(1, 2000, 40000) >= bq(1, 1000, 40000) + 1000 * (8 + 16) - 2 * 256  # alignment
+    assert bq(0, 10, 100) == bq(1, 0, 100) == bq(1, 10, 0) == 0
+    knn = lib.pointops_knn_workspace_bytes
+    assert knn(1, 100000, 100000) > 0
+    assert knn(1, 100, 8191) == 0 and knn(1, 10, 100000) == 0
