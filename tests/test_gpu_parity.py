@@ -391,3 +391,10 @@ def test_invalid_arguments_raise(gpu):
         gpu.ball_query(x, x, -1.0, 3)
     with pytest.raises(gpu.PointopsError):
         gpu.knn(x.double(), x.double(), 2)
+
+
+def test_fps_two_large_clouds(gpu, oracle_mod):
+    """Two clouds of 400k points: each would take 256 workgroups, which do not
+    fit on the device at once, so the plan falls back to fewer per cloud."""
+    xyz = W.uniform_cube(61, 2, 400000)
+    check_fps(gpu, oracle_mod, xyz, 40, 7, "2 x 400k")

@@ -211,3 +211,11 @@ def test_ragged_invalid_arguments(gpu):
                                  ctypes.c_void_p(off.ctypes.data), ctypes.c_void_p(cnt.ctypes.data),
                                  2, 4, 1, o.data_ptr(), oi.data_ptr(), ws.data_ptr(), 4096, None)
     assert rc == 1
+
+
+def test_fps_ragged_cloud_beyond_128_workgroups(gpu, oracle_mod):
+    """A cloud of 2.1M points takes more than 128 workgroups (at most 16
+    points per thread), so its exchange carries up to 512 candidates (eight
+    slots per lane of the certifying wave); two small clouds ride along."""
+    r = W.ragged_batch(21, [2_100_000, 5000, 300])
+    check_fps(gpu, oracle_mod, r.xyz, r.ptr, np.array([48, 50, 10]), what="2.1M-point cloud")
