@@ -236,6 +236,21 @@ int pointops_ball_query_backward(const float *query, const float *ref, const int
 size_t pointops_ragged_workspace_bytes(int64_t B);
 
 /*
+ * Workspace bytes with which pointops_knn_ragged takes the grid search (the
+ * culled search of the dense kNN, project page "mps-pointops", roadmap:
+ * spatial structures for large clouds) for clouds with these query and
+ * reference counts (host arrays of B entries) and this k; the results do not
+ * change. It is pointops_ragged_workspace_bytes(B) when the full scan is the
+ * better search, and about 16 * B * (max q_cnt + max r_cnt) bytes plus the
+ * grid's cell counts otherwise (the grid is not taken when that padding would
+ * exceed eight times the points' own room). With a smaller workspace
+ * pointops_knn_ragged scans every reference of each cloud. 0 for invalid
+ * counts.
+ */
+size_t pointops_knn_ragged_workspace_bytes(const int64_t *q_cnt, const int64_t *r_cnt, int64_t B,
+                                           int64_t k);
+
+/*
  * kNN of ragged batches. For each cloud b, the queries are rows q_off[b] ..
  * of `query` and the references rows r_off[b] .. of `ref`; output row r of
  * out_dist / out_idx ((q_rows, k), device) belongs to query row r. Where a

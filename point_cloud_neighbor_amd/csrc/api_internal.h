@@ -23,7 +23,7 @@ hipError_t launch_ball_query_grid(const float*, const float*, int64_t, int64_t, 
 int knn_grid_level(int64_t P);
 size_t ball_query_grid_bytes(int64_t B, int64_t Q, int64_t P);
 hipError_t launch_knn_grid(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
-                           int64_t*, int, int, void*, int, hipStream_t);
+                           int64_t*, int, int, void*, int, const int64_t*, hipStream_t);
 size_t knn_grid_workspace_bytes(int64_t B, int64_t Q, int64_t P);
 hipError_t launch_fps(const float*, int64_t, int64_t, int64_t, int64_t, int64_t*, float*, void*,
                       int, int, int, uint32_t, hipStream_t, const int64_t*, int, int64_t);
@@ -92,8 +92,32 @@ int knn_waves(int kcap, int64_t tiles, int cus);
 bool knn_use_grid(int64_t B, int64_t Q, int64_t P);
 // ... and the grid search beats the full scans for this k and shape.
 bool knn_grid_pays(int64_t k, int64_t B, int64_t Q, int64_t P);
-// Waves per workgroup of the grid search.
+// The same two rules for `pairs` query-reference pairs in all and at most P
+// references per cloud (ragged batches).
+bool knn_use_grid_pairs(int64_t pairs, int64_t P);
+bool knn_grid_pays_pairs(int64_t k, int64_t pairs, int64_t P);
+// kNN of a ragged batch through the grid search: the workspace holds the
+// per-cloud records (grid.h, GridCloud) at `clouds`, then the grid at `grid`;
+// P and Q are the largest reference and query counts (every cloud keeps that
+// many slots). `use` is false when the grid does not pay for these counts or
+// the padding to the largest cloud would take more than eight times the
+// points' own room; `total` then is the full scan's need alone.
+struct RaggedKnnGrid {
+    bool use = false;
+    int64_t P = 0, Q = 0;
+    size_t clouds = 0, grid = 0, total = 0;
+    size_t grid_bytes = 0;  // the grid's own room (at `grid`)
+};
+RaggedKnnGrid ragged_knn_grid(const int64_t* q_cnt, const int64_t* r_cnt, int64_t B, int64_t k);
+// Writes the records of the clouds (q_off[b], q_cnt[b], r_off[b], r_cnt[b],
+// index base) to `dev` on `stream`.
+int upload_grid_clouds(const int64_t* q_off, const int64_t* q_cnt, const int64_t* r_off,
+                       const int64_t* r_cnt, int64_t B, bool global_index, int64_t* dev,
+                       hipStream_t s);
+// Waves per workgroup of the grid search (one query per lane).
 int knn_grid_waves(int kcap);
+// The grid search's launch: 0 for one query per wave, else knn_grid_waves.
+int knn_grid_nw(int64_t k, int kcap, int64_t queries, int64_t refs);
 int bq_queries_per_wave(int64_t rows, int cus, int max_qw);
 bool bq_grid_possible(int64_t P);
 int bq_scan_budget();

@@ -159,7 +159,8 @@ hipError_t launch_ball_query_grid(const float* query, const float* ref, int64_t 
                                             (float*)(ws + l.box), budget, state, flag, stream);
     if (e != hipSuccess) return e;
     GridView v;
-    e = launch_grid_build(query, ref, B, Q, P, level, ws + l.grid, flag, stream, &v);
+    e = launch_grid_build(query, ref, B, Q, P, level, ws + l.grid, flag, nullptr, stream,
+                          &v);
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)((Q + kBqgWaves - 1) / kBqgWaves), (unsigned)B);
     hipLaunchKernelGGL(ball_query_grid_kernel, grid, dim3(kBqgWaves * kWave), 0, stream,

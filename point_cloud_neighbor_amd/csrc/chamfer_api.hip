@@ -108,8 +108,8 @@ int nearest(const float* a, const float* bpts, int64_t B, int64_t n, int64_t m,
     hipError_t e;
     if (!la && !lb && m > 0 && knn_use_grid(B, n, m) && knn_grid_pays(1, B, n, m) &&
         grid_bytes >= pointops::knn_grid_workspace_bytes(B, n, m)) {
-        e = pointops::launch_knn_grid(a, bpts, B, n, m, 1, dist, idx, 1, knn_grid_waves(1),
-                                      grid_ws, 1, s);
+        e = pointops::launch_knn_grid(a, bpts, B, n, m, 1, dist, idx, 1,
+                                      knn_grid_nw(1, 1, B * n, B * m), grid_ws, 1, nullptr, s);
         return e == hipSuccess ? POINTOPS_OK : hip_fail(e, "nearest launch");
     }
     if (!la && !lb) {
@@ -133,11 +133,26 @@ int nearest(const float* a, const float* bpts, int64_t B, int64_t n, int64_t m,
         queries += qc[(size_t)b];
         if (qc[(size_t)b] > 0) max_refs = std::max(max_refs, rc[(size_t)b]);
     }
+    e = pointops::launch_chamfer_pad(dist, idx, B, n, dev_la, s);
+    if (e != hipSuccess) return hip_fail(e, "chamfer pad");
+    // The grid search over the clouds' own counts when it pays and the grid's
+    // room (sized for the full clouds) holds it; the cloud records go where
+    // the full scan's table would.
+    const RaggedKnnGrid g = ragged_knn_grid(qc.data(), rc.data(), B, 1);
+    if (g.use && table_bytes >= g.grid && grid_bytes >= g.grid_bytes) {
+        int64_t* clouds = (int64_t*)table_ws;
+        int st = upload_grid_clouds(qo.data(), qc.data(), ro.data(), rc.data(), B, false, clouds,
+                                    s);
+        if (st != POINTOPS_OK) return st;
+        int64_t refs = 0;
+        for (int64_t b = 0; b < B; ++b) refs += rc[(size_t)b];
+        e = pointops::launch_knn_grid(a, bpts, B, g.Q, g.P, 1, dist, idx, 1,
+                                      knn_grid_nw(1, 1, queries, refs), grid_ws, 1, clouds, s);
+        return e == hipSuccess ? POINTOPS_OK : hip_fail(e, "nearest launch");
+    }
     const KnnWavePlan wp = knn_wave_plan(1, queries, max_refs, dev.cus);
     const Table t = search_table(qo.data(), qc.data(), ro.data(), rc.data(), B,
                                  wp.nw ? wp.nw * wp.qw : 64, false);
-    e = pointops::launch_chamfer_pad(dist, idx, B, n, dev_la, s);
-    if (e != hipSuccess) return hip_fail(e, "chamfer pad");
     if (t.units == 0) return POINTOPS_OK;
     int64_t* table = nullptr;
     int st = upload(t, table_ws, table_bytes, s, &table);

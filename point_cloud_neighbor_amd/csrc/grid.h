@@ -80,6 +80,16 @@ __device__ __forceinline__ float box_bound(const float* __restrict__ o, float qx
     return (gx * gx + gy * gy) + gz * gz;
 }
 
+// Ragged batches: the build and the kNN search can take a table of kGcWords
+// words per cloud in device memory. Cloud b's references are then rows
+// [ROff, ROff + RCnt) of the reference buffer and its queries rows
+// [QOff, QOff + QCnt) of the query buffer; its sorted copies keep the slots
+// [b * P, b * P + RCnt) and [b * Q, b * Q + QCnt), P and Q being the largest
+// counts of the batch. The search writes a query's row QOff + its index in
+// the cloud and reports reference indices IdxBase + index in the cloud.
+enum GridCloud { kGcROff = 0, kGcRCnt, kGcQOff, kGcQCnt, kGcIdxBase };
+constexpr int kGcWords = 8;
+
 // The build's outputs inside its workspace.
 struct GridView {
     GridParams* gp;      // per cloud
@@ -99,8 +109,10 @@ size_t grid_workspace_bytes(int64_t B, int64_t Q, int64_t P, int L);
 // queries into `workspace` (grid_workspace_bytes(B, Q, P, L) bytes). With
 // `gate` non-null every build kernel reads *gate first and does nothing when
 // it is 0 (the caller decides on the device whether the grid is needed).
+// With `clouds` non-null (a ragged batch, see GridCloud) P and Q are the
+// largest counts and every cloud takes its points from its table record.
 hipError_t launch_grid_build(const float* query, const float* ref, int64_t B, int64_t Q,
                              int64_t P, int L, void* workspace, const uint32_t* gate,
-                             hipStream_t stream, GridView* view);
+                             const int64_t* clouds, hipStream_t stream, GridView* view);
 
 }  // namespace pointops

@@ -35,6 +35,7 @@
 
 #include "common.h"
 #include "grid.h"
+#include "wave_list.h"
 
 namespace pointops {
 
@@ -74,12 +75,14 @@ __global__ void grid_init_kernel(uint32_t* __restrict__ enc, int64_t B,
 __global__ __launch_bounds__(256) void grid_bounds_kernel(const float* __restrict__ ref, int64_t B,
                                                           int P, int L, uint32_t* __restrict__ enc,
                                                           GridParams* __restrict__ gp,
-                                                          const uint32_t* __restrict__ gate) {
+                                                          const uint32_t* __restrict__ gate,
+                                                          const int64_t* __restrict__ clouds) {
     if (gate && *gate == 0) return;  // the grid is not needed
     __shared__ uint32_t sh[6];
     __shared__ bool last;
     const int b = blockIdx.y;
-    const float* xb = ref + (size_t)b * P * 3;
+    const float* xb = ref + (clouds ? clouds[kGcWords * b + kGcROff] : (int64_t)b * P) * 3;
+    if (clouds) P = (int)clouds[kGcWords * b + kGcRCnt];
     uint32_t* e = enc + (size_t)b * kEncWords;
     if (threadIdx.x < 6) sh[threadIdx.x] = threadIdx.x < 3 ? 0xFFFFFFFFu : 0u;
     __syncthreads();
@@ -133,7 +136,8 @@ __global__ __launch_bounds__(256) void grid_bounds_kernel(const float* __restric
 __global__ void grid_count_kernel(const float* __restrict__ ref, const float* __restrict__ query,
                                   int64_t B, int P, int Q, int L,
                                   const GridParams* __restrict__ gp, uint32_t* __restrict__ rcnt,
-                                  uint32_t* __restrict__ qcnt, const uint32_t* __restrict__ gate) {
+                                  uint32_t* __restrict__ qcnt, const uint32_t* __restrict__ gate,
+                                  const int64_t* __restrict__ clouds) {
     if (gate && *gate == 0) return;  // the grid is not needed
     const int64_t C = (int64_t)1 << (3 * L);
     const int64_t nr = B * P;
@@ -141,8 +145,15 @@ __global__ void grid_count_kernel(const float* __restrict__ ref, const float* __
          e += (int64_t)gridDim.x * blockDim.x) {
         const bool is_ref = e < nr;
         const int64_t i = is_ref ? e : e - nr;
-        const int64_t b = i / (is_ref ? P : Q);
-        const float* p = (is_ref ? ref : query) + i * 3;
+        const int64_t n = is_ref ? P : Q;
+        const int64_t b = i / n;
+        int64_t row = i;
+        if (clouds) {  // slot i - b * n of cloud b, if the cloud has that many points
+            const int64_t loc = i - b * n;
+            if (loc >= clouds[kGcWords * b + (is_ref ? kGcRCnt : kGcQCnt)]) continue;
+            row = clouds[kGcWords * b + (is_ref ? kGcROff : kGcQOff)] + loc;
+        }
+        const float* p = (is_ref ? ref : query) + row * 3;
         atomicAdd(&(is_ref ? rcnt : qcnt)[b * C + cell_code(gp[b], p[0], p[1], p[2], L)], 1u);
     }
 }
@@ -234,7 +245,8 @@ __global__ void grid_scatter_kernel(const float* __restrict__ ref, const float* 
                                     const uint32_t* __restrict__ rstart, uint32_t* __restrict__ rfill,
                                     const uint32_t* __restrict__ qstart, uint32_t* __restrict__ qfill,
                                     float4* __restrict__ rout, float4* __restrict__ qout,
-                                    const uint32_t* __restrict__ gate) {
+                                    const uint32_t* __restrict__ gate,
+                                    const int64_t* __restrict__ clouds) {
     if (gate && *gate == 0) return;  // the grid is not needed
     const int64_t C = (int64_t)1 << (3 * L);
     const int64_t nr = B * P;
@@ -245,7 +257,12 @@ __global__ void grid_scatter_kernel(const float* __restrict__ ref, const float* 
         const int n = is_ref ? P : Q;
         const int64_t b = i / n;
         const int j = (int)(i - b * n);
-        const float* p = (is_ref ? ref : query) + i * 3;
+        int64_t row = i;
+        if (clouds) {
+            if (j >= clouds[kGcWords * b + (is_ref ? kGcRCnt : kGcQCnt)]) continue;
+            row = clouds[kGcWords * b + (is_ref ? kGcROff : kGcQOff)] + j;
+        }
+        const float* p = (is_ref ? ref : query) + row * 3;
         const uint32_t code = cell_code(gp[b], p[0], p[1], p[2], L);
         const uint32_t pos = (is_ref ? rstart : qstart)[b * C + code] +
                              atomicAdd(&(is_ref ? rfill : qfill)[b * C + code], 1u);
@@ -260,17 +277,19 @@ __global__ __launch_bounds__(1024) void grid_boxes_kernel(const float4* __restri
                                                           int64_t B, int P, int nblk, int nsb,
                                                           float* __restrict__ box,
                                                           float* __restrict__ sbox,
-                                                          const uint32_t* __restrict__ gate) {
+                                                          const uint32_t* __restrict__ gate,
+                                                          const int64_t* __restrict__ clouds) {
     if (gate && *gate == 0) return;  // the grid is not needed
     __shared__ float sh[kWave][6];
     const int64_t b = blockIdx.y;
+    const int Pb = clouds ? (int)clouds[kGcWords * b + kGcRCnt] : P;  // real points of this cloud
     const int sb = blockIdx.x;
     const int t = threadIdx.x;
     const int j = sb * kWave * kGridBlk + t;
     const int k = sb * kWave + t / kGridBlk;  // this thread's block
     const float inf = __builtin_inff();
     float v[6] = {inf, inf, inf, -inf, -inf, -inf};
-    if (j < P) {
+    if (j < Pb) {
         const float4 p = sr[b * P + j];
         v[0] = v[3] = p.x;
         v[1] = v[4] = p.y;
@@ -318,17 +337,32 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
     const float4* __restrict__ sq, const float4* __restrict__ sr, int Q, int P, int k,
     const float* __restrict__ box, const float* __restrict__ sbox, int nblk, int nsb,
     const uint32_t* __restrict__ ref_start, const GridParams* __restrict__ gp, int L,
-    float* __restrict__ out_dist, int64_t* __restrict__ out_idx, int squared) {
+    float* __restrict__ out_dist, int64_t* __restrict__ out_idx, int squared,
+    const int64_t* __restrict__ clouds) {
     constexpr int ROWS = kGridBuf > KCAP ? kGridBuf : KCAP;
     extern __shared__ uint2 lds[];             // per wave ROWS x 64 entries
     __shared__ uint32_t thr[NW][kWave];        // each wave's lanes' k-th key (high half)
 
     const int b = blockIdx.y;
+    // This cloud's counts (a ragged batch: its own; the slots keep the
+    // strides Q, P, nblk and nsb), first output row and index base.
+    int Qb = Q, Pb = P, nbb = nblk, nsbb = nsb;
+    int64_t orow0 = (int64_t)b * Q, ibase = 0;
+    if (clouds) {
+        const int64_t* c = clouds + (size_t)b * kGcWords;
+        Qb = (int)c[kGcQCnt];
+        Pb = (int)c[kGcRCnt];
+        nbb = (Pb + kGridBlk - 1) / kGridBlk;
+        nsbb = (nbb + kWave - 1) / kWave;
+        orow0 = c[kGcQOff];
+        ibase = c[kGcIdxBase];
+    }
+    if ((int)blockIdx.x * kWave >= Qb) return;  // the whole workgroup: no query of its cloud
     const int lane = threadIdx.x % kWave;
     const int w = uniform((int)(threadIdx.x / kWave));
     const int qi = blockIdx.x * kWave + lane;
-    const bool qvalid = qi < Q;
-    const float4 q = sq[(size_t)b * Q + (qvalid ? qi : Q - 1)];
+    const bool qvalid = qi < Qb;
+    const float4 q = sq[(size_t)b * Q + (qvalid ? qi : Qb - 1)];
     const float4* rb = sr + (size_t)b * P;
     const float* bx = box + (size_t)b * nblk * 8;
     const float* sbx = sbox + (size_t)b * nsb * 8;
@@ -336,19 +370,23 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
 
     TopK64<KCAP> top;
     top.init(k);
-    uint32_t lim = qvalid ? 0xFFFFFFFFu : 0u;  // accept key high half u <= lim; none without a query
+    // Accept a key whose high half u <= lim; none without a query. Real keys
+    // have u <= bits(+inf) + 1, so the start 0xFFFFFFFE admits them all but
+    // never the marker 0xFFFFFFFF of the local pass's references (which a
+    // cloud with fewer than k references would otherwise take twice).
+    uint32_t lim = qvalid ? 0xFFFFFFFEu : 0u;
     thr[w][lane] = lim;
     int cnt = 0;
 
     // Each lane's own neighbourhood in sorted order: the kGridLocal references
     // around the first reference of its grid cell.
-    const int nloc = min(P, kGridLocal);
+    const int nloc = min(Pb, kGridLocal);
     int loc0;
     {
         const int64_t C = (int64_t)1 << (3 * L);
         const uint32_t code = cell_code(gp[b], q.x, q.y, q.z, L);
         const int pos = (int)ref_start[(int64_t)b * C + code];
-        loc0 = max(0, min(pos - nloc / 2, P - nloc));
+        loc0 = max(0, min(pos - nloc / 2, Pb - nloc));
     }
 
     auto flush = [&]() {
@@ -391,7 +429,7 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
     // Every wave skips, in later blocks, the references of its lane's local
     // pass: they are in wave 0's list already.
     auto scan_block = [&](int blk) {
-        const int j0 = blk * kGridBlk, j1 = min(P, j0 + kGridBlk);
+        const int j0 = blk * kGridBlk, j1 = min(Pb, j0 + kGridBlk);
         int j = j0;
         for (; j + 8 <= j1; j += 8) {
             uint32_t u[8];
@@ -467,11 +505,11 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
         const float gz = fmaxf(fmaxf(o[2] - gh[2], gl[2] - o[5]), 0.0f);
         return (gx * gx + gy * gy) + gz * gz;
     };
-    for (int sb0 = 0; sb0 < nsb; sb0 += kWave) {
+    for (int sb0 = 0; sb0 < nsbb; sb0 += kWave) {
         uint32_t mlim = wave_max_u32(lim);
         const int my_sb = sb0 + lane;
-        uint64_t cs = ballot(my_sb < nsb &&
-                             f2u(group_bound(sbx + (size_t)min(my_sb, nsb - 1) * 8)) + 1u <= mlim);
+        uint64_t cs = ballot(my_sb < nsbb &&
+                             f2u(group_bound(sbx + (size_t)min(my_sb, nsbb - 1) * 8)) + 1u <= mlim);
         while (cs) {
             const int s = sb0 + __builtin_ctzll(cs);
             cs &= cs - 1;
@@ -479,8 +517,8 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
                 continue;
             mlim = wave_max_u32(lim);
             const int my_blk = s * kWave + lane;
-            const bool mine = my_blk < nblk && my_blk % NW == w;
-            uint64_t cb = ballot(mine && f2u(group_bound(bx + (size_t)min(my_blk, nblk - 1) * 8)) +
+            const bool mine = my_blk < nbb && my_blk % NW == w;
+            uint64_t cb = ballot(mine && f2u(group_bound(bx + (size_t)min(my_blk, nbb - 1) * 8)) +
                                              1u <= mlim);
             while (cb) {
                 const int blk = s * kWave + __builtin_ctzll(cb);
@@ -524,17 +562,136 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
         if (w != 0) return;
     }
     if (!qvalid) return;
-    const int64_t row = (int64_t)b * Q + __float_as_int(q.w);
+    const int64_t row = orow0 + __float_as_int(q.w);
     float* od = out_dist + row * k;
     int64_t* oi = out_idx + row * k;
     const int front = KCAP - k;
 #pragma unroll
     for (int p = 0; p < KCAP; ++p) {
         if (p >= front) {
+            // an empty slot only in a cloud with fewer than k references:
+            // (+inf, -1), or (0, -1) for squared distances
+            const bool empty = top.key[p] == ~0ull;
             const float sv = u2f((uint32_t)(top.key[p] >> 32) - 1u);
-            od[p - front] = squared ? sv : sqrtf(sv);
-            oi[p - front] = (int64_t)(uint32_t)top.key[p];
+            od[p - front] = empty ? (squared ? 0.0f : __builtin_inff()) : squared ? sv : sqrtf(sv);
+            oi[p - front] = empty ? (int64_t)-1 : ibase + (int64_t)(uint32_t)top.key[p];
         }
+    }
+}
+
+// One query per wave (k <= 32), for launches with few queries per cloud or
+// queries much sparser than the references (a lane-per-query workgroup then
+// has few waves and a wide box of queries). A workgroup holds kKgwWaves
+// queries in grid order, one per wave. The wave first sorts the 64
+// references around its query's grid position into its list (wave_list.h,
+// keys (bits(s) << 32) | index) and takes the k-th key's high word as its
+// bound; then its lanes test 64 superblock boxes at a time and, in a
+// surviving superblock, 64 block boxes, and test the references of up to four
+// surviving blocks at a time, one per lane. A box is visited when its lower
+// bound's bits do not exceed the bound (a point with equal bits may still
+// enter by a smaller index), and a reference is offered under the same
+// inclusive test; the merges keep the 32 smallest keys, so any visiting order
+// gives the (s, j) order. No barriers: the waves of a workgroup are
+// independent.
+constexpr int kKgwWaves = 4;
+
+__global__ __launch_bounds__(kKgwWaves* kWave) void knn_grid_wave_kernel(
+    const float4* __restrict__ sq, const float4* __restrict__ sr, int Q, int P, int k,
+    const float* __restrict__ box, const float* __restrict__ sbox, int nblk, int nsb,
+    const uint32_t* __restrict__ ref_start, const GridParams* __restrict__ gp, int L,
+    float* __restrict__ out_dist, int64_t* __restrict__ out_idx, int squared,
+    const int64_t* __restrict__ clouds) {
+    __shared__ uint64_t cbuf[kKgwWaves][kKwBuf];
+    const int b = blockIdx.y;
+    int Qb = Q, Pb = P, nbb = nblk, nsbb = nsb;
+    int64_t orow0 = (int64_t)b * Q, ibase = 0;
+    if (clouds) {
+        const int64_t* c = clouds + (size_t)b * kGcWords;
+        Qb = (int)c[kGcQCnt];
+        Pb = (int)c[kGcRCnt];
+        nbb = (Pb + kGridBlk - 1) / kGridBlk;
+        nsbb = (nbb + kWave - 1) / kWave;
+        orow0 = c[kGcQOff];
+        ibase = c[kGcIdxBase];
+    }
+    const int lane = lane_id();
+    const int w = uniform((int)(threadIdx.x / kWave));
+    const int qi = (int)blockIdx.x * kKgwWaves + w;
+    if (qi >= Qb) return;  // whole waves
+    const float4 q = sq[(size_t)b * Q + qi];
+    const float4* rb = sr + (size_t)b * P;
+    const float* bx = box + (size_t)b * nblk * 8;
+    const float* sbx = sbox + (size_t)b * nsb * 8;
+
+    // 1. The kWave references around the query's own grid position.
+    const int nloc = min(Pb, kWave);
+    int loc0;
+    {
+        const int64_t C = (int64_t)1 << (3 * L);
+        const uint32_t code = cell_code(gp[b], q.x, q.y, q.z, L);
+        const int pos = (int)ref_start[(int64_t)b * C + code];
+        loc0 = max(0, min(pos - nloc / 2, Pb - nloc));
+    }
+    KwQuery st{kKwEmpty, ~0u, 0, cbuf[w]};
+    {
+        uint64_t key = kKwEmpty;
+        if (lane < nloc) {
+            const float4 p = rb[loc0 + lane];
+            key = ((uint64_t)f2u(s32(q.x, q.y, q.z, p.x, p.y, p.z)) << 32) |
+                  (uint32_t)__float_as_int(p.w);
+        }
+        st.list = kw_sort_merge(key, lane);
+        st.bound = lane_value((uint32_t)(st.list >> 32), k - 1);
+    }
+
+    // 2. Superblocks, then the blocks of a surviving one, then the references
+    //    of up to four surviving blocks at a time (16 lanes each); the local
+    //    references are in the list already.
+    for (int sb0 = 0; sb0 < nsbb; sb0 += kWave) {
+        const int my_sb = sb0 + lane;
+        uint64_t ms = ballot(my_sb < nsbb &&
+                             f2u(box_bound(sbx + (size_t)min(my_sb, nsbb - 1) * 8, q.x, q.y,
+                                           q.z)) <= st.bound);
+        while (ms) {
+            const int s = sb0 + __builtin_ctzll(ms);
+            ms &= ms - 1;
+            const int my_blk = s * kWave + lane;
+            uint64_t mb = ballot(my_blk < nbb &&
+                                 f2u(box_bound(bx + (size_t)min(my_blk, nbb - 1) * 8, q.x, q.y,
+                                               q.z)) <= st.bound);
+            while (mb) {
+                int blk[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    blk[r] = mb ? s * kWave + __builtin_ctzll(mb) : -1;
+                    mb &= mb - 1;  // no-op once empty
+                }
+                const int g = lane >> 4;
+                const int mine = g == 0 ? blk[0] : g == 1 ? blk[1] : g == 2 ? blk[2] : blk[3];
+                const int j = mine * kGridBlk + (lane & (kGridBlk - 1));
+                bool cand = false;
+                uint32_t u = 0u, idx = 0u;
+                if (mine >= 0 && j < Pb && (uint32_t)(j - loc0) >= (uint32_t)nloc) {
+                    const float4 p = rb[j];
+                    u = f2u(s32(q.x, q.y, q.z, p.x, p.y, p.z));
+                    idx = (uint32_t)__float_as_int(p.w);
+                    cand = u <= st.bound;
+                }
+                kw_offer<true>(st, cand, u, (int)idx, lane, k);
+            }
+        }
+    }
+    if (st.cnt > 0) kw_merge(st, lane, k);
+
+    // 3. Lane n < k writes the n-th key; empty only in a cloud with fewer
+    //    than k references.
+    if (lane < k) {
+        const uint64_t e = st.list;
+        const bool empty = e == kKwEmpty;
+        const float sv = u2f((uint32_t)(e >> 32));
+        const int64_t o = (orow0 + __float_as_int(q.w)) * k + lane;
+        out_dist[o] = empty ? (squared ? 0.0f : __builtin_inff()) : squared ? sv : sqrtf(sv);
+        out_idx[o] = empty ? (int64_t)-1 : ibase + (int64_t)(uint32_t)e;
     }
 }
 
@@ -588,7 +745,7 @@ static unsigned grid_blocks(int64_t n) {
 
 hipError_t launch_grid_build(const float* query, const float* ref, int64_t B, int64_t Q,
                              int64_t P, int L, void* workspace, const uint32_t* gate,
-                             hipStream_t stream, GridView* view) {
+                             const int64_t* clouds, hipStream_t stream, GridView* view) {
     const int64_t C = (int64_t)1 << (3 * L);
     const int nblk = (int)((P + kGridBlk - 1) / kGridBlk), nsb = (nblk + kWave - 1) / kWave;
     const GridLayout g = grid_layout(B, Q, P, L);
@@ -620,10 +777,10 @@ hipError_t launch_grid_build(const float* query, const float* ref, int64_t B, in
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_bounds_kernel,
                                       dim3((unsigned)std::min<int64_t>((P + 1023) / 1024, 256),
                                            (unsigned)B),
-                                      dim3(256), 0, stream, ref, B, (int)P, L, enc, gp, gate));
+                                      dim3(256), 0, stream, ref, B, (int)P, L, enc, gp, gate, clouds));
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_count_kernel, dim3(grid_blocks(B * (P + Q))), dim3(256),
                                       0, stream, ref, query, B, (int)P, (int)Q, L, gp, rcnt, qcnt,
-                                      gate));
+                                      gate, clouds));
     const unsigned nchunk = (unsigned)((C + kScanChunk - 1) / kScanChunk);
     uint32_t* sums = (uint32_t*)(ws + g.sums);
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_chunk_sums_kernel, dim3(nchunk, (unsigned)B, 2),
@@ -633,22 +790,36 @@ hipError_t launch_grid_build(const float* query, const float* ref, int64_t B, in
                                       gate));
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_scatter_kernel, dim3(grid_blocks(B * (P + Q))),
                                       dim3(256), 0, stream, ref, query, B, (int)P, (int)Q, L, gp,
-                                      rcnt, rfill, qcnt, qfill, sref, squery, gate));
+                                      rcnt, rfill, qcnt, qfill, sref, squery, gate, clouds));
     POINTOPS_CHECK(hipLaunchKernelGGL(grid_boxes_kernel, dim3((unsigned)nsb, (unsigned)B),
                                       dim3(1024), 0, stream, sref, B, (int)P, nblk, nsb, box,
-                                      sbox, gate));
+                                      sbox, gate, clouds));
 #undef POINTOPS_CHECK
     return hipSuccess;
 }
 
 // squared != 0: out_dist holds s itself (the Chamfer distance's nearest points).
+// With `clouds` (device memory, B records; see GridCloud) P and Q are the
+// largest counts of the ragged batch.
+// nw == 0: one query per wave (knn_grid_wave_kernel, k <= 32); otherwise
+// one query per lane with nw waves per workgroup.
 hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int64_t Q, int64_t P,
                            int64_t k, float* out_dist, int64_t* out_idx, int kcap, int nw,
-                           void* workspace, int squared, hipStream_t stream) {
+                           void* workspace, int squared, const int64_t* clouds,
+                           hipStream_t stream) {
+    if (nw == 0 && (k < 1 || k > kKwBuf)) return hipErrorInvalidValue;
     GridView v;
     hipError_t e = launch_grid_build(query, ref, B, Q, P, knn_grid_level(P), workspace, nullptr,
-                                     stream, &v);
+                                     clouds, stream, &v);
     if (e != hipSuccess) return e;
+    if (nw == 0) {
+        hipLaunchKernelGGL(knn_grid_wave_kernel,
+                           dim3((unsigned)((Q + kKgwWaves - 1) / kKgwWaves), (unsigned)B),
+                           dim3(kKgwWaves * kWave), 0, stream, v.squery, v.sref, (int)Q, (int)P,
+                           (int)k, v.box, v.sbox, v.nblk, v.nsb, v.ref_start, v.gp, v.L,
+                           out_dist, out_idx, squared, clouds);
+        return hipGetLastError();
+    }
 #define POINTOPS_CHECK(x) \
     do {                   \
         x;                 \
@@ -668,7 +839,7 @@ hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int6
         POINTOPS_CHECK(hipLaunchKernelGGL((knn_grid_kernel<KC, W>), grid, dim3(W * kWave), lds, \
                                           stream, v.squery, v.sref, (int)Q, (int)P, (int)k,    \
                                           v.box, v.sbox, v.nblk, v.nsb, v.ref_start, v.gp, v.L,\
-                                          out_dist, out_idx, squared));                        \
+                                          out_dist, out_idx, squared, clouds));                \
         return hipSuccess;                                                                     \
     }
     POINTOPS_GRID_CASE(1, 2) POINTOPS_GRID_CASE(2, 2) POINTOPS_GRID_CASE(4, 2)

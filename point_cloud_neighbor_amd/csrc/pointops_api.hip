@@ -104,29 +104,33 @@ int knn_waves(int kcap, int64_t tiles, int cus) {
 }
 
 // kNN takes the grid path (sort, boxes, culled search) when the references
-// are many enough for the sort to pay: at least 8192 per cloud and 2^27
+// are many enough for the sort to pay: at least 8192 per cloud and 2^22
 // query-reference pairs in all. POINTOPS_KNN_GRID=0 / 1 forces either path.
-bool knn_use_grid(int64_t B, int64_t Q, int64_t P) {
+bool knn_use_grid_pairs(int64_t pairs, int64_t P) {
     const long env = env_long("POINTOPS_KNN_GRID", -1);
     if (env == 0 || env == 1) return env == 1 && P >= 1;
-    return P >= 8192 && B * Q * P >= ((int64_t)1 << 27);
+    return P >= 8192 && pairs >= ((int64_t)1 << 22);
 }
 
-// The grid pays once a full scan would be long enough to hide its sort and
-// launches: from 2^28 query-reference pairs for k <= 4, 2^30 for k <= 16 and
-// 2^31 for k <= 32 (uniform clouds, best full scan / grid: 8192 queries on
-// 100k references, k = 16: 0.32 / 0.43 ms; 16384 on 100k: 0.47 / 0.36 ms;
-// 16384 on 100k, k = 32: 0.53 / 0.73 ms; 32768 on 100k: 0.99 / 0.71 ms;
-// 4 clouds of 8192 queries on 16384 references, k = 1: 0.15 / 0.13 ms). Points
-// on a surface fill few cells and favour the scan further (32 clouds of 8192
-// points near a sphere, 512 queries, k = 16: 0.10 / 0.31 ms). Above k = 32
-// only the lane-per-query scan remains, and the grid pays from 32768
-// references. POINTOPS_KNN_GRID=1 forces the grid.
-bool knn_grid_pays(int64_t k, int64_t B, int64_t Q, int64_t P) {
+bool knn_use_grid(int64_t B, int64_t Q, int64_t P) { return knn_use_grid_pairs(B * Q * P, P); }
+
+// With one query per wave (k <= 32) the grid search, its sort and box build
+// included, is at least as fast as the best full scan wherever it is taken
+// (uniform clouds, grid / full scan: 256 queries on 100k references, k = 16:
+// 0.064 / 0.18 ms; 16384 on 100k, k = 32: 0.091 / 0.47 ms; 256 on 16384,
+// k = 1: 0.044 / 0.047 ms; 4096 on 16384, k = 16: 0.056 / 0.065 ms; 1024 on
+// 2^20, k = 16: 0.18 / 1.18 ms; 32 clouds of 512 queries on 8192 points near
+// a sphere, k = 32: 0.094 / 0.108 ms). Above k = 32 only the lane-per-query
+// grid kernel remains, and it pays from 32768 references. POINTOPS_KNN_GRID=1
+// forces the grid.
+bool knn_grid_pays_pairs(int64_t k, int64_t pairs, int64_t P) {
+    (void)pairs;
     if (env_long("POINTOPS_KNN_GRID", -1) == 1) return true;
-    if (k > 32) return P >= 32768;
-    const int64_t need = k <= 4 ? (int64_t)1 << 28 : k <= 16 ? (int64_t)1 << 30 : (int64_t)1 << 31;
-    return B * Q * P >= need;
+    return k <= 32 || P >= 32768;
+}
+
+bool knn_grid_pays(int64_t k, int64_t B, int64_t Q, int64_t P) {
+    return knn_grid_pays_pairs(k, B * Q * P, P);
 }
 
 // Full scans with k <= 32 take one query per wave (knn_wave.hip): its lists
@@ -165,6 +169,21 @@ int knn_grid_waves(int kcap) {
     const long env = env_long("POINTOPS_KNN_GRID_WAVES", 0);
     if (kcap == 16 && (env == 1 || env == 2 || env == 4 || env == 8)) return (int)env;
     return 2;
+}
+
+// The grid search's kernel: one query per wave (0) for k <= 32, else one
+// query per lane (knn_grid_waves). Measured (uniform clouds, build included,
+// per lane / per wave): 100k queries on 100k references, k = 16: 0.31 / 0.20
+// ms; k = 3: 0.18 / 0.15 ms; 12500 on 100k, k = 16: 0.38 / 0.08 ms; 16384 on
+// 2^20, k = 32: 1.54 / 0.21 ms; the ragged 16-cloud batch (35k queries,
+// k = 16): 0.47 / 0.17 ms. POINTOPS_KNN_GRID_WAVE=0 / 1 forces either (1 only
+// for k <= 32).
+int knn_grid_nw(int64_t k, int kcap, int64_t queries, int64_t refs) {
+    (void)queries;
+    (void)refs;
+    const long env = env_long("POINTOPS_KNN_GRID_WAVE", -1);
+    if (k > 32 || env == 0) return knn_grid_waves(kcap);
+    return 0;
 }
 
 // Ball Query: queries per wave. Fewer queries per wave until the grid is about
@@ -476,8 +495,8 @@ int pointops_knn(const float* query, const float* ref, int64_t B, int64_t Q, int
     }
     if (workspace && knn_use_grid(B, Q, P) && knn_grid_pays(k, B, Q, P)) {
         hipError_t e = pointops::launch_knn_grid(query, ref, B, Q, P, k, out_dist, out_idx, kcap,
-                                                 knn_grid_waves(kcap), workspace, 0,
-                                                 (hipStream_t)stream);
+                                                 knn_grid_nw(k, kcap, B * Q, B * P), workspace,
+                                                 0, nullptr, (hipStream_t)stream);
         if (e != hipSuccess) return hip_fail(e, "knn launch");
         return POINTOPS_OK;
     }

@@ -13,6 +13,7 @@
 
 #include "../../include/pointops.h"
 #include "api_internal.h"
+#include "grid.h"
 #include "segments.h"
 
 using namespace pointops::api;
@@ -59,6 +60,50 @@ Table search_table(const int64_t* q_off, const int64_t* q_cnt, const int64_t* r_
     std::stable_sort(order.begin(), order.end(),
                      [&](int64_t a, int64_t c) { return r_cnt[a] > r_cnt[c]; });
     return make_table(order, units, recs);
+}
+
+static size_t al256(size_t n) { return (n + 255) / 256 * 256; }
+
+// The grid's room grows with B times the largest counts; clouds of similar
+// sizes waste little of it, one large cloud among many small ones would waste
+// most (such batches keep the full scan).
+constexpr int64_t kGridPadRatio = 8;
+
+RaggedKnnGrid ragged_knn_grid(const int64_t* q_cnt, const int64_t* r_cnt, int64_t B, int64_t k) {
+    RaggedKnnGrid g;
+    int64_t pairs = 0, points = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        g.P = std::max(g.P, r_cnt[b]);
+        g.Q = std::max(g.Q, q_cnt[b]);
+        pairs += q_cnt[b] * r_cnt[b];
+        points += q_cnt[b] + r_cnt[b];
+    }
+    g.clouds = 0;
+    g.total = B > 0 ? (size_t)seg_table_words(B) * sizeof(int64_t) : 0;  // the full scan's table
+    if (B < 1 || B > kMaxGridY || g.P < 1 || g.Q < 1) return g;
+    if (!knn_use_grid_pairs(pairs, g.P) || !knn_grid_pays_pairs(k, pairs, g.P)) return g;
+    if (B * (g.P + g.Q) > kGridPadRatio * points) return g;
+    g.use = true;
+    g.grid = al256((size_t)B * kGcWords * sizeof(int64_t));
+    g.grid_bytes = al256(pointops::grid_workspace_bytes(B, g.Q, g.P, pointops::knn_grid_level(g.P)));
+    g.total = std::max(g.total, g.grid + g.grid_bytes);
+    return g;
+}
+
+int upload_grid_clouds(const int64_t* q_off, const int64_t* q_cnt, const int64_t* r_off,
+                       const int64_t* r_cnt, int64_t B, bool global_index, int64_t* dev,
+                       hipStream_t s) {
+    std::vector<int64_t> w((size_t)B * kGcWords, 0);
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t* r = w.data() + b * kGcWords;
+        r[kGcROff] = r_off[b];
+        r[kGcRCnt] = r_cnt[b];
+        r[kGcQOff] = q_off[b];
+        r[kGcQCnt] = q_cnt[b];
+        r[kGcIdxBase] = global_index ? r_off[b] : 0;
+    }
+    hipError_t e = pointops::upload_words(w.data(), (int64_t)w.size(), dev, s);
+    return e == hipSuccess ? POINTOPS_OK : hip_fail(e, "cloud record upload");
 }
 
 int upload(const Table& t, void* workspace, size_t workspace_bytes, hipStream_t s,
@@ -279,6 +324,15 @@ size_t pointops_ragged_workspace_bytes(int64_t B) {
     return B < 0 ? 0 : (size_t)seg_table_words(B) * sizeof(int64_t);
 }
 
+size_t pointops_knn_ragged_workspace_bytes(const int64_t* q_cnt, const int64_t* r_cnt, int64_t B,
+                                           int64_t k) {
+    if (B < 0 || (B > 0 && (!q_cnt || !r_cnt))) return 0;
+    for (int64_t b = 0; b < B; ++b)
+        if (q_cnt[b] < 0 || r_cnt[b] < 0 || q_cnt[b] >= kMaxPoints || r_cnt[b] >= kMaxPoints)
+            return 0;
+    return std::max(pointops_ragged_workspace_bytes(B), ragged_knn_grid(q_cnt, r_cnt, B, k).total);
+}
+
 int pointops_knn_ragged(const float* query, int64_t q_rows, const int64_t* q_off,
                         const int64_t* q_cnt, const float* ref, int64_t r_rows,
                         const int64_t* r_off, const int64_t* r_cnt, int64_t B, int64_t k,
@@ -300,12 +354,31 @@ int pointops_knn_ragged(const float* query, int64_t q_rows, const int64_t* q_off
         queries += q_cnt[b];
         if (q_cnt[b] > 0) max_refs = std::max(max_refs, r_cnt[b]);
     }
+    if (queries == 0) return POINTOPS_OK;
+    hipStream_t s = (hipStream_t)stream;
+    int kcap = 1;
+    while (kcap < k) kcap *= 2;
+    // Grid search when it pays and the workspace has its room; otherwise the
+    // full scans below.
+    const RaggedKnnGrid g = ragged_knn_grid(q_cnt, r_cnt, B, k);
+    if (g.use && workspace && workspace_bytes >= g.total) {
+        char* ws = (char*)workspace;
+        int64_t* clouds = (int64_t*)(ws + g.clouds);
+        st = upload_grid_clouds(q_off, q_cnt, r_off, r_cnt, B, global_index != 0, clouds, s);
+        if (st != POINTOPS_OK) return st;
+        int64_t refs = 0;
+        for (int64_t b = 0; b < B; ++b) refs += q_cnt[b] > 0 ? r_cnt[b] : 0;
+        hipError_t e = pointops::launch_knn_grid(query, ref, B, g.Q, g.P, k, out_dist, out_idx,
+                                                 kcap, knn_grid_nw(k, kcap, queries, refs),
+                                                 ws + g.grid, 0, clouds, s);
+        if (e != hipSuccess) return hip_fail(e, "knn launch");
+        return POINTOPS_OK;
+    }
     const KnnWavePlan wp = knn_wave_plan(k, queries, max_refs, dev->cus);
     const Table t = search_table(q_off, q_cnt, r_off, r_cnt, B, wp.nw ? wp.nw * wp.qw : 64,
                                  global_index != 0);
     if (t.units == 0) return POINTOPS_OK;
     if (t.units >= kMaxPoints) return fail(POINTOPS_UNSUPPORTED, "too many workgroups");
-    hipStream_t s = (hipStream_t)stream;
     int64_t* table = nullptr;
     st = upload(t, workspace, workspace_bytes, s, &table);
     if (st != POINTOPS_OK) return st;
@@ -315,8 +388,6 @@ int pointops_knn_ragged(const float* query, int64_t q_rows, const int64_t* q_off
         if (e != hipSuccess) return hip_fail(e, "knn launch");
         return POINTOPS_OK;
     }
-    int kcap = 1;
-    while (kcap < k) kcap *= 2;
     hipError_t e = pointops::launch_knn(query, ref, 0, 0, 0, k, out_dist, out_idx, kcap,
                                         knn_waves(kcap, t.units, dev->cus), table, t.nseg,
                                         t.units, 0, s);

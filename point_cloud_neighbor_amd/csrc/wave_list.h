@@ -1,7 +1,7 @@
 // A wave's sorted list of its 32 smallest 64-bit keys, fed with candidates
 // in batches of 32 and merged by a bitonic network of lane moves: used by the
-// one-query-per-wave kNN scan (keys (bits(s) << 32) | index) and the Ball
-// Query grid pass (keys (index << 32) | bits(s)).
+// one-query-per-wave kNN scan and grid search (keys (bits(s) << 32) | index)
+// and the Ball Query grid pass (keys (index << 32) | bits(s)).
 //
 // Lanes 0..31 hold the list, ascending. Candidates go, in ballot order, to a
 // 32-entry buffer of the query in LDS; when it fills (and at the end) lanes
@@ -133,7 +133,10 @@ __device__ __forceinline__ void kw_merge(KwQuery& st, int lane, int k) {
 
 // Appends this lane's candidate key (u << 32) | j if `cand`; merges whenever
 // the buffer fills and re-tests what did not fit against the new bound
-// (u < bound).
+// (u < bound; with INCL u <= bound, for callers that visit keys out of the
+// order of their low words, where a key with the bound's high word can still
+// enter by a smaller low word).
+template <bool INCL = false>
 __device__ __forceinline__ void kw_offer(KwQuery& st, bool cand, uint32_t u, int j, int lane,
                                          int k) {
     uint64_t m = ballot(cand);
@@ -144,7 +147,7 @@ __device__ __forceinline__ void kw_offer(KwQuery& st, bool cand, uint32_t u, int
         if (st.cnt < kKwBuf) break;
         st.cnt = kKwBuf;
         kw_merge(st, lane, k);
-        cand = cand && pos >= kKwBuf && u < st.bound;
+        cand = cand && pos >= kKwBuf && (INCL ? u <= st.bound : u < st.bound);
         m = ballot(cand);
     }
 }

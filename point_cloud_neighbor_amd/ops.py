@@ -69,6 +69,8 @@ def _load():
         lib.pointops_ball_query_backward.restype = ctypes.c_int
         lib.pointops_ragged_workspace_bytes.argtypes = [i64]
         lib.pointops_ragged_workspace_bytes.restype = ctypes.c_size_t
+        lib.pointops_knn_ragged_workspace_bytes.argtypes = [vp, vp, i64, i64]
+        lib.pointops_knn_ragged_workspace_bytes.restype = ctypes.c_size_t
         lib.pointops_knn_ragged.argtypes = [vp, i64, vp, vp, vp, i64, vp, vp, i64, i64,
                                             ctypes.c_int, vp, vp, vp, ctypes.c_size_t, vp]
         lib.pointops_knn_ragged.restype = ctypes.c_int
@@ -335,7 +337,9 @@ def _vp(a: np.ndarray):
 
 
 def _search_ragged(fn, query, q_off, q_cnt, ref, r_off, r_cnt, width, extra, global_index,
-                   pad_dist, out=None):
+                   pad_dist, out=None, grid_k=None):
+    """grid_k: a kNN call's k, whose workspace then has the grid search's room
+    when that search pays (pointops_knn_ragged_workspace_bytes)."""
     lib = _load()
     query = _flat_points(query, "query")
     ref = _flat_points(ref, "ref")
@@ -353,8 +357,13 @@ def _search_ragged(fn, query, q_off, q_cnt, ref, r_off, r_cnt, width, extra, glo
             idx = torch.full((rows, width), -1, dtype=torch.int64, device=query.device)
         else:
             dist, idx = out
-        ws = torch.empty(max(1, int(lib.pointops_ragged_workspace_bytes(B))), dtype=torch.uint8,
-                         device=query.device)
+        if grid_k is None:
+            need = int(lib.pointops_ragged_workspace_bytes(B))
+        else:
+            need = int(lib.pointops_knn_ragged_workspace_bytes(_vp(q_cnt), _vp(r_cnt), B, grid_k))
+            if need == 0:
+                raise PointopsError(1, "invalid segment counts")
+        ws = torch.empty(max(1, need), dtype=torch.uint8, device=query.device)
         rc = fn(query.data_ptr(), rows, _vp(q_off), _vp(q_cnt), ref.data_ptr(), ref.shape[0],
                 _vp(r_off), _vp(r_cnt), B, *extra, int(bool(global_index)), dist.data_ptr(),
                 idx.data_ptr(), ws.data_ptr(), ws.numel(), _stream(query.device))
@@ -363,15 +372,27 @@ def _search_ragged(fn, query, q_off, q_cnt, ref, r_off, r_cnt, width, extra, glo
 
 
 def knn_ragged(query: torch.Tensor, q_ptr, ref: torch.Tensor, r_ptr, k: int,
-               global_index: bool = True):
+               global_index: bool = True, grid: bool = True):
     """kNN within each cloud of a flat batch: cloud b has query rows
     q_ptr[b]..q_ptr[b+1] and reference rows r_ptr[b]..r_ptr[b+1] ->
     (dist, idx), (query rows, k). Indices are reference rows (or local indices);
-    slots a cloud with fewer than k references cannot fill hold (+inf, -1)."""
+    slots a cloud with fewer than k references cannot fill hold (+inf, -1).
+    grid=False withholds the grid search's workspace (full scans only)."""
     q_off, q_cnt = _ptr_segments(q_ptr, "q_ptr")
     r_off, r_cnt = _ptr_segments(r_ptr, "r_ptr")
     return _search_ragged(_load().pointops_knn_ragged, query, q_off, q_cnt, ref, r_off, r_cnt,
-                          int(k), (int(k),), global_index, float("inf"))
+                          int(k), (int(k),), global_index, float("inf"),
+                          grid_k=int(k) if grid else None)
+
+
+def knn_ragged_uses_grid(q_cnt, r_cnt, k: int) -> bool:
+    """True when pointops_knn_ragged takes the grid search for these counts
+    (given the workspace pointops_knn_ragged_workspace_bytes asks for)."""
+    lib = _load()
+    q_cnt, r_cnt = _host_i64(q_cnt, "q_cnt"), _host_i64(r_cnt, "r_cnt")
+    B = len(q_cnt)
+    return int(lib.pointops_knn_ragged_workspace_bytes(_vp(q_cnt), _vp(r_cnt), B, int(k))) > \
+        int(lib.pointops_ragged_workspace_bytes(B))
 
 
 def ball_query_ragged(query: torch.Tensor, q_ptr, ref: torch.Tensor, r_ptr, radius: float,
@@ -467,7 +488,7 @@ def knn_padded(query: torch.Tensor, ref: torch.Tensor, k: int, lengths1=None, le
     d, i = _search_ragged(_load().pointops_knn_ragged, query.view(-1, 3),
                           np.arange(B, dtype=np.int64) * Qm, l1, ref.view(-1, 3),
                           np.arange(B, dtype=np.int64) * Pm, l2, int(k), (int(k),), False,
-                          float("inf"))
+                          float("inf"), grid_k=int(k))
     return d.view(B, Qm, k), i.view(B, Qm, k)
 
 

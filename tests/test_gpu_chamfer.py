@@ -162,16 +162,25 @@ def test_chamfer_invalid_arguments(gpu):
 
 
 @pytest.mark.parametrize("case", ["uniform", "integer"])
-def test_chamfer_and_three_nn_grid_search_forced(gpu, oracle_mod, case, monkeypatch):
+@pytest.mark.parametrize("lengths", [False, True])
+@pytest.mark.parametrize("per_wave", ["0", "1"])
+def test_chamfer_and_three_nn_grid_search_forced(gpu, oracle_mod, case, lengths, per_wave,
+                                                 monkeypatch):
     """The nearest points of the Chamfer distance and three_nn through the
-    kNN grid search (forced on at small sizes), against the oracle."""
+    kNN grid search (forced on at small sizes, one query per lane or per
+    wave), dense and with lengths (a cloud without y points among them),
+    against the oracle."""
     monkeypatch.setenv("POINTOPS_KNN_GRID", "1")
+    monkeypatch.setenv("POINTOPS_KNN_GRID_WAVE", per_wave)
     if case == "uniform":
         x, y = W.uniform_cube(21, 2, 700), W.uniform_cube(22, 2, 1300)
+        xl, yl = ([700, 9], [1000, 0]) if lengths else (None, None)
     else:
         x, y = W.integer_cloud(23, 2, 900, 0, 5), W.integer_cloud(24, 2, 600, 0, 5)
+        xl, yl = ([300, 900], [600, 17]) if lengths else (None, None)
     for single in (False, True):
-        check_chamfer(gpu, oracle_mod, x, y, single=single, what=f"grid {case}")
+        check_chamfer(gpu, oracle_mod, x, y, xl, yl, single=single,
+                      what=f"grid {case} lengths={lengths}")
     d, i = gpu.three_nn(dev(x), dev(y))
     wd, wi = oracle_mod.three_nn(x, y, threads=8)
     assert_idx_equal(host(i), wi, "three_nn grid idx")

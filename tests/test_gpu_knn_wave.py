@@ -109,14 +109,20 @@ def test_ragged(gpu, oracle_mod, wave, sizes, k):
 
 def test_search_choice(gpu):
     """pointops_knn_search reports the library's choice; the cases follow
-    the measured rule (grid for long scans, the wave scan for k <= 32 with
-    few queries, the lane scan for small k with many queries on small
-    clouds), and a shape pointops_knn rejects is an error."""
+    the measured rule (the grid from 8192 references per cloud and 2^22 pairs,
+    for k > 32 from 32768 references; without it the wave scan for k <= 32,
+    the lane scan for small k with many queries on small clouds), and a shape
+    pointops_knn rejects is an error."""
     from point_cloud_neighbor_amd import ops
     assert ops.knn_search(1, 100000, 100000, 16) == "grid"
     assert ops.knn_search(1, 100000, 100000, 16, grid=False) == "full scan, queries per wave"
-    assert ops.knn_search(32, 512, 8192, 32) == "full scan, queries per wave"
-    assert ops.knn_search(1, 1024, 100000, 16) == "full scan, queries per wave"
+    assert ops.knn_search(32, 512, 8192, 32) == "grid"
+    assert ops.knn_search(32, 512, 8192, 32, grid=False) == "full scan, queries per wave"
+    assert ops.knn_search(1, 1024, 100000, 16) == "grid"
+    assert ops.knn_search(1, 1024, 100000, 16, grid=False) == "full scan, queries per wave"
+    assert ops.knn_search(1, 64, 8192, 16) == "full scan, queries per wave"  # < 2^22 pairs
+    assert ops.knn_search(1, 1024, 100000, 33) == "grid"
+    assert ops.knn_search(1, 1024, 20000, 33) == "full scan, one query per lane"
     assert ops.knn_search(16, 8192, 2048, 3) == "full scan, one query per lane"
     assert ops.knn_search(1, 100, 1000, 33) == "full scan, one query per lane"
     with pytest.raises(gpu.PointopsError):

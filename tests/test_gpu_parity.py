@@ -28,21 +28,26 @@ def check_fps(gpu, oracle_mod, xyz, M, start=0, what=""):
 
 
 def check_knn(gpu, oracle_mod, q, x, k, what=""):
-    """Both searches: the full scan and the grid search (forced on, whatever
-    the size)."""
+    """Every search: the full scan and the grid search (forced on, whatever
+    the size), the latter with one query per lane and, for k <= 32, one per
+    wave."""
     wd, wi = oracle_mod.knn(q, x, k, threads=8)
-    for grid in (False, True):
-        old = os.environ.get("POINTOPS_KNN_GRID")
-        os.environ["POINTOPS_KNN_GRID"] = "1" if grid else "0"
+    runs = [("0", "0"), ("1", "0")] + ([("1", "1")] if k <= 32 else [])
+    for grid, per_wave in runs:
+        old = {n: os.environ.get(n) for n in ("POINTOPS_KNN_GRID", "POINTOPS_KNN_GRID_WAVE")}
+        os.environ["POINTOPS_KNN_GRID"] = grid
+        os.environ["POINTOPS_KNN_GRID_WAVE"] = per_wave
         try:
             d, i = gpu.knn(dev(q), dev(x), k)
         finally:
-            if old is None:
-                del os.environ["POINTOPS_KNN_GRID"]
-            else:
-                os.environ["POINTOPS_KNN_GRID"] = old
-        assert_idx_equal(host(i), wi, f"knn idx {what} grid={grid}")
-        assert_dist_close(host(d), wd, f"knn dist {what} grid={grid}")
+            for n, v in old.items():
+                if v is None:
+                    del os.environ[n]
+                else:
+                    os.environ[n] = v
+        how = f"grid={grid} per_wave={per_wave}"
+        assert_idx_equal(host(i), wi, f"knn idx {what} {how}")
+        assert_dist_close(host(d), wd, f"knn dist {what} {how}")
 
 
 def check_bq(gpu, oracle_mod, q, x, r, K, what=""):
