@@ -251,6 +251,24 @@ size_t pointops_knn_ragged_workspace_bytes(const int64_t *q_cnt, const int64_t *
                                            int64_t k);
 
 /*
+ * Workspace bytes with which pointops_ball_query_ragged takes its culled
+ * search for clouds with these counts (host arrays of B entries) and this K:
+ * an index-order scan that stops each query at K hits or at a budget of
+ * references (or early, when the query's hit rate is too low to reach K
+ * within it), then, only if a query was left, a uniform grid of each cloud
+ * and the dense Ball Query's grid pass for the hits from where the scan
+ * stopped (project page "mps-pointops", roadmap: spatial structures for large
+ * clouds). The first-K result does not change. It is
+ * pointops_ragged_workspace_bytes(B) when the plain scan is taken (K > 32,
+ * clouds below 8192 references, or padding to the largest cloud above eight
+ * times the points' own room), about 16 * B * (max q_cnt + max r_cnt) bytes
+ * plus the grid's cell counts otherwise. With a smaller workspace
+ * pointops_ball_query_ragged takes the plain scan. 0 for invalid counts.
+ */
+size_t pointops_ball_query_ragged_workspace_bytes(const int64_t *q_cnt, const int64_t *r_cnt,
+                                                  int64_t B, int64_t K);
+
+/*
  * kNN of ragged batches. For each cloud b, the queries are rows q_off[b] ..
  * of `query` and the references rows r_off[b] .. of `ref`; output row r of
  * out_dist / out_idx ((q_rows, k), device) belongs to query row r. Where a

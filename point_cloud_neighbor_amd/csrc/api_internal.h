@@ -9,11 +9,13 @@
 #include <array>
 #include <vector>
 
+#include "segments.h"
+
 namespace pointops {
 
 hipError_t launch_ball_query(const float*, const float*, int64_t, int64_t, int64_t, float,
                              int64_t, float*, int64_t*, int, const int64_t*, int, int64_t,
-                             hipStream_t);
+                             hipStream_t, BqBudget = BqBudget{nullptr, nullptr, 0, 0, 0});
 hipError_t launch_ball_query_culled(const float*, const float*, int64_t, int64_t, int64_t,
                                     float, int64_t, float*, int64_t*, int, float*, int, uint2*,
                                     uint32_t*, hipStream_t);
@@ -22,6 +24,10 @@ hipError_t launch_ball_query_grid(const float*, const float*, int64_t, int64_t, 
                                   int64_t, float*, int64_t*, int, int, int, void*, hipStream_t);
 int knn_grid_level(int64_t P);
 size_t ball_query_grid_bytes(int64_t B, int64_t Q, int64_t P);
+size_t ball_query_ragged_grid_bytes(int64_t B, int64_t Q, int64_t P, int level);
+hipError_t launch_ball_query_ragged_grid(const float*, const float*, int64_t, int64_t, int64_t,
+                                         float, int64_t, float*, int64_t*, int, const int64_t*,
+                                         uint32_t*, uint2*, void*, hipStream_t);
 hipError_t launch_knn_grid(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
                            int64_t*, int, int, void*, int, const int64_t*, hipStream_t);
 size_t knn_grid_workspace_bytes(int64_t B, int64_t Q, int64_t P);
@@ -109,8 +115,27 @@ struct RaggedKnnGrid {
     size_t grid_bytes = 0;  // the grid's own room (at `grid`)
 };
 RaggedKnnGrid ragged_knn_grid(const int64_t* q_cnt, const int64_t* r_cnt, int64_t B, int64_t k);
+// Ball Query of a ragged batch through the index-order scan with a budget and
+// the grid pass: the scan's cloud table at 0, the grid's records and then the
+// flag word at `clouds`, the per-query state (B x Q) at `state` and the grid
+// of 2^level cells per axis at `grid`; `use` for K <= 32 and clouds of 8192
+// references or more (POINTOPS_BQ_GRID=0 / 1 forbids or allows it at any
+// size), with the same padding limit as the kNN grid.
+struct RaggedBqGrid {
+    bool use = false;
+    int64_t P = 0, Q = 0;
+    int level = 2;
+    size_t clouds = 0, state = 0, grid = 0, total = 0;
+};
+RaggedBqGrid ragged_bq_grid(const int64_t* q_cnt, const int64_t* r_cnt, int64_t B, int64_t K);
+// The ragged scan's probe (references after which a query whose hit rate
+// would need more than the budget leaves for the grid) and budget, both
+// multiples of 64 (POINTOPS_BQ_PROBE, POINTOPS_BQ_RAGGED_BUDGET override).
+int bq_ragged_probe();
+int bq_ragged_budget();
 // Writes the records of the clouds (q_off[b], q_cnt[b], r_off[b], r_cnt[b],
-// index base) to `dev` on `stream`.
+// index base) to `dev` on `stream`, then one zero word (a flag for the
+// kernels that follow).
 int upload_grid_clouds(const int64_t* q_off, const int64_t* q_cnt, const int64_t* r_off,
                        const int64_t* r_cnt, int64_t B, bool global_index, int64_t* dev,
                        hipStream_t s);

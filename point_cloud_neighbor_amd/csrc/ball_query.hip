@@ -18,18 +18,28 @@
 //
 // Ragged batches (a cloud table, see segments.h): waves are numbered cloud
 // after cloud, QW queries each, and scan their own cloud's references.
+//
+// Budgeted scan (BqBudget with a state array; the ragged batches' first step
+// before the grid pass of ball_query_grid.hip): a query also stops after
+// `budget` references, or after the first `probe` when its hit count is too
+// low to reach K within the budget at that rate. Its first hits are then in
+// place (they are the first ones: every later index is larger), the rest of
+// its row is padding, and it records (hits, references examined) for the
+// grid pass, or done; a query left raises the flag.
 #include "common.h"
 #include "segments.h"
 
 namespace pointops {
 
+constexpr uint32_t kBqDone = 0xFFFFFFFFu;  // state: the query is complete
+
 template <int QW>
 __global__ __launch_bounds__(kWave) void ball_query_kernel(
     const float* __restrict__ query, const float* __restrict__ ref, int Q, int P, float r2,
     int K, float* __restrict__ out_d2, int64_t* __restrict__ out_idx,
-    const int64_t* __restrict__ seg, int nseg) {
+    const int64_t* __restrict__ seg, int nseg, BqBudget bud) {
     // this wave's cloud: its first query row, reference row, sizes
-    int64_t qrow0, rrow0, ibase, unit;
+    int64_t qrow0, rrow0, ibase, unit, cloud;
     if (seg) {
         const int b = seg_find(seg, nseg, blockIdx.x);
         const int64_t* rec = seg_record(seg, nseg, b);
@@ -39,12 +49,15 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
         rrow0 = rec[kSrROff];
         P = (int)rec[kSrRCnt];
         ibase = rec[kSrIdxBase];
+        cloud = rec[kSrCloud];
     } else {
         unit = blockIdx.x;
         qrow0 = (int64_t)blockIdx.y * Q;
         rrow0 = (int64_t)blockIdx.y * P;
         ibase = 0;
+        cloud = blockIdx.y;
     }
+    const int n = bud.state ? min(P, bud.budget) : P;  // references this wave may scan
     const int row0 = (int)unit * QW;
     const int lane = threadIdx.x;
     const float* qb = query + qrow0 * 3;
@@ -53,6 +66,7 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
 
     float qx[QW], qy[QW], qz[QW];
     int cnt[QW];
+    bool stopped[QW];  // left at the probe (budgeted scan)
 #pragma unroll
     for (int i = 0; i < QW; ++i) {
         const int row = row0 + i < Q ? row0 + i : Q - 1;
@@ -60,6 +74,7 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
         qy[i] = qb[(size_t)3 * row + 1];
         qz[i] = qb[(size_t)3 * row + 2];
         cnt[i] = row0 + i < Q ? 0 : K;  // rows past the end take no hits
+        stopped[i] = false;
     }
 
     // Software-pipelined reference loads: block n+1 is in flight while block n
@@ -67,25 +82,26 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
     // distance compares false against R2, so no separate range test is needed.
     const float nan = __builtin_nanf("");
     float nx = nan, ny = nan, nz = nan;
-    if (lane < P) {
+    if (lane < n) {
         nx = xb[(size_t)3 * lane + 0];
         ny = xb[(size_t)3 * lane + 1];
         nz = xb[(size_t)3 * lane + 2];
     }
-    for (int base = 0; base < P; base += kWave) {
+    for (int base = 0; base < n; base += kWave) {
         const int j = base + lane;
         const float x = nx, y = ny, z = nz;
         const int jn = j + kWave;
         nx = ny = nz = nan;
-        if (jn < P) {
+        if (jn < n) {
             nx = xb[(size_t)3 * jn + 0];
             ny = xb[(size_t)3 * jn + 1];
             nz = xb[(size_t)3 * jn + 2];
         }
+        const bool at_probe = bud.state && base + kWave == bud.probe;
         bool live = false;
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
-            if (cnt[i] < K) {
+            if (cnt[i] < K && !stopped[i]) {
                 const float s = s32(qx[i], qy[i], qz[i], x, y, z);
                 const uint64_t m = ballot(s < r2);
                 if (m) {
@@ -96,7 +112,11 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
                     }
                     cnt[i] += __popcll(m);
                 }
-                live |= cnt[i] < K;
+                // at this rate K hits would take more than the budget
+                if (at_probe && cnt[i] < K &&
+                    (int64_t)cnt[i] * bud.budget < (int64_t)K * bud.probe)
+                    stopped[i] = true;
+                live |= cnt[i] < K && !stopped[i];
             }
         }
         if (!live) break;
@@ -112,6 +132,25 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
             }
         }
     }
+    if (bud.state && lane == 0) {
+        // a query that neither has K hits nor stopped scanned all n references
+        bool left = false;
+#pragma unroll
+        for (int i = 0; i < QW; ++i) {
+            if (row0 + i < Q) {
+                const int seen = stopped[i] ? bud.probe : n;
+                const bool done = cnt[i] >= K || seen >= P;
+                bud.state[(size_t)cloud * bud.stride + row0 + i] =
+                    done ? make_uint2(0u, kBqDone) : make_uint2((uint32_t)cnt[i], (uint32_t)seen);
+                left |= !done;
+            }
+        }
+        // only the waves that still see the flag clear raise it (one atomic
+        // per wave on one word would serialise at its L2 channel)
+        if (left &&
+            __hip_atomic_load(bud.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u)
+            atomicOr(bud.flag, 1u);
+    }
 }
 
 // Launch helper used by the C ABI: grid (ceil(Q / QW), B), one wave per group;
@@ -120,7 +159,7 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
 hipError_t launch_ball_query(const float* query, const float* ref, int64_t B, int64_t Q,
                              int64_t P, float r2, int64_t K, float* out_d2, int64_t* out_idx,
                              int qw, const int64_t* seg, int nseg, int64_t waves,
-                             hipStream_t stream) {
+                             hipStream_t stream, BqBudget bud) {
     dim3 block(kWave);
     switch (qw) {
 #define POINTOPS_BQ_CASE(W)                                                                  \
@@ -128,7 +167,7 @@ hipError_t launch_ball_query(const float* query, const float* ref, int64_t B, in
         dim3 grid = seg ? dim3((unsigned)waves, 1)                                           \
                         : dim3((unsigned)((Q + W - 1) / W), (unsigned)B);                    \
         hipLaunchKernelGGL(ball_query_kernel<W>, grid, block, 0, stream, query, ref, (int)Q, \
-                           (int)P, r2, (int)K, out_d2, out_idx, seg, nseg);                  \
+                           (int)P, r2, (int)K, out_d2, out_idx, seg, nseg, bud);             \
         break;                                                                               \
     }
         POINTOPS_BQ_CASE(1)
@@ -216,7 +255,6 @@ __global__ __launch_bounds__(256) void ball_query_boxes_kernel(const float* __re
 // sets *flag; every other query records (count, kBqDone). The grid pass then
 // looks only at references from that index on, so the hits it adds come
 // after these in index order.
-constexpr uint32_t kBqDone = 0xFFFFFFFFu;
 
 // One wave per 64 blocks: their union box, sbox[(b * nsb + s) * 8 + 0..5].
 __global__ __launch_bounds__(256) void ball_query_superboxes_kernel(const float* __restrict__ box,
@@ -393,7 +431,10 @@ __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
             }
         }
     }
-    if (left) atomicOr(flag, 1u);  // lane 0 only
+    // lane 0 only; only the waves that still see the flag clear raise it (one
+    // atomic per wave on one word would serialise at its L2 channel)
+    if (left && __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u)
+        atomicOr(flag, 1u);
 }
 
 // Boxes of the 64-reference blocks, then of every 64 blocks.

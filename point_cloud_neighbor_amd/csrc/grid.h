@@ -5,8 +5,9 @@
 // Build (knn_grid.hip): per cloud, the references' bounding box, a uniform grid
 // of 2^L cells per axis over it, counting-sorted copies (x, y, z, original
 // index) of references and queries in Morton order of their cells, a box for
-// every kGridBlk consecutive sorted references and one for every 64 blocks. The
-// cell formula only decides the order: no result depends on it.
+// every kGridBlk consecutive sorted references and one for every 64 blocks
+// (each with the range of its references' original indices). The cell formula
+// only decides the order: no result depends on it.
 #pragma once
 
 #include "common.h"
@@ -96,7 +97,8 @@ struct GridView {
     uint32_t* ref_start; // per cloud and cell: first sorted reference
     float4* sref;        // (B, P) sorted references (x, y, z, original index bits)
     float4* squery;      // (B, Q) sorted queries
-    float* box;          // (B, nblk) x 8: min x, y, z, max x, y, z of each block
+    float* box;          // (B, nblk) x 8: min x, y, z, max x, y, z of each block, then
+                         // its smallest and largest original index (int32 bits)
     float* sbox;         // (B, nsb) x 8: the same for every 64 blocks
     int L, nblk, nsb;
 };

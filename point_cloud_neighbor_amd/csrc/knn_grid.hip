@@ -272,7 +272,10 @@ __global__ void grid_scatter_kernel(const float* __restrict__ ref, const float* 
 
 // One 1024-thread workgroup per superblock (64 blocks of 16 sorted
 // references): every block's box, box[(b * nblk + k) * 8 + 0..5], then the
-// superblock's, sbox[(b * nsb + s) * 8 + 0..5].
+// superblock's, sbox[(b * nsb + s) * 8 + 0..5]. Words 6 and 7 of each hold
+// the smallest and largest original index of its references (int32 bits;
+// 0x7FFFFFFF and -1 for an empty box), which Ball Query's grid pass tests
+// against its index window.
 __global__ __launch_bounds__(1024) void grid_boxes_kernel(const float4* __restrict__ sr,
                                                           int64_t B, int P, int nblk, int nsb,
                                                           float* __restrict__ box,
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(1024) void grid_boxes_kernel(const float4* __restri
                                                           const uint32_t* __restrict__ gate,
                                                           const int64_t* __restrict__ clouds) {
     if (gate && *gate == 0) return;  // the grid is not needed
-    __shared__ float sh[kWave][6];
+    __shared__ float sh[kWave][8];
     const int64_t b = blockIdx.y;
     const int Pb = clouds ? (int)clouds[kGcWords * b + kGcRCnt] : P;  // real points of this cloud
     const int sb = blockIdx.x;
@@ -289,43 +292,50 @@ __global__ __launch_bounds__(1024) void grid_boxes_kernel(const float4* __restri
     const int k = sb * kWave + t / kGridBlk;  // this thread's block
     const float inf = __builtin_inff();
     float v[6] = {inf, inf, inf, -inf, -inf, -inf};
+    int ilo = 0x7FFFFFFF, ihi = -1;
     if (j < Pb) {
         const float4 p = sr[b * P + j];
         v[0] = v[3] = p.x;
         v[1] = v[4] = p.y;
         v[2] = v[5] = p.z;
+        ilo = ihi = __float_as_int(p.w);
     }
-#pragma unroll
-    for (int o = kGridBlk / 2; o >= 1; o /= 2)
+    auto fold = [&](int o) {
 #pragma unroll
         for (int d = 0; d < 3; ++d) {
             v[d] = fminf(v[d], __shfl_xor(v[d], o));
             v[3 + d] = fmaxf(v[3 + d], __shfl_xor(v[3 + d], o));
         }
+        ilo = min(ilo, __shfl_xor(ilo, o));
+        ihi = max(ihi, __shfl_xor(ihi, o));
+    };
+#pragma unroll
+    for (int o = kGridBlk / 2; o >= 1; o /= 2) fold(o);
     if (t % kGridBlk == 0) {
 #pragma unroll
         for (int d = 0; d < 6; ++d) sh[t / kGridBlk][d] = v[d];
+        sh[t / kGridBlk][6] = __int_as_float(ilo);
+        sh[t / kGridBlk][7] = __int_as_float(ihi);
         if (k < nblk) {
             float* o = box + ((size_t)b * nblk + k) * 8;
 #pragma unroll
-            for (int d = 0; d < 6; ++d) o[d] = v[d];
+            for (int d = 0; d < 8; ++d) o[d] = sh[t / kGridBlk][d];
         }
     }
     __syncthreads();
     if (t < kWave) {
 #pragma unroll
         for (int d = 0; d < 6; ++d) v[d] = sh[t][d];  // empty boxes past the end
+        ilo = __float_as_int(sh[t][6]);
+        ihi = __float_as_int(sh[t][7]);
 #pragma unroll
-        for (int o = kWave / 2; o >= 1; o /= 2)
-#pragma unroll
-            for (int d = 0; d < 3; ++d) {
-                v[d] = fminf(v[d], __shfl_xor(v[d], o));
-                v[3 + d] = fmaxf(v[3 + d], __shfl_xor(v[3 + d], o));
-            }
+        for (int o = kWave / 2; o >= 1; o /= 2) fold(o);
         if (t == 0) {
             float* o = sbox + ((size_t)b * nsb + sb) * 8;
 #pragma unroll
             for (int d = 0; d < 6; ++d) o[d] = v[d];
+            o[6] = __int_as_float(ilo);
+            o[7] = __int_as_float(ihi);
         }
     }
 }

@@ -54,7 +54,7 @@ Table search_table(const int64_t* q_off, const int64_t* q_cnt, const int64_t* r_
     for (int64_t b = 0; b < B; ++b) {
         units[(size_t)b] = (q_cnt[b] + per_unit - 1) / per_unit;
         recs[(size_t)b] = {q_off[b], q_cnt[b], r_off[b], r_cnt[b], global_index ? r_off[b] : 0,
-                           0, 0, 0};
+                           b, 0, 0};
         if (units[(size_t)b] > 0) order.push_back(b);
     }
     std::stable_sort(order.begin(), order.end(),
@@ -84,16 +84,50 @@ RaggedKnnGrid ragged_knn_grid(const int64_t* q_cnt, const int64_t* r_cnt, int64_
     if (!knn_use_grid_pairs(pairs, g.P) || !knn_grid_pays_pairs(k, pairs, g.P)) return g;
     if (B * (g.P + g.Q) > kGridPadRatio * points) return g;
     g.use = true;
-    g.grid = al256((size_t)B * kGcWords * sizeof(int64_t));
+    g.grid = al256(((size_t)B * kGcWords + 1) * sizeof(int64_t));  // records, flag word
     g.grid_bytes = al256(pointops::grid_workspace_bytes(B, g.Q, g.P, pointops::knn_grid_level(g.P)));
     g.total = std::max(g.total, g.grid + g.grid_bytes);
+    return g;
+}
+
+static int round64(long v) { return (int)((v + 63) / 64 * 64); }
+
+int bq_ragged_probe() {
+    const long env = env_long("POINTOPS_BQ_PROBE", 0);
+    return env > 0 && env < (1L << 24) ? round64(env) : 256;
+}
+
+int bq_ragged_budget() {
+    const long env = env_long("POINTOPS_BQ_RAGGED_BUDGET", 0);
+    return env > 0 && env < (1L << 24) ? round64(env) : 2048;
+}
+
+RaggedBqGrid ragged_bq_grid(const int64_t* q_cnt, const int64_t* r_cnt, int64_t B, int64_t K) {
+    RaggedBqGrid g;
+    int64_t points = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        g.P = std::max(g.P, r_cnt[b]);
+        g.Q = std::max(g.Q, q_cnt[b]);
+        points += q_cnt[b] + r_cnt[b];
+    }
+    g.total = B > 0 ? (size_t)seg_table_words(B) * sizeof(int64_t) : 0;  // the scan's table
+    if (K < 1 || K > 32 || B < 1 || B > kMaxGridY || g.P < 1 || g.Q < 1) return g;
+    const long env = env_long("POINTOPS_BQ_GRID", -1);
+    if (env == 0 || (env != 1 && g.P < 8192)) return g;
+    if (B * (g.P + g.Q) > kGridPadRatio * points) return g;
+    g.use = true;
+    g.level = bq_grid_level(g.P);
+    g.clouds = al256((size_t)seg_table_words(B) * sizeof(int64_t));     // the scan's table
+    g.state = g.clouds + al256(((size_t)B * kGcWords + 1) * sizeof(int64_t));  // records, flag
+    g.grid = g.state + al256((size_t)B * g.Q * sizeof(uint2));
+    g.total = g.grid + al256(pointops::ball_query_ragged_grid_bytes(B, g.Q, g.P, g.level));
     return g;
 }
 
 int upload_grid_clouds(const int64_t* q_off, const int64_t* q_cnt, const int64_t* r_off,
                        const int64_t* r_cnt, int64_t B, bool global_index, int64_t* dev,
                        hipStream_t s) {
-    std::vector<int64_t> w((size_t)B * kGcWords, 0);
+    std::vector<int64_t> w((size_t)B * kGcWords + 1, 0);  // the last word: the flag
     for (int64_t b = 0; b < B; ++b) {
         int64_t* r = w.data() + b * kGcWords;
         r[kGcROff] = r_off[b];
@@ -324,6 +358,15 @@ size_t pointops_ragged_workspace_bytes(int64_t B) {
     return B < 0 ? 0 : (size_t)seg_table_words(B) * sizeof(int64_t);
 }
 
+size_t pointops_ball_query_ragged_workspace_bytes(const int64_t* q_cnt, const int64_t* r_cnt,
+                                                  int64_t B, int64_t K) {
+    if (B < 0 || (B > 0 && (!q_cnt || !r_cnt))) return 0;
+    for (int64_t b = 0; b < B; ++b)
+        if (q_cnt[b] < 0 || r_cnt[b] < 0 || q_cnt[b] >= kMaxPoints || r_cnt[b] >= kMaxPoints)
+            return 0;
+    return std::max(pointops_ragged_workspace_bytes(B), ragged_bq_grid(q_cnt, r_cnt, B, K).total);
+}
+
 size_t pointops_knn_ragged_workspace_bytes(const int64_t* q_cnt, const int64_t* r_cnt, int64_t B,
                                            int64_t k) {
     if (B < 0 || (B > 0 && (!q_cnt || !r_cnt))) return 0;
@@ -414,6 +457,11 @@ int pointops_ball_query_ragged(const float* query, int64_t q_rows, const int64_t
     if (st != POINTOPS_OK) return st;
     int64_t rows = 0;
     for (int64_t b = 0; b < B; ++b) rows += q_cnt[b];
+    if (rows == 0) return POINTOPS_OK;
+    hipStream_t s = (hipStream_t)stream;
+    // R2 = fl32(r32 * r32), as for dense batches.
+    volatile float r32 = radius;
+    const float r2 = r32 * r32;
     // At most 2 queries per wave: clouds differ in size and queries stop at K
     // at different points, so short waves balance better (measured on ragged
     // batches of 35k queries: 0.26 ms with 1 or 2, 0.37 ms with 8).
@@ -421,13 +469,30 @@ int pointops_ball_query_ragged(const float* query, int64_t q_rows, const int64_t
     const Table t = search_table(q_off, q_cnt, r_off, r_cnt, B, qw, global_index != 0);
     if (t.units == 0) return POINTOPS_OK;
     if (t.units >= kMaxPoints) return fail(POINTOPS_UNSUPPORTED, "too many waves");
-    hipStream_t s = (hipStream_t)stream;
     int64_t* table = nullptr;
     st = upload(t, workspace, workspace_bytes, s, &table);
     if (st != POINTOPS_OK) return st;
-    // R2 = fl32(r32 * r32), as for dense batches.
-    volatile float r32 = radius;
-    const float r2 = r32 * r32;
+    // With the grid's room: the scan in its budgeted mode, then (gated on the
+    // device by the flag) the grid build and the grid pass.
+    const RaggedBqGrid g = ragged_bq_grid(q_cnt, r_cnt, B, K);
+    if (g.use && workspace_bytes >= g.total) {
+        char* ws = (char*)workspace;
+        int64_t* clouds = (int64_t*)(ws + g.clouds);
+        uint32_t* flag = (uint32_t*)(clouds + B * pointops::kGcWords);
+        uint2* state = (uint2*)(ws + g.state);
+        st = upload_grid_clouds(q_off, q_cnt, r_off, r_cnt, B, global_index != 0, clouds, s);
+        if (st != POINTOPS_OK) return st;
+        const pointops::BqBudget bud{state, flag, bq_ragged_probe(), bq_ragged_budget(),
+                                     (int)g.Q};
+        hipError_t e = pointops::launch_ball_query(query, ref, 0, 0, 0, r2, K, out_dist2,
+                                                   out_idx, qw, table, t.nseg, t.units, s, bud);
+        if (e != hipSuccess) return hip_fail(e, "ball_query launch");
+        e = pointops::launch_ball_query_ragged_grid(query, ref, B, g.Q, g.P, r2, K, out_dist2,
+                                                    out_idx, g.level, clouds, flag, state,
+                                                    ws + g.grid, s);
+        if (e != hipSuccess) return hip_fail(e, "ball_query launch");
+        return POINTOPS_OK;
+    }
     hipError_t e = pointops::launch_ball_query(query, ref, 0, 0, 0, r2, K, out_dist2, out_idx,
                                                qw, table, t.nseg, t.units, s);
     if (e != hipSuccess) return hip_fail(e, "ball_query launch");

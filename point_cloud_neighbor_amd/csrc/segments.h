@@ -21,11 +21,22 @@ namespace pointops {
 
 constexpr int kSegRecWords = 8;
 
-// Record of a kNN / Ball Query cloud.
-enum SearchRec { kSrQOff = 0, kSrQCnt, kSrROff, kSrRCnt, kSrIdxBase };
+// Record of a kNN / Ball Query cloud (kSrCloud: its index in the caller's
+// arrays, since the table orders the clouds by size).
+enum SearchRec { kSrQOff = 0, kSrQCnt, kSrROff, kSrRCnt, kSrIdxBase, kSrCloud };
 // Record of an FPS cloud: points, outputs, local start index, first exchange
 // word, candidates published per workgroup.
 enum FpsRec { kFrXOff = 0, kFrXCnt, kFrOOff, kFrOCnt, kFrIdxBase, kFrStart, kFrWOff, kFrRG };
+
+// The budgeted mode of the Ball Query scan (ball_query.hip): with `state`
+// non-null a query also stops after `budget` references, or after `probe`
+// when its hits come too slowly, and records its state at
+// state[cloud * stride + row]; a query left raises *flag.
+struct BqBudget {
+    uint2* state;
+    uint32_t* flag;
+    int probe, budget, stride;
+};
 
 __host__ __device__ inline int64_t seg_ptr_words(int64_t B) { return (B + 1 + 7) / 8 * 8; }
 __host__ __device__ inline int64_t seg_table_words(int64_t B) { return seg_ptr_words(B) + B * kSegRecWords; }

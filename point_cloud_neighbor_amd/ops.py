@@ -71,6 +71,8 @@ def _load():
         lib.pointops_ragged_workspace_bytes.restype = ctypes.c_size_t
         lib.pointops_knn_ragged_workspace_bytes.argtypes = [vp, vp, i64, i64]
         lib.pointops_knn_ragged_workspace_bytes.restype = ctypes.c_size_t
+        lib.pointops_ball_query_ragged_workspace_bytes.argtypes = [vp, vp, i64, i64]
+        lib.pointops_ball_query_ragged_workspace_bytes.restype = ctypes.c_size_t
         lib.pointops_knn_ragged.argtypes = [vp, i64, vp, vp, vp, i64, vp, vp, i64, i64,
                                             ctypes.c_int, vp, vp, vp, ctypes.c_size_t, vp]
         lib.pointops_knn_ragged.restype = ctypes.c_int
@@ -337,9 +339,11 @@ def _vp(a: np.ndarray):
 
 
 def _search_ragged(fn, query, q_off, q_cnt, ref, r_off, r_cnt, width, extra, global_index,
-                   pad_dist, out=None, grid_k=None):
-    """grid_k: a kNN call's k, whose workspace then has the grid search's room
-    when that search pays (pointops_knn_ragged_workspace_bytes)."""
+                   pad_dist, out=None, ws_fn=None):
+    """ws_fn: the workspace-size call that gives the grid search its room
+    when it pays (pointops_knn_ragged_workspace_bytes or
+    pointops_ball_query_ragged_workspace_bytes, with k or K = width); None
+    for the table alone (the full scans)."""
     lib = _load()
     query = _flat_points(query, "query")
     ref = _flat_points(ref, "ref")
@@ -357,10 +361,10 @@ def _search_ragged(fn, query, q_off, q_cnt, ref, r_off, r_cnt, width, extra, glo
             idx = torch.full((rows, width), -1, dtype=torch.int64, device=query.device)
         else:
             dist, idx = out
-        if grid_k is None:
+        if ws_fn is None:
             need = int(lib.pointops_ragged_workspace_bytes(B))
         else:
-            need = int(lib.pointops_knn_ragged_workspace_bytes(_vp(q_cnt), _vp(r_cnt), B, grid_k))
+            need = int(ws_fn(_vp(q_cnt), _vp(r_cnt), B, int(width)))
             if need == 0:
                 raise PointopsError(1, "invalid segment counts")
         ws = torch.empty(max(1, need), dtype=torch.uint8, device=query.device)
@@ -380,9 +384,10 @@ def knn_ragged(query: torch.Tensor, q_ptr, ref: torch.Tensor, r_ptr, k: int,
     grid=False withholds the grid search's workspace (full scans only)."""
     q_off, q_cnt = _ptr_segments(q_ptr, "q_ptr")
     r_off, r_cnt = _ptr_segments(r_ptr, "r_ptr")
-    return _search_ragged(_load().pointops_knn_ragged, query, q_off, q_cnt, ref, r_off, r_cnt,
+    lib = _load()
+    return _search_ragged(lib.pointops_knn_ragged, query, q_off, q_cnt, ref, r_off, r_cnt,
                           int(k), (int(k),), global_index, float("inf"),
-                          grid_k=int(k) if grid else None)
+                          ws_fn=lib.pointops_knn_ragged_workspace_bytes if grid else None)
 
 
 def knn_ragged_uses_grid(q_cnt, r_cnt, k: int) -> bool:
@@ -396,29 +401,44 @@ def knn_ragged_uses_grid(q_cnt, r_cnt, k: int) -> bool:
 
 
 def ball_query_ragged(query: torch.Tensor, q_ptr, ref: torch.Tensor, r_ptr, radius: float,
-                      K: int, global_index: bool = True):
+                      K: int, global_index: bool = True, grid: bool = True):
     """First-K Ball Query within each cloud of a flat batch -> (dist2, idx),
     (query rows, K), indices as reference rows (or local), (-1, 0) padding.
     Differentiable like ``ball_query`` when an input requires grad and the
-    indices are global."""
+    indices are global. grid=False withholds the grid pass's workspace (the
+    index-order scan only)."""
     if torch.is_grad_enabled() and global_index and (
             getattr(query, "requires_grad", False) or getattr(ref, "requires_grad", False)):
-        return _BallQueryRaggedFn.apply(query, q_ptr, ref, r_ptr, radius, K)
-    return _ball_query_ragged(query, q_ptr, ref, r_ptr, radius, K, global_index)
+        return _BallQueryRaggedFn.apply(query, q_ptr, ref, r_ptr, radius, K, grid)
+    return _ball_query_ragged(query, q_ptr, ref, r_ptr, radius, K, global_index, grid)
 
 
-def _ball_query_ragged(query, q_ptr, ref, r_ptr, radius, K, global_index):
+def ball_query_ragged_uses_grid(q_cnt, r_cnt, K: int) -> bool:
+    """True when pointops_ball_query_ragged takes the grid pass for these
+    counts (given the workspace pointops_ball_query_ragged_workspace_bytes
+    asks for)."""
+    lib = _load()
+    q_cnt, r_cnt = _host_i64(q_cnt, "q_cnt"), _host_i64(r_cnt, "r_cnt")
+    B = len(q_cnt)
+    return int(lib.pointops_ball_query_ragged_workspace_bytes(_vp(q_cnt), _vp(r_cnt), B,
+                                                              int(K))) > \
+        int(lib.pointops_ragged_workspace_bytes(B))
+
+
+def _ball_query_ragged(query, q_ptr, ref, r_ptr, radius, K, global_index, grid=True):
     q_off, q_cnt = _ptr_segments(q_ptr, "q_ptr")
     r_off, r_cnt = _ptr_segments(r_ptr, "r_ptr")
-    return _search_ragged(_load().pointops_ball_query_ragged, query, q_off, q_cnt, ref, r_off,
+    lib = _load()
+    return _search_ragged(lib.pointops_ball_query_ragged, query, q_off, q_cnt, ref, r_off,
                           r_cnt, int(K), (ctypes.c_float(float(radius)), int(K)), global_index,
-                          0.0)
+                          0.0, ws_fn=lib.pointops_ball_query_ragged_workspace_bytes if grid
+                          else None)
 
 
 class _BallQueryRaggedFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, query, q_ptr, ref, r_ptr, radius, K):
-        d2, idx = _ball_query_ragged(query, q_ptr, ref, r_ptr, radius, K, True)
+    def forward(ctx, query, q_ptr, ref, r_ptr, radius, K, grid):
+        d2, idx = _ball_query_ragged(query, q_ptr, ref, r_ptr, radius, K, True, grid)
         ctx.save_for_backward(query, ref, idx)
         ctx.mark_non_differentiable(idx)
         return d2, idx
@@ -427,12 +447,12 @@ class _BallQueryRaggedFn(torch.autograd.Function):
     def backward(ctx, grad_d2, grad_idx):
         query, ref, idx = ctx.saved_tensors
         if grad_d2 is None:
-            return (None,) * 6
+            return (None,) * 7
         # global indices: the flat batch is one cloud for the gradient formulas
         gq, gx = ball_query_backward(query[None], ref[None], idx[None], grad_d2[None],
                                      ctx.needs_input_grad[0], ctx.needs_input_grad[2])
         return (gq[0] if gq is not None else None, None, gx[0] if gx is not None else None,
-                None, None, None)
+                None, None, None, None)
 
 
 def fps_ragged(xyz: torch.Tensor, ptr, counts, start=None, global_index: bool = True,
@@ -488,7 +508,7 @@ def knn_padded(query: torch.Tensor, ref: torch.Tensor, k: int, lengths1=None, le
     d, i = _search_ragged(_load().pointops_knn_ragged, query.view(-1, 3),
                           np.arange(B, dtype=np.int64) * Qm, l1, ref.view(-1, 3),
                           np.arange(B, dtype=np.int64) * Pm, l2, int(k), (int(k),), False,
-                          float("inf"), grid_k=int(k))
+                          float("inf"), ws_fn=_load().pointops_knn_ragged_workspace_bytes)
     return d.view(B, Qm, k), i.view(B, Qm, k)
 
 
@@ -505,7 +525,8 @@ def ball_query_padded(query: torch.Tensor, ref: torch.Tensor, radius: float, K: 
     d, i = _search_ragged(_load().pointops_ball_query_ragged, query.view(-1, 3),
                           np.arange(B, dtype=np.int64) * Qm, l1, ref.view(-1, 3),
                           np.arange(B, dtype=np.int64) * Pm, l2, int(K),
-                          (ctypes.c_float(float(radius)), int(K)), False, 0.0)
+                          (ctypes.c_float(float(radius)), int(K)), False, 0.0,
+                          ws_fn=_load().pointops_ball_query_ragged_workspace_bytes)
     return d.view(B, Qm, K), i.view(B, Qm, K)
 
 
