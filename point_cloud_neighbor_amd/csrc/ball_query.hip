@@ -33,7 +33,9 @@ namespace pointops {
 
 constexpr uint32_t kBqDone = 0xFFFFFFFFu;  // state: the query is complete
 
-template <int QW>
+// BUD: the budgeted mode (bud.state non-null); a template parameter, so the
+// plain scan's loop carries none of its tests.
+template <int QW, bool BUD>
 __global__ __launch_bounds__(kWave) void ball_query_kernel(
     const float* __restrict__ query, const float* __restrict__ ref, int Q, int P, float r2,
     int K, float* __restrict__ out_d2, int64_t* __restrict__ out_idx,
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
         ibase = 0;
         cloud = blockIdx.y;
     }
-    const int n = bud.state ? min(P, bud.budget) : P;  // references this wave may scan
+    const int n = BUD ? min(P, bud.budget) : P;  // references this wave may scan
     const int row0 = (int)unit * QW;
     const int lane = threadIdx.x;
     const float* qb = query + qrow0 * 3;
@@ -97,11 +99,11 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
             ny = xb[(size_t)3 * jn + 1];
             nz = xb[(size_t)3 * jn + 2];
         }
-        const bool at_probe = bud.state && base + kWave == bud.probe;
+        const bool at_probe = BUD && base + kWave == bud.probe;
         bool live = false;
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
-            if (cnt[i] < K && !stopped[i]) {
+            if (cnt[i] < K && (!BUD || !stopped[i])) {
                 const float s = s32(qx[i], qy[i], qz[i], x, y, z);
                 const uint64_t m = ballot(s < r2);
                 if (m) {
@@ -112,11 +114,15 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
                     }
                     cnt[i] += __popcll(m);
                 }
-                // at this rate K hits would take more than the budget
-                if (at_probe && cnt[i] < K &&
-                    (int64_t)cnt[i] * bud.budget < (int64_t)K * bud.probe)
-                    stopped[i] = true;
-                live |= cnt[i] < K && !stopped[i];
+                if constexpr (BUD) {
+                    // at this rate K hits would take more than the budget
+                    if (at_probe && cnt[i] < K &&
+                        (int64_t)cnt[i] * bud.budget < (int64_t)K * bud.probe)
+                        stopped[i] = true;
+                    live |= cnt[i] < K && !stopped[i];
+                } else {
+                    live |= cnt[i] < K;
+                }
             }
         }
         if (!live) break;
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
             }
         }
     }
-    if (bud.state && lane == 0) {
+    if (BUD && lane == 0) {
         // a query that neither has K hits nor stopped scanned all n references
         bool left = false;
 #pragma unroll
@@ -166,8 +172,14 @@ hipError_t launch_ball_query(const float* query, const float* ref, int64_t B, in
     case W: {                                                                                \
         dim3 grid = seg ? dim3((unsigned)waves, 1)                                           \
                         : dim3((unsigned)((Q + W - 1) / W), (unsigned)B);                    \
-        hipLaunchKernelGGL(ball_query_kernel<W>, grid, block, 0, stream, query, ref, (int)Q, \
-                           (int)P, r2, (int)K, out_d2, out_idx, seg, nseg, bud);             \
+        if (bud.state)                                                                       \
+            hipLaunchKernelGGL((ball_query_kernel<W, true>), grid, block, 0, stream, query,   \
+                               ref, (int)Q, (int)P, r2, (int)K, out_d2, out_idx, seg, nseg,  \
+                               bud);                                                         \
+        else                                                                                 \
+            hipLaunchKernelGGL((ball_query_kernel<W, false>), grid, block, 0, stream, query,  \
+                               ref, (int)Q, (int)P, r2, (int)K, out_d2, out_idx, seg, nseg,  \
+                               bud);                                                         \
         break;                                                                               \
     }
         POINTOPS_BQ_CASE(1)
