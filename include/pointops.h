@@ -94,11 +94,13 @@ size_t pointops_fps_workspace_bytes(int64_t B, int64_t N, int64_t M);
  *   keep the first k; out_idx = j, out_dist = sqrtf(s32) correctly rounded.
  * With a workspace of pointops_knn_workspace_bytes(B, Q, P) bytes (when that
  * is not 0) the call may counting-sort references and queries into a uniform
- * grid, bound every 64 sorted references by a box, and visit near boxes
- * first, skipping a box when the lower bound of s32 over it (taken in the
- * float32 order of s32, so never above it) exceeds a query's current k-th
- * distance; it does so when the full scan would be long enough to hide the
- * sort (pointops_knn_search tells which search a shape takes). Otherwise, and
+ * grid, bound every 16 (and every 1024) sorted references by a box, start
+ * each query from the references around its own grid position and skip a box
+ * when the lower bound of s32 over it (taken in the float32 order of s32, so
+ * never above it) exceeds the query's current k-th distance; it does so from
+ * 8192 references per cloud and 2^22 query-reference pairs on, for k > 32
+ * from 32768 references (pointops_knn_search tells which search a shape
+ * takes). Otherwise, and
  * with workspace NULL, every reference is scanned: for k <= 32 one query per
  * wave with a merged top-32 list, else (and for k <= 8 with many queries on
  * small clouds) one query per lane. Results are identical, bit for bit,
