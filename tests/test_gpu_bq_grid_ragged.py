@@ -9,6 +9,8 @@ a radius that covers whole clouds, radii through dyadic points, clouds in
 grid order, local indices and padded clouds with lengths; at its default on
 the ragged benchmark workload's counts. All calls go through the C ABI (via
 the thin Python binding)."""
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -152,3 +154,22 @@ def test_small_clouds_keep_the_scan(gpu):
     from point_cloud_neighbor_amd import ops
     assert not ops.ball_query_ragged_uses_grid([100, 100], [4000, 8000], 32)
     assert ops.ball_query_ragged_uses_grid([100, 100], [4000, 8192], 32)
+
+
+def test_shared_reference_rows(gpu, oracle_mod, grid):
+    """Clouds whose reference segments overlap (the C ABI allows it; each
+    cloud's grid holds its own copies), flat and local indices."""
+    from point_cloud_neighbor_amd import ops
+    lib = ops._load()
+    x = W.uniform_cube(101, 1, 30000)[0]
+    r_off, r_cnt = np.array([0, 10000, 29990]), np.array([20000, 20000, 10])
+    q = W.uniform_cube(102, 1, 300)[0]
+    q_off, q_cnt = np.array([0, 100, 200]), np.array([100, 100, 100])
+    for K, gi in ((32, True), (9, False)):
+        d2, i = ops._search_ragged(lib.pointops_ball_query_ragged, dev(q), q_off, q_cnt, dev(x),
+                                   r_off, r_cnt, K, (ctypes.c_float(0.04), K), gi, 0.0,
+                                   ws_fn=lib.pointops_ball_query_ragged_workspace_bytes)
+        wd2, wi = oracle_mod.ball_query_ragged(q, q_off, q_cnt, x, r_off, r_cnt, 0.04, K,
+                                               global_index=gi, threads=8)
+        assert_idx_equal(host(i), wi, f"shared rows K={K} global={gi}")
+        assert_dist_close(host(d2), wd2, f"shared rows K={K} global={gi}")

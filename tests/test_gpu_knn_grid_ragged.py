@@ -144,3 +144,22 @@ def test_skewed_batch_keeps_the_scan(gpu):
     xcnt = np.array([60000, 50000, 40000])
     qcnt = np.array([9000, 8000, 7000])
     assert ops.knn_ragged_uses_grid(qcnt, xcnt, 16)
+
+
+def test_shared_reference_rows(gpu, oracle_mod, grid):
+    """Clouds whose reference segments overlap (the C ABI allows it; each
+    cloud's grid holds its own copies), flat and local indices."""
+    from point_cloud_neighbor_amd import ops
+    lib = ops._load()
+    x = W.uniform_cube(78, 1, 9000)[0]
+    r_off, r_cnt = np.array([0, 3000, 8990]), np.array([6000, 6000, 10])
+    q = W.uniform_cube(79, 1, 300)[0]
+    q_off, q_cnt = np.array([0, 100, 200]), np.array([100, 100, 100])
+    for k, gi in ((16, True), (12, False)):
+        d, i = ops._search_ragged(lib.pointops_knn_ragged, dev(q), q_off, q_cnt, dev(x), r_off,
+                                  r_cnt, k, (k,), gi, float("inf"),
+                                  ws_fn=lib.pointops_knn_ragged_workspace_bytes)
+        wd, wi = oracle_mod.knn_ragged(q, q_off, q_cnt, x, r_off, r_cnt, k, global_index=gi,
+                                       threads=8)
+        assert_idx_equal(host(i), wi, f"shared rows k={k} global={gi}")
+        assert_dist_close(host(d), wd, f"shared rows k={k} global={gi}")
