@@ -13,9 +13,14 @@
 
 namespace pointops {
 
+// mode: 0 plain, 1 budgeted, 2 resume (ball_query.hip)
 hipError_t launch_ball_query(const float*, const float*, int64_t, int64_t, int64_t, float,
                              int64_t, float*, int64_t*, int, const int64_t*, int, int64_t,
-                             hipStream_t, BqBudget = BqBudget{nullptr, nullptr, 0, 0, 0});
+                             hipStream_t, int = 0,
+                             BqBudget = BqBudget{nullptr, nullptr, nullptr, 0, 0, 0});
+hipError_t launch_ball_query_decide(const unsigned long long*, unsigned long long, uint32_t*,
+                                    hipStream_t);
+hipError_t launch_zero_f32(float*, size_t, hipStream_t);  // a fill kernel (ball_query_backward.hip)
 hipError_t launch_ball_query_culled(const float*, const float*, int64_t, int64_t, int64_t,
                                     float, int64_t, float*, int64_t*, int, float*, int, uint2*,
                                     uint32_t*, hipStream_t);
@@ -115,17 +120,21 @@ struct RaggedKnnGrid {
     size_t grid_bytes = 0;  // the grid's own room (at `grid`)
 };
 RaggedKnnGrid ragged_knn_grid(const int64_t* q_cnt, const int64_t* r_cnt, int64_t B, int64_t k);
-// Ball Query of a ragged batch through the index-order scan with a budget and
-// the grid pass: the scan's cloud table at 0, the grid's records and then the
-// flag word at `clouds`, the per-query state (B x Q) at `state` and the grid
+// Ball Query of a ragged batch through the index-order scan with a budget,
+// then the grid pass or the resumed scan: the scan's cloud table at 0, the
+// grid's records at `clouds` followed by kBqGateWords words (two gate words,
+// the estimate counters), the per-query state (B x Q) at `state` and the grid
 // of 2^level cells per axis at `grid`; `use` for K <= 32 and clouds of 8192
 // references or more (POINTOPS_BQ_GRID=0 / 1 forbids or allows it at any
-// size), with the same padding limit as the kNN grid.
+// size), with the same padding limit as the kNN grid. `grid_pairs`: the
+// estimated reference tests left from which the grid pass pays.
+constexpr int kBqGateWords = 1 + kBqEstimates;
 struct RaggedBqGrid {
     bool use = false;
     int64_t P = 0, Q = 0;
     int level = 2;
     size_t clouds = 0, state = 0, grid = 0, total = 0;
+    unsigned long long grid_pairs = 0;
 };
 RaggedBqGrid ragged_bq_grid(const int64_t* q_cnt, const int64_t* r_cnt, int64_t B, int64_t K);
 // The ragged scan's probe (references after which a query whose hit rate
@@ -134,11 +143,11 @@ RaggedBqGrid ragged_bq_grid(const int64_t* q_cnt, const int64_t* r_cnt, int64_t 
 int bq_ragged_probe();
 int bq_ragged_budget();
 // Writes the records of the clouds (q_off[b], q_cnt[b], r_off[b], r_cnt[b],
-// index base) to `dev` on `stream`, then one zero word (a flag for the
-// kernels that follow).
+// index base) to `dev` on `stream`, then `extra` zero words (gates and
+// counters of the kernels that follow).
 int upload_grid_clouds(const int64_t* q_off, const int64_t* q_cnt, const int64_t* r_off,
                        const int64_t* r_cnt, int64_t B, bool global_index, int64_t* dev,
-                       hipStream_t s);
+                       int extra, hipStream_t s);
 // Waves per workgroup of the grid search (one query per lane).
 int knn_grid_waves(int kcap);
 // The grid search's launch: 0 for one query per wave, else knn_grid_waves.

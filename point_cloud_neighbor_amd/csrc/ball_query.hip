@@ -19,13 +19,16 @@
 // Ragged batches (a cloud table, see segments.h): waves are numbered cloud
 // after cloud, QW queries each, and scan their own cloud's references.
 //
-// Budgeted scan (BqBudget with a state array; the ragged batches' first step
-// before the grid pass of ball_query_grid.hip): a query also stops after
-// `budget` references, or after the first `probe` when its hit count is too
-// low to reach K within the budget at that rate. Its first hits are then in
-// place (they are the first ones: every later index is larger), the rest of
-// its row is padding, and it records (hits, references examined) for the
-// grid pass, or done; a query left raises the flag.
+// Budgeted scan (the ragged batches' first step, see BqBudget): a query also
+// stops after `budget` references, or after the first `probe` when its hit
+// count is too low to reach K within the budget at that rate. Its first hits
+// are then in place (they are the first ones: every later index is larger),
+// the rest of its row is padding, and it records (hits, references examined),
+// or done. A query left adds its estimate of the references it still needs
+// (from its hit rate so far); the sum decides (ball_query_decide_kernel)
+// whether the grid pass of ball_query_grid.hip takes the queries left, or
+// the resume mode of this kernel, which continues each from its first
+// unexamined index with its count so far: the same first K either way.
 #include "common.h"
 #include "segments.h"
 
@@ -33,9 +36,11 @@ namespace pointops {
 
 constexpr uint32_t kBqDone = 0xFFFFFFFFu;  // state: the query is complete
 
-// BUD: the budgeted mode (bud.state non-null); a template parameter, so the
-// plain scan's loop carries none of its tests.
-template <int QW, bool BUD>
+// MODE: kBqPlain, kBqBudgeted or kBqResume (see BqBudget); a template
+// parameter, so the plain scan's loop carries none of the others' tests.
+constexpr int kBqPlain = 0, kBqBudgeted = 1, kBqResume = 2;
+
+template <int QW, int MODE>
 __global__ __launch_bounds__(kWave) void ball_query_kernel(
     const float* __restrict__ query, const float* __restrict__ ref, int Q, int P, float r2,
     int K, float* __restrict__ out_d2, int64_t* __restrict__ out_idx,
@@ -59,6 +64,8 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
         ibase = 0;
         cloud = blockIdx.y;
     }
+    constexpr bool BUD = MODE == kBqBudgeted;
+    if (MODE == kBqResume && *bud.gate == 0) return;  // the grid pass takes the queries left
     const int n = BUD ? min(P, bud.budget) : P;  // references this wave may scan
     const int row0 = (int)unit * QW;
     const int lane = threadIdx.x;
@@ -69,6 +76,8 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
     float qx[QW], qy[QW], qz[QW];
     int cnt[QW];
     bool stopped[QW];  // left at the probe (budgeted scan)
+    int from[QW];      // first index a resumed query takes
+    int start = 0;     // first block of the scan
 #pragma unroll
     for (int i = 0; i < QW; ++i) {
         const int row = row0 + i < Q ? row0 + i : Q - 1;
@@ -77,6 +86,22 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
         qz[i] = qb[(size_t)3 * row + 2];
         cnt[i] = row0 + i < Q ? 0 : K;  // rows past the end take no hits
         stopped[i] = false;
+        from[i] = 0;
+    }
+    if constexpr (MODE == kBqResume) {
+        // done queries take no hits; the others keep their count and go on
+        // from the first index they did not examine
+        start = n;
+#pragma unroll
+        for (int i = 0; i < QW; ++i) {
+            if (row0 + i < Q) {
+                const uint2 st = bud.state[(size_t)cloud * bud.stride + row0 + i];
+                cnt[i] = st.y == kBqDone ? K : (int)st.x;
+                from[i] = st.y == kBqDone ? n : (int)st.y;
+                start = min(start, from[i]);
+            }
+        }
+        start &= ~(kWave - 1);
     }
 
     // Software-pipelined reference loads: block n+1 is in flight while block n
@@ -84,12 +109,12 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
     // distance compares false against R2, so no separate range test is needed.
     const float nan = __builtin_nanf("");
     float nx = nan, ny = nan, nz = nan;
-    if (lane < n) {
-        nx = xb[(size_t)3 * lane + 0];
-        ny = xb[(size_t)3 * lane + 1];
-        nz = xb[(size_t)3 * lane + 2];
+    if (start + lane < n) {
+        nx = xb[(size_t)3 * (start + lane) + 0];
+        ny = xb[(size_t)3 * (start + lane) + 1];
+        nz = xb[(size_t)3 * (start + lane) + 2];
     }
-    for (int base = 0; base < n; base += kWave) {
+    for (int base = start; base < n; base += kWave) {
         const int j = base + lane;
         const float x = nx, y = ny, z = nz;
         const int jn = j + kWave;
@@ -105,7 +130,7 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
         for (int i = 0; i < QW; ++i) {
             if (cnt[i] < K && (!BUD || !stopped[i])) {
                 const float s = s32(qx[i], qy[i], qz[i], x, y, z);
-                const uint64_t m = ballot(s < r2);
+                const uint64_t m = ballot(s < r2 && (MODE != kBqResume || j >= from[i]));
                 if (m) {
                     const int slot = cnt[i] + (int)lanes_below(m);
                     if (((m >> lane) & 1ull) && slot < K) {
@@ -139,8 +164,10 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
         }
     }
     if (BUD && lane == 0) {
-        // a query that neither has K hits nor stopped scanned all n references
-        bool left = false;
+        // A query that neither has K hits nor stopped scanned all n
+        // references. A query left estimates the references it still needs
+        // from its hit rate so far (the rest of its cloud without a hit).
+        unsigned long long est = 0;
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
             if (row0 + i < Q) {
@@ -148,38 +175,72 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
                 const bool done = cnt[i] >= K || seen >= P;
                 bud.state[(size_t)cloud * bud.stride + row0 + i] =
                     done ? make_uint2(0u, kBqDone) : make_uint2((uint32_t)cnt[i], (uint32_t)seen);
-                left |= !done;
+                if (!done) {
+                    const float rest = (float)(P - seen);
+                    const float need = cnt[i] > 0
+                                           ? (float)(K - cnt[i]) * (float)seen / (float)cnt[i] + 1.0f
+                                           : rest;
+                    est += (unsigned long long)fminf(rest, need);
+                }
             }
         }
-        // only the waves that still see the flag clear raise it (one atomic
-        // per wave on one word would serialise at its L2 channel)
-        if (left &&
-            __hip_atomic_load(bud.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u)
-            atomicOr(bud.flag, 1u);
+        // spread over kBqEstimates counters: one word would serialise the
+        // waves' atomics at its L2 channel
+        if (est) atomicAdd(&bud.estimate[blockIdx.x % kBqEstimates], est);
     }
+}
+
+// One wave: the sum of the estimates decides between the grid pass (gate[0])
+// and resuming the scan (gate[1]) for the queries left; neither when none is.
+__global__ __launch_bounds__(kWave) void ball_query_decide_kernel(
+    const unsigned long long* __restrict__ estimate, unsigned long long grid_pairs,
+    uint32_t* __restrict__ gate) {
+    static_assert(kBqEstimates % kWave == 0, "counters split evenly over the lanes");
+    unsigned long long v = 0;
+#pragma unroll
+    for (int i = 0; i < kBqEstimates / kWave; ++i) v += estimate[i * kWave + threadIdx.x];
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o /= 2) v += __shfl_xor(v, o);
+    if (threadIdx.x == 0) {
+        gate[0] = v >= grid_pairs ? 1u : 0u;
+        gate[1] = v > 0 && v < grid_pairs ? 1u : 0u;
+    }
+}
+
+hipError_t launch_ball_query_decide(const unsigned long long* estimate,
+                                    unsigned long long grid_pairs, uint32_t* gate,
+                                    hipStream_t stream) {
+    hipLaunchKernelGGL(ball_query_decide_kernel, dim3(1), dim3(kWave), 0, stream, estimate,
+                       grid_pairs, gate);
+    return hipGetLastError();
 }
 
 // Launch helper used by the C ABI: grid (ceil(Q / QW), B), one wave per group;
 // ragged (seg != nullptr): grid (waves, 1) with waves = the table's
 // tile_ptr[nseg], Q and P unused.
+// mode: kBqPlain, kBqBudgeted or kBqResume (the last two with `bud`).
 hipError_t launch_ball_query(const float* query, const float* ref, int64_t B, int64_t Q,
                              int64_t P, float r2, int64_t K, float* out_d2, int64_t* out_idx,
                              int qw, const int64_t* seg, int nseg, int64_t waves,
-                             hipStream_t stream, BqBudget bud) {
+                             hipStream_t stream, int mode, BqBudget bud) {
     dim3 block(kWave);
     switch (qw) {
 #define POINTOPS_BQ_CASE(W)                                                                  \
     case W: {                                                                                \
         dim3 grid = seg ? dim3((unsigned)waves, 1)                                           \
                         : dim3((unsigned)((Q + W - 1) / W), (unsigned)B);                    \
-        if (bud.state)                                                                       \
-            hipLaunchKernelGGL((ball_query_kernel<W, true>), grid, block, 0, stream, query,   \
-                               ref, (int)Q, (int)P, r2, (int)K, out_d2, out_idx, seg, nseg,  \
-                               bud);                                                         \
+        if (mode == kBqBudgeted)                                                             \
+            hipLaunchKernelGGL((ball_query_kernel<W, kBqBudgeted>), grid, block, 0, stream,   \
+                               query, ref, (int)Q, (int)P, r2, (int)K, out_d2, out_idx, seg, \
+                               nseg, bud);                                                   \
+        else if (mode == kBqResume)                                                          \
+            hipLaunchKernelGGL((ball_query_kernel<W, kBqResume>), grid, block, 0, stream,     \
+                               query, ref, (int)Q, (int)P, r2, (int)K, out_d2, out_idx, seg, \
+                               nseg, bud);                                                   \
         else                                                                                 \
-            hipLaunchKernelGGL((ball_query_kernel<W, false>), grid, block, 0, stream, query,  \
-                               ref, (int)Q, (int)P, r2, (int)K, out_d2, out_idx, seg, nseg,  \
-                               bud);                                                         \
+            hipLaunchKernelGGL((ball_query_kernel<W, kBqPlain>), grid, block, 0, stream,      \
+                               query, ref, (int)Q, (int)P, r2, (int)K, out_d2, out_idx, seg, \
+                               nseg, bud);                                                   \
         break;                                                                               \
     }
         POINTOPS_BQ_CASE(1)

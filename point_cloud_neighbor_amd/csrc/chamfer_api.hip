@@ -142,7 +142,7 @@ int nearest(const float* a, const float* bpts, int64_t B, int64_t n, int64_t m,
     if (g.use && table_bytes >= g.grid && grid_bytes >= g.grid_bytes) {
         int64_t* clouds = (int64_t*)table_ws;
         int st = upload_grid_clouds(qo.data(), qc.data(), ro.data(), rc.data(), B, false, clouds,
-                                    s);
+                                    0, s);
         if (st != POINTOPS_OK) return st;
         int64_t refs = 0;
         for (int64_t b = 0; b < B; ++b) refs += rc[(size_t)b];

@@ -84,7 +84,7 @@ RaggedKnnGrid ragged_knn_grid(const int64_t* q_cnt, const int64_t* r_cnt, int64_
     if (!knn_use_grid_pairs(pairs, g.P) || !knn_grid_pays_pairs(k, pairs, g.P)) return g;
     if (B * (g.P + g.Q) > kGridPadRatio * points) return g;
     g.use = true;
-    g.grid = al256(((size_t)B * kGcWords + 1) * sizeof(int64_t));  // records, flag word
+    g.grid = al256((size_t)B * kGcWords * sizeof(int64_t));  // the records
     g.grid_bytes = al256(pointops::grid_workspace_bytes(B, g.Q, g.P, pointops::knn_grid_level(g.P)));
     g.total = std::max(g.total, g.grid + g.grid_bytes);
     return g;
@@ -117,17 +117,24 @@ RaggedBqGrid ragged_bq_grid(const int64_t* q_cnt, const int64_t* r_cnt, int64_t 
     if (B * (g.P + g.Q) > kGridPadRatio * points) return g;
     g.use = true;
     g.level = bq_grid_level(g.P);
-    g.clouds = al256((size_t)seg_table_words(B) * sizeof(int64_t));     // the scan's table
-    g.state = g.clouds + al256(((size_t)B * kGcWords + 1) * sizeof(int64_t));  // records, flag
+    g.clouds = al256((size_t)seg_table_words(B) * sizeof(int64_t));  // the scan's table
+    g.state = g.clouds + al256(((size_t)B * kGcWords + kBqGateWords) * sizeof(int64_t));
     g.grid = g.state + al256((size_t)B * g.Q * sizeof(uint2));
     g.total = g.grid + al256(pointops::ball_query_ragged_grid_bytes(B, g.Q, g.P, g.level));
+    // The grid pays once the reference tests left would take longer than its
+    // build and pass: measured on the ragged 16-cloud batch (317k points),
+    // about 40 us plus 0.25 ns per point, against scans of about 1.1 * 10^12
+    // tests per second. POINTOPS_BQ_GRID_PAIRS overrides.
+    const long env_pairs = env_long("POINTOPS_BQ_GRID_PAIRS", -1);
+    g.grid_pairs = env_pairs >= 0 ? (unsigned long long)env_pairs
+                                  : (unsigned long long)(1.1e6 * (40.0 + 2.5e-4 * (double)points));
     return g;
 }
 
 int upload_grid_clouds(const int64_t* q_off, const int64_t* q_cnt, const int64_t* r_off,
                        const int64_t* r_cnt, int64_t B, bool global_index, int64_t* dev,
-                       hipStream_t s) {
-    std::vector<int64_t> w((size_t)B * kGcWords + 1, 0);  // the last word: the flag
+                       int extra, hipStream_t s) {
+    std::vector<int64_t> w((size_t)B * kGcWords + (size_t)extra, 0);
     for (int64_t b = 0; b < B; ++b) {
         int64_t* r = w.data() + b * kGcWords;
         r[kGcROff] = r_off[b];
@@ -407,7 +414,7 @@ int pointops_knn_ragged(const float* query, int64_t q_rows, const int64_t* q_off
     if (g.use && workspace && workspace_bytes >= g.total) {
         char* ws = (char*)workspace;
         int64_t* clouds = (int64_t*)(ws + g.clouds);
-        st = upload_grid_clouds(q_off, q_cnt, r_off, r_cnt, B, global_index != 0, clouds, s);
+        st = upload_grid_clouds(q_off, q_cnt, r_off, r_cnt, B, global_index != 0, clouds, 0, s);
         if (st != POINTOPS_OK) return st;
         int64_t refs = 0;
         for (int64_t b = 0; b < B; ++b) refs += q_cnt[b] > 0 ? r_cnt[b] : 0;
@@ -472,24 +479,33 @@ int pointops_ball_query_ragged(const float* query, int64_t q_rows, const int64_t
     int64_t* table = nullptr;
     st = upload(t, workspace, workspace_bytes, s, &table);
     if (st != POINTOPS_OK) return st;
-    // With the grid's room: the scan in its budgeted mode, then (gated on the
-    // device by the flag) the grid build and the grid pass.
+    // With the grid's room: the scan in its budgeted mode; then, as the
+    // estimate of the tests left decides on the device (no host round trip),
+    // the grid build and the grid pass, or the scan resumed where each query
+    // left off. Every step after the first reads its gate and may do nothing.
     const RaggedBqGrid g = ragged_bq_grid(q_cnt, r_cnt, B, K);
     if (g.use && workspace_bytes >= g.total) {
         char* ws = (char*)workspace;
         int64_t* clouds = (int64_t*)(ws + g.clouds);
-        uint32_t* flag = (uint32_t*)(clouds + B * pointops::kGcWords);
+        uint32_t* gate = (uint32_t*)(clouds + B * pointops::kGcWords);  // grid, resume
+        unsigned long long* estimate = (unsigned long long*)(clouds + B * pointops::kGcWords + 1);
         uint2* state = (uint2*)(ws + g.state);
-        st = upload_grid_clouds(q_off, q_cnt, r_off, r_cnt, B, global_index != 0, clouds, s);
+        st = upload_grid_clouds(q_off, q_cnt, r_off, r_cnt, B, global_index != 0, clouds, 1, s);
         if (st != POINTOPS_OK) return st;
-        const pointops::BqBudget bud{state, flag, bq_ragged_probe(), bq_ragged_budget(),
-                                     (int)g.Q};
+        hipError_t ez = pointops::launch_zero_f32((float*)estimate, 2 * pointops::kBqEstimates, s);
+        if (ez != hipSuccess) return hip_fail(ez, "ball_query estimate clear");
+        pointops::BqBudget bud{state, estimate, gate + 1, bq_ragged_probe(), bq_ragged_budget(),
+                               (int)g.Q};
         hipError_t e = pointops::launch_ball_query(query, ref, 0, 0, 0, r2, K, out_dist2,
-                                                   out_idx, qw, table, t.nseg, t.units, s, bud);
-        if (e != hipSuccess) return hip_fail(e, "ball_query launch");
-        e = pointops::launch_ball_query_ragged_grid(query, ref, B, g.Q, g.P, r2, K, out_dist2,
-                                                    out_idx, g.level, clouds, flag, state,
-                                                    ws + g.grid, s);
+                                                   out_idx, qw, table, t.nseg, t.units, s, 1, bud);
+        if (e == hipSuccess) e = pointops::launch_ball_query_decide(estimate, g.grid_pairs, gate, s);
+        if (e == hipSuccess)
+            e = pointops::launch_ball_query_ragged_grid(query, ref, B, g.Q, g.P, r2, K, out_dist2,
+                                                        out_idx, g.level, clouds, gate, state,
+                                                        ws + g.grid, s);
+        if (e == hipSuccess)
+            e = pointops::launch_ball_query(query, ref, 0, 0, 0, r2, K, out_dist2, out_idx, qw,
+                                            table, t.nseg, t.units, s, 2, bud);
         if (e != hipSuccess) return hip_fail(e, "ball_query launch");
         return POINTOPS_OK;
     }

@@ -28,13 +28,17 @@ enum SearchRec { kSrQOff = 0, kSrQCnt, kSrROff, kSrRCnt, kSrIdxBase, kSrCloud };
 // word, candidates published per workgroup.
 enum FpsRec { kFrXOff = 0, kFrXCnt, kFrOOff, kFrOCnt, kFrIdxBase, kFrStart, kFrWOff, kFrRG };
 
-// The budgeted mode of the Ball Query scan (ball_query.hip): with `state`
-// non-null a query also stops after `budget` references, or after `probe`
-// when its hits come too slowly, and records its state at
-// state[cloud * stride + row]; a query left raises *flag.
+// The budgeted and resume modes of the Ball Query scan (ball_query.hip).
+// Budgeted: a query also stops after `budget` references, or after `probe`
+// when its hits come too slowly, records its state at
+// state[cloud * stride + row], and adds its estimate of the references it
+// still needs to one of kBqEstimates 64-bit counters at `estimate`. Resume
+// (only while *gate != 0): the queries left continue from their state.
+constexpr int kBqEstimates = 256;
 struct BqBudget {
     uint2* state;
-    uint32_t* flag;
+    unsigned long long* estimate;
+    const uint32_t* gate;
     int probe, budget, stride;
 };
 

@@ -1,11 +1,12 @@
 """Ball Query's culled search on ragged batches (an index-order scan with a
 budget, then, for the queries it leaves, the grid pass over per-cloud records
-with slots as large as the batch's largest cloud) versus the oracle's ragged
-composition: indices bit-exact, squared distances bit-exact. Forced on at
-small sizes (POINTOPS_BQ_GRID=1) with scan budgets of one chunk (nearly every
-query reaches the grid holding some hits), the default, and the default with a
-probe of one chunk; with empty clouds, clouds without queries or references,
-a radius that covers whole clouds, radii through dyadic points, clouds in
+with slots as large as the batch's largest cloud, or the scan resumed where
+each stopped) versus the oracle's ragged composition: indices bit-exact,
+squared distances bit-exact. Forced on at small sizes (POINTOPS_BQ_GRID=1)
+with scan budgets of one chunk (nearly every query is left holding some
+hits) and the grid pass or the resumed scan taking them, a probe of one
+chunk, and the defaults; with empty clouds, clouds without queries or
+references, a radius that covers whole clouds, radii through dyadic points, clouds in
 grid order, local indices and padded clouds with lengths; at its default on
 the ragged benchmark workload's counts. All calls go through the C ABI (via
 the thin Python binding)."""
@@ -20,12 +21,18 @@ from tests.gpu_util import assert_dist_close, assert_idx_equal, dev, host
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=[("64", "64"), ("512", "4096"), ("64", "4096")],
-                ids=["budget64", "default", "probe64"])
+@pytest.fixture(params=[("64", "64", "0"), ("64", "64", "1000000000000000000"),
+                        ("64", "4096", ""), ("", "", "")],
+                ids=["budget64_grid", "budget64_resume", "probe64", "default"])
 def grid(monkeypatch, request):
+    """The culled search forced on; (probe, budget, the tests left from which
+    the grid pass is taken): a one-chunk budget with the grid pass or the
+    resumed scan taking every query left, a one-chunk probe, the defaults."""
     monkeypatch.setenv("POINTOPS_BQ_GRID", "1")
-    monkeypatch.setenv("POINTOPS_BQ_PROBE", request.param[0])
-    monkeypatch.setenv("POINTOPS_BQ_RAGGED_BUDGET", request.param[1])
+    for name, v in zip(("POINTOPS_BQ_PROBE", "POINTOPS_BQ_RAGGED_BUDGET",
+                        "POINTOPS_BQ_GRID_PAIRS"), request.param):
+        if v:
+            monkeypatch.setenv(name, v)
     return monkeypatch
 
 
