@@ -123,7 +123,7 @@ def test_workspace_sizes(lib):
     """Host-only size queries: the Ball Query's workspace grows by the grid
     pass's room (per query, sorted copies, histograms) above 32768 references
     and is zero for empty shapes; kNN's grid workspace starts at 8192
-    references and 2^27 pairs."""
+    references and 2^22 pairs."""
     i64 = ctypes.c_int64
     lib.pointops_ball_query_workspace_bytes.argtypes = [i64, i64, i64]
     lib.pointops_ball_query_workspace_bytes.restype = ctypes.c_size_t
@@ -139,3 +139,42 @@ def test_workspace_sizes(lib):
     knn = lib.pointops_knn_workspace_bytes
     assert knn(1, 100000, 100000) > 0
     assert knn(1, 100, 8191) == 0 and knn(1, 10, 100000) == 0
+
+
+def test_ragged_workspace_sizes(lib):
+    """Host-only size queries of the ragged culled searches: more than the
+    scan's table exactly when the search is taken (clouds of 8192 references
+    or more, K <= 32 for Ball Query, padding to the largest cloud within
+    eight times the points), room for every cloud's slots at the largest
+    counts, and 0 for invalid counts."""
+    import numpy as np
+    i64 = ctypes.c_int64
+    vp = ctypes.c_void_p
+    for f in (lib.pointops_knn_ragged_workspace_bytes,
+              lib.pointops_ball_query_ragged_workspace_bytes):
+        f.argtypes = [vp, vp, i64, i64]
+        f.restype = ctypes.c_size_t
+    lib.pointops_ragged_workspace_bytes.argtypes = [i64]
+    lib.pointops_ragged_workspace_bytes.restype = ctypes.c_size_t
+    table = lib.pointops_ragged_workspace_bytes
+
+    def sizes(f, q, r, k):
+        q, r = np.asarray(q, dtype=np.int64), np.asarray(r, dtype=np.int64)
+        return f(q.ctypes.data, r.ctypes.data, len(q), k)
+
+    knn, bq = lib.pointops_knn_ragged_workspace_bytes, lib.pointops_ball_query_ragged_workspace_bytes
+    q, r = [6000, 3000, 200], [50000, 24000, 1600]
+    for f, k in ((knn, 16), (bq, 32)):
+        n = sizes(f, q, r, k)
+        # sorted float4 copies of every cloud at the largest counts, at least
+        assert n > table(3) + 3 * (50000 + 6000) * 16, f
+    # small clouds, large K, a skewed batch: the scans' table alone
+    assert sizes(knn, [100, 100], [4000, 8000], 16) == table(2)
+    assert sizes(bq, [100, 100], [4000, 8000], 32) == table(2)
+    assert sizes(bq, q, r, 33) == table(3)
+    skew_q, skew_r = [25000] + [10] * 200, [200000] + [100] * 200
+    assert sizes(knn, skew_q, skew_r, 16) == table(201)
+    assert sizes(bq, skew_q, skew_r, 32) == table(201)
+    # no clouds: the table's minimum; invalid counts: 0
+    assert sizes(knn, [], [], 16) == table(0)
+    assert sizes(knn, [-1], [10], 16) == 0 and sizes(bq, [1], [-5], 8) == 0
