@@ -150,7 +150,8 @@ int upload_grid_clouds(const int64_t* q_off, const int64_t* q_cnt, const int64_t
                        int extra, hipStream_t s);
 // Waves per workgroup of the grid search (one query per lane).
 int knn_grid_waves(int kcap);
-// The grid search's launch: 0 for one query per wave, else knn_grid_waves.
+// The grid search's launch: 0 / -2 for one / two queries per wave, else
+// knn_grid_waves (one query per lane).
 int knn_grid_nw(int64_t k, int kcap, int64_t queries, int64_t refs);
 int bq_queries_per_wave(int64_t rows, int cus, int max_qw);
 bool bq_grid_possible(int64_t P);

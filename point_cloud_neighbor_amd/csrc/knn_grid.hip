@@ -589,10 +589,10 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
     }
 }
 
-// One query per wave (k <= 32), for launches with few queries per cloud or
-// queries much sparser than the references (a lane-per-query workgroup then
-// has few waves and a wide box of queries). A workgroup holds kKgwWaves
-// queries in grid order, one per wave. The wave first sorts the 64
+// One or two (QW) queries per wave (k <= 32). A workgroup holds kKgwWaves
+// waves of consecutive queries in grid order; with QW = 2 a wave's two
+// neighbouring queries share every box test (a box is opened for either)
+// and every reference load. The wave first sorts the 64
 // references around its query's grid position into its list (wave_list.h,
 // keys (bits(s) << 32) | index) and takes the k-th key's high word as its
 // bound; then its lanes test 64 superblock boxes at a time and, in a
@@ -605,13 +605,14 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
 // independent.
 constexpr int kKgwWaves = 4;
 
+template <int QW>
 __global__ __launch_bounds__(kKgwWaves* kWave) void knn_grid_wave_kernel(
     const float4* __restrict__ sq, const float4* __restrict__ sr, int Q, int P, int k,
     const float* __restrict__ box, const float* __restrict__ sbox, int nblk, int nsb,
     const uint32_t* __restrict__ ref_start, const GridParams* __restrict__ gp, int L,
     float* __restrict__ out_dist, int64_t* __restrict__ out_idx, int squared,
     const int64_t* __restrict__ clouds) {
-    __shared__ uint64_t cbuf[kKgwWaves][kKwBuf];
+    __shared__ uint64_t cbuf[kKgwWaves][QW][kKwBuf];
     const int b = blockIdx.y;
     int Qb = Q, Pb = P, nbb = nblk, nsbb = nsb;
     int64_t orow0 = (int64_t)b * Q, ibase = 0;
@@ -626,49 +627,54 @@ __global__ __launch_bounds__(kKgwWaves* kWave) void knn_grid_wave_kernel(
     }
     const int lane = lane_id();
     const int w = uniform((int)(threadIdx.x / kWave));
-    const int qi = (int)blockIdx.x * kKgwWaves + w;
-    if (qi >= Qb) return;  // whole waves
-    const float4 q = sq[(size_t)b * Q + qi];
+    const int q0 = ((int)blockIdx.x * kKgwWaves + w) * QW;  // this wave's first query
+    if (q0 >= Qb) return;  // whole waves
     const float4* rb = sr + (size_t)b * P;
     const float* bx = box + (size_t)b * nblk * 8;
     const float* sbx = sbox + (size_t)b * nsb * 8;
-
-    // 1. The kWave references around the query's own grid position.
     const int nloc = min(Pb, kWave);
-    int loc0;
-    {
-        const int64_t C = (int64_t)1 << (3 * L);
-        const uint32_t code = cell_code(gp[b], q.x, q.y, q.z, L);
+    const int64_t C = (int64_t)1 << (3 * L);
+
+    // 1. Per query, the kWave references around its own grid position. A
+    //    query past the cloud's last (QW > 1) takes bound 0: nothing enters.
+    float4 q[QW];
+    int loc0[QW];
+    KwQuery st[QW];
+#pragma unroll
+    for (int h = 0; h < QW; ++h) {
+        const bool valid = q0 + h < Qb;
+        q[h] = sq[(size_t)b * Q + (valid ? q0 + h : q0)];
+        const uint32_t code = cell_code(gp[b], q[h].x, q[h].y, q[h].z, L);
         const int pos = (int)ref_start[(int64_t)b * C + code];
-        loc0 = max(0, min(pos - nloc / 2, Pb - nloc));
-    }
-    KwQuery st{kKwEmpty, ~0u, 0, cbuf[w]};
-    {
+        loc0[h] = max(0, min(pos - nloc / 2, Pb - nloc));
         uint64_t key = kKwEmpty;
         if (lane < nloc) {
-            const float4 p = rb[loc0 + lane];
-            key = ((uint64_t)f2u(s32(q.x, q.y, q.z, p.x, p.y, p.z)) << 32) |
+            const float4 p = rb[loc0[h] + lane];
+            key = ((uint64_t)f2u(s32(q[h].x, q[h].y, q[h].z, p.x, p.y, p.z)) << 32) |
                   (uint32_t)__float_as_int(p.w);
         }
-        st.list = kw_sort_merge(key, lane);
-        st.bound = lane_value((uint32_t)(st.list >> 32), k - 1);
+        st[h] = KwQuery{kw_sort_merge(key, lane), 0u, 0, cbuf[w][h]};
+        st[h].bound = valid ? lane_value((uint32_t)(st[h].list >> 32), k - 1) : 0u;
     }
+    auto open = [&](const float* o) {  // the box may hold a reference some query takes
+        bool any = false;
+#pragma unroll
+        for (int h = 0; h < QW; ++h)
+            any |= f2u(box_bound(o, q[h].x, q[h].y, q[h].z)) <= st[h].bound;
+        return any;
+    };
 
     // 2. Superblocks, then the blocks of a surviving one, then the references
-    //    of up to four surviving blocks at a time (16 lanes each); the local
-    //    references are in the list already.
+    //    of up to four surviving blocks at a time (16 lanes each), each read
+    //    once for the QW queries; a query's local references are in its list.
     for (int sb0 = 0; sb0 < nsbb; sb0 += kWave) {
         const int my_sb = sb0 + lane;
-        uint64_t ms = ballot(my_sb < nsbb &&
-                             f2u(box_bound(sbx + (size_t)min(my_sb, nsbb - 1) * 8, q.x, q.y,
-                                           q.z)) <= st.bound);
+        uint64_t ms = ballot(my_sb < nsbb && open(sbx + (size_t)min(my_sb, nsbb - 1) * 8));
         while (ms) {
             const int s = sb0 + __builtin_ctzll(ms);
             ms &= ms - 1;
             const int my_blk = s * kWave + lane;
-            uint64_t mb = ballot(my_blk < nbb &&
-                                 f2u(box_bound(bx + (size_t)min(my_blk, nbb - 1) * 8, q.x, q.y,
-                                               q.z)) <= st.bound);
+            uint64_t mb = ballot(my_blk < nbb && open(bx + (size_t)min(my_blk, nbb - 1) * 8));
             while (mb) {
                 int blk[4];
 #pragma unroll
@@ -679,29 +685,36 @@ __global__ __launch_bounds__(kKgwWaves* kWave) void knn_grid_wave_kernel(
                 const int g = lane >> 4;
                 const int mine = g == 0 ? blk[0] : g == 1 ? blk[1] : g == 2 ? blk[2] : blk[3];
                 const int j = mine * kGridBlk + (lane & (kGridBlk - 1));
-                bool cand = false;
-                uint32_t u = 0u, idx = 0u;
-                if (mine >= 0 && j < Pb && (uint32_t)(j - loc0) >= (uint32_t)nloc) {
-                    const float4 p = rb[j];
-                    u = f2u(s32(q.x, q.y, q.z, p.x, p.y, p.z));
-                    idx = (uint32_t)__float_as_int(p.w);
-                    cand = u <= st.bound;
+                const bool in = mine >= 0 && j < Pb;
+                const float4 p = in ? rb[j] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+                for (int h = 0; h < QW; ++h) {
+                    bool cand = false;
+                    uint32_t u = 0u;
+                    if (in && (uint32_t)(j - loc0[h]) >= (uint32_t)nloc) {
+                        u = f2u(s32(q[h].x, q[h].y, q[h].z, p.x, p.y, p.z));
+                        cand = u <= st[h].bound;
+                    }
+                    kw_offer<true>(st[h], cand, u, __float_as_int(p.w), lane, k);
                 }
-                kw_offer<true>(st, cand, u, (int)idx, lane, k);
             }
         }
     }
-    if (st.cnt > 0) kw_merge(st, lane, k);
 
-    // 3. Lane n < k writes the n-th key; empty only in a cloud with fewer
-    //    than k references.
-    if (lane < k) {
-        const uint64_t e = st.list;
-        const bool empty = e == kKwEmpty;
-        const float sv = u2f((uint32_t)(e >> 32));
-        const int64_t o = (orow0 + __float_as_int(q.w)) * k + lane;
-        out_dist[o] = empty ? (squared ? 0.0f : __builtin_inff()) : squared ? sv : sqrtf(sv);
-        out_idx[o] = empty ? (int64_t)-1 : ibase + (int64_t)(uint32_t)e;
+    // 3. Lane n < k writes the n-th key of each query; empty only in a cloud
+    //    with fewer than k references.
+#pragma unroll
+    for (int h = 0; h < QW; ++h) {
+        if (q0 + h >= Qb) break;
+        if (st[h].cnt > 0) kw_merge(st[h], lane, k);
+        if (lane < k) {
+            const uint64_t e = st[h].list;
+            const bool empty = e == kKwEmpty;
+            const float sv = u2f((uint32_t)(e >> 32));
+            const int64_t o = (orow0 + __float_as_int(q[h].w)) * k + lane;
+            out_dist[o] = empty ? (squared ? 0.0f : __builtin_inff()) : squared ? sv : sqrtf(sv);
+            out_idx[o] = empty ? (int64_t)-1 : ibase + (int64_t)(uint32_t)e;
+        }
     }
 }
 
@@ -811,23 +824,28 @@ hipError_t launch_grid_build(const float* query, const float* ref, int64_t B, in
 // squared != 0: out_dist holds s itself (the Chamfer distance's nearest points).
 // With `clouds` (device memory, B records; see GridCloud) P and Q are the
 // largest counts of the ragged batch.
-// nw == 0: one query per wave (knn_grid_wave_kernel, k <= 32); otherwise
-// one query per lane with nw waves per workgroup.
+// nw == 0 / -2: one / two queries per wave (knn_grid_wave_kernel, k <= 32);
+// otherwise one query per lane with nw waves per workgroup.
 hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int64_t Q, int64_t P,
                            int64_t k, float* out_dist, int64_t* out_idx, int kcap, int nw,
                            void* workspace, int squared, const int64_t* clouds,
                            hipStream_t stream) {
-    if (nw == 0 && (k < 1 || k > kKwBuf)) return hipErrorInvalidValue;
+    if (nw <= 0 && (k < 1 || k > kKwBuf)) return hipErrorInvalidValue;
     GridView v;
     hipError_t e = launch_grid_build(query, ref, B, Q, P, knn_grid_level(P), workspace, nullptr,
                                      clouds, stream, &v);
     if (e != hipSuccess) return e;
-    if (nw == 0) {
-        hipLaunchKernelGGL(knn_grid_wave_kernel,
-                           dim3((unsigned)((Q + kKgwWaves - 1) / kKgwWaves), (unsigned)B),
-                           dim3(kKgwWaves * kWave), 0, stream, v.squery, v.sref, (int)Q, (int)P,
-                           (int)k, v.box, v.sbox, v.nblk, v.nsb, v.ref_start, v.gp, v.L,
-                           out_dist, out_idx, squared, clouds);
+    if (nw <= 0) {  // 0: one query per wave, -2: two
+        const int qw = nw == -2 ? 2 : 1;
+        const dim3 grid((unsigned)((Q + kKgwWaves * qw - 1) / (kKgwWaves * qw)), (unsigned)B);
+        if (qw == 2)
+            hipLaunchKernelGGL(knn_grid_wave_kernel<2>, grid, dim3(kKgwWaves * kWave), 0, stream,
+                               v.squery, v.sref, (int)Q, (int)P, (int)k, v.box, v.sbox, v.nblk,
+                               v.nsb, v.ref_start, v.gp, v.L, out_dist, out_idx, squared, clouds);
+        else
+            hipLaunchKernelGGL(knn_grid_wave_kernel<1>, grid, dim3(kKgwWaves * kWave), 0, stream,
+                               v.squery, v.sref, (int)Q, (int)P, (int)k, v.box, v.sbox, v.nblk,
+                               v.nsb, v.ref_start, v.gp, v.L, out_dist, out_idx, squared, clouds);
         return hipGetLastError();
     }
 #define POINTOPS_CHECK(x) \

@@ -171,19 +171,21 @@ int knn_grid_waves(int kcap) {
     return 2;
 }
 
-// The grid search's kernel: one query per wave (0) for k <= 32, else one
-// query per lane (knn_grid_waves). Measured (uniform clouds, build included,
-// per lane / per wave): 100k queries on 100k references, k = 16: 0.31 / 0.20
-// ms; k = 3: 0.18 / 0.15 ms; 12500 on 100k, k = 16: 0.38 / 0.08 ms; 16384 on
-// 2^20, k = 32: 1.54 / 0.21 ms; the ragged 16-cloud batch (35k queries,
-// k = 16): 0.47 / 0.17 ms. POINTOPS_KNN_GRID_WAVE=0 / 1 forces either (1 only
-// for k <= 32).
+// The grid search's kernel: for k <= 32 one query per wave (0), or two (-2)
+// where the queries are at least half as many as the references (neighbours
+// in grid order then open nearly the same boxes and share their loads); else
+// one query per lane (knn_grid_waves). Measured (uniform clouds, build
+// included, per lane / one per wave / two per wave): 100k queries on 100k
+// references, k = 16: 0.31 / 0.20 / 0.184 ms; k = 3: 0.18 / 0.156 / 0.144 ms;
+// 12500 on 100k, k = 16: 0.38 / 0.079 / 0.083 ms; 16384 on 2^20, k = 32:
+// 1.54 / 0.218 / 0.224 ms; the ragged 16-cloud batch (35k queries, k = 16):
+// 0.47 / 0.177 / 0.175 ms. POINTOPS_KNN_GRID_WAVE=0 / 1 / 2 forces one
+// (1 and 2 only for k <= 32).
 int knn_grid_nw(int64_t k, int kcap, int64_t queries, int64_t refs) {
-    (void)queries;
-    (void)refs;
     const long env = env_long("POINTOPS_KNN_GRID_WAVE", -1);
     if (k > 32 || env == 0) return knn_grid_waves(kcap);
-    return 0;
+    if (env == 1) return 0;
+    return env == 2 || queries * 2 >= refs ? -2 : 0;
 }
 
 // Ball Query: queries per wave. Fewer queries per wave until the grid is about

@@ -163,7 +163,7 @@ def test_chamfer_invalid_arguments(gpu):
 
 @pytest.mark.parametrize("case", ["uniform", "integer"])
 @pytest.mark.parametrize("lengths", [False, True])
-@pytest.mark.parametrize("per_wave", ["0", "1"])
+@pytest.mark.parametrize("per_wave", ["0", "1", "2"])
 def test_chamfer_and_three_nn_grid_search_forced(gpu, oracle_mod, case, lengths, per_wave,
                                                  monkeypatch):
     """The nearest points of the Chamfer distance and three_nn through the

@@ -15,7 +15,7 @@ from tests.gpu_util import assert_dist_close, assert_idx_equal, dev, host
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["0", "1"], ids=["per_lane", "per_wave"])
+@pytest.fixture(params=["0", "1", "2"], ids=["per_lane", "per_wave", "two_per_wave"])
 def grid(monkeypatch, request):
     """The grid search forced on, with one query per lane or (k <= 32) per
     wave."""
@@ -117,7 +117,7 @@ def test_workload_takes_the_grid_and_matches_the_scan(gpu, oracle_mod):
     d, i, d0, i0 = host(d), host(i), host(d0), host(i0)
     assert np.array_equal(i, i0)
     assert np.array_equal(d.view(np.uint32), d0.view(np.uint32))
-    for per_wave in ("0", "1"):  # both grid kernels, whichever the default is
+    for per_wave in ("0", "1", "2"):  # every grid kernel, whichever the default is
         import os
         os.environ["POINTOPS_KNN_GRID_WAVE"] = per_wave
         try:

@@ -29,10 +29,10 @@ def check_fps(gpu, oracle_mod, xyz, M, start=0, what=""):
 
 def check_knn(gpu, oracle_mod, q, x, k, what=""):
     """Every search: the full scan and the grid search (forced on, whatever
-    the size), the latter with one query per lane and, for k <= 32, one per
-    wave."""
+    the size), the latter with one query per lane and, for k <= 32, one or
+    two per wave."""
     wd, wi = oracle_mod.knn(q, x, k, threads=8)
-    runs = [("0", "0"), ("1", "0")] + ([("1", "1")] if k <= 32 else [])
+    runs = [("0", "0"), ("1", "0")] + ([("1", "1"), ("1", "2")] if k <= 32 else [])
     for grid, per_wave in runs:
         old = {n: os.environ.get(n) for n in ("POINTOPS_KNN_GRID", "POINTOPS_KNN_GRID_WAVE")}
         os.environ["POINTOPS_KNN_GRID"] = grid
