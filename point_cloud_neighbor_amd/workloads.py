@@ -32,6 +32,7 @@ against that cloud.
 from __future__ import annotations
 
 import dataclasses
+import hashlib
 import math
 
 import numpy as np
@@ -49,6 +50,31 @@ R2_BITS = {
 
 def bits_to_f32(bits: int) -> np.float32:
     return np.array([bits], dtype=np.uint32).view(np.float32)[0]
+
+
+# ----------------------------------------------------------------- output digests
+#
+# Whole outputs at the full workload sizes are compared by SHA-256 of their
+# bytes: indices as little-endian int64, distances as little-endian float32
+# bit patterns, row-major. Chunk digests over fixed runs of rows locate a
+# mismatch without storing the outputs. These are byte hashes only.
+
+DIGEST_DTYPES = {"idx": "<i8", "dist": "<f4"}
+
+
+def output_digest(a: np.ndarray, kind: str) -> str:
+    a = np.ascontiguousarray(a, dtype=np.dtype(DIGEST_DTYPES[kind]))
+    return hashlib.sha256(a.tobytes()).hexdigest()
+
+
+def output_rows(a: np.ndarray) -> np.ndarray:
+    """The output as rows: (B, Q, K) -> (B*Q, K); (B, M) -> (B*M, 1)."""
+    return a.reshape(-1, a.shape[-1]) if a.ndim == 3 else a.reshape(-1, 1)
+
+
+def chunk_digests(a: np.ndarray, kind: str, rows_per_chunk: int) -> list:
+    r = output_rows(a)
+    return [output_digest(r[i:i + rows_per_chunk], kind) for i in range(0, len(r), rows_per_chunk)]
 
 
 @dataclasses.dataclass
