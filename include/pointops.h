@@ -51,7 +51,9 @@ enum pointops_status {
     POINTOPS_INVALID_ARGUMENT = 1, /* a size, index, radius or pointer is out of range */
     POINTOPS_UNSUPPORTED = 2,      /* valid request beyond a compiled limit (k > KMAX, sizes) */
     POINTOPS_UNSUPPORTED_DEVICE = 3, /* current device is not gfx950 with 64-wide waves */
-    POINTOPS_HIP_ERROR = 4         /* a HIP runtime call failed; see pointops_last_error() */
+    POINTOPS_HIP_ERROR = 4,        /* a HIP runtime call failed; see pointops_last_error() */
+    POINTOPS_EXEC_TIMEOUT = 5      /* an FPS launch gave up a bounded cross-workgroup wait;
+                                      reported by pointops_fps_status */
 };
 
 /* Largest k accepted by pointops_knn. The project page, section "Contracts",
@@ -85,6 +87,39 @@ int pointops_fps(const float *xyz, int64_t B, int64_t N, int64_t M, int64_t star
 
 /* Bytes of device workspace pointops_fps needs for this shape (it may be 0). */
 size_t pointops_fps_workspace_bytes(int64_t B, int64_t N, int64_t M);
+
+/*
+ * Execution status of the last pointops_fps or pointops_fps_ragged call that
+ * used `workspace` (the workspace and byte count given to that call) and
+ * sampled at least one point; a call with nothing to sample (B, M or every
+ * count 0) touches no workspace and leaves its word as it was.
+ * The project page's contracts never let a failure pass silently (section
+ * "Quick start": no silent fallback), and errors during execution surface at
+ * the caller's next synchronisation (the conventions above); this is that
+ * synchronisation for FPS.
+ *
+ * A multi-workgroup FPS launch keeps every workgroup of a cloud waiting on the
+ * others at each exchange. Every such wait is bounded. A workgroup that gives
+ * up raises a status word at the start of the workspace, and the output slots
+ * its cloud had not reached hold -1. That can only happen when the cloud's
+ * workgroups cannot all run at once, for example when another persistent
+ * launch holds the compute units.
+ *
+ * The call waits for `stream` (hipStreamSynchronize), then copies the status
+ * word to the host. It returns POINTOPS_OK, POINTOPS_EXEC_TIMEOUT (with a
+ * message in pointops_last_error), POINTOPS_INVALID_ARGUMENT (NULL workspace,
+ * or fewer than 8 bytes) or POINTOPS_HIP_ERROR. It writes nothing to the
+ * device. The word stays raised until the next FPS call on that workspace
+ * clears it.
+ *
+ *   exchanges  host int64, or NULL: set to the number of cross-workgroup
+ *              exchanges the first cloud of that call made (in launch order;
+ *              0 when the cloud ran in one workgroup). A measure of the
+ *              call's latency chain: each exchange is one round trip through
+ *              device memory between the cloud's workgroups.
+ */
+int pointops_fps_status(const void *workspace, size_t workspace_bytes, int64_t *exchanges,
+                        void *stream);
 
 /*
  * k nearest neighbours.
@@ -403,7 +438,7 @@ const char *pointops_status_string(int status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char *pointops_last_error(void);
 
-/* Library ABI version: 3. */
+/* Library ABI version: 4. */
 int pointops_abi_version(void);
 
 #ifdef __cplusplus

@@ -247,6 +247,8 @@ __global__ __launch_bounds__(BLOCK) void fps_kernel(
             if (oxb) { oxb[3 * t + 0] = cx; oxb[3 * t + 1] = cy; oxb[3 * t + 2] = cz; }
         }
     }
+    // header word 1: the exchanges of the launch's first cloud (one per step)
+    if (blockIdx.x == 0 && tid == 0) status[1] = G > 1 && M > 1 ? (uint32_t)(M - 1) : 0u;
 }
 
 // ---------------------------------------------------------------- batched FPS
@@ -818,10 +820,12 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
         if (g == 0)
             for (int v = sh_t; v < M; ++v) ob[v] = -1;
     }
+    // header word 1: the exchanges of the launch's first cloud
+    if (blockIdx.x == 0 && tid == 0) status[1] = G > 1 ? batch : 0u;
 }
 
-// Workspace: a 256-byte header (status word), then two parity sets of G slots
-// per cloud.
+// Workspace: a 256-byte header (word 0: status, word 1: the exchanges of the
+// launch's first cloud), then two parity sets of G slots per cloud.
 size_t fps_workspace_bytes(int64_t B, int64_t G) {
     return G > 1 ? 256 + (size_t)B * 2 * (size_t)G * sizeof(FpsSlot) : 256;
 }

@@ -381,7 +381,7 @@ using namespace pointops::api;
 
 extern "C" {
 
-int pointops_abi_version(void) { return 3; }
+int pointops_abi_version(void) { return 4; }
 
 const char* pointops_status_string(int status) {
     switch (status) {
@@ -390,6 +390,7 @@ const char* pointops_status_string(int status) {
         case POINTOPS_UNSUPPORTED: return "unsupported (beyond a compiled limit)";
         case POINTOPS_UNSUPPORTED_DEVICE: return "unsupported device (needs gfx950, wave64)";
         case POINTOPS_HIP_ERROR: return "HIP runtime error";
+        case POINTOPS_EXEC_TIMEOUT: return "FPS gave up a bounded wait (workgroups not co-resident)";
         default: return "unknown status";
     }
 }
@@ -449,6 +450,27 @@ int pointops_fps(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t star
     return POINTOPS_OK;
 }
 
+int pointops_fps_status(const void* workspace, size_t workspace_bytes, int64_t* exchanges,
+                        void* stream) {
+    g_err[0] = 0;
+    if (!workspace || workspace_bytes < 2 * sizeof(uint32_t))
+        return fail(POINTOPS_INVALID_ARGUMENT, "FPS status needs the call's workspace");
+    // the copy is ordered after the FPS launch on `stream`; the synchronize
+    // waits for both (pageable host memory: no registration involved)
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t words[2] = {0, 0};  // status, exchanges of the first cloud
+    hipError_t e = hipMemcpyAsync(words, workspace, sizeof words, hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "fps status: read status word");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "fps status: stream synchronize");
+    if (exchanges) *exchanges = (int64_t)words[1];
+    if (words[0] != 0)
+        return fail(POINTOPS_EXEC_TIMEOUT,
+                    "FPS gave up waiting for a workgroup of its cloud (status word %u); output "
+                    "slots from that step on hold -1",
+                    words[0]);
+    return POINTOPS_OK;
+}
 
 size_t pointops_knn_workspace_bytes(int64_t B, int64_t Q, int64_t P) {
     if (B <= 0 || Q <= 0 || P <= 0 || !knn_use_grid(B, Q, P)) return 0;

@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpointops.so")
 
 STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "UNSUPPORTED_DEVICE",
-          4: "HIP_ERROR"}
+          4: "HIP_ERROR", 5: "EXEC_TIMEOUT"}
 KNN_KMAX = 64
 
 
@@ -50,6 +50,8 @@ def _load():
         lib.pointops_fps.restype = ctypes.c_int
         lib.pointops_fps_workspace_bytes.argtypes = [i64, i64, i64]
         lib.pointops_fps_workspace_bytes.restype = ctypes.c_size_t
+        lib.pointops_fps_status.argtypes = [vp, ctypes.c_size_t, vp, vp]
+        lib.pointops_fps_status.restype = ctypes.c_int
         lib.pointops_knn.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp, ctypes.c_size_t,
                                      vp]
         lib.pointops_knn_workspace_bytes.argtypes = [i64, i64, i64]
@@ -140,10 +142,28 @@ def fps_workspace_bytes(B: int, N: int, M: int) -> int:
     return int(_load().pointops_fps_workspace_bytes(B, N, M))
 
 
+def fps_status(workspace: torch.Tensor) -> int:
+    """Wait for the current stream and raise ``PointopsError`` (EXEC_TIMEOUT)
+    if the last FPS call that sampled with ``workspace`` gave up a bounded
+    wait (its unreached output slots then hold -1). Returns the number of
+    cross-workgroup exchanges that call's first cloud made."""
+    n = ctypes.c_int64(0)
+    with torch.cuda.device(workspace.device):
+        _check(_load().pointops_fps_status(workspace.data_ptr(), workspace.numel(),
+                                           ctypes.byref(n), _stream(workspace.device)))
+    return int(n.value)
+
+
 def furthest_point_sample(xyz: torch.Tensor, npoint: int, start_idx: int = 0,
-                          return_xyz: bool = False, workspace: torch.Tensor | None = None):
+                          return_xyz: bool = False, workspace: torch.Tensor | None = None,
+                          check: bool = True):
     """Farthest point sampling of (B, N, 3) float32 clouds -> int64 (B, npoint)
-    (and the sampled coordinates (B, npoint, 3) when ``return_xyz``)."""
+    (and the sampled coordinates (B, npoint, 3) when ``return_xyz``).
+
+    ``check`` (default) waits for the launch and raises ``PointopsError`` if
+    it gave up a bounded wait between its workgroups. With ``check=False`` the
+    call stays asynchronous; pass a ``workspace`` and call
+    ``fps_status(workspace)`` later."""
     lib = _load()
     xyz = _points(xyz, "xyz")
     B, N, _ = xyz.shape
@@ -157,6 +177,8 @@ def furthest_point_sample(xyz: torch.Tensor, npoint: int, start_idx: int = 0,
                               oxyz.data_ptr() if oxyz is not None else None,
                               workspace.data_ptr(), workspace.numel(), _stream(xyz.device))
         _check(rc)
+        if check and need > 0 and B > 0 and npoint > 0:
+            fps_status(workspace)
     return (out, oxyz) if return_xyz else out
 
 
@@ -456,11 +478,12 @@ class _BallQueryRaggedFn(torch.autograd.Function):
 
 
 def fps_ragged(xyz: torch.Tensor, ptr, counts, start=None, global_index: bool = True,
-               return_xyz: bool = False):
+               return_xyz: bool = False, check: bool = True):
     """Farthest point sampling of each cloud of a flat batch (rows ptr[b] ..
     ptr[b+1]), counts[b] samples each, from local index start[b] (default 0)
     -> int64 (sum of counts,), cloud after cloud; indices are rows of ``xyz``
-    (or local). With ``return_xyz`` also the sampled coordinates."""
+    (or local). With ``return_xyz`` also the sampled coordinates. ``check`` as
+    for ``furthest_point_sample``."""
     lib = _load()
     xyz = _flat_points(xyz, "xyz")
     x_off, x_cnt = _ptr_segments(ptr, "ptr")
@@ -484,6 +507,8 @@ def fps_ragged(xyz: torch.Tensor, ptr, counts, start=None, global_index: bool = 
                                      _vp(o_off), _vp(counts), int(bool(global_index)),
                                      ws.data_ptr(), ws.numel(), _stream(xyz.device))
         _check(rc)
+        if check and need > 0 and total > 0:
+            fps_status(ws)
     return (out, oxyz) if return_xyz else out
 
 

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pointops.h")
 LIB = os.path.join(ROOT, "point_cloud_neighbor_amd", "libpointops.so")
 
-OK, INVALID, UNSUPPORTED, UNSUPPORTED_DEVICE, HIP_ERROR = range(5)
+OK, INVALID, UNSUPPORTED, UNSUPPORTED_DEVICE, HIP_ERROR, EXEC_TIMEOUT = range(6)
 
 
 def declared_functions():
@@ -33,6 +33,7 @@ def lib():
     lib.pointops_knn.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp, ctypes.c_size_t, vp]
     lib.pointops_ball_query.argtypes = [vp, vp, i64, i64, i64, f32, i64, vp, vp, vp,
                                         ctypes.c_size_t, vp]
+    lib.pointops_fps_status.argtypes = [vp, ctypes.c_size_t, vp, vp]
     lib.pointops_status_string.restype = ctypes.c_char_p
     lib.pointops_last_error.restype = ctypes.c_char_p
     return lib
@@ -40,7 +41,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for required in ("pointops_fps", "pointops_fps_workspace_bytes", "pointops_knn",
+    for required in ("pointops_fps", "pointops_fps_workspace_bytes", "pointops_fps_status",
+                     "pointops_knn",
                      "pointops_ball_query", "pointops_device_check", "pointops_status_string",
                      "pointops_last_error", "pointops_abi_version"):
         assert required in names
@@ -52,13 +54,20 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pointops_abi_version() == 3
-    for code in range(5):
-        assert lib.pointops_status_string(code)
+    assert lib.pointops_abi_version() == 4
+    for code in range(6):
+        assert lib.pointops_status_string(code) != b"unknown status"
     assert lib.pointops_status_string(99) == b"unknown status"
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def test_fps_status_argument_checks(lib):
+    # no workspace, or too small for the status word: rejected before any HIP call
+    assert lib.pointops_fps_status(None, 1 << 20, None, None) == INVALID
+    assert lib.pointops_fps_status(FAKE, 7, None, None) == INVALID
+    assert b"workspace" in lib.pointops_last_error()
 
 
 def test_fps_argument_checks(lib):

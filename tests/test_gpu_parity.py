@@ -364,11 +364,28 @@ def test_fps_bounded_wait_terminates(gpu, mode, monkeypatch):
     monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", "8")
     monkeypatch.setenv("POINTOPS_FPS_SPIN_LIMIT", "0")
     xyz = dev(W.uniform_cube(4, 1, 20000))
-    out = host(gpu.furthest_point_sample(xyz, 500))
+    ws = torch.empty(gpu.fps_workspace_bytes(1, 20000, 500), dtype=torch.uint8, device="cuda")
+    out = host(gpu.furthest_point_sample(xyz, 500, workspace=ws, check=False))
     torch.cuda.synchronize()
     assert ((out >= 0) & (out < 20000) | (out == -1)).all()
     first_bad = np.argmax(out[0] == -1) if (out == -1).any() else 500
     assert (out[0, first_bad:] == -1).all()
+    # the give-up is reported: through the status query of the C ABI and as
+    # an exception of the checked binding (a zero bound gives up at the first
+    # poll that finds a workgroup missing: over 499 steps of 8 workgroups
+    # some poll always does)
+    with pytest.raises(gpu.PointopsError) as err:
+        gpu.fps_status(ws)
+    assert err.value.status == 5
+    assert (out == -1).any()
+    with pytest.raises(gpu.PointopsError) as err:
+        gpu.furthest_point_sample(xyz, 500)
+    assert err.value.status == 5
+    # without the bound the same call succeeds and its status clears
+    monkeypatch.delenv("POINTOPS_FPS_SPIN_LIMIT")
+    out = host(gpu.furthest_point_sample(xyz, 500, workspace=ws))
+    gpu.fps_status(ws)
+    assert (out >= 0).all()
 
 
 def test_unsupported_device_is_an_error(gpu):
