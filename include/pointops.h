@@ -89,6 +89,26 @@ int pointops_fps(const float *xyz, int64_t B, int64_t N, int64_t M, int64_t star
 size_t pointops_fps_workspace_bytes(int64_t B, int64_t N, int64_t M);
 
 /*
+ * pointops_fps without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, results and errors as pointops_fps;
+ * it calls no hipMalloc, hipFree or allocating library routine.
+ *
+ * Its scratch is a static device array of 1 MiB in the library, one per GPU,
+ * held until the process ends; every FPS plan the library makes for default
+ * settings fits (the largest, many clouds of 3-4k points over three
+ * workgroups each, needs about 0.75 MB; 2^20 points, 32 KB). A shape that
+ * needs more returns POINTOPS_UNSUPPORTED before anything is launched. The
+ * call clears what it uses first, on `stream`. All calls on one GPU share its
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and must be ordered by the caller. A bounded wait that gives up (see
+ * pointops_fps_status) leaves -1 in the unreached output slots; its status
+ * word is not readable by the caller here.
+ */
+int pointops_fps_noalloc(const float *xyz, int64_t B, int64_t N, int64_t M, int64_t start_idx,
+                         int64_t *out_idx, float *out_xyz, void *stream);
+
+/*
  * Execution status of the last pointops_fps or pointops_fps_ragged call that
  * used `workspace` (the workspace and byte count given to that call) and
  * sampled at least one point; a call with nothing to sample (B, M or every

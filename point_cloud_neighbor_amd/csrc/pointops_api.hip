@@ -375,6 +375,40 @@ size_t plan_workspace_bytes(int64_t B, const FpsPlan& p) {
                    : pointops::fps_workspace_bytes(B, p.G);
 }
 
+// The static scratch of pointops_fps_noalloc: FPS's workspace (status word,
+// exchange words) for callers that cannot allocate device memory. Each GPU
+// holds its own copy for the life of the process; its device address comes
+// from hipGetSymbolAddress once per device (the array's name is only a host
+// stand-in), and only that address is ever passed to a kernel or a fill.
+constexpr size_t kFpsScratchBytes = (size_t)1 << 20;
+static __device__ __align__(256) uint8_t scratch[kFpsScratchBytes];
+void* g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `device`'s scratch (the device is current), after
+// checking that `need` bytes fit. POINTOPS_FPS_SCRATCH_LIMIT lowers the limit
+// (so a test can reach the refusal); it never raises it.
+int static_scratch(int device, size_t need, void** out) {
+    size_t limit = kFpsScratchBytes;
+    const long env = env_long("POINTOPS_FPS_SCRATCH_LIMIT", 0);
+    if (env > 0 && (size_t)env < limit) limit = (size_t)env;
+    if (need > limit)
+        return fail(POINTOPS_UNSUPPORTED,
+                    "this FPS needs %zu bytes of scratch; the static scratch holds %zu "
+                    "(use pointops_fps with a workspace)",
+                    need, limit);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[device]) {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(POINTOPS_HIP_ERROR, "hipGetSymbolAddress(scratch) gave NULL");
+        g_scratch[device] = p;
+    }
+    *out = g_scratch[device];
+    return POINTOPS_OK;
+}
+
 }  // namespace
 
 using namespace pointops::api;
@@ -413,9 +447,16 @@ size_t pointops_fps_workspace_bytes(int64_t B, int64_t N, int64_t M) {
     return p.err == POINTOPS_OK ? plan_workspace_bytes(B, p) : 0;
 }
 
-int pointops_fps(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t start_idx,
-                 int64_t* out_idx, float* out_xyz, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by pointops_fps and pointops_fps_noalloc: validation, plan and launch
+// on `ws` (a workspace of ws_bytes bytes, or the static scratch when
+// ws_limit is set: then the plan's need is checked against that limit).
+int fps_run(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t start_idx,
+            int64_t* out_idx, float* out_xyz, void* ws, size_t ws_bytes, bool scratch,
+            void* stream) {
     g_err[0] = 0;
     if (B < 0 || N < 0 || M < 0) return fail(POINTOPS_INVALID_ARGUMENT, "negative size");
     if (B == 0 || M == 0) return POINTOPS_OK;
@@ -426,28 +467,51 @@ int pointops_fps(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t star
     if (N >= kMaxPoints || M >= kMaxPoints)
         return fail(POINTOPS_UNSUPPORTED, "N and M must be below 2^31");
     if (!xyz || !out_idx) return fail(POINTOPS_INVALID_ARGUMENT, "null pointer");
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     DeviceInfo* dev = nullptr;
-    int st = current_device(&dev);
+    int st = check_device(device, &dev);
     if (st != POINTOPS_OK) return st;
     const FpsPlan p = fps_plan(B, N, *dev);
     if (p.err != POINTOPS_OK) return p.err;
     const size_t need = plan_workspace_bytes(B, p);
-    if (!workspace || workspace_bytes < need)
+    if (scratch) {
+        st = static_scratch(device, need, &ws);
+        if (st != POINTOPS_OK) return st;
+    } else if (!ws || ws_bytes < need) {
         return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
-                    workspace_bytes, need);
+                    ws_bytes, need);
+    }
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = pointops::launch_fps_clear(workspace, need, s);
+    e = pointops::launch_fps_clear(ws, need, s);
     if (e != hipSuccess) return hip_fail(e, "fps workspace clear");
     const uint32_t spin = (uint32_t)env_long("POINTOPS_FPS_SPIN_LIMIT", 1L << 22);
     if (p.batch)
-        e = pointops::launch_fps_batch(xyz, B, N, M, start_idx, out_idx, out_xyz, workspace, p.G,
+        e = pointops::launch_fps_batch(xyz, B, N, M, start_idx, out_idx, out_xyz, ws, p.G,
                                        p.ppt, p.block, p.rg, p.cpl, spin, s, nullptr, 0, 0,
                                        nullptr, 0);
     else
-        e = pointops::launch_fps(xyz, B, N, M, start_idx, out_idx, out_xyz, workspace, p.G, p.ppt,
+        e = pointops::launch_fps(xyz, B, N, M, start_idx, out_idx, out_xyz, ws, p.G, p.ppt,
                                  p.block, spin, s, nullptr, 0, 0);
     if (e != hipSuccess) return hip_fail(e, "fps launch");
     return POINTOPS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pointops_fps(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t start_idx,
+                 int64_t* out_idx, float* out_xyz, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    return fps_run(xyz, B, N, M, start_idx, out_idx, out_xyz, workspace, workspace_bytes, false,
+                   stream);
+}
+
+int pointops_fps_noalloc(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t start_idx,
+                         int64_t* out_idx, float* out_xyz, void* stream) {
+    return fps_run(xyz, B, N, M, start_idx, out_idx, out_xyz, nullptr, 0, true, stream);
 }
 
 int pointops_fps_status(const void* workspace, size_t workspace_bytes, int64_t* exchanges,
