@@ -29,6 +29,8 @@
 // whether the grid pass of ball_query_grid.hip takes the queries left, or
 // the resume mode of this kernel, which continues each from its first
 // unexamined index with its count so far: the same first K either way.
+#include <type_traits>
+
 #include "common.h"
 #include "segments.h"
 
@@ -114,15 +116,24 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
         ny = xb[(size_t)3 * (start + lane) + 1];
         nz = xb[(size_t)3 * (start + lane) + 2];
     }
-    for (int base = start; base < n; base += kWave) {
+    // One block of 64 references for every live query. FULL: the next block
+    // is complete (base + 2 * kWave <= n), so its load needs no range test.
+    auto block = [&](int base, auto full_) -> bool {
+        constexpr bool FULL = decltype(full_)::value;
         const int j = base + lane;
         const float x = nx, y = ny, z = nz;
         const int jn = j + kWave;
-        nx = ny = nz = nan;
-        if (jn < n) {
+        if constexpr (FULL) {
             nx = xb[(size_t)3 * jn + 0];
             ny = xb[(size_t)3 * jn + 1];
             nz = xb[(size_t)3 * jn + 2];
+        } else {
+            nx = ny = nz = nan;
+            if (jn < n) {
+                nx = xb[(size_t)3 * jn + 0];
+                ny = xb[(size_t)3 * jn + 1];
+                nz = xb[(size_t)3 * jn + 2];
+            }
         }
         const bool at_probe = BUD && base + kWave == bud.probe;
         bool live = false;
@@ -150,8 +161,12 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
                 }
             }
         }
-        if (!live) break;
-    }
+        return live;
+    };
+    int base = start;
+    bool live = true;
+    for (; live && base + 2 * kWave <= n; base += kWave) live = block(base, std::true_type{});
+    for (; live && base < n; base += kWave) live = block(base, std::false_type{});
 
     // Padding: slots count..K-1 of each row hold (-1, +0.0f).
 #pragma unroll

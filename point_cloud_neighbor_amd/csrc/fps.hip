@@ -49,6 +49,7 @@
 // points, outputs, start index and exchange words. Clouds never interact; the
 // argmax of each step is taken over that cloud's workgroups only.
 #include <algorithm>
+#include <cstdlib>
 #include <tuple>
 #include <type_traits>
 #include <utility>
@@ -333,14 +334,14 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     const float* __restrict__ xyz, int N, int M, int start_idx, int G, int slice, int RG,
     int64_t* __restrict__ out_idx, float* __restrict__ out_xyz, uint64_t* __restrict__ words,
     int stride, uint32_t* __restrict__ status, uint32_t spin_limit,
-    const int64_t* __restrict__ seg, int nseg) {
+    const int64_t* __restrict__ seg, int nseg, int solo) {
     constexpr int NW = BLOCK / kWave;
-    // Every wave but the certifying wave 0 holds points. Waves go round-robin
-    // over the 4 SIMDs of a CU, so wave 0 shares its SIMD with the point waves
-    // 4, 8, 12; it runs at a higher priority, so they take the issue cycles it
-    // leaves idle.
-    constexpr int NPW = NW - 1;
-    static_assert(NW % 4 == 0 && NPW >= 1 && 2 * NPW <= kWave, "wave count");
+    // Wave 0 certifies; the others hold points. Waves go round-robin over the
+    // 4 SIMDs of a CU, so wave 0 shares its SIMD with waves 4, 8, 12. With
+    // `solo` those waves hold no points and wait at the barriers, so no other
+    // wave of the workgroup issues on the certifying wave's SIMD; otherwise
+    // they hold points too and wave 0 runs at a higher priority.
+    static_assert(NW % 4 == 0 && 2 * (NW - 1) <= kWave, "wave count");
     // Certified centres of the batch: x, y, z bits and the point's index. An
     // entry is written before the count that includes it (LDS performs one
     // wave's operations in issue order), and readers load the count first.
@@ -392,8 +393,9 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     const float* xb = xyz + xrow0 * 3;
     const int lo = g * slice;
     const int cnt = min(N, lo + slice) - lo;  // >= 1
-    const bool point_wave = wave != 0;
-    const int pw = wave - 1;                  // index among the point waves
+    const int NPW = solo ? NW - NW / 4 : NW - 1;
+    const bool point_wave = solo ? (wave & 3) != 0 : wave != 0;
+    const int pw = solo ? wave - wave / 4 - 1 : wave - 1;  // index among the point waves
     const int u = pw * kWave + lane;          // point-thread id
     const int wbase = pw * kWave * PPT;       // first slice position of this wave
 
@@ -896,7 +898,16 @@ int fps_batch_ppt_round(int ppt) {
 
 int fps_batch_stride(int rg) { return 3 * rg + 2; }  // words per workgroup
 
-int fps_batch_point_waves(int block) { return block / kWave - 1; }
+// The certifying wave alone on its SIMD (waves 4, 8, 12 hold no points).
+bool fps_batch_solo() {
+    const char* v = getenv("POINTOPS_FPS_SOLO");
+    return v && v[0] == '1';
+}
+
+int fps_batch_point_waves(int block) {
+    const int nw = block / kWave;
+    return fps_batch_solo() ? nw - nw / 4 : nw - 1;
+}
 
 size_t fps_batch_workspace_bytes(int64_t B, int64_t G, int rg) {
     return G > 1 ? 256 + (size_t)B * 2 * (size_t)G * fps_batch_stride(rg) * sizeof(uint64_t) : 256;
@@ -965,7 +976,7 @@ hipError_t launch_fps_batch(const float* xyz, int64_t B, int64_t N, int64_t M, i
         hipLaunchKernelGGL((fps_batch_kernel<C::PPT, C::BLOCK, C::CPL>), dim3(grid),
                            dim3(C::BLOCK), lds, stream, xyz, (int)N, (int)M, (int)start_idx, G,
                            slice, rg, out_idx, out_xyz, words, fps_batch_stride(rg), status,
-                           spin_limit, seg, nseg);
+                           spin_limit, seg, nseg, (int)fps_batch_solo());
         e = hipGetLastError();
     });
     return e;

@@ -15,15 +15,17 @@
 // reference it reads serves its QW queries: each pair costs the eight float32
 // operations of s32 and about one operation of candidate test.
 //
-// List. The wave keeps, per query, its 32 best pairs so far as 64-bit keys
-// (bits(s) << 32) | j, ascending across lanes 0..31: s >= +0, so the high word
+// List. The wave keeps, per query, its KL best pairs so far (32, or 16 when
+// k <= 16) as 64-bit keys (bits(s) << 32) | j, ascending across lanes
+// 0..KL-1: s >= +0, so the high word
 // orders like s and the low word breaks ties by index. Lane k-1's key bounds
 // the k-th neighbour; because the list holds only earlier references (smaller
 // indices), a new reference can enter it only with bits(s) strictly below
 // that key's high word, the candidate test.
 //
-// Merge. Candidates go to a 32-entry LDS buffer of the query and are merged
-// into the list 32 at a time by a bitonic network of lane moves (wave_list.h).
+// Merge. Candidates go to an LDS buffer of the query and are merged into the
+// list 32 at a time (48 when k <= 16: the list then keeps 16 lanes) by a
+// bitonic network of lane moves (wave_list.h).
 //
 // Ragged batches (a cloud table, see segments.h): workgroups are numbered
 // cloud after cloud, NW * QW queries each. A cloud with fewer than k references
@@ -36,8 +38,9 @@ namespace pointops {
 
 constexpr int kKwTile = 1024;            // references per LDS tile
 // NW waves per workgroup, QW queries per wave (consecutive rows): each
-// reference read from LDS serves the QW queries.
-template <int NW, int QW>
+// reference read from LDS serves the QW queries. KL list lanes: 16 when
+// k <= 16 (a 48-entry candidate buffer, so a third fewer merges), else 32.
+template <int NW, int QW, int KL>
 __global__ __launch_bounds__(NW* kWave) void knn_wave_kernel(
     const float* __restrict__ query, const float* __restrict__ ref, int Q, int P, int k,
     float* __restrict__ out_dist, int64_t* __restrict__ out_idx, const int64_t* __restrict__ seg,
@@ -46,7 +49,7 @@ __global__ __launch_bounds__(NW* kWave) void knn_wave_kernel(
     constexpr int PER = kKwTile / NT;  // tile points each thread loads
     static_assert(kKwTile % NT == 0, "tile must split evenly over the threads");
     __shared__ float tile[2][3][kKwTile];
-    __shared__ uint64_t cbuf[NW][QW][kKwBuf];
+    __shared__ uint64_t cbuf[NW][QW][kWave - KL];
 
     int64_t qrow0, rrow0, ibase, qtile;
     if (seg) {
@@ -162,15 +165,12 @@ __global__ __launch_bounds__(NW* kWave) void knn_wave_kernel(
                 for (int h = 0; h < QW; ++h) {
                     const uint32_t mn = min(min(u[h][0], u[h][1]), min(u[h][2], u[h][3]));
                     if (ballot(mn < st[h].bound)) {
-#pragma unroll 1
-                        for (int r = 0; r < 4; ++r) {
-                            const uint32_t ur = r == 0   ? u[h][0]
-                                                : r == 1 ? u[h][1]
-                                                : r == 2 ? u[h][2]
-                                                         : u[h][3];
-                            kw_offer(st[h], ur < st[h].bound, ur, j0 + (c + r) * kWave + lane,
-                                     lane, k);
-                        }
+                        // unrolled, so each offer tests its chunk's value in
+                        // place (no run-time choice among the four)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            kw_offer<false, KL>(st[h], u[h][r] < st[h].bound, u[h][r],
+                                                j0 + (c + r) * kWave + lane, lane, k);
                     }
                 }
             }
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(NW* kWave) void knn_wave_kernel(
 #pragma unroll
     for (int h = 0; h < QW; ++h) {
         if (q0 + h >= Q) break;
-        if (st[h].cnt > 0) kw_merge(st[h], lane, k);
+        if (st[h].cnt > 0) kw_merge<KL>(st[h], lane, k);
         if (lane < k) {
             const uint64_t e = st[h].list;
             const bool empty = e == kKwEmpty;  // only when the cloud has < k references
@@ -207,9 +207,14 @@ hipError_t launch_knn_wave(const float* query, const float* ref, int64_t B, int6
     const dim3 grid = seg ? dim3((unsigned)tiles, 1) : dim3((unsigned)((Q + per - 1) / per), (unsigned)B);
 #define POINTOPS_KNN_WAVE_CASE(W, H)                                                         \
     if (nw == W && qw == H) {                                                                \
-        hipLaunchKernelGGL((knn_wave_kernel<W, H>), grid, dim3(W * kWave), 0, stream, query,\
-                           ref, (int)Q, (int)P, (int)k, out_dist, out_idx, seg, nseg,        \
-                           squared);                                                         \
+        if (k <= 16)                                                                         \
+            hipLaunchKernelGGL((knn_wave_kernel<W, H, 16>), grid, dim3(W * kWave), 0, stream, \
+                               query, ref, (int)Q, (int)P, (int)k, out_dist, out_idx, seg,   \
+                               nseg, squared);                                               \
+        else                                                                                 \
+            hipLaunchKernelGGL((knn_wave_kernel<W, H, 32>), grid, dim3(W * kWave), 0, stream, \
+                               query, ref, (int)Q, (int)P, (int)k, out_dist, out_idx, seg,   \
+                               nseg, squared);                                               \
         return hipGetLastError();                                                            \
     }
     POINTOPS_KNN_WAVE_CASE(4, 1) POINTOPS_KNN_WAVE_CASE(8, 1) POINTOPS_KNN_WAVE_CASE(16, 1)

@@ -1,5 +1,6 @@
-// A wave's sorted list of its 32 smallest 64-bit keys, fed with candidates
-// in batches of 32 and merged by a bitonic network of lane moves: used by the
+// A wave's sorted list of its 32 (or 16) smallest 64-bit keys, fed with
+// candidates in batches of 32 (or 48) and merged by a bitonic network of lane
+// moves: used by the
 // one-query-per-wave kNN scan and grid search (keys (bits(s) << 32) | index)
 // and the Ball Query grid pass (keys (index << 32) | bits(s)).
 //
@@ -115,14 +116,19 @@ struct KwQuery {
     uint64_t* buf;
 };
 
-// Merges the buffered candidates into the list (the buffer holds cnt <= 32).
+// Merges the buffered candidates into the list. L is the number of list lanes
+// kept (32, or 16 when k <= 16); the buffer holds cnt <= 64 - L candidates,
+// which lanes L..63 load. The network sorts all 64 keys, so lanes 0..L-1 end
+// up holding the L smallest, ascending.
+template <int L = kKwBuf>
 __device__ __forceinline__ void kw_merge(KwQuery& st, int lane, int k) {
+    static_assert(L == 16 || L == 32, "list lanes");
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int e = lane - kKwBuf;
+    const int e = lane - L;
     uint64_t v = st.list;
-    if (e >= 0) v = e < st.cnt ? st.buf[e] : kKwEmpty;  // e < 32: in bounds
+    if (e >= 0) v = e < st.cnt ? st.buf[e] : kKwEmpty;  // e < 64 - L: in bounds
     st.list = kw_sort_merge(v, lane);
     st.bound = lane_value((uint32_t)(st.list >> 32), k - 1);
     st.cnt = 0;
@@ -136,18 +142,19 @@ __device__ __forceinline__ void kw_merge(KwQuery& st, int lane, int k) {
 // (u < bound; with INCL u <= bound, for callers that visit keys out of the
 // order of their low words, where a key with the bound's high word can still
 // enter by a smaller low word).
-template <bool INCL = false>
+template <bool INCL = false, int L = kKwBuf>
 __device__ __forceinline__ void kw_offer(KwQuery& st, bool cand, uint32_t u, int j, int lane,
                                          int k) {
+    constexpr int CAP = kWave - L;  // buffer entries
     uint64_t m = ballot(cand);
     while (m) {
         const int pos = st.cnt + (int)lanes_below(m);
-        if (cand && pos < kKwBuf) st.buf[pos] = ((uint64_t)u << 32) | (uint32_t)j;
+        if (cand && pos < CAP) st.buf[pos] = ((uint64_t)u << 32) | (uint32_t)j;
         st.cnt += (int)__builtin_popcountll(m);
-        if (st.cnt < kKwBuf) break;
-        st.cnt = kKwBuf;
-        kw_merge(st, lane, k);
-        cand = cand && pos >= kKwBuf && (INCL ? u <= st.bound : u < st.bound);
+        if (st.cnt < CAP) break;
+        st.cnt = CAP;
+        kw_merge<L>(st, lane, k);
+        cand = cand && pos >= CAP && (INCL ? u <= st.bound : u < st.bound);
         m = ballot(cand);
     }
 }
