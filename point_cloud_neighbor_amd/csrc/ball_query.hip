@@ -37,6 +37,7 @@
 namespace pointops {
 
 constexpr uint32_t kBqDone = 0xFFFFFFFFu;  // state: the query is complete
+constexpr int kXcds = 8;  // accelerator complex dies of the device, one L2 each
 
 // MODE: kBqPlain, kBqBudgeted or kBqResume (see BqBudget); a template
 // parameter, so the plain scan's loop carries none of the others' tests.
@@ -367,20 +368,33 @@ __global__ __launch_bounds__(256) void ball_query_superboxes_kernel(const float*
     }
 }
 
-template <int QW>
+template <int QW, bool STAGE>
 __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
     const float* __restrict__ query, const float* __restrict__ ref, int Q, int P, float r2,
     int K, float* __restrict__ out_d2, int64_t* __restrict__ out_idx,
     const float* __restrict__ box, int nblk, const float* __restrict__ sbox, int nsb, int budget,
     uint2* __restrict__ state, uint32_t* __restrict__ flag) {
     const int b = blockIdx.y;
-    const int row0 = blockIdx.x * QW;
+    // Workgroups go round-robin to the 8 XCDs, each with its own L2: XCD x
+    // takes the x-th contiguous run of query groups, so on a spatially
+    // sorted cloud its L2 holds only its region's references.
+    const int groups = (Q + QW - 1) / QW;
+    const int per_xcd = (groups + kXcds - 1) / kXcds;
+    const int group = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    if (group >= groups) return;
+    const int row0 = group * QW;
     const int lane = threadIdx.x;
     const float* qb = query + (size_t)b * Q * 3;
     const float* xb = ref + (size_t)b * P * 3;
     const float* bb = box + (size_t)b * nblk * kBoxFloats;
     const float* sbb = sbox + (size_t)b * nsb * kBoxFloats;
     const size_t out0 = ((size_t)b * Q + row0) * (size_t)K;
+    // STAGE (K <= 64): hits go to the wave's rows in LDS, and each row is
+    // written to HBM once at the end, in whole lines with its padding,
+    // instead of a few slots per block (a partial line is read before it is
+    // written).
+    __shared__ int32_t stage_j[STAGE ? QW : 1][kWave];
+    __shared__ float stage_s[STAGE ? QW : 1][kWave];
 
     float qx[QW], qy[QW], qz[QW];
     int cnt[QW];
@@ -486,8 +500,13 @@ __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
                     if (m) {
                         const int slot = cnt[i] + (int)lanes_below(m);
                         if (((m >> lane) & 1ull) && slot < K) {
-                            out_idx[out0 + (size_t)i * K + slot] = j;
-                            out_d2[out0 + (size_t)i * K + slot] = s;
+                            if constexpr (STAGE) {
+                                stage_j[i][slot] = j;
+                                stage_s[i][slot] = s;
+                            } else {
+                                out_idx[out0 + (size_t)i * K + slot] = j;
+                                out_d2[out0 + (size_t)i * K + slot] = s;
+                            }
                         }
                         cnt[i] += __popcll(m);
                     }
@@ -504,12 +523,27 @@ __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
     }
 
     bool left = false;
+    if constexpr (STAGE) {
+        // the rows' LDS stores (any lane) before the reads of every lane: one
+        // wave, whose LDS operations complete in order
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 #pragma unroll
     for (int i = 0; i < QW; ++i) {
         if (row0 + i < Q) {
-            for (int slot = cnt[i] + lane; slot < K; slot += kWave) {
-                out_idx[out0 + (size_t)i * K + slot] = -1;
-                out_d2[out0 + (size_t)i * K + slot] = 0.0f;
+            if constexpr (STAGE) {
+                if (lane < K) {  // lane = slot: hits, then (-1, +0.0) padding
+                    const bool hit = lane < cnt[i];
+                    out_idx[out0 + (size_t)i * K + lane] = hit ? (int64_t)stage_j[i][lane] : -1;
+                    out_d2[out0 + (size_t)i * K + lane] = hit ? stage_s[i][lane] : 0.0f;
+                }
+            } else {
+                for (int slot = cnt[i] + lane; slot < K; slot += kWave) {
+                    out_idx[out0 + (size_t)i * K + slot] = -1;
+                    out_d2[out0 + (size_t)i * K + slot] = 0.0f;
+                }
             }
             if (state && lane == 0) {
                 const bool open = stop_blk >= 0 && cnt[i] < K;
@@ -558,10 +592,15 @@ hipError_t launch_ball_query_culled(const float* query, const float* ref, int64_
     switch (qw) {
 #define POINTOPS_BQC_CASE(W)                                                                  \
     case W: {                                                                                 \
-        dim3 grid((unsigned)((Q + W - 1) / W), (unsigned)B);                                  \
-        hipLaunchKernelGGL(ball_query_cull_kernel<W>, grid, block, 0, stream, query, ref,     \
-                           (int)Q, (int)P, r2, (int)K, out_d2, out_idx, box, nblk, sbox, nsb, \
-                           budget, state, flag);                                              \
+        dim3 grid((unsigned)(((Q + W - 1) / W + kXcds - 1) / kXcds * kXcds), (unsigned)B);  \
+        if (K <= kWave)                                                                       \
+            hipLaunchKernelGGL((ball_query_cull_kernel<W, true>), grid, block, 0, stream,     \
+                               query, ref, (int)Q, (int)P, r2, (int)K, out_d2, out_idx, box,  \
+                               nblk, sbox, nsb, budget, state, flag);                         \
+        else                                                                                  \
+            hipLaunchKernelGGL((ball_query_cull_kernel<W, false>), grid, block, 0, stream,    \
+                               query, ref, (int)Q, (int)P, r2, (int)K, out_d2, out_idx, box,  \
+                               nblk, sbox, nsb, budget, state, flag);                         \
         break;                                                                                \
     }
         POINTOPS_BQC_CASE(1)
