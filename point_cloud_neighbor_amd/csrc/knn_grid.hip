@@ -605,14 +605,14 @@ __global__ __launch_bounds__(NW* kWave) void knn_grid_kernel(
 // independent.
 constexpr int kKgwWaves = 4;
 
-template <int QW>
+template <int QW, int KL>
 __global__ __launch_bounds__(kKgwWaves* kWave) void knn_grid_wave_kernel(
     const float4* __restrict__ sq, const float4* __restrict__ sr, int Q, int P, int k,
     const float* __restrict__ box, const float* __restrict__ sbox, int nblk, int nsb,
     const uint32_t* __restrict__ ref_start, const GridParams* __restrict__ gp, int L,
     float* __restrict__ out_dist, int64_t* __restrict__ out_idx, int squared,
     const int64_t* __restrict__ clouds) {
-    __shared__ uint64_t cbuf[kKgwWaves][QW][kKwBuf];
+    __shared__ uint64_t cbuf[kKgwWaves][QW][kWave - KL];
     const int b = blockIdx.y;
     int Qb = Q, Pb = P, nbb = nblk, nsbb = nsb;
     int64_t orow0 = (int64_t)b * Q, ibase = 0;
@@ -636,13 +636,16 @@ __global__ __launch_bounds__(kKgwWaves* kWave) void knn_grid_wave_kernel(
     const int64_t C = (int64_t)1 << (3 * L);
 
     // 1. Per query, the kWave references around its own grid position. A
-    //    query past the cloud's last (QW > 1) takes bound 0: nothing enters.
+    //    query slot past the cloud's last (QW > 1, odd count) repeats the
+    //    first query; it opens no box and takes no candidate.
     float4 q[QW];
     int loc0[QW];
+    bool real[QW];
     KwQuery st[QW];
 #pragma unroll
     for (int h = 0; h < QW; ++h) {
         const bool valid = q0 + h < Qb;
+        real[h] = valid;
         q[h] = sq[(size_t)b * Q + (valid ? q0 + h : q0)];
         const uint32_t code = cell_code(gp[b], q[h].x, q[h].y, q[h].z, L);
         const int pos = (int)ref_start[(int64_t)b * C + code];
@@ -660,7 +663,7 @@ __global__ __launch_bounds__(kKgwWaves* kWave) void knn_grid_wave_kernel(
         bool any = false;
 #pragma unroll
         for (int h = 0; h < QW; ++h)
-            any |= f2u(box_bound(o, q[h].x, q[h].y, q[h].z)) <= st[h].bound;
+            any |= real[h] && f2u(box_bound(o, q[h].x, q[h].y, q[h].z)) <= st[h].bound;
         return any;
     };
 
@@ -691,11 +694,11 @@ __global__ __launch_bounds__(kKgwWaves* kWave) void knn_grid_wave_kernel(
                 for (int h = 0; h < QW; ++h) {
                     bool cand = false;
                     uint32_t u = 0u;
-                    if (in && (uint32_t)(j - loc0[h]) >= (uint32_t)nloc) {
+                    if (real[h] && in && (uint32_t)(j - loc0[h]) >= (uint32_t)nloc) {
                         u = f2u(s32(q[h].x, q[h].y, q[h].z, p.x, p.y, p.z));
                         cand = u <= st[h].bound;
                     }
-                    kw_offer<true>(st[h], cand, u, __float_as_int(p.w), lane, k);
+                    kw_offer<true, KL>(st[h], cand, u, __float_as_int(p.w), lane, k);
                 }
             }
         }
@@ -706,7 +709,7 @@ __global__ __launch_bounds__(kKgwWaves* kWave) void knn_grid_wave_kernel(
 #pragma unroll
     for (int h = 0; h < QW; ++h) {
         if (q0 + h >= Qb) break;
-        if (st[h].cnt > 0) kw_merge(st[h], lane, k);
+        if (st[h].cnt > 0) kw_merge<KL>(st[h], lane, k);
         if (lane < k) {
             const uint64_t e = st[h].list;
             const bool empty = e == kKwEmpty;
@@ -838,14 +841,17 @@ hipError_t launch_knn_grid(const float* query, const float* ref, int64_t B, int6
     if (nw <= 0) {  // 0: one query per wave, -2: two
         const int qw = nw == -2 ? 2 : 1;
         const dim3 grid((unsigned)((Q + kKgwWaves * qw - 1) / (kKgwWaves * qw)), (unsigned)B);
-        if (qw == 2)
-            hipLaunchKernelGGL(knn_grid_wave_kernel<2>, grid, dim3(kKgwWaves * kWave), 0, stream,
-                               v.squery, v.sref, (int)Q, (int)P, (int)k, v.box, v.sbox, v.nblk,
-                               v.nsb, v.ref_start, v.gp, v.L, out_dist, out_idx, squared, clouds);
-        else
-            hipLaunchKernelGGL(knn_grid_wave_kernel<1>, grid, dim3(kKgwWaves * kWave), 0, stream,
-                               v.squery, v.sref, (int)Q, (int)P, (int)k, v.box, v.sbox, v.nblk,
-                               v.nsb, v.ref_start, v.gp, v.L, out_dist, out_idx, squared, clouds);
+        // k <= 16: a 16-lane list and 48 buffered candidates per merge
+#define POINTOPS_KGW(QWV, KLV)                                                                \
+    hipLaunchKernelGGL((knn_grid_wave_kernel<QWV, KLV>), grid, dim3(kKgwWaves * kWave), 0,     \
+                       stream, v.squery, v.sref, (int)Q, (int)P, (int)k, v.box, v.sbox, v.nblk, \
+                       v.nsb, v.ref_start, v.gp, v.L, out_dist, out_idx, squared, clouds)
+        if (qw == 2) {
+            if (k <= 16) POINTOPS_KGW(2, 16); else POINTOPS_KGW(2, 32);
+        } else {
+            if (k <= 16) POINTOPS_KGW(1, 16); else POINTOPS_KGW(1, 32);
+        }
+#undef POINTOPS_KGW
         return hipGetLastError();
     }
 #define POINTOPS_CHECK(x) \
