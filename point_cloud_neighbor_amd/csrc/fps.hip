@@ -274,6 +274,7 @@ __global__ __launch_bounds__(BLOCK) void fps_kernel(
 // communication is batched.
 
 constexpr int kFpsMaxBatch = 256;  // centres certified per batch at most
+constexpr int kCertBlock = 4;       // certification steps between exit tests
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 
 // Key order: larger m first, then smaller index.
@@ -334,13 +335,13 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     const float* __restrict__ xyz, int N, int M, int start_idx, int G, int slice, int RG,
     int64_t* __restrict__ out_idx, float* __restrict__ out_xyz, uint64_t* __restrict__ words,
     int stride, uint32_t* __restrict__ status, uint32_t spin_limit,
-    const int64_t* __restrict__ seg, int nseg, int solo) {
+    const int64_t* __restrict__ seg, int nseg) {
     constexpr int NW = BLOCK / kWave;
     // Wave 0 certifies; the others hold points. Waves go round-robin over the
-    // 4 SIMDs of a CU, so wave 0 shares its SIMD with waves 4, 8, 12. With
-    // `solo` those waves hold no points and wait at the barriers, so no other
-    // wave of the workgroup issues on the certifying wave's SIMD; otherwise
-    // they hold points too and wave 0 runs at a higher priority.
+    // 4 SIMDs of a CU, so wave 0 shares its SIMD with waves 4, 8, 12, which
+    // hold points too; wave 0 runs at a higher priority. (Leaving those three
+    // waves without points, so nothing else issues on wave 0's SIMD, measured
+    // slower: 1.23 against 1.17 ms on the 100k-point cloud).
     static_assert(NW % 4 == 0 && 2 * (NW - 1) <= kWave, "wave count");
     // Certified centres of the batch: x, y, z bits and the point's index. An
     // entry is written before the count that includes it (LDS performs one
@@ -393,9 +394,9 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     const float* xb = xyz + xrow0 * 3;
     const int lo = g * slice;
     const int cnt = min(N, lo + slice) - lo;  // >= 1
-    const int NPW = solo ? NW - NW / 4 : NW - 1;
-    const bool point_wave = solo ? (wave & 3) != 0 : wave != 0;
-    const int pw = solo ? wave - wave / 4 - 1 : wave - 1;  // index among the point waves
+    const int NPW = NW - 1;
+    const bool point_wave = wave != 0;
+    const int pw = wave - 1;  // index among the point waves
     const int u = pw * kWave + lane;          // point-thread id
     const int wbase = pw * kWave * PPT;       // first slice position of this wave
 
@@ -755,11 +756,22 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
             // come first in lane-major order; the other slots hold key 0,
             // which the min update keeps at 0, so they can win only when every
             // live key is 0, and then lane 0, slot 0 (live) is the first entry
-            // holding the maximum. So no slot needs a validity mask, the index
-            // is read only when the key reaches the bound, and the winning lane
-            // publishes its own entry and the count (the others write their
-            // sink slots, so no branch splits the wave). With two slots each lane offers its
-            // better one, slot 0 on ties (the smaller index).
+            // holding the maximum. So no slot needs a validity mask, and the
+            // winning lane publishes its own entry (the others write their
+            // sink slots, so no branch splits the wave). With two slots each
+            // lane offers its better one, slot 0 on ties (the smaller index).
+            //
+            // Steps go in blocks of kCertBlock with no exit test inside: a
+            // step's test (key above the bound's, or the batch's first centre)
+            // is only recorded, and each step writes its entry and folds
+            // anyway. After the block the count takes the leading steps that
+            // passed; the entries past it are never read, and the candidates'
+            // keys are not used after the batch, so the steps past a failure
+            // need no undoing. (A test inside the loop costs a branch per
+            // step, which the loop's latency chain pays in full.) A key equal
+            // to the bound's can still pass by its index: a block that stops
+            // there rewinds to its start, replays the steps that passed and
+            // goes on one step at a time with the full test.
             auto certify_fast = [&](auto c_) {
                 constexpr int C = decltype(c_)::value;
                 constexpr int S1 = CPL > 1 ? 1 : 0;
@@ -768,39 +780,70 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 const uint32_t x1 = cxv[S1], y1 = cyv[S1], z1 = czv[S1], j1 = cj[S1];
                 const int limit = min(M - t0, kFpsMaxBatch);
                 int nc = 0;
-                // keys at or below floor_m take the slow path: the bound check,
-                // or the exit once the batch is full (the first centre is
-                // certified whatever its key)
-                uint32_t floor_m = 0;
+                auto fold = [&](float X, float Y, float Z) {
+                    m0 = min(m0, f2u(s32(X, Y, Z, u2f(x0), u2f(y0), u2f(z0))));
+                    if (C == 2) m1 = min(m1, f2u(s32(X, Y, Z, u2f(x1), u2f(y1), u2f(z1))));
+                };
                 // the candidates' LDS loads are complete here, so the loop's
                 // only LDS operations are its own stores, which need no wait
                 __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                bool tied = false;
                 while (true) {
+                    const uint32_t r0 = m0, r1 = m1;  // the block's start
+                    uint32_t fail = 0, tie = 0;
+#pragma unroll
+                    for (int s = 0; s < kCertBlock; ++s) {
+                        const bool second = C == 2 && m1 > m0;
+                        const uint32_t lm = second ? m1 : m0;
+                        const uint32_t wx = second ? x1 : x0, wy = second ? y1 : y0,
+                                       wz = second ? z1 : z0, wj = second ? j1 : j0;
+                        const uint32_t mx = wave_max_u32(lm);
+                        const int kl = (int)__builtin_ctzll(ballot(lm == mx));
+                        fail |= (uint32_t)(mx <= beta_m) << s;
+                        tie |= (uint32_t)(mx == beta_m) << s;
+                        const bool win = lane == kl && nc + s < limit;
+                        *(win ? &cen[nc + s] : &sink_rec[lane]) = make_uint4(wx, wy, wz, wj);
+                        fold(u2f(lane_value(wx, kl)), u2f(lane_value(wy, kl)),
+                             u2f(lane_value(wz, kl)));
+                    }
+                    if (nc == 0) fail &= ~1u;  // the batch's first centre: the cloud's largest key
+                    const int room = limit - nc;
+                    if (room < kCertBlock) fail |= ~0u << room;
+                    const int pass = fail ? (int)__builtin_ctz(fail) : kCertBlock;
+                    nc += pass;
+                    __asm__ __volatile__("" ::: "memory");  // entries before the count
+                    __hip_atomic_store(lane == 0 ? &cen_count : &sink_cnt[lane], nc,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    if (pass == kCertBlock) continue;
+                    tied = pass < room && ((tie >> pass) & 1u);
+                    if (tied) {
+                        m0 = r0;
+                        m1 = r1;
+                        for (int i = nc - pass; i < nc; ++i) {
+                            const uint4 c = cen[i];
+                            fold(u2f(c.x), u2f(c.y), u2f(c.z));
+                        }
+                    }
+                    break;
+                }
+                // one step at a time with the full test: a key equal to the
+                // bound's passes when its index is smaller
+                while (tied && nc < limit) {
                     const bool second = C == 2 && m1 > m0;
                     const uint32_t lm = second ? m1 : m0;
                     const uint32_t wx = second ? x1 : x0, wy = second ? y1 : y0,
                                    wz = second ? z1 : z0, wj = second ? j1 : j0;
                     const uint32_t mx = wave_max_u32(lm);
                     const int kl = (int)__builtin_ctzll(ballot(lm == mx));
-                    if (mx <= floor_m) {
-                        if (nc >= limit) break;
-                        // certified only while the key exceeds the bound
-                        const uint32_t kj = lane_value(wj, kl);
-                        if (nc > 0 && (mx < beta_m || kj >= beta_j)) break;
-                    }
-                    {
-                        const bool win = lane == kl;
-                        *(win ? &cen[nc] : &sink_rec[lane]) = make_uint4(wx, wy, wz, wj);
-                        __asm__ __volatile__("" ::: "memory");  // entry before count
-                        __hip_atomic_store(win ? &cen_count : &sink_cnt[lane], nc + 1,
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                    }
-                    const float X = u2f(lane_value(wx, kl)), Y = u2f(lane_value(wy, kl)),
-                                Z = u2f(lane_value(wz, kl));
+                    if (!key_gt(mx, lane_value(wj, kl), beta_m, beta_j)) break;
+                    const bool win = lane == kl;
+                    *(win ? &cen[nc] : &sink_rec[lane]) = make_uint4(wx, wy, wz, wj);
+                    __asm__ __volatile__("" ::: "memory");  // entry before count
+                    __hip_atomic_store(win ? &cen_count : &sink_cnt[lane], nc + 1,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                     ++nc;
-                    floor_m = nc >= limit ? 0xFFFFFFFFu : beta_m;
-                    m0 = min(m0, f2u(s32(X, Y, Z, u2f(x0), u2f(y0), u2f(z0))));
-                    if (C == 2) m1 = min(m1, f2u(s32(X, Y, Z, u2f(x1), u2f(y1), u2f(z1))));
+                    fold(u2f(lane_value(wx, kl)), u2f(lane_value(wy, kl)),
+                         u2f(lane_value(wz, kl)));
                 }
                 t = t0 + nc;
             };
@@ -898,16 +941,7 @@ int fps_batch_ppt_round(int ppt) {
 
 int fps_batch_stride(int rg) { return 3 * rg + 2; }  // words per workgroup
 
-// The certifying wave alone on its SIMD (waves 4, 8, 12 hold no points).
-bool fps_batch_solo() {
-    const char* v = getenv("POINTOPS_FPS_SOLO");
-    return v && v[0] == '1';
-}
-
-int fps_batch_point_waves(int block) {
-    const int nw = block / kWave;
-    return fps_batch_solo() ? nw - nw / 4 : nw - 1;
-}
+int fps_batch_point_waves(int block) { return block / kWave - 1; }
 
 size_t fps_batch_workspace_bytes(int64_t B, int64_t G, int rg) {
     return G > 1 ? 256 + (size_t)B * 2 * (size_t)G * fps_batch_stride(rg) * sizeof(uint64_t) : 256;
@@ -976,7 +1010,7 @@ hipError_t launch_fps_batch(const float* xyz, int64_t B, int64_t N, int64_t M, i
         hipLaunchKernelGGL((fps_batch_kernel<C::PPT, C::BLOCK, C::CPL>), dim3(grid),
                            dim3(C::BLOCK), lds, stream, xyz, (int)N, (int)M, (int)start_idx, G,
                            slice, rg, out_idx, out_xyz, words, fps_batch_stride(rg), status,
-                           spin_limit, seg, nseg, (int)fps_batch_solo());
+                           spin_limit, seg, nseg);
         e = hipGetLastError();
     });
     return e;

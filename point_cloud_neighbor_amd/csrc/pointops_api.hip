@@ -192,12 +192,15 @@ int knn_grid_nw(int64_t k, int kcap, int64_t queries, int64_t refs) {
 // one device-full of waves; at most 8 (measured faster than 16 on 100k x 100k:
 // the shorter waves balance better).
 // Up to 256 candidates per cloud (four slots per lane of the certifying wave),
-// at most the workgroup's 2 * npw reports.
+// at most the workgroup's 2 * npw reports; POINTOPS_FPS_RG overrides it up to
+// 512 candidates (eight slots per lane, the most the kernel holds).
 int fps_batch_rg(int64_t G, int npw) {
     const long env = env_long("POINTOPS_FPS_RG", 0);
+    const int64_t g = std::max<int64_t>(G, 1);
     const int64_t total = G > 128 ? 512 : 256;  // candidates per exchange in all
-    const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(2 * npw, total / std::max<int64_t>(G, 1)));
-    return (int)(env > 0 ? std::min<int64_t>(env, cap) : cap);
+    const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(2 * npw, total / g));
+    const int64_t most = std::max<int64_t>(1, std::min<int64_t>(2 * npw, 512 / g));
+    return (int)(env > 0 ? std::min<int64_t>(env, most) : cap);
 }
 
 // Ball Query with a workspace: the culled index-order scan, and for clouds of
