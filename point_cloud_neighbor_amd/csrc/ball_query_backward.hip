@@ -85,14 +85,20 @@ __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_kernel
 // reach device memory: on a spatially sorted cloud neighbouring rows select
 // mostly the same references, so one set of atomics per distinct reference of
 // the tile replaces one per selected slot. A workgroup takes `tile` rows (its
-// waves a row at a time) and adds each term into an LDS table keyed by the
-// reference's flat row b * P + j (open addressing, linear probing, at most
-// kBwdProbes probes; a term that finds no slot goes straight to device
-// memory, so the result never depends on the table's size); after a barrier
-// the table's entries go out with float atomics. The query gradients are the
-// fixed DPP tree, as above.
+// waves a row at a time) and adds each term into LDS, keyed by the
+// reference's flat row b * P + j, in two levels: a direct window of kBwdWin
+// consecutive flat rows placed on the data (around the middle row's middle
+// selection: on a sorted cloud queried by its own points, about 85% of the
+// terms), with a bit per entry marking those touched; and for the rest a
+// table with open addressing (linear probing, at most kBwdProbes probes; a
+// term that finds no slot goes straight to device memory, so the result
+// never depends on either size). After a barrier the touched entries go out
+// with float atomics. The window's adds need no returned value, unlike the
+// table's claim of a slot: on the sorted 100k cloud, K = 64, 0.166 -> 0.146
+// ms. The query gradients are the fixed DPP tree, as above.
 constexpr int kBwdTable = 2048;
 constexpr int kBwdProbes = 64;  // probes before a term goes straight to device memory
+constexpr int kBwdWin = 2048;   // window entries
 
 __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_tiled_kernel(
     const float* __restrict__ query, const float* __restrict__ ref,
@@ -100,6 +106,8 @@ __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_tiled_
     int P, int K, int tile, float* __restrict__ grad_query, float* __restrict__ grad_ref) {
     __shared__ int key[kBwdTable];
     __shared__ float ax[kBwdTable], ay[kBwdTable], az[kBwdTable];
+    __shared__ float wx[kBwdWin], wy[kBwdWin], wz[kBwdWin];
+    __shared__ uint32_t wbits[kBwdWin / 32];
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
     const int wave = uniform((int)(tid / kWave));
@@ -107,11 +115,30 @@ __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_tiled_
         key[i] = -1;
         ax[i] = ay[i] = az[i] = 0.0f;
     }
+    for (int i = tid; i < kBwdWin; i += kBqBwdWaves * kWave) wx[i] = wy[i] = wz[i] = 0.0f;
+    for (int i = tid; i < kBwdWin / 32; i += kBqBwdWaves * kWave) wbits[i] = 0u;
+    const int64_t r0 = (int64_t)blockIdx.x * tile;  // < rows
+    // the window: centred on the middle row's middle selection (else its
+    // first); none when neither is a reference
+    int64_t wbase = -(int64_t)2 * kBwdWin;
+    {
+        const int64_t rm = min(r0 + tile / 2, rows - 1);
+        int64_t j = idx[rm * K + K / 2];
+        if (j < 0 || j >= P) j = idx[rm * K];
+        if (j >= 0 && j < P) wbase = (rm / Q) * P + j - kBwdWin / 2;
+    }
     __syncthreads();
-    const int64_t r0 = (int64_t)blockIdx.x * tile;
-    // Adds a term to the table (a free or matching slot within the table,
-    // which holds at most half its size of distinct keys).
+    // Adds a term: into the window, or the table (a free or matching slot
+    // within the table, which holds at most half its size of distinct keys).
     auto add_ref = [&](int flat, float tx, float ty, float tz) {
+        const int64_t wi = (int64_t)flat - wbase;
+        if (wi >= 0 && wi < kBwdWin) {
+            atomicAdd(&wx[wi], -tx);
+            atomicAdd(&wy[wi], -ty);
+            atomicAdd(&wz[wi], -tz);
+            atomicOr(&wbits[wi >> 5], 1u << (wi & 31));
+            return;
+        }
         uint32_t h = ((uint32_t)flat * 2654435761u) >> 21;  // 11 bits: kBwdTable slots
         for (int probe = 0; probe < kBwdProbes; ++probe) {
             const int old = atomicCAS(&key[h], -1, flat);
@@ -166,6 +193,14 @@ __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_tiled_
     }
     if (!grad_ref) return;
     __syncthreads();
+    for (int i = tid; i < kBwdWin; i += kBqBwdWaves * kWave) {
+        if ((wbits[i >> 5] >> (i & 31)) & 1u) {  // touched: wbase + i is a reference row
+            float* o = grad_ref + (size_t)(wbase + i) * 3;
+            unsafeAtomicAdd(o + 0, wx[i]);
+            unsafeAtomicAdd(o + 1, wy[i]);
+            unsafeAtomicAdd(o + 2, wz[i]);
+        }
+    }
     for (int i = tid; i < kBwdTable; i += kBqBwdWaves * kWave) {
         const int flat = key[i];
         if (flat >= 0) {

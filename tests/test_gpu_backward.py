@@ -95,6 +95,31 @@ def test_backward_sorted_workload_subset(gpu, oracle_mod):
     check_backward(gpu, oracle_mod, q, x, idx, g, "sorted_bq subset")
 
 
+def test_backward_sorted_workload_whole_output(gpu, oracle_mod):
+    """Full size as the benchmark runs it (every point of the sorted cloud a
+    query): both gradients of every row and every reference against the
+    oracle. Neighbouring rows select neighbouring references here, so most
+    reference terms go through the per-tile window, the others through the
+    table."""
+    wl = W.workload("sorted_bq")
+    x = wl.xyz
+    _, idx = oracle_mod.ball_query(x, x, wl.bq_radius, wl.bq_k, threads=8)
+    g = seeded_grad(9, idx.shape)
+    check_backward(gpu, oracle_mod, x, x, idx, g, "sorted_bq whole")
+
+
+@pytest.mark.parametrize("tile", ["4", "37", "1024"])
+def test_backward_tile_sizes(gpu, oracle_mod, monkeypatch, tile):
+    """Rows per workgroup forced to the extremes (and an odd size) on a sorted
+    self-query, where the window and the table both take terms."""
+    monkeypatch.setenv("POINTOPS_BQ_BWD_TILE", tile)
+    wl = W.workload("sorted_bq")
+    x = wl.xyz[:, :20000].copy()
+    _, idx = oracle_mod.ball_query(x, x, 0.08, 64, threads=8)
+    g = seeded_grad(10, idx.shape)
+    check_backward(gpu, oracle_mod, x, x, idx, g, f"tile {tile}")
+
+
 def test_backward_sorted_workload_full(gpu, oracle_mod):
     """Full size (every point a query, as the benchmark runs it): grad_query
     on sampled row blocks against the oracle (a row's gradient depends only on
