@@ -251,6 +251,9 @@ int pointops_ball_query(const float *query, const float *ref, int64_t B, int64_t
  *   grad_dist2    G, (B, Q, K) float32, device.
  *   grad_query    (B, Q, 3) float32, device, overwritten; or NULL to skip.
  *   grad_ref      (B, P, 3) float32, device, overwritten; or NULL to skip.
+ *   workspace     NULL, or pointops_ball_query_backward_workspace_bytes()
+ *                 bytes of device memory (smaller: INVALID_ARGUMENT); used
+ *                 only when query == ref and Q == P, ignored otherwise.
  * float32 arithmetic: each term is 2 * (G * fl32(q - x)); a query's terms are
  * summed in a fixed order (deterministic); a reference's terms are added with
  * atomics in no fixed order, so grad_ref may differ between runs in the last
@@ -258,7 +261,19 @@ int pointops_ball_query(const float *query, const float *ref, int64_t B, int64_t
  */
 int pointops_ball_query_backward(const float *query, const float *ref, const int64_t *idx,
                                  const float *grad_dist2, int64_t B, int64_t Q, int64_t P,
-                                 int64_t K, float *grad_query, float *grad_ref, void *stream);
+                                 int64_t K, float *grad_query, float *grad_ref,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of the Ball Query backward's optional workspace (device memory,
+ * caller-owned): used only when the query and reference buffers are the same
+ * (query == ref, Q == P: a cloud queried by its own points). Then each tile
+ * of rows writes its partial reference sums for a fixed window of reference
+ * rows there, and a second kernel adds them, in tile order, in place of
+ * most of the float atomics. 0 when Q != P or nothing to do. Reads
+ * POINTOPS_BQ_BWD_TILE like the call. Allocation-free.
+ */
+size_t pointops_ball_query_backward_workspace_bytes(int64_t B, int64_t Q, int64_t P, int64_t K);
 
 /*
  * Ragged batches: clouds of different sizes in one call.
@@ -458,7 +473,7 @@ const char *pointops_status_string(int status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char *pointops_last_error(void);
 
-/* Library ABI version: 4. */
+/* Library ABI version: 5. */
 int pointops_abi_version(void);
 
 #ifdef __cplusplus

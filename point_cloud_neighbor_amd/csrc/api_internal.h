@@ -54,8 +54,9 @@ hipError_t launch_knn(const float*, const float*, int64_t, int64_t, int64_t, int
 hipError_t launch_knn_wave(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
                            int64_t*, int, int, const int64_t*, int, int64_t, int, hipStream_t);
 hipError_t launch_ball_query_backward(const float*, const float*, const int64_t*, const float*,
-                                      int64_t, int64_t, int64_t, int64_t, float*, float*,
+                                      int64_t, int64_t, int64_t, int64_t, float*, float*, void*,
                                       hipStream_t);
+size_t bq_backward_workspace_bytes(int64_t B, int64_t Q, int64_t K);
 
 namespace api {
 

@@ -96,6 +96,15 @@ __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_kernel
 // with float atomics. The window's adds need no returned value, unlike the
 // table's claim of a slot: on the sorted 100k cloud, K = 64, 0.166 -> 0.146
 // ms. The query gradients are the fixed DPP tree, as above.
+//
+// A cloud queried by its own points (the query and reference buffers are one,
+// Q = P) with a workspace: the window of tile t is fixed by its position,
+// flat rows [t * tile + tile / 2 - kBwdWin / 2, ... + kBwdWin), and is written
+// whole to the workspace (its partial sums, zeros where untouched) instead of
+// going out with atomics; a second kernel adds, for each reference, the
+// partials of the windows that cover it in tile order. Only the table's
+// entries still use atomics. (A reference is covered by kBwdWin / tile
+// windows, and on a sorted cloud most of its terms are in them.)
 constexpr int kBwdTable = 2048;
 constexpr int kBwdProbes = 64;  // probes before a term goes straight to device memory
 constexpr int kBwdWin = 2048;   // window entries
@@ -103,7 +112,8 @@ constexpr int kBwdWin = 2048;   // window entries
 __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_tiled_kernel(
     const float* __restrict__ query, const float* __restrict__ ref,
     const int64_t* __restrict__ idx, const float* __restrict__ grad, int64_t rows, int Q,
-    int P, int K, int tile, float* __restrict__ grad_query, float* __restrict__ grad_ref) {
+    int P, int K, int tile, float* __restrict__ grad_query, float* __restrict__ grad_ref,
+    float* __restrict__ part) {
     __shared__ int key[kBwdTable];
     __shared__ float ax[kBwdTable], ay[kBwdTable], az[kBwdTable];
     __shared__ float wx[kBwdWin], wy[kBwdWin], wz[kBwdWin];
@@ -118,10 +128,13 @@ __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_tiled_
     for (int i = tid; i < kBwdWin; i += kBqBwdWaves * kWave) wx[i] = wy[i] = wz[i] = 0.0f;
     for (int i = tid; i < kBwdWin / 32; i += kBqBwdWaves * kWave) wbits[i] = 0u;
     const int64_t r0 = (int64_t)blockIdx.x * tile;  // < rows
-    // the window: centred on the middle row's middle selection (else its
-    // first); none when neither is a reference
+    // the window: fixed by the tile's position (partials to `part`), or
+    // centred on the middle row's middle selection (else its first; none when
+    // neither is a reference)
     int64_t wbase = -(int64_t)2 * kBwdWin;
-    {
+    if (part) {
+        wbase = r0 + tile / 2 - kBwdWin / 2;
+    } else {
         const int64_t rm = min(r0 + tile / 2, rows - 1);
         int64_t j = idx[rm * K + K / 2];
         if (j < 0 || j >= P) j = idx[rm * K];
@@ -136,7 +149,7 @@ __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_tiled_
             atomicAdd(&wx[wi], -tx);
             atomicAdd(&wy[wi], -ty);
             atomicAdd(&wz[wi], -tz);
-            atomicOr(&wbits[wi >> 5], 1u << (wi & 31));
+            if (!part) atomicOr(&wbits[wi >> 5], 1u << (wi & 31));
             return;
         }
         uint32_t h = ((uint32_t)flat * 2654435761u) >> 21;  // 11 bits: kBwdTable slots
@@ -193,7 +206,15 @@ __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_tiled_
     }
     if (!grad_ref) return;
     __syncthreads();
-    for (int i = tid; i < kBwdWin; i += kBqBwdWaves * kWave) {
+    if (part) {  // the whole window, x then y then z planes
+        float* pt = part + (size_t)blockIdx.x * 3 * kBwdWin;
+        for (int i = tid; i < kBwdWin; i += kBqBwdWaves * kWave) {
+            pt[i] = wx[i];
+            pt[kBwdWin + i] = wy[i];
+            pt[2 * kBwdWin + i] = wz[i];
+        }
+    }
+    for (int i = tid; i < kBwdWin && !part; i += kBqBwdWaves * kWave) {
         if ((wbits[i >> 5] >> (i & 31)) & 1u) {  // touched: wbase + i is a reference row
             float* o = grad_ref + (size_t)(wbase + i) * 3;
             unsafeAtomicAdd(o + 0, wx[i]);
@@ -212,6 +233,31 @@ __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_tiled_
     }
 }
 
+// Adds to each reference row f its partials from the fixed windows that cover
+// it (tile t covers [t * tile + tile / 2 - kBwdWin / 2, ... + kBwdWin)), in
+// tile order; each row has one thread, so no atomics.
+__global__ void ball_query_backward_merge_kernel(const float* __restrict__ part, int64_t ntiles,
+                                                 int tile, int64_t nref,
+                                                 float* __restrict__ grad_ref) {
+    for (int64_t f = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; f < nref;
+         f += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t lo_num = f - kBwdWin / 2 - tile / 2 + 1;  // t >= ceil(lo_num / tile)
+        const int64_t t_lo = lo_num <= 0 ? 0 : (lo_num + tile - 1) / tile;
+        const int64_t t_hi = min(ntiles - 1, (f + kBwdWin / 2 - tile / 2) / tile);
+        float sx = 0.f, sy = 0.f, sz = 0.f;
+        for (int64_t t = t_lo; t <= t_hi; ++t) {
+            const int64_t i = f - (t * tile + tile / 2 - kBwdWin / 2);  // in [0, kBwdWin)
+            const float* pt = part + (size_t)t * 3 * kBwdWin;
+            sx += pt[i];
+            sy += pt[kBwdWin + i];
+            sz += pt[2 * kBwdWin + i];
+        }
+        grad_ref[3 * f + 0] += sx;
+        grad_ref[3 * f + 1] += sy;
+        grad_ref[3 * f + 2] += sz;
+    }
+}
+
 __global__ void zero_f32_kernel(float* __restrict__ p, size_t n) {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
          i += (size_t)gridDim.x * blockDim.x)
@@ -227,28 +273,50 @@ hipError_t launch_zero_f32(float* p, size_t n, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Rows per tile: about 8192 selected slots (128 rows at K = 64; the sorted
+// 100k workload, rows per tile 16 / 32 / 64 / 128 / 256: 0.224 / 0.185 /
+// 0.170 / 0.166 / 0.163 ms): a sorted cloud's tile selects a few hundred
+// distinct references; a tile with more than the table takes sends the excess
+// straight out, so any shape is exact. POINTOPS_BQ_BWD_TILE sets it.
+int64_t bq_backward_tile(int64_t K) {
+    const char* te = getenv("POINTOPS_BQ_BWD_TILE");
+    int64_t tile = std::min<int64_t>(128, std::max<int64_t>(kBqBwdWaves, 8192 / std::max<int64_t>(K, 1)));
+    if (te && atol(te) >= kBqBwdWaves && atol(te) <= 1024) tile = atol(te);
+    return tile;
+}
+
+// Workspace of the self-query mode: one window of partials (3 planes) per tile.
+size_t bq_backward_workspace_bytes(int64_t B, int64_t Q, int64_t K) {
+    const int64_t tile = bq_backward_tile(K);
+    const int64_t ntiles = (B * Q + tile - 1) / tile;
+    return (size_t)ntiles * 3 * kBwdWin * sizeof(float);
+}
+
 hipError_t launch_ball_query_backward(const float* query, const float* ref, const int64_t* idx,
                                       const float* grad, int64_t B, int64_t Q, int64_t P,
                                       int64_t K, float* grad_query, float* grad_ref,
-                                      hipStream_t stream) {
+                                      void* workspace, hipStream_t stream) {
     if (grad_ref && B * P > 0) {
         hipError_t e = launch_zero_f32(grad_ref, (size_t)B * P * 3, stream);
         if (e != hipSuccess) return e;
     }
     const int64_t rows = B * Q;
-    // tiles of about 8192 selected slots (128 rows at K = 64; the sorted 100k
-    // workload, rows per tile 16 / 32 / 64 / 128 / 256: 0.224 / 0.185 / 0.170
-    // / 0.166 / 0.163 ms): a sorted cloud's tile selects a few hundred
-    // distinct references; a tile with more than the table takes sends the
-    // excess straight out, so any shape is exact
-    const char* te = getenv("POINTOPS_BQ_BWD_TILE");
-    int64_t tile = std::min<int64_t>(128, std::max<int64_t>(kBqBwdWaves, 8192 / std::max<int64_t>(K, 1)));
-    if (te && atol(te) >= kBqBwdWaves && atol(te) <= 1024) tile = atol(te);
+    const int64_t tile = bq_backward_tile(K);
     if (B * P < ((int64_t)1 << 31)) {
         const unsigned blocks = (unsigned)((rows + tile - 1) / tile);
+        // the self-query mode: the caller's workspace holds the windows
+        float* part = workspace && grad_ref && query == ref && Q == P && rows > 0
+                          ? (float*)workspace
+                          : nullptr;
         hipLaunchKernelGGL(ball_query_backward_tiled_kernel, dim3(blocks),
                            dim3(kBqBwdWaves * kWave), 0, stream, query, ref, idx, grad, rows,
-                           (int)Q, (int)P, (int)K, (int)tile, grad_query, grad_ref);
+                           (int)Q, (int)P, (int)K, (int)tile, grad_query, grad_ref, part);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || !part) return e;
+        const int64_t nref = B * P;
+        hipLaunchKernelGGL(ball_query_backward_merge_kernel,
+                           dim3((unsigned)std::min<int64_t>((nref + 255) / 256, 8192)), dim3(256),
+                           0, stream, part, (int64_t)blocks, (int)tile, nref, grad_ref);
         return hipGetLastError();
     }
     const unsigned blocks = (unsigned)((rows + kBqBwdWaves - 1) / kBqBwdWaves);

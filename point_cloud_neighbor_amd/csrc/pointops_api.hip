@@ -418,7 +418,7 @@ using namespace pointops::api;
 
 extern "C" {
 
-int pointops_abi_version(void) { return 4; }
+int pointops_abi_version(void) { return 5; }
 
 const char* pointops_status_string(int status) {
     switch (status) {
@@ -663,10 +663,17 @@ int pointops_ball_query(const float* query, const float* ref, int64_t B, int64_t
 
 }  // extern "C"
 
+extern "C" size_t pointops_ball_query_backward_workspace_bytes(int64_t B, int64_t Q, int64_t P,
+                                                              int64_t K) {
+    if (B <= 0 || Q <= 0 || K < 1 || Q != P) return 0;
+    return pointops::bq_backward_workspace_bytes(B, Q, K);
+}
+
 extern "C" int pointops_ball_query_backward(const float* query, const float* ref,
                                             const int64_t* idx, const float* grad_dist2,
                                             int64_t B, int64_t Q, int64_t P, int64_t K,
-                                            float* grad_query, float* grad_ref, void* stream) {
+                                            float* grad_query, float* grad_ref, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     if (B < 0 || Q < 0 || P < 0) return fail(POINTOPS_INVALID_ARGUMENT, "negative size");
     if (K < 1) return fail(POINTOPS_INVALID_ARGUMENT, "K must be >= 1");
@@ -679,11 +686,19 @@ extern "C" int pointops_ball_query_backward(const float* query, const float* ref
     if ((rows && (!query || !idx || !grad_dist2 || (!ref && P > 0))) ||
         (grad_ref && B * P > 0 && !ref))
         return fail(POINTOPS_INVALID_ARGUMENT, "null pointer");
+    // the workspace serves only a cloud queried by its own points
+    const bool self = rows && query == ref && Q == P;
+    if (workspace && self) {
+        const size_t need = pointops::bq_backward_workspace_bytes(B, Q, K);
+        if (workspace_bytes < need)
+            return fail(POINTOPS_INVALID_ARGUMENT, "workspace of %zu bytes given, %zu needed",
+                        workspace_bytes, need);
+    }
     int st = current_device(nullptr);
     if (st != POINTOPS_OK) return st;
     hipError_t e = pointops::launch_ball_query_backward(
         query, ref, idx, grad_dist2, rows ? B : 0, rows ? Q : 0, P, K, grad_query, grad_ref,
-        (hipStream_t)stream);
+        self ? workspace : nullptr, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "ball_query_backward launch");
     return POINTOPS_OK;
 }

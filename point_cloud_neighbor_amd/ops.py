@@ -67,8 +67,10 @@ def _load():
         lib.pointops_ball_query_workspace_bytes.restype = ctypes.c_size_t
         lib.pointops_ball_query.restype = ctypes.c_int
         lib.pointops_ball_query_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp,
-                                                     vp]
+                                                     vp, ctypes.c_size_t, vp]
         lib.pointops_ball_query_backward.restype = ctypes.c_int
+        lib.pointops_ball_query_backward_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        lib.pointops_ball_query_backward_workspace_bytes.restype = ctypes.c_size_t
         lib.pointops_ragged_workspace_bytes.argtypes = [i64]
         lib.pointops_ragged_workspace_bytes.restype = ctypes.c_size_t
         lib.pointops_knn_ragged_workspace_bytes.argtypes = [vp, vp, i64, i64]
@@ -274,7 +276,8 @@ def ball_query_backward(query: torch.Tensor, ref: torch.Tensor, idx: torch.Tenso
     """Gradients of L through Ball Query's squared distances, given
     G = dL/dS (B, Q, K) and the forward's indices -> (grad_query (B, Q, 3) or
     None, grad_ref (B, P, 3) or None), float32. Slots with a negative index
-    contribute nothing."""
+    contribute nothing. A cloud queried by its own points (one tensor for
+    both) gets the workspace of the self-query mode."""
     lib = _load()
     query = _points(query, "query")
     ref = _points(ref, "ref")
@@ -295,10 +298,16 @@ def ball_query_backward(query: torch.Tensor, ref: torch.Tensor, idx: torch.Tenso
     with torch.cuda.device(query.device):
         gq = torch.empty_like(query) if need_query else None
         gx = torch.empty_like(ref) if need_ref else None
+        ws = None
+        if need_ref and query.data_ptr() == ref.data_ptr() and Q == P:
+            nb = lib.pointops_ball_query_backward_workspace_bytes(B, Q, P, K)
+            ws = torch.empty(nb, dtype=torch.uint8, device=query.device) if nb else None
         rc = lib.pointops_ball_query_backward(
             query.data_ptr(), ref.data_ptr(), idx.data_ptr(), grad_dist2.data_ptr(), B, Q, P,
             K, gq.data_ptr() if gq is not None else None,
-            gx.data_ptr() if gx is not None else None, _stream(query.device))
+            gx.data_ptr() if gx is not None else None,
+            ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+            _stream(query.device))
         _check(rc)
     return gq, gx
 

@@ -54,7 +54,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pointops_abi_version() == 4
+    assert lib.pointops_abi_version() == 5
     for code in range(6):
         assert lib.pointops_status_string(code) != b"unknown status"
     assert lib.pointops_status_string(99) == b"unknown status"
@@ -187,3 +187,26 @@ def test_ragged_workspace_sizes(lib):
     # no clouds: the table's minimum; invalid counts: 0
     assert sizes(knn, [], [], 16) == table(0)
     assert sizes(knn, [-1], [10], 16) == 0 and sizes(bq, [1], [-5], 8) == 0
+
+
+def test_ball_query_backward_workspace(lib):
+    """The self-query workspace: one window of partials (3 planes of 2048
+    floats) per tile of 128 rows at K = 64; nothing when Q != P; a call that
+    would use it refuses one too small before touching the device."""
+    i64 = ctypes.c_int64
+    f = lib.pointops_ball_query_backward_workspace_bytes
+    f.argtypes = [i64, i64, i64, i64]
+    f.restype = ctypes.c_size_t
+    assert f(1, 100000, 100000, 64) == 782 * 3 * 2048 * 4
+    assert f(2, 1000, 1000, 64) == 16 * 3 * 2048 * 4
+    assert f(1, 1000, 2000, 64) == 0
+    assert f(0, 1000, 1000, 64) == 0
+    vp = ctypes.c_void_p
+    lib.pointops_ball_query_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp,
+                                                 vp, ctypes.c_size_t, vp]
+    lib.pointops_ball_query_backward.restype = ctypes.c_int
+    fake = vp(0x1000)
+    rc = lib.pointops_ball_query_backward(fake, fake, fake, fake, 1, 1000, 1000, 64, fake, fake,
+                                          fake, 16, None)
+    assert rc == 1, lib.pointops_last_error()
+    assert b"workspace" in lib.pointops_last_error()

@@ -36,8 +36,14 @@ def uses_per_ref(idx, P):
     return out
 
 
-def check_backward(gpu, oracle_mod, q, x, idx, g, what, exact=False):
-    gq, gx = gpu.ball_query_backward(dev(q), dev(x), dev(idx), dev(g))
+def check_backward(gpu, oracle_mod, q, x, idx, g, what, exact=False, same=False):
+    """same: q is x, passed as one device tensor (the self-query mode, whose
+    reference sums go through per-tile windows in a workspace)."""
+    if same:
+        xd = dev(x)
+        gq, gx = gpu.ball_query_backward(xd, xd, dev(idx), dev(g))
+    else:
+        gq, gx = gpu.ball_query_backward(dev(q), dev(x), dev(idx), dev(g))
     gq, gx = host(gq), host(gx)
     clean = np.where((idx >= 0) & (idx < x.shape[1]), idx, -1)
     wq, wx, aq, ax = oracle_mod.ball_query_backward(q, x, clean, g)
@@ -95,17 +101,19 @@ def test_backward_sorted_workload_subset(gpu, oracle_mod):
     check_backward(gpu, oracle_mod, q, x, idx, g, "sorted_bq subset")
 
 
-def test_backward_sorted_workload_whole_output(gpu, oracle_mod):
+@pytest.mark.parametrize("same", [False, True])
+def test_backward_sorted_workload_whole_output(gpu, oracle_mod, same):
     """Full size as the benchmark runs it (every point of the sorted cloud a
     query): both gradients of every row and every reference against the
     oracle. Neighbouring rows select neighbouring references here, so most
     reference terms go through the per-tile window, the others through the
-    table."""
+    table; with one tensor for both sets (as the benchmark passes it), the
+    windows are the fixed ones of the self-query mode."""
     wl = W.workload("sorted_bq")
     x = wl.xyz
     _, idx = oracle_mod.ball_query(x, x, wl.bq_radius, wl.bq_k, threads=8)
     g = seeded_grad(9, idx.shape)
-    check_backward(gpu, oracle_mod, x, x, idx, g, "sorted_bq whole")
+    check_backward(gpu, oracle_mod, x, x, idx, g, f"sorted_bq whole same={same}", same=same)
 
 
 @pytest.mark.parametrize("tile", ["4", "37", "1024"])
@@ -118,6 +126,44 @@ def test_backward_tile_sizes(gpu, oracle_mod, monkeypatch, tile):
     _, idx = oracle_mod.ball_query(x, x, 0.08, 64, threads=8)
     g = seeded_grad(10, idx.shape)
     check_backward(gpu, oracle_mod, x, x, idx, g, f"tile {tile}")
+
+
+@pytest.mark.parametrize("tile", [None, "4", "37", "1024"])
+def test_backward_self_query_mode(gpu, oracle_mod, monkeypatch, tile):
+    """One tensor as query and reference set: the window partials in the
+    workspace and their merge, against the oracle, on a sorted cloud (most
+    terms in the windows), with forced tile sizes."""
+    if tile:
+        monkeypatch.setenv("POINTOPS_BQ_BWD_TILE", tile)
+    wl = W.workload("sorted_bq")
+    x = wl.xyz[:, :30000].copy()
+    _, idx = oracle_mod.ball_query(x, x, 0.07, 64, threads=8)
+    g = seeded_grad(11, idx.shape)
+    check_backward(gpu, oracle_mod, x, x, idx, g, f"self tile {tile}", same=True)
+
+
+def test_backward_self_query_unsorted_and_batched(gpu, oracle_mod):
+    """Self-query on clouds in random order (few terms in the windows, most
+    through the table) and on two clouds, whose tiles straddle the boundary
+    between them; K above 64 (two passes per row) on the second."""
+    x = W.uniform_cube(71, 2, 6000)
+    _, idx = oracle_mod.ball_query(x, x, 0.12, 48, threads=8)
+    g = seeded_grad(12, idx.shape)
+    check_backward(gpu, oracle_mod, x, x, idx, g, "self unsorted B=2", same=True)
+    wl = W.workload("sorted_bq")
+    x = np.concatenate([wl.xyz[:, :5000], wl.xyz[:, 5000:10000]], axis=0).copy()
+    _, idx = oracle_mod.ball_query(x, x, 0.12, 100, threads=8)
+    g = seeded_grad(13, idx.shape)
+    check_backward(gpu, oracle_mod, x, x, idx, g, "self sorted B=2 K=100", same=True)
+
+
+def test_backward_self_query_exact(gpu, oracle_mod):
+    """Self-query on a small-integer cloud with dyadic G: every sum is exact,
+    so both gradients must equal the oracle's bit for bit."""
+    x = W.integer_cloud(3, 2, 900, 0, 4)
+    _, idx = oracle_mod.ball_query(x, x, 1.5, 48, threads=8)
+    g = seeded_grad(14, idx.shape, dyadic=True)
+    check_backward(gpu, oracle_mod, x, x, idx, g, "self integer", exact=True, same=True)
 
 
 def test_backward_sorted_workload_full(gpu, oracle_mod):
@@ -202,7 +248,7 @@ def test_backward_overwrites_grad_ref(gpu, oracle_mod):
     gx = torch.full_like(tx, 12345.0)
     rc = lib.pointops_ball_query_backward(tq.data_ptr(), tx.data_ptr(), ti.data_ptr(),
                                           tg.data_ptr(), 1, 64, 300, 16, gq.data_ptr(),
-                                          gx.data_ptr(), None)
+                                          gx.data_ptr(), None, 0, None)
     assert rc == 0
     torch.cuda.synchronize()
     wq, wx, _, _ = oracle_mod.ball_query_backward(q, x, idx, g)
@@ -256,4 +302,8 @@ def test_backward_rejects_bad_arguments(gpu):
     lib = ops._load()
     assert lib.pointops_ball_query_backward(q.data_ptr(), x.data_ptr(), idx.data_ptr(),
                                             g.data_ptr(), -1, 4, 5, 2, q.data_ptr(), None,
-                                            None) == 1
+                                            None, 0, None) == 1
+    # the self-query workspace, when given, must be large enough
+    assert lib.pointops_ball_query_backward(x.data_ptr(), x.data_ptr(), idx.data_ptr(),
+                                            g.data_ptr(), 1, 5, 5, 2, None, x.data_ptr(),
+                                            x.data_ptr(), 8, None) == 1
