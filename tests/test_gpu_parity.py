@@ -137,6 +137,22 @@ def test_fps_ties_and_duplicates(gpu, oracle_mod, mode, monkeypatch):
     check_fps(gpu, oracle_mod, line, 1030, 0, "line")
 
 
+@pytest.mark.parametrize("G,rg", [("4", "4"), ("16", "2"), ("16", "8")])
+def test_fps_batches_past_the_distinct_points(gpu, oracle_mod, monkeypatch, G, rg):
+    """Certified batches over several workgroups once every distinct location
+    is taken: 64 locations among 5000 points, 3000 samples, so from the 65th
+    sample on every key is 0 and equals the bound's, and each centre passes
+    only by its index (the full test that a certification block falls back
+    to); also a cloud of one repeated point."""
+    monkeypatch.setenv("POINTOPS_FPS_MODE", "batch")
+    monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", G)
+    monkeypatch.setenv("POINTOPS_FPS_RG", rg)
+    xyz = W.integer_cloud(77, 1, 5000, 0, 4)
+    check_fps(gpu, oracle_mod, xyz, 3000, 17, f"64 locations G={G} rg={rg}")
+    same = np.full((1, 3000, 3), 0.25, dtype=np.float32)
+    check_fps(gpu, oracle_mod, same, 700, 5, f"one location G={G} rg={rg}")
+
+
 @pytest.mark.parametrize("G,rg,block", [(1, 0, 256), (1, 0, 1024), (4, 1, 1024), (4, 15, 1024),
                                         (4, 30, 1024), (9, 3, 1024), (40, 2, 1024),
                                         (63, 4, 1024), (70, 1, 1024), (130, 1, 1024),
