@@ -546,8 +546,14 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
         if (wave != 0) continue;
 
         // ---- wave 0: exchange, then certify centres ----------------------------
-        // Reports r = 2 * wave + k (k = 0, 1) are in index order, as are the
-        // waves: lane order is index order in every reduction below.
+        // Reports r = 2 * wave + k (k = 0, 1): the waves are in index order,
+        // but a wave's two reports are in key order, so the larger key comes
+        // first even when its index is the larger. The candidates that wave 0
+        // certifies must be in index order (the first lane holding the
+        // largest key must hold the smallest index: two keys that differ at
+        // the exchange can become equal as centres are folded in), so the
+        // reports of a wave are put in index order wherever they become
+        // candidates.
         uint32_t beta_m = 0, beta_j = kNone;
         uint32_t abort = 0;
         uint32_t total = 0;  // live candidates, compacted into live_a / live_z
@@ -571,7 +577,13 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
             if (G == 1) {
                 int l;
                 wave_max_key(wbd.x, wbd.y, wbd.y != kNone, beta_m, beta_j, l);
-                keep(true, r.x, r.y, r.z, r.w, rz);
+                // the pair's smaller index to its even lane (an empty report,
+                // index kNone, sorts last)
+                const uint4 rp = rep[lane ^ 1];
+                const uint32_t rpz = rep_z[lane ^ 1];
+                const bool sw = (lane & 1) == 0 ? rp.y < r.y : rp.y > r.y;
+                keep(true, sw ? rp.x : r.x, sw ? rp.y : r.y, sw ? rp.z : r.z, sw ? rp.w : r.w,
+                     sw ? rpz : rz);
             } else {
                 // publish this workgroup's RG best reports (in index order) and
                 // its bound: the best of the wave bounds and unpublished reports
@@ -601,10 +613,16 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 const uint32_t tag = batch;
                 uint64_t* set = cw + (size_t)(batch & 1) * G * stride;
                 const int nsel = __popcll(sel);
+                // the published slot, in index order: when both reports of a
+                // wave are published, the smaller index takes the first slot
+                const uint32_t pj = rep[lane ^ 1].y;  // the pair's other report
+                int slot = (int)lanes_below(sel);
+                if ((sel >> (lane ^ 1)) & 1ull)
+                    slot += (lane & 1) == 0 ? (pj < r.y ? 1 : 0) : (pj > r.y ? -1 : 0);
                 if ((sel >> lane) & 1ull) {
                     uint64_t w0, w1, w2;
                     pack_candidate(r.x, r.y, r.z, r.w, rz, w0, w1, w2);
-                    uint64_t* w = set + (size_t)(g * RG + (int)lanes_below(sel)) * 3;
+                    uint64_t* w = set + (size_t)(g * RG + slot) * 3;
                     __hip_atomic_store(&w[0], tag8(w0, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     __hip_atomic_store(&w[1], tag8(w1, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     __hip_atomic_store(&w[2], tag8(w2, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

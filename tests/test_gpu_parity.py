@@ -153,6 +153,25 @@ def test_fps_batches_past_the_distinct_points(gpu, oracle_mod, monkeypatch, G, r
     check_fps(gpu, oracle_mod, same, 700, 5, f"one location G={G} rg={rg}")
 
 
+@pytest.mark.parametrize("G,rg", [("1", "30"), ("2", "8"), ("4", "3"), ("8", "2"), ("8", "3")])
+def test_fps_candidates_in_index_order(gpu, oracle_mod, monkeypatch, G, rg):
+    """A wave reports its two largest keys in key order, so the larger key can
+    carry the larger index; keys that differ at the exchange can become equal
+    as centres are folded in (here: 0, once every distinct point is taken),
+    and then the smaller index must win. Small clouds sampled past their
+    distinct points, over several workgroup and candidate counts; the first
+    is the cloud where index 1 was taken instead of 0."""
+    monkeypatch.setenv("POINTOPS_FPS_MODE", "batch")
+    monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", G)
+    monkeypatch.setenv("POINTOPS_FPS_RG", rg)
+    check_fps(gpu, oracle_mod, W.clustered_cloud(570096078, N=64, n_clusters=5, sigma=0.02),
+              73, 63, f"clustered 64 G={G} rg={rg}")
+    for seed in range(12):
+        x = (W.clustered_cloud(seed, N=96, n_clusters=4, sigma=0.03) if seed % 2
+             else W.uniform_cube(seed, 2, 96))
+        check_fps(gpu, oracle_mod, x, 120, seed % 96, f"seed {seed} G={G} rg={rg}")
+
+
 @pytest.mark.parametrize("G,rg,block", [(1, 0, 256), (1, 0, 1024), (4, 1, 1024), (4, 15, 1024),
                                         (4, 30, 1024), (9, 3, 1024), (40, 2, 1024),
                                         (63, 4, 1024), (70, 1, 1024), (130, 1, 1024),
