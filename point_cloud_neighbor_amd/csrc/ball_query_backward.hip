@@ -39,6 +39,25 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 
 constexpr int kBqBwdWaves = 4;
 
+// *p += v in LDS, as a float add of the current value retried through an
+// integer compare-and-swap. Measured on gfx950 (random addresses in a
+// 2048-word array, four waves per workgroup): the LDS float atomic add runs
+// at about 0.33 lanes per clock per CU, the integer atomics at 9-12, and this
+// loop at 2.6 (4.2 on distinct addresses). Each successful swap applies one
+// float32 add (the VALU's: round to nearest even, subnormals kept) to the
+// value it replaces, so the result is a sum of the same terms in some order,
+// as with the atomic. No retry is needed unless another lane or wave changed
+// the word in between.
+__device__ __forceinline__ void lds_add_f32(float* p, float v) {
+    uint32_t* u = reinterpret_cast<uint32_t*>(p);
+    uint32_t old = *u;
+    while (true) {
+        const uint32_t prev = atomicCAS(u, old, __float_as_uint(__uint_as_float(old) + v));
+        if (prev == old) break;
+        old = prev;
+    }
+}
+
 __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_kernel(
     const float* __restrict__ query, const float* __restrict__ ref,
     const int64_t* __restrict__ idx, const float* __restrict__ grad, int64_t rows, int Q,
@@ -93,9 +112,12 @@ __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_kernel
 // table with open addressing (linear probing, at most kBwdProbes probes; a
 // term that finds no slot goes straight to device memory, so the result
 // never depends on either size). After a barrier the touched entries go out
-// with float atomics. The window's adds need no returned value, unlike the
-// table's claim of a slot: on the sorted 100k cloud, K = 64, 0.166 -> 0.146
-// ms. The query gradients are the fixed DPP tree, as above.
+// with float atomics. The LDS adds are lds_add_f32's read and swap, not the
+// LDS float atomic (see there). On the sorted 100k cloud, K = 64: 0.166 ms
+// with the table alone, 0.146 with the window in front of it, 0.139 with the
+// self-query mode below, 0.095 with the swapped adds and the rows' loads
+// issued kBwdRows at a time. The query gradients are the fixed DPP tree, as
+// above.
 //
 // A cloud queried by its own points (the query and reference buffers are one,
 // Q = P) with a workspace: the window of tile t is fixed by its position,
@@ -105,9 +127,11 @@ __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_kernel
 // partials of the windows that cover it in tile order. Only the table's
 // entries still use atomics. (A reference is covered by kBwdWin / tile
 // windows, and on a sorted cloud most of its terms are in them.)
-constexpr int kBwdTable = 2048;
+constexpr int kBwdTableBits = 11;
+constexpr int kBwdTable = 1 << kBwdTableBits;
 constexpr int kBwdProbes = 64;  // probes before a term goes straight to device memory
 constexpr int kBwdWin = 2048;   // window entries
+constexpr int kBwdRows = 8;     // rows a wave loads at once
 
 __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_tiled_kernel(
     const float* __restrict__ query, const float* __restrict__ ref,
@@ -146,19 +170,22 @@ __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_tiled_
     auto add_ref = [&](int flat, float tx, float ty, float tz) {
         const int64_t wi = (int64_t)flat - wbase;
         if (wi >= 0 && wi < kBwdWin) {
-            atomicAdd(&wx[wi], -tx);
-            atomicAdd(&wy[wi], -ty);
-            atomicAdd(&wz[wi], -tz);
+            lds_add_f32(&wx[wi], -tx);
+            lds_add_f32(&wy[wi], -ty);
+            lds_add_f32(&wz[wi], -tz);
             if (!part) atomicOr(&wbits[wi >> 5], 1u << (wi & 31));
             return;
         }
-        uint32_t h = ((uint32_t)flat * 2654435761u) >> 21;  // 11 bits: kBwdTable slots
+        uint32_t h = ((uint32_t)flat * 2654435761u) >> (32 - kBwdTableBits);  // a slot
+        // not unrolled: unrolled, each probe kept its own exec masks in scalar
+        // registers, which spilled
+#pragma nounroll
         for (int probe = 0; probe < kBwdProbes; ++probe) {
             const int old = atomicCAS(&key[h], -1, flat);
             if (old == -1 || old == flat) {
-                atomicAdd(&ax[h], -tx);
-                atomicAdd(&ay[h], -ty);
-                atomicAdd(&az[h], -tz);
+                lds_add_f32(&ax[h], -tx);
+                lds_add_f32(&ay[h], -ty);
+                lds_add_f32(&az[h], -tz);
                 return;
             }
             h = (h + 1) & (kBwdTable - 1);
@@ -179,7 +206,75 @@ __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_tiled_
             grad_query[3 * row + 2] = sz;
         }
     };
-    {
+    if (K <= kWave && P > 0) {
+        // One slot per lane; a wave's rows are r0 + wave, + kBqBwdWaves, ...,
+        // taken kBwdRows at a time: the indices and G of all of them are
+        // loaded, then the query points and the references they name, then
+        // the rows are added in. A wave so waits out two round trips per
+        // kBwdRows rows instead of two per row (index, then the reference it
+        // names). Every load is issued unconditionally (rows past the tile
+        // and lanes past K read a clamped, valid address and are flagged):
+        // loads complete in order, so each wait covers exactly the loads it
+        // needs, which a load that may be skipped would prevent. The query
+        // point goes through a vector load for the same reason (scalar loads
+        // complete out of order).
+        constexpr int W = kBqBwdWaves;
+        const int64_t rend = min(r0 + (int64_t)tile, rows);
+        const int kc = lane < K ? lane : K - 1;
+        int64_t bg = (r0 + wave) / Q, rqg = (r0 + wave) - bg * Q;  // batch of the next row
+        for (int64_t rb = r0 + wave; rb < rend; rb += kBwdRows * W) {
+            int64_t j[kBwdRows];
+            float g[kBwdRows], x[kBwdRows], y[kBwdRows], z[kBwdRows], qx[kBwdRows],
+                qy[kBwdRows], qz[kBwdRows];
+            int f[kBwdRows];  // flat reference row, -1 when the slot contributes nothing
+            int64_t rowb[kBwdRows];  // the rows' batches (before the loads: no branch among them)
+#pragma unroll
+            for (int i = 0; i < kBwdRows; ++i) {
+                rowb[i] = bg;
+                rqg += W;
+                while (rqg >= Q) {
+                    rqg -= Q;
+                    ++bg;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kBwdRows; ++i) {
+                const int64_t r = rb + i * W, rc = r < rend ? r : rend - 1;
+                j[i] = idx[rc * K + kc];
+                g[i] = grad[rc * K + kc];
+            }
+#pragma unroll
+            for (int i = 0; i < kBwdRows; ++i) {
+                const int64_t r = rb + i * W;
+                int rv = (int)(r < rend ? r : rend - 1);
+                __asm__("v_mov_b32 %0, %1" : "=v"(rv) : "s"(rv));  // a vector load, see above
+                const float* q = query + (size_t)rv * 3;
+                qx[i] = q[0];
+                qy[i] = q[1];
+                qz[i] = q[2];
+                // bitwise, not short-circuit: no branch for the compiler to
+                // sink the index load into
+                const bool ok = (r < rend) & (lane < K) & ((uint64_t)j[i] < (uint64_t)P);
+                f[i] = ok ? (int)(rowb[i] * P + j[i]) : -1;
+                const float* p = ref + (size_t)(ok ? f[i] : 0) * 3;
+                x[i] = p[0];
+                y[i] = p[1];
+                z[i] = p[2];
+            }
+#pragma unroll
+            for (int i = 0; i < kBwdRows; ++i) {
+                const int64_t r = rb + i * W;
+                if (r >= rend) break;
+                const bool ok = f[i] >= 0;
+                const float tx = ok ? 2.0f * (g[i] * (qx[i] - x[i])) : 0.f;
+                const float ty = ok ? 2.0f * (g[i] * (qy[i] - y[i])) : 0.f;
+                const float tz = ok ? 2.0f * (g[i] * (qz[i] - z[i])) : 0.f;
+                // a sum from +0, as for any row (a -0 term leaves +0)
+                finish_row(r, 0.f + tx, 0.f + ty, 0.f + tz);
+                if (grad_ref && ok) add_ref(f[i], tx, ty, tz);
+            }
+        }
+    } else {
         for (int rr = wave; rr < tile; rr += kBqBwdWaves) {
             const int64_t r = r0 + rr;
             if (r >= rows) break;
