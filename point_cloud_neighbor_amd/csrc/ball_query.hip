@@ -106,6 +106,11 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
         }
         start &= ~(kWave - 1);
     }
+    // the queries still taking hits, bit i for query i (wave-uniform): short
+    // of K and not stopped at the probe
+    uint32_t open = 0;
+#pragma unroll
+    for (int i = 0; i < QW; ++i) open |= (cnt[i] < K ? 1u : 0u) << i;
 
     // Software-pipelined reference loads: block n+1 is in flight while block n
     // is compared. Lanes past the last reference hold NaN coordinates, whose
@@ -137,32 +142,32 @@ __global__ __launch_bounds__(kWave) void ball_query_kernel(
             }
         }
         const bool at_probe = BUD && base + kWave == bud.probe;
-        bool live = false;
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
-            if (cnt[i] < K && (!BUD || !stopped[i])) {
+            if ((open >> i) & 1u) {
                 const float s = s32(qx[i], qy[i], qz[i], x, y, z);
-                const uint64_t m = ballot(s < r2 && (MODE != kBqResume || j >= from[i]));
+                const bool h = s < r2 && (MODE != kBqResume || j >= from[i]);
+                const uint64_t m = ballot(h);
                 if (m) {
                     const int slot = cnt[i] + (int)lanes_below(m);
-                    if (((m >> lane) & 1ull) && slot < K) {
+                    if (h && slot < K) {
                         out_idx[out0 + (size_t)i * K + slot] = ibase + j;
                         out_d2[out0 + (size_t)i * K + slot] = s;
                     }
                     cnt[i] += __popcll(m);
+                    if (cnt[i] >= K) open &= ~(1u << i);
                 }
                 if constexpr (BUD) {
                     // at this rate K hits would take more than the budget
                     if (at_probe && cnt[i] < K &&
-                        (int64_t)cnt[i] * bud.budget < (int64_t)K * bud.probe)
+                        (int64_t)cnt[i] * bud.budget < (int64_t)K * bud.probe) {
                         stopped[i] = true;
-                    live |= cnt[i] < K && !stopped[i];
-                } else {
-                    live |= cnt[i] < K;
+                        open &= ~(1u << i);
+                    }
                 }
             }
         }
-        return live;
+        return open != 0;
     };
     int base = start;
     bool live = true;
@@ -406,6 +411,10 @@ __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
         qz[i] = qb[(size_t)3 * row + 2];
         cnt[i] = row0 + i < Q ? 0 : K;
     }
+    // the queries still short of K hits, bit i for query i (wave-uniform)
+    uint32_t open = 0;
+#pragma unroll
+    for (int i = 0; i < QW; ++i) open |= (cnt[i] < K ? 1u : 0u) << i;
     const float nan = __builtin_nanf("");
     const float inf = __builtin_inff();
     // the box of the group's queries (rows past Q repeat row Q - 1)
@@ -450,19 +459,18 @@ __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
         const float gz = fmaxf(fmaxf(lz - gQz, gqz - hz), 0.0f);
         const float lb = (gx * gx + gy * gy) + gz * gz;
         if (ballot(lb < r2) == 0) continue;
-        uint64_t want[QW];
-        uint64_t any = 0;
+        // lane l: bit i set when query i can reach block c0 + l (the same
+        // bound per query); a block is scanned for the queries of its mask
+        // that are still open
+        uint32_t qm = 0;
 #pragma unroll
         for (int i = 0; i < QW; ++i) {
-            want[i] = 0;
-            if (cnt[i] < K) {
-                const float ex = fmaxf(fmaxf(lx - qx[i], qx[i] - hx), 0.0f);
-                const float ey = fmaxf(fmaxf(ly - qy[i], qy[i] - hy), 0.0f);
-                const float ez = fmaxf(fmaxf(lz - qz[i], qz[i] - hz), 0.0f);
-                want[i] = ballot((ex * ex + ey * ey) + ez * ez < r2);
-                any |= want[i];
-            }
+            const float ex = fmaxf(fmaxf(lx - qx[i], qx[i] - hx), 0.0f);
+            const float ey = fmaxf(fmaxf(ly - qy[i], qy[i] - hy), 0.0f);
+            const float ez = fmaxf(fmaxf(lz - qz[i], qz[i] - hz), 0.0f);
+            qm |= ((ex * ex + ey * ey) + ez * ez < r2 ? 1u : 0u) << i;
         }
+        const uint64_t any = ballot((qm & open) != 0);
         if (any == 0) continue;
         // candidate blocks in increasing order, the next one's load in flight
         int cur = __builtin_ctzll(any);
@@ -491,15 +499,16 @@ __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
                 cur = -1;
             }
             const int j = (c0 + blk) * kWave + lane;
-            live = false;
+            const uint32_t act = (uint32_t)__builtin_amdgcn_readlane((int)qm, blk) & open;
 #pragma unroll
             for (int i = 0; i < QW; ++i) {
-                if (cnt[i] < K && ((want[i] >> blk) & 1ull)) {
+                if ((act >> i) & 1u) {
                     const float s = s32(qx[i], qy[i], qz[i], x, y, z);
-                    const uint64_t m = ballot(s < r2);
+                    const bool h = s < r2;
+                    const uint64_t m = ballot(h);
                     if (m) {
                         const int slot = cnt[i] + (int)lanes_below(m);
-                        if (((m >> lane) & 1ull) && slot < K) {
+                        if (h && slot < K) {
                             if constexpr (STAGE) {
                                 stage_j[i][slot] = j;
                                 stage_s[i][slot] = s;
@@ -509,10 +518,11 @@ __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
                             }
                         }
                         cnt[i] += __popcll(m);
+                        if (cnt[i] >= K) open &= ~(1u << i);
                     }
                 }
-                live |= cnt[i] < K;
             }
+            live = open != 0;
             if (!live || cur < 0) break;
         }
         if (!live || stop_blk >= 0) {
