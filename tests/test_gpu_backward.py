@@ -166,6 +166,23 @@ def test_backward_self_query_exact(gpu, oracle_mod):
     check_backward(gpu, oracle_mod, x, x, idx, g, "self integer", exact=True, same=True)
 
 
+@pytest.mark.parametrize("same,K,B", [(True, 64, 1), (False, 64, 1), (True, 64, 2),
+                                      (False, 130, 1)])
+def test_backward_contended_exact(gpu, oracle_mod, same, K, B):
+    """Every row selects the same K references (4096 points on {0, 1}^3, a
+    radius that holds them all), so each of those references takes 4096 terms
+    per cloud: in the first tile through its window, in every other tile
+    through the hash table, with many lanes and waves adding into one word at
+    once. The terms and sums are dyadic, exact in float32 in any order, so
+    both gradients must equal the oracle's bit for bit."""
+    x = W.integer_cloud(21, B, 4096, 0, 2)
+    _, idx = oracle_mod.ball_query(x, x, 2.0, K, threads=8)
+    assert (idx[:, :, :K] == np.arange(K)).all()
+    g = seeded_grad(22, idx.shape, dyadic=True)
+    check_backward(gpu, oracle_mod, x, x, idx, g, f"contended same={same} K={K} B={B}",
+                   exact=True, same=same)
+
+
 def test_backward_sorted_workload_full(gpu, oracle_mod):
     """Full size (every point a query, as the benchmark runs it): grad_query
     on sampled row blocks against the oracle (a row's gradient depends only on
