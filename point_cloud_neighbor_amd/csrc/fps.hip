@@ -791,30 +791,68 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
             // there rewinds to its start, replays the steps that passed and
             // goes on one step at a time with the full test.
             auto certify_fast = [&](auto c_) {
-                constexpr int C = decltype(c_)::value;
-                constexpr int S1 = CPL > 1 ? 1 : 0;
-                uint32_t m0 = cm[0], m1 = C == 2 ? cm[S1] : 0u;
-                const uint32_t x0 = cxv[0], y0 = cyv[0], z0 = czv[0], j0 = cj[0];
-                const uint32_t x1 = cxv[S1], y1 = cyv[S1], z1 = czv[S1], j1 = cj[S1];
+                constexpr int C = decltype(c_)::value;  // slots per lane, <= CPL
+                uint32_t m[C], xs[C], ys[C], zs[C], js[C];
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    m[c] = cm[c];
+                    xs[c] = cxv[c];
+                    ys[c] = cyv[c];
+                    zs[c] = czv[c];
+                    js[c] = cj[c];
+                }
                 const int limit = min(M - t0, kFpsMaxBatch);
                 int nc = 0;
                 auto fold = [&](float X, float Y, float Z) {
-                    m0 = min(m0, f2u(s32(X, Y, Z, u2f(x0), u2f(y0), u2f(z0))));
-                    if (C == 2) m1 = min(m1, f2u(s32(X, Y, Z, u2f(x1), u2f(y1), u2f(z1))));
+#pragma unroll
+                    for (int c = 0; c < C; ++c)
+                        m[c] = min(m[c], f2u(s32(X, Y, Z, u2f(xs[c]), u2f(ys[c]), u2f(zs[c]))));
+                };
+                // the lane's best slot and its entry: a tree of strict
+                // compares, so on equal keys the earlier slot (the smaller
+                // index) is kept
+                auto best = [&](uint32_t& lm, uint32_t& wx, uint32_t& wy, uint32_t& wz,
+                                uint32_t& wj) {
+                    uint32_t bm[C], bx_[C], by_[C], bz_[C], bj[C];
+#pragma unroll
+                    for (int c = 0; c < C; ++c) {
+                        bm[c] = m[c];
+                        bx_[c] = xs[c];
+                        by_[c] = ys[c];
+                        bz_[c] = zs[c];
+                        bj[c] = js[c];
+                    }
+#pragma unroll
+                    for (int w = 1; w < C; w *= 2) {
+#pragma unroll
+                        for (int c = 0; c + w < C; c += 2 * w) {
+                            const bool t = bm[c + w] > bm[c];
+                            bm[c] = t ? bm[c + w] : bm[c];
+                            bx_[c] = t ? bx_[c + w] : bx_[c];
+                            by_[c] = t ? by_[c + w] : by_[c];
+                            bz_[c] = t ? bz_[c + w] : bz_[c];
+                            bj[c] = t ? bj[c + w] : bj[c];
+                        }
+                    }
+                    lm = bm[0];
+                    wx = bx_[0];
+                    wy = by_[0];
+                    wz = bz_[0];
+                    wj = bj[0];
                 };
                 // the candidates' LDS loads are complete here, so the loop's
                 // only LDS operations are its own stores, which need no wait
                 __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
                 bool tied = false;
                 while (true) {
-                    const uint32_t r0 = m0, r1 = m1;  // the block's start
+                    uint32_t r[C];  // the block's start
+#pragma unroll
+                    for (int c = 0; c < C; ++c) r[c] = m[c];
                     uint32_t fail = 0, tie = 0;
 #pragma unroll
                     for (int s = 0; s < kCertBlock; ++s) {
-                        const bool second = C == 2 && m1 > m0;
-                        const uint32_t lm = second ? m1 : m0;
-                        const uint32_t wx = second ? x1 : x0, wy = second ? y1 : y0,
-                                       wz = second ? z1 : z0, wj = second ? j1 : j0;
+                        uint32_t lm, wx, wy, wz, wj;
+                        best(lm, wx, wy, wz, wj);
                         const uint32_t mx = wave_max_u32(lm);
                         const int kl = (int)__builtin_ctzll(ballot(lm == mx));
                         fail |= (uint32_t)(mx <= beta_m) << s;
@@ -835,8 +873,8 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                     if (pass == kCertBlock) continue;
                     tied = pass < room && ((tie >> pass) & 1u);
                     if (tied) {
-                        m0 = r0;
-                        m1 = r1;
+#pragma unroll
+                        for (int c = 0; c < C; ++c) m[c] = r[c];
                         for (int i = nc - pass; i < nc; ++i) {
                             const uint4 c = cen[i];
                             fold(u2f(c.x), u2f(c.y), u2f(c.z));
@@ -847,10 +885,8 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 // one step at a time with the full test: a key equal to the
                 // bound's passes when its index is smaller
                 while (tied && nc < limit) {
-                    const bool second = C == 2 && m1 > m0;
-                    const uint32_t lm = second ? m1 : m0;
-                    const uint32_t wx = second ? x1 : x0, wy = second ? y1 : y0,
-                                   wz = second ? z1 : z0, wj = second ? j1 : j0;
+                    uint32_t lm, wx, wy, wz, wj;
+                    best(lm, wx, wy, wz, wj);
                     const uint32_t mx = wave_max_u32(lm);
                     const int kl = (int)__builtin_ctzll(ballot(lm == mx));
                     if (!key_gt(mx, lane_value(wj, kl), beta_m, beta_j)) break;
@@ -869,6 +905,8 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 certify_fast(std::integral_constant<int, 1>{});
             else if (CPL >= 2 && used <= 2)
                 certify_fast(std::integral_constant<int, (CPL >= 2 ? 2 : 1)>{});
+            else if (CPL >= 4 && used <= 4)
+                certify_fast(std::integral_constant<int, (CPL >= 4 ? 4 : 1)>{});
             else
                 certify(std::integral_constant<int, CPL>{});
         }
