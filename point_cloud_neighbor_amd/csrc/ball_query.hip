@@ -472,7 +472,13 @@ __global__ __launch_bounds__(kWave) void ball_query_cull_kernel(
         }
         const uint64_t any = ballot((qm & open) != 0);
         if (any == 0) continue;
-        // candidate blocks in increasing order, the next one's load in flight
+        // Candidate blocks in increasing order. The next block's load is
+        // issued before the current one is tested, but the compiler waits
+        // for it with the current one (it is skippable, and copied into the
+        // current registers); a form with two register sets in turn and
+        // unconditional loads, whose waits cover only the current block,
+        // measured no faster (0.087 against 0.084 ms on the sorted 100k
+        // workload): the scan is bound by issue, not by these loads.
         int cur = __builtin_ctzll(any);
         float nx = nan, ny = nan, nz = nan;
         {
