@@ -246,9 +246,10 @@ __global__ __launch_bounds__(kBqBwdWaves* kWave) void ball_query_backward_tiled_
 #pragma unroll
             for (int i = 0; i < kBwdRows; ++i) {
                 const int64_t r = rb + i * W;
-                int rv = (int)(r < rend ? r : rend - 1);
+                // the row's offset in the tile (< tile; rows may pass 2^31)
+                int rv = (int)((r < rend ? r : rend - 1) - r0);
                 __asm__("v_mov_b32 %0, %1" : "=v"(rv) : "s"(rv));  // a vector load, see above
-                const float* q = query + (size_t)rv * 3;
+                const float* q = query + (size_t)(r0 + rv) * 3;
                 qx[i] = q[0];
                 qy[i] = q[1];
                 qz[i] = q[2];
