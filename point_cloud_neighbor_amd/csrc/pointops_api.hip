@@ -191,14 +191,18 @@ int knn_grid_nw(int64_t k, int kcap, int64_t queries, int64_t refs) {
 // Ball Query: queries per wave. Fewer queries per wave until the grid is about
 // one device-full of waves; at most 8 (measured faster than 16 on 100k x 100k:
 // the shorter waves balance better).
-// Up to 256 candidates per cloud (four slots per lane of the certifying wave),
-// at most the workgroup's 2 * npw reports; POINTOPS_FPS_RG overrides it up to
-// 512 candidates (eight slots per lane, the most the kernel holds).
+// Up to 256 candidates per cloud (four slots per lane of the certifying wave)
+// and at most 8 per workgroup (beyond that the exchanges hardly fall while each
+// grows: 32 clouds of 8192 points on 6 workgroups each, 4 / 6 / 8 / 12 / 30
+// candidates per workgroup: 0.354 / 0.305 / 0.295 / 0.308 / 0.366 ms);
+// POINTOPS_FPS_RG overrides it up to 512 candidates (eight slots per lane,
+// the most the kernel holds) or the workgroup's 2 * npw reports.
 int fps_batch_rg(int64_t G, int npw) {
     const long env = env_long("POINTOPS_FPS_RG", 0);
     const int64_t g = std::max<int64_t>(G, 1);
     const int64_t total = G > 128 ? 512 : 256;  // candidates per exchange in all
-    const int64_t cap = std::max<int64_t>(1, std::min<int64_t>(2 * npw, total / g));
+    const int64_t cap =
+        std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(2 * npw, 8), total / g));
     const int64_t most = std::max<int64_t>(1, std::min<int64_t>(2 * npw, 512 / g));
     return (int)(env > 0 ? std::min<int64_t>(env, most) : cap);
 }
