@@ -339,9 +339,11 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     constexpr int NW = BLOCK / kWave;
     // Wave 0 certifies; the others hold points. Waves go round-robin over the
     // 4 SIMDs of a CU, so wave 0 shares its SIMD with waves 4, 8, 12, which
-    // hold points too; wave 0 runs at a higher priority. (Leaving those three
-    // waves without points, so nothing else issues on wave 0's SIMD, measured
-    // slower: 1.23 against 1.17 ms on the 100k-point cloud).
+    // hold points too; wave 0 runs at the highest priority, the point waves
+    // one below it, above the waves of other kernels sharing the CU (about
+    // 0.5% on the 100k-point cloud). (Leaving those three waves without
+    // points, so nothing else issues on wave 0's SIMD, measured slower: 1.23
+    // against 1.17 ms on the 100k-point cloud).
     static_assert(NW % 4 == 0 && 2 * (NW - 1) <= kWave, "wave count");
     // Certified centres of the batch: x, y, z bits and the point's index. An
     // entry is written before the count that includes it (LDS performs one
@@ -433,6 +435,8 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
         rep_z[lane] = 0u;
         bnd[lane] = make_uint2(0u, kNone);
         __builtin_amdgcn_s_setprio(3);
+    } else {
+        __builtin_amdgcn_s_setprio(2);
     }
     __syncthreads();
 
@@ -774,15 +778,20 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
             // come first in lane-major order; the other slots hold key 0,
             // which the min update keeps at 0, so they can win only when every
             // live key is 0, and then lane 0, slot 0 (live) is the first entry
-            // holding the maximum. So no slot needs a validity mask, and the
-            // winning lane publishes its own entry (the others write their
-            // sink slots, so no branch splits the wave). With two slots each
-            // lane offers its better one, slot 0 on ties (the smaller index).
+            // holding the maximum. So no slot needs a validity mask. With
+            // several slots each lane offers its best one, the earlier slot on
+            // ties (the smaller index).
             //
             // Steps go in blocks of kCertBlock with no exit test inside: a
             // step's test (key above the bound's, or the batch's first centre)
             // is only recorded, and each step writes its entry and folds
-            // anyway. After the block the count takes the leading steps that
+            // anyway. A step's entry stays in scalar registers (the lane reads
+            // that the fold needs anyway, plus the index); after the block
+            // v_writelane puts entry s into lane s and lanes 0-3 store the
+            // four entries at once, so no step waits behind an LDS store (a
+            // per-step store of the winning lane's entry, with the other lanes
+            // writing sink slots, measured 1.09 against 1.02 ms on the 100k
+            // cloud). After the block the count takes the leading steps that
             // passed; the entries past it are never read, and the candidates'
             // keys are not used after the batch, so the steps past a failure
             // need no undoing. (A test inside the loop costs a branch per
@@ -849,6 +858,8 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
 #pragma unroll
                     for (int c = 0; c < C; ++c) r[c] = m[c];
                     uint32_t fail = 0, tie = 0;
+                    // the block's entries, wave-uniform (scalar registers)
+                    uint32_t sx[kCertBlock], sy[kCertBlock], sz[kCertBlock], sj[kCertBlock];
 #pragma unroll
                     for (int s = 0; s < kCertBlock; ++s) {
                         uint32_t lm, wx, wy, wz, wj;
@@ -857,11 +868,28 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                         const int kl = (int)__builtin_ctzll(ballot(lm == mx));
                         fail |= (uint32_t)(mx <= beta_m) << s;
                         tie |= (uint32_t)(mx == beta_m) << s;
-                        const bool win = lane == kl && nc + s < limit;
-                        *(win ? &cen[nc + s] : &sink_rec[lane]) = make_uint4(wx, wy, wz, wj);
-                        fold(u2f(lane_value(wx, kl)), u2f(lane_value(wy, kl)),
-                             u2f(lane_value(wz, kl)));
+                        sx[s] = lane_value(wx, kl);
+                        sy[s] = lane_value(wy, kl);
+                        sz[s] = lane_value(wz, kl);
+                        sj[s] = lane_value(wj, kl);
+                        fold(u2f(sx[s]), u2f(sy[s]), u2f(sz[s]));
                     }
+                    static_assert(kCertBlock == 4, "entry lanes");
+                    uint32_t ex = 0, ey = 0, ez = 0, ej = 0;  // entry s in lane s
+#define POINTOPS_ENTRY_LANE(S)                                                        \
+    __asm__("v_writelane_b32 %0, %1, " #S : "+v"(ex) : "s"(sx[S]));                  \
+    __asm__("v_writelane_b32 %0, %1, " #S : "+v"(ey) : "s"(sy[S]));                  \
+    __asm__("v_writelane_b32 %0, %1, " #S : "+v"(ez) : "s"(sz[S]));                  \
+    __asm__("v_writelane_b32 %0, %1, " #S : "+v"(ej) : "s"(sj[S]));
+                    POINTOPS_ENTRY_LANE(0)
+                    POINTOPS_ENTRY_LANE(1)
+                    POINTOPS_ENTRY_LANE(2)
+                    POINTOPS_ENTRY_LANE(3)
+#undef POINTOPS_ENTRY_LANE
+                    // one store for the block's entries, before the count that
+                    // takes them (the entries past a failure are never read)
+                    if (lane < kCertBlock && nc + lane < limit)
+                        cen[nc + lane] = make_uint4(ex, ey, ez, ej);
                     if (nc == 0) fail &= ~1u;  // the batch's first centre: the cloud's largest key
                     const int room = limit - nc;
                     if (room < kCertBlock) fail |= ~0u << room;
