@@ -875,12 +875,20 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                         fold(u2f(sx[s]), u2f(sy[s]), u2f(sz[s]));
                     }
                     static_assert(kCertBlock == 4, "entry lanes");
-                    uint32_t ex = 0, ey = 0, ez = 0, ej = 0;  // entry s in lane s
+                    // entry s into lane s. The scalar registers come from
+                    // v_readlane, and a VALU read of an SGPR that a VALU
+                    // wrote needs two wait states on gfx950 (the compiler
+                    // keeps them in its own code but cannot see inside an
+                    // asm statement), hence the s_nop 1 that leads each one.
+                    uint32_t ex = 0, ey = 0, ez = 0, ej = 0;
 #define POINTOPS_ENTRY_LANE(S)                                                        \
-    __asm__("v_writelane_b32 %0, %1, " #S : "+v"(ex) : "s"(sx[S]));                  \
-    __asm__("v_writelane_b32 %0, %1, " #S : "+v"(ey) : "s"(sy[S]));                  \
-    __asm__("v_writelane_b32 %0, %1, " #S : "+v"(ez) : "s"(sz[S]));                  \
-    __asm__("v_writelane_b32 %0, %1, " #S : "+v"(ej) : "s"(sj[S]));
+    __asm__("s_nop 1\n\t"                                                              \
+            "v_writelane_b32 %0, %4, " #S "\n\t"                                        \
+            "v_writelane_b32 %1, %5, " #S "\n\t"                                        \
+            "v_writelane_b32 %2, %6, " #S "\n\t"                                        \
+            "v_writelane_b32 %3, %7, " #S                                              \
+            : "+v"(ex), "+v"(ey), "+v"(ez), "+v"(ej)                                    \
+            : "s"(sx[S]), "s"(sy[S]), "s"(sz[S]), "s"(sj[S]));
                     POINTOPS_ENTRY_LANE(0)
                     POINTOPS_ENTRY_LANE(1)
                     POINTOPS_ENTRY_LANE(2)
