@@ -47,7 +47,7 @@ hipError_t fps_batch_capacity(int ppt, int block, int cpl, size_t lds, int cus, 
 size_t fps_batch_workspace_bytes(int64_t B, int64_t G, int rg);
 size_t fps_batch_lds_bytes(int G, int rg);
 int fps_batch_ppt_round(int ppt);
-int fps_batch_stride(int rg);
+int fps_batch_set_words(int G, int rg);
 int fps_batch_point_waves(int block);  // waves of a workgroup that hold points
 hipError_t launch_knn(const float*, const float*, int64_t, int64_t, int64_t, int64_t, float*,
                       int64_t*, int, int, const int64_t*, int, int64_t, int, hipStream_t);

@@ -330,11 +330,22 @@ __device__ __forceinline__ void wave_max_key(uint32_t m, uint32_t j, bool use, u
     oj = lane_value(j, olane);
 }
 
-template <int PPT, int BLOCK, int CPL>
+// The exchange words of one cloud and batch parity: three for each of the
+// G * rg candidates and two for each of the G bounds, both counts rounded up to
+// a multiple of 64 (a gather's lanes past the end read within the set).
+__host__ __device__ __forceinline__ int pad64(int n) { return (n + 63) & ~63; }
+__host__ __device__ __forceinline__ int fps_set_words(int G, int rg) {
+    return 3 * pad64(G * rg) + 2 * pad64(G);
+}
+
+// STAGED: the exchange words go through LDS (clouds of more than 64
+// workgroups or 256 candidates); otherwise straight into registers. The two
+// are separate kernels so that neither carries the other's registers.
+template <int PPT, int BLOCK, int CPL, bool STAGED>
 __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     const float* __restrict__ xyz, int N, int M, int start_idx, int G, int slice, int RG,
     int64_t* __restrict__ out_idx, float* __restrict__ out_xyz, uint64_t* __restrict__ words,
-    int stride, uint32_t* __restrict__ status, uint32_t spin_limit,
+    uint32_t* __restrict__ status, uint32_t spin_limit,
     const int64_t* __restrict__ seg, int nseg) {
     constexpr int NW = BLOCK / kWave;
     // Wave 0 certifies; the others hold points. Waves go round-robin over the
@@ -360,7 +371,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     __shared__ uint2 bnd[kWave];
     __shared__ uint4 live_a[kWave * CPL];  // compacted live candidates: m, index, x, y
     __shared__ uint32_t live_z[kWave * CPL];  // and z
-    extern __shared__ uint64_t stage[];  // gathered payloads, G * (3 * RG + 2)
+    extern __shared__ uint64_t stage[];  // the gathered words (STAGED)
     constexpr int kPoll = 16;  // loads per lane in flight per poll
 
     // this workgroup's cloud
@@ -377,7 +388,6 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
         M = (int)rec[kFrOCnt];
         start_idx = (int)rec[kFrStart];
         RG = (int)rec[kFrRG];
-        stride = 3 * RG + 2;
         xrow0 = rec[kFrXOff];
         orow0 = rec[kFrOOff];
         jbase = rec[kFrIdxBase];
@@ -388,7 +398,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
         xrow0 = (int64_t)b * N;
         orow0 = (int64_t)b * M;
         jbase = 0;
-        cw = words + (size_t)b * 2 * G * stride;
+        cw = words + (size_t)b * 2 * fps_set_words(G, RG);
     }
     const int tid = threadIdx.x;
     const int wave = uniform(tid / kWave);
@@ -612,10 +622,14 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 uint32_t gm, gj;
                 int gl;
                 wave_max_key(um, uj, uj != kNone, gm, gj, gl);
-                // this batch's word set: G * RG candidates of 3 words, then G
-                // bounds of 2 words
+                // This batch's word set: the three words of candidate q = g * RG
+                // + rank at 3q, then the two of each workgroup's bound (each
+                // workgroup's words are contiguous). The set is sized for Q =
+                // G * RG rounded up to 64 candidates and G rounded up to 64
+                // bounds, so that every lane of a gather loads within it.
                 const uint32_t tag = batch;
-                uint64_t* set = cw + (size_t)(batch & 1) * G * stride;
+                const int Q = G * RG;
+                uint64_t* set = cw + (size_t)(batch & 1) * fps_set_words(G, RG);
                 const int nsel = __popcll(sel);
                 // the published slot, in index order: when both reports of a
                 // wave are published, the smaller index takes the first slot
@@ -623,95 +637,141 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 int slot = (int)lanes_below(sel);
                 if ((sel >> (lane ^ 1)) & 1ull)
                     slot += (lane & 1) == 0 ? (pj < r.y ? 1 : 0) : (pj > r.y ? -1 : 0);
-                if ((sel >> lane) & 1ull) {
+                auto put = [&](uint64_t* w, uint64_t v) {
+                    __hip_atomic_store(w, tag8(v, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                };
+                auto put_candidate = [&](int q, uint32_t m, uint32_t j, uint32_t x, uint32_t y,
+                                         uint32_t z) {
                     uint64_t w0, w1, w2;
-                    pack_candidate(r.x, r.y, r.z, r.w, rz, w0, w1, w2);
-                    uint64_t* w = set + (size_t)(g * RG + slot) * 3;
-                    __hip_atomic_store(&w[0], tag8(w0, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&w[1], tag8(w1, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&w[2], tag8(w2, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
+                    pack_candidate(m, j, x, y, z, w0, w1, w2);
+                    uint64_t* w = set + (size_t)q * 3;
+                    put(w, w0);
+                    put(w + 1, w1);
+                    put(w + 2, w2);
+                };
+                if ((sel >> lane) & 1ull) put_candidate(g * RG + slot, r.x, r.y, r.z, r.w, rz);
                 if (nsel < RG) {
                     // unused candidate ranks are published as empty
-                    for (int k = nsel + lane; k < RG; k += kWave) {
-                        uint64_t w0, w1, w2;
-                        pack_candidate(0u, kNone, 0u, 0u, 0u, w0, w1, w2);
-                        uint64_t* w = set + (size_t)(g * RG + k) * 3;
-                        __hip_atomic_store(&w[0], tag8(w0, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        __hip_atomic_store(&w[1], tag8(w1, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        __hip_atomic_store(&w[2], tag8(w2, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
+                    for (int k = nsel + lane; k < RG; k += kWave)
+                        put_candidate(g * RG + k, 0u, kNone, 0u, 0u, 0u);
                 }
                 if (lane == 0) {
-                    uint64_t* w = set + (size_t)G * RG * 3 + (size_t)g * 2;
-                    __hip_atomic_store(&w[0], tag8(gm, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&w[1], tag8(gj, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    put(set + 3 * Q + 2 * g, gm);
+                    put(set + 3 * Q + 2 * g + 1, gj);
                 }
-                // gather the whole set into LDS: up to kPoll loads per lane in
-                // flight per poll, so a poll costs one round trip
-                const int words_total = G * stride;
-                for (int w0 = 0; w0 < words_total && !abort; w0 += kPoll * kWave) {
+                auto poll = [&](uint64_t w) {
+                    return __hip_atomic_load(&set[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                };
+                auto shows_tag = [&](uint64_t v) { return (uint32_t)(v & 0xFFu) == (tag & 0xFFu); };
+                // beta: the largest bound over the workgroups (lane order =
+                // workgroup order = index order)
+                auto merge_bound = [&](bool in, uint32_t m, uint32_t j) {
+                    uint32_t om, oj;
+                    int ol;
+                    wave_max_key(m, j, in && j != kNone, om, oj, ol);
+                    if (ol >= 0 && (beta_j == kNone || key_gt(om, oj, beta_m, beta_j))) {
+                        beta_m = om;
+                        beta_j = oj;
+                    }
+                };
+                if constexpr (!STAGED) {
+                    // Gather straight into registers: lane l polls candidates
+                    // k * 64 + l and the bound of workgroup l, every load of
+                    // the poll in flight at once.
+                    constexpr int KC = CPL < 2 ? CPL : 2;
+                    uint64_t c0[KC], c1[KC], c2[KC], b0, b1;
                     uint32_t spins = 0;
-                    while (true) {
-                        uint64_t v[kPoll];
+                    // the host launches this form only for sets it holds
+                    if (G > kWave || Q > KC * kWave) abort = 1;
+                    while (!abort) {
 #pragma unroll
-                        for (int k = 0; k < kPoll; ++k) {
-                            const int w = w0 + k * kWave + lane;
-                            v[k] = w < words_total ? __hip_atomic_load(&set[w], __ATOMIC_RELAXED,
-                                                                       __HIP_MEMORY_SCOPE_AGENT)
-                                                   : tag8(0, tag);
+                        for (int k = 0; k < KC; ++k) {
+                            if (k * kWave >= Q) break;  // wave-uniform
+                            const int q = k * kWave + lane;
+                            c0[k] = poll(3 * q);
+                            c1[k] = poll(3 * q + 1);
+                            c2[k] = poll(3 * q + 2);
                         }
-                        bool ready = true;
+                        b0 = poll(3 * Q + 2 * lane);
+                        b1 = poll(3 * Q + 2 * lane + 1);
+                        // padding slots are never written
+                        bool ready = lane >= G || (shows_tag(b0) && shows_tag(b1));
 #pragma unroll
-                        for (int k = 0; k < kPoll; ++k) ready &= (uint32_t)(v[k] & 0xFFu) == (tag & 0xFFu);
-                        if (ballot(!ready) == 0) {
-#pragma unroll
-                            for (int k = 0; k < kPoll; ++k) {
-                                const int w = w0 + k * kWave + lane;
-                                if (w < words_total) stage[w] = v[k] >> 8;
-                            }
-                            break;
+                        for (int k = 0; k < KC; ++k) {
+                            if (k * kWave >= Q) break;
+                            ready &= k * kWave + lane >= Q ||
+                                     (shows_tag(c0[k]) && shows_tag(c1[k]) && shows_tag(c2[k]));
                         }
+                        if (ballot(!ready) == 0) break;
                         if (++spins > spin_limit) { abort = 1; break; }
                         __builtin_amdgcn_s_sleep(1);
                     }
-                }
-                __builtin_amdgcn_s_waitcnt(0);  // LDS writes of this wave complete
-                __builtin_amdgcn_wave_barrier();
-                if (!abort) {
-                    // candidates q = wg * RG + r (index order), three words each,
-                    // 64 at a time (at most CPL rounds); all loads first
-                    uint64_t cw0[CPL], cw1[CPL], cw2[CPL];
+                    if (!abort) {
+                        merge_bound(lane < G, (uint32_t)(b0 >> 8), (uint32_t)(b1 >> 8));
 #pragma unroll
-                    for (int k = 0; k < CPL; ++k) {
-                        const int q = k * kWave + lane;
-                        const uint64_t* c = stage + (q < G * RG ? q : 0) * 3;
-                        cw0[k] = c[0];
-                        cw1[k] = c[1];
-                        cw2[k] = c[2];
-                    }
-                    // beta: the largest bound over the workgroups (lane order =
-                    // index order)
-                    const uint64_t* bw = stage + G * RG * 3;
-                    for (int base = 0; base < G; base += kWave) {
-                        const int wg = base + lane;
-                        const bool in = wg < G;
-                        const uint32_t m = in ? (uint32_t)bw[wg * 2 + 0] : 0u;
-                        const uint32_t j = in ? (uint32_t)bw[wg * 2 + 1] : kNone;
-                        uint32_t om, oj;
-                        int ol;
-                        wave_max_key(m, j, in && j != kNone, om, oj, ol);
-                        if (ol >= 0 && (beta_j == kNone || key_gt(om, oj, beta_m, beta_j))) {
-                            beta_m = om;
-                            beta_j = oj;
+                        for (int k = 0; k < KC; ++k) {
+                            if (k * kWave >= Q) break;
+                            const int q = k * kWave + lane;
+                            uint32_t m, j, x, y, z;
+                            unpack_candidate(c0[k] >> 8, c1[k] >> 8, c2[k] >> 8, m, j, x, y, z);
+                            keep(q < Q, m, j, x, y, z);
                         }
                     }
+                } else {
+                    // More words than one poll holds: gather the whole set
+                    // into LDS, kPoll loads per lane in flight per poll, then
+                    // read it back by candidate.
+                    const int words_total = 3 * Q + 2 * G;
+                    for (int w0 = 0; w0 < words_total && !abort; w0 += kPoll * kWave) {
+                        uint32_t spins = 0;
+                        while (true) {
+                            uint64_t v[kPoll];
 #pragma unroll
-                    for (int k = 0; k < CPL; ++k) {
-                        const int q = k * kWave + lane;
-                        uint32_t m, j, x, y, z;
-                        unpack_candidate(cw0[k], cw1[k], cw2[k], m, j, x, y, z);
-                        keep(q < G * RG, m, j, x, y, z);
+                            for (int k = 0; k < kPoll; ++k) {
+                                const int w = w0 + k * kWave + lane;
+                                v[k] = w < words_total ? poll(w) : tag8(0, tag);
+                            }
+                            bool ready = true;
+#pragma unroll
+                            for (int k = 0; k < kPoll; ++k) ready &= shows_tag(v[k]);
+                            if (ballot(!ready) == 0) {
+#pragma unroll
+                                for (int k = 0; k < kPoll; ++k) {
+                                    const int w = w0 + k * kWave + lane;
+                                    if (w < words_total) stage[w] = v[k] >> 8;
+                                }
+                                break;
+                            }
+                            if (++spins > spin_limit) { abort = 1; break; }
+                            __builtin_amdgcn_s_sleep(1);
+                        }
+                    }
+                    __builtin_amdgcn_s_waitcnt(0);  // LDS writes of this wave complete
+                    __builtin_amdgcn_wave_barrier();
+                    if (!abort) {
+                        uint64_t cw0[CPL], cw1[CPL], cw2[CPL];
+#pragma unroll
+                        for (int k = 0; k < CPL; ++k) {
+                            const int q = k * kWave + lane;
+                            const uint64_t* c = stage + (q < Q ? q : 0) * 3;
+                            cw0[k] = c[0];
+                            cw1[k] = c[1];
+                            cw2[k] = c[2];
+                        }
+                        const uint64_t* bw = stage + 3 * Q;
+                        for (int base = 0; base < G; base += kWave) {
+                            const int wg = base + lane;
+                            const bool in = wg < G;
+                            merge_bound(in, in ? (uint32_t)bw[wg * 2 + 0] : 0u,
+                                        in ? (uint32_t)bw[wg * 2 + 1] : kNone);
+                        }
+#pragma unroll
+                        for (int k = 0; k < CPL; ++k) {
+                            const int q = k * kWave + lane;
+                            uint32_t m, j, x, y, z;
+                            unpack_candidate(cw0[k], cw1[k], cw2[k], m, j, x, y, z);
+                            keep(q < Q, m, j, x, y, z);
+                        }
                     }
                 }
             }
@@ -857,17 +917,17 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                     uint32_t r[C];  // the block's start
 #pragma unroll
                     for (int c = 0; c < C; ++c) r[c] = m[c];
-                    uint32_t fail = 0, tie = 0;
-                    // the block's entries, wave-uniform (scalar registers)
-                    uint32_t sx[kCertBlock], sy[kCertBlock], sz[kCertBlock], sj[kCertBlock];
+                    // the block's entries and each step's largest key,
+                    // wave-uniform (scalar registers)
+                    uint32_t sx[kCertBlock], sy[kCertBlock], sz[kCertBlock], sj[kCertBlock],
+                        sm[kCertBlock];
 #pragma unroll
                     for (int s = 0; s < kCertBlock; ++s) {
                         uint32_t lm, wx, wy, wz, wj;
                         best(lm, wx, wy, wz, wj);
                         const uint32_t mx = wave_max_u32(lm);
                         const int kl = (int)__builtin_ctzll(ballot(lm == mx));
-                        fail |= (uint32_t)(mx <= beta_m) << s;
-                        tie |= (uint32_t)(mx == beta_m) << s;
+                        sm[s] = mx;
                         sx[s] = lane_value(wx, kl);
                         sy[s] = lane_value(wy, kl);
                         sz[s] = lane_value(wz, kl);
@@ -875,20 +935,23 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                         fold(u2f(sx[s]), u2f(sy[s]), u2f(sz[s]));
                     }
                     static_assert(kCertBlock == 4, "entry lanes");
-                    // entry s into lane s. The scalar registers come from
-                    // v_readlane, and a VALU read of an SGPR that a VALU
-                    // wrote needs two wait states on gfx950 (the compiler
-                    // keeps them in its own code but cannot see inside an
-                    // asm statement), hence the s_nop 1 that leads each one.
-                    uint32_t ex = 0, ey = 0, ez = 0, ej = 0;
+                    // entry s and step s's largest key into lane s. The scalar
+                    // registers come from v_readlane, and a VALU read of an
+                    // SGPR that a VALU wrote needs two wait states on gfx950
+                    // (the compiler keeps them in its own code but cannot see
+                    // inside an asm statement), hence the s_nop 1 that leads
+                    // each one. The steps' tests against the bound are then
+                    // two compares of `mxv` for the whole block.
+                    uint32_t ex = 0, ey = 0, ez = 0, ej = 0, mxv = 0;
 #define POINTOPS_ENTRY_LANE(S)                                                        \
     __asm__("s_nop 1\n\t"                                                              \
-            "v_writelane_b32 %0, %4, " #S "\n\t"                                        \
-            "v_writelane_b32 %1, %5, " #S "\n\t"                                        \
-            "v_writelane_b32 %2, %6, " #S "\n\t"                                        \
-            "v_writelane_b32 %3, %7, " #S                                              \
-            : "+v"(ex), "+v"(ey), "+v"(ez), "+v"(ej)                                    \
-            : "s"(sx[S]), "s"(sy[S]), "s"(sz[S]), "s"(sj[S]));
+            "v_writelane_b32 %0, %5, " #S "\n\t"                                        \
+            "v_writelane_b32 %1, %6, " #S "\n\t"                                        \
+            "v_writelane_b32 %2, %7, " #S "\n\t"                                        \
+            "v_writelane_b32 %3, %8, " #S "\n\t"                                        \
+            "v_writelane_b32 %4, %9, " #S                                              \
+            : "+v"(ex), "+v"(ey), "+v"(ez), "+v"(ej), "+v"(mxv)                         \
+            : "s"(sx[S]), "s"(sy[S]), "s"(sz[S]), "s"(sj[S]), "s"(sm[S]));
                     POINTOPS_ENTRY_LANE(0)
                     POINTOPS_ENTRY_LANE(1)
                     POINTOPS_ENTRY_LANE(2)
@@ -898,6 +961,9 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                     // takes them (the entries past a failure are never read)
                     if (lane < kCertBlock && nc + lane < limit)
                         cen[nc + lane] = make_uint4(ex, ey, ez, ej);
+                    constexpr uint64_t kSteps = (1ull << kCertBlock) - 1;
+                    uint32_t fail = (uint32_t)(ballot(mxv <= beta_m) & kSteps);
+                    const uint32_t tie = (uint32_t)(ballot(mxv == beta_m) & kSteps);
                     if (nc == 0) fail &= ~1u;  // the batch's first centre: the cloud's largest key
                     const int room = limit - nc;
                     if (room < kCertBlock) fail |= ~0u << room;
@@ -1031,25 +1097,35 @@ int fps_batch_ppt_round(int ppt) {
     return -1;
 }
 
-int fps_batch_stride(int rg) { return 3 * rg + 2; }  // words per workgroup
+int fps_batch_set_words(int G, int rg) { return fps_set_words(G, rg); }
 
 int fps_batch_point_waves(int block) { return block / kWave - 1; }
 
 size_t fps_batch_workspace_bytes(int64_t B, int64_t G, int rg) {
-    return G > 1 ? 256 + (size_t)B * 2 * (size_t)G * fps_batch_stride(rg) * sizeof(uint64_t) : 256;
+    return G > 1 ? 256 + (size_t)B * 2 * (size_t)fps_set_words((int)G, rg) * sizeof(uint64_t) : 256;
 }
 
-size_t fps_batch_lds_bytes(int G, int rg) { return G > 1 ? (size_t)G * (3 * rg + 2) * 8 : 0; }
+// Dynamic LDS: the staged word set, for clouds of more than 64 workgroups or
+// 128 candidates (smaller sets are gathered straight into registers; with up
+// to 256 candidates the registers of a four-slot gather measured slower than
+// the staging they save: 100k points, 63 workgroups of 4 candidates, 1.077
+// against 1.040 ms).
+size_t fps_batch_lds_bytes(int G, int rg) {
+    return G > 64 || G * rg > 128 ? (size_t)G * (3 * rg + 2) * 8 : 0;
+}
 
 // The (points per thread, block, candidates per lane) triples that are built.
-template <int PPT_, int BLOCK_, int CPL_>
+template <int PPT_, int BLOCK_, int CPL_, bool STAGED_>
 struct BatchCfg {
     static constexpr int PPT = PPT_, BLOCK = BLOCK_, CPL = CPL_;
+    static constexpr bool STAGED = STAGED_;
 };
 
 template <int P>
-using BatchCfgsFor = std::tuple<BatchCfg<P, 1024, 1>, BatchCfg<P, 1024, 2>, BatchCfg<P, 1024, 4>,
-                                BatchCfg<P, 1024, 8>, BatchCfg<P, 256, 1>>;
+using BatchCfgsFor =
+    std::tuple<BatchCfg<P, 1024, 1, false>, BatchCfg<P, 1024, 2, false>,
+               BatchCfg<P, 1024, 1, true>, BatchCfg<P, 1024, 2, true>, BatchCfg<P, 1024, 4, true>,
+               BatchCfg<P, 1024, 8, true>, BatchCfg<P, 256, 1, false>, BatchCfg<P, 256, 1, true>>;
 
 using BatchCfgs = decltype(std::tuple_cat(BatchCfgsFor<1>{}, BatchCfgsFor<2>{}, BatchCfgsFor<3>{},
                                           BatchCfgsFor<4>{}, BatchCfgsFor<5>{}, BatchCfgsFor<6>{},
@@ -1057,13 +1133,15 @@ using BatchCfgs = decltype(std::tuple_cat(BatchCfgsFor<1>{}, BatchCfgsFor<2>{}, 
                                           BatchCfgsFor<12>{}, BatchCfgsFor<16>{}));
 
 // Calls fn(Cfg{}) for the built configuration matching the runtime values;
-// false when none does.
+// false when none does. A launch that needs dynamic LDS stages its words.
 template <typename Fn>
-static bool with_batch_cfg(int ppt, int block, int cpl, Fn&& fn) {
+static bool with_batch_cfg(int ppt, int block, int cpl, size_t lds, Fn&& fn) {
+    const bool staged = lds > 0;
     return std::apply(
         [&](auto... cfg) {
             return ((decltype(cfg)::PPT == ppt && decltype(cfg)::BLOCK == block &&
-                     decltype(cfg)::CPL == cpl && (fn(cfg), true)) ||
+                     decltype(cfg)::CPL == cpl && decltype(cfg)::STAGED == staged &&
+                     (fn(cfg), true)) ||
                     ...);
         },
         BatchCfgs{});
@@ -1073,10 +1151,11 @@ static bool with_batch_cfg(int ppt, int block, int cpl, Fn&& fn) {
 hipError_t fps_batch_capacity(int ppt, int block, int cpl, size_t lds, int cus, int* out) {
     hipError_t e = hipErrorInvalidValue;
     int per_cu = 0;
-    with_batch_cfg(ppt, block, cpl, [&](auto cfg) {
+    with_batch_cfg(ppt, block, cpl, lds, [&](auto cfg) {
         using C = decltype(cfg);
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, (const void*)fps_batch_kernel<C::PPT, C::BLOCK, C::CPL>, C::BLOCK, lds);
+            &per_cu, (const void*)fps_batch_kernel<C::PPT, C::BLOCK, C::CPL, C::STAGED>, C::BLOCK,
+            lds);
     });
     *out = per_cu * cus;
     return e;
@@ -1097,11 +1176,11 @@ hipError_t launch_fps_batch(const float* xyz, int64_t B, int64_t N, int64_t M, i
     const size_t lds = seg ? seg_lds : fps_batch_lds_bytes(G, rg);
     const unsigned grid = (unsigned)(seg ? units : B * G);
     hipError_t e = hipErrorInvalidValue;
-    with_batch_cfg(ppt, block, cpl, [&](auto cfg) {
+    with_batch_cfg(ppt, block, cpl, lds, [&](auto cfg) {
         using C = decltype(cfg);
-        hipLaunchKernelGGL((fps_batch_kernel<C::PPT, C::BLOCK, C::CPL>), dim3(grid),
+        hipLaunchKernelGGL((fps_batch_kernel<C::PPT, C::BLOCK, C::CPL, C::STAGED>), dim3(grid),
                            dim3(C::BLOCK), lds, stream, xyz, (int)N, (int)M, (int)start_idx, G,
-                           slice, rg, out_idx, out_xyz, words, fps_batch_stride(rg), status,
+                           slice, rg, out_idx, out_xyz, words, status,
                            spin_limit, seg, nseg);
         e = hipGetLastError();
     });

@@ -323,7 +323,7 @@ RaggedFps plan_fps_ragged(const int64_t* x_off, const int64_t* x_cnt, const int6
             recs[(size_t)b][pointops::kFrRG] = rg[(size_t)b];
             if (G[(size_t)b] > 1) {
                 recs[(size_t)b][pointops::kFrWOff] = p.words;
-                p.words += 2 * G[(size_t)b] * pointops::fps_batch_stride((int)rg[(size_t)b]);
+                p.words += 2 * pointops::fps_batch_set_words((int)G[(size_t)b], (int)rg[(size_t)b]);
             }
         }
         p.table = make_table(order, units, recs);
