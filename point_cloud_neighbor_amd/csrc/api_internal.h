@@ -41,9 +41,14 @@ hipError_t launch_fps(const float*, int64_t, int64_t, int64_t, int64_t, int64_t*
 hipError_t launch_fps_clear(void*, size_t, hipStream_t);
 size_t fps_workspace_bytes(int64_t B, int64_t G);
 hipError_t launch_fps_batch(const float*, int64_t, int64_t, int64_t, int64_t, int64_t*, float*,
-                            void*, int, int, int, int, int, uint32_t, hipStream_t,
+                            void*, int, int, int, int, int, bool, uint32_t, hipStream_t,
                             const int64_t*, int, int64_t, uint64_t*, size_t);
-hipError_t fps_batch_capacity(int ppt, int block, int cpl, size_t lds, int cus, int* out);
+hipError_t fps_batch_capacity(int ppt, int block, int cpl, size_t lds, bool group, int cus,
+                              int* out);
+bool fps_batch_group_built(int ppt, int block);
+constexpr int kFpsGroupMaxSlice = 8192;  // points per slice that the grouping sorts in LDS
+size_t fps_batch_group_bytes(int64_t B, int64_t N);
+size_t fps_batch_group_offset(int64_t B, int64_t G, int rg);
 size_t fps_batch_workspace_bytes(int64_t B, int64_t G, int rg);
 size_t fps_batch_lds_bytes(int G, int rg);
 int fps_batch_ppt_round(int ppt);

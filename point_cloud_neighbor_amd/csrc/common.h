@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 // Every translation unit is also built with -ffp-contract=off; the pragma makes
 // the rule local to the code that needs it.
 #pragma clang fp contract(off)
@@ -42,7 +44,9 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
+// Lane 0's value of a 32-bit integer (a float would be converted: pass its bits).
 template <typename T> __device__ __forceinline__ T uniform(T v) {
+    static_assert(std::is_integral<T>::value && sizeof(T) == 4, "32-bit integers only");
     return __builtin_amdgcn_readfirstlane(v);
 }
 

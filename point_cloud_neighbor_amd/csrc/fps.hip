@@ -54,6 +54,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "api_internal.h"
 #include "common.h"
 #include "segments.h"
 
@@ -330,6 +331,147 @@ __device__ __forceinline__ void wave_max_key(uint32_t m, uint32_t j, bool use, u
     oj = lane_value(j, olane);
 }
 
+// Like wave_max_key, for lanes in any index order: among the lanes holding the
+// largest m, the one with the smallest index (rare: an extra reduction).
+__device__ __forceinline__ void wave_max_key_any(uint32_t m, uint32_t j, bool use, uint32_t& om,
+                                                 uint32_t& oj, int& olane) {
+    const uint32_t mx = wave_max_u32(use ? m : 0u);
+    uint64_t mask = ballot(use && m == mx);
+    if (mask == 0) {
+        om = 0;
+        oj = kNone;
+        olane = -1;
+        return;
+    }
+    if (mask & (mask - 1)) {
+        const bool in = (mask >> lane_id()) & 1ull;
+        const uint32_t jm = ~wave_max_u32(in ? ~j : 0u);
+        mask &= ballot(j == jm);
+    }
+    olane = __builtin_ctzll(mask);
+    om = mx;
+    oj = lane_value(j, olane);
+}
+
+// ------------------------------------------------------- grouping of the slices
+//
+// For the batched kernel on clouds where a centre's fold over a workgroup's
+// points outweighs its certification (several points per thread), each slice
+// is first reordered so that every point wave holds a spatially compact group:
+// the slice's points sorted by the Morton code of their position in the
+// slice's bounding box (ties by index), cut into runs of one wave's capacity,
+// and each run put back in index order. Within a wave, position order is then
+// index order as before, so a wave's tie rules are unchanged; across the waves
+// of a workgroup it is not, and the certifying wave breaks ties by index
+// explicitly. A point wave then folds a centre only if the centre's lower
+// bound to the wave's box is below the largest m in the wave. The result is
+// unchanged: a skipped fold leaves every m of the wave as it was.
+
+constexpr int kGroupMaxSlice = kFpsGroupMaxSlice;
+
+// 10-bit coordinate in [lo, hi] (0 for NaN), spread to every third bit.
+__device__ __forceinline__ uint32_t morton_part(float v, float lo, float scale) {
+    float t = (v - lo) * scale;
+    uint32_t q = t >= 1023.f ? 1023u : (t >= 0.f ? (uint32_t)t : 0u);
+    q = (q | (q << 16)) & 0x030000FFu;
+    q = (q | (q << 8)) & 0x0300F00Fu;
+    q = (q | (q << 4)) & 0x030C30C3u;
+    q = (q | (q << 2)) & 0x09249249u;
+    return q;
+}
+
+// Ascending bitonic sort of n (a power of two) 64-bit keys in LDS by BLOCK threads.
+template <int BLOCK>
+__device__ void lds_bitonic_sort(uint64_t* key, int n) {
+    for (int k = 2; k <= n; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < n; i += BLOCK) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const uint64_t a = key[i], b = key[l];
+                    const bool up = (i & k) == 0;
+                    if ((a > b) == up) {
+                        key[i] = b;
+                        key[l] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// One workgroup per slice: writes the slice's points, grouped, as (x, y, z,
+// cloud index) to `grouped` (B x N float4, slice positions in place).
+template <int BLOCK>
+__global__ __launch_bounds__(BLOCK) void fps_group_kernel(const float* __restrict__ xyz, int N,
+                                                          int G, int slice, int cap,
+                                                          float4* __restrict__ grouped) {
+    __shared__ uint64_t key[kGroupMaxSlice];
+    __shared__ float red[6][BLOCK / kWave];
+    const int b = blockIdx.x / G, g = blockIdx.x - b * G;
+    const int lo = g * slice;
+    const int cnt = min(N, lo + slice) - lo;
+    const float* xb = xyz + ((int64_t)b * N + lo) * 3;
+    float4* ob = grouped + (int64_t)b * N + lo;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    // the slice's bounding box (NaN coordinates take no part: fminf/fmaxf)
+    float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
+    for (int i = tid; i < cnt; i += BLOCK)
+        for (int a = 0; a < 3; ++a) {
+            mn[a] = fminf(mn[a], xb[3 * i + a]);
+            mx[a] = fmaxf(mx[a], xb[3 * i + a]);
+        }
+    for (int a = 0; a < 3; ++a)
+        for (int off = 32; off >= 1; off >>= 1) {
+            mn[a] = fminf(mn[a], __shfl_xor(mn[a], off, kWave));
+            mx[a] = fmaxf(mx[a], __shfl_xor(mx[a], off, kWave));
+        }
+    if (lane == 0)
+        for (int a = 0; a < 3; ++a) {
+            red[a][wave] = mn[a];
+            red[3 + a][wave] = mx[a];
+        }
+    __syncthreads();
+    for (int a = 0; a < 3; ++a) {
+        mn[a] = red[a][0];
+        mx[a] = red[3 + a][0];
+        for (int w = 1; w < BLOCK / kWave; ++w) {
+            mn[a] = fminf(mn[a], red[a][w]);
+            mx[a] = fmaxf(mx[a], red[3 + a][w]);
+        }
+    }
+    float sc[3];
+    for (int a = 0; a < 3; ++a) {
+        const float ext = mx[a] - mn[a];
+        sc[a] = ext > 0.f && ext < INFINITY ? 1024.f / ext : 0.f;
+        if (!(mn[a] > -INFINITY)) mn[a] = 0.f;
+    }
+    int n2 = 1;
+    while (n2 < cnt) n2 <<= 1;
+    for (int i = tid; i < n2; i += BLOCK) {
+        uint64_t k = ~0ull;
+        if (i < cnt) {
+            const uint32_t mc = morton_part(xb[3 * i + 0], mn[0], sc[0]) |
+                                (morton_part(xb[3 * i + 1], mn[1], sc[1]) << 1) |
+                                (morton_part(xb[3 * i + 2], mn[2], sc[2]) << 2);
+            k = ((uint64_t)mc << 32) | (uint32_t)i;
+        }
+        key[i] = k;
+    }
+    __syncthreads();
+    lds_bitonic_sort<BLOCK>(key, n2);
+    // rank r in Morton order -> run r / cap; sort again by (run, index)
+    for (int i = tid; i < cnt; i += BLOCK) key[i] = ((uint64_t)(i / cap) << 32) | (uint32_t)key[i];
+    __syncthreads();
+    lds_bitonic_sort<BLOCK>(key, n2);
+    for (int i = tid; i < cnt; i += BLOCK) {
+        const int j = (int)(uint32_t)key[i];
+        ob[i] = make_float4(xb[3 * j + 0], xb[3 * j + 1], xb[3 * j + 2],
+                            __uint_as_float((uint32_t)(lo + j)));
+    }
+}
+
 // The exchange words of one cloud and batch parity: three for each of the
 // G * rg candidates and two for each of the G bounds, both counts rounded up to
 // a multiple of 64 (a gather's lanes past the end read within the set).
@@ -339,11 +481,14 @@ __host__ __device__ __forceinline__ int fps_set_words(int G, int rg) {
 }
 
 // STAGED: the exchange words go through LDS (clouds of more than 64
-// workgroups or 256 candidates); otherwise straight into registers. The two
-// are separate kernels so that neither carries the other's registers.
-template <int PPT, int BLOCK, int CPL, bool STAGED>
+// workgroups or 128 candidates); otherwise straight into registers. GROUPED:
+// the points come from the grouped slices (`grouped`) and folds are culled by
+// each wave's box. Each combination is its own kernel, so that none carries
+// another's registers.
+template <int PPT, int BLOCK, int CPL, bool STAGED, bool GROUPED>
 __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
-    const float* __restrict__ xyz, int N, int M, int start_idx, int G, int slice, int RG,
+    const float* __restrict__ xyz, const float4* __restrict__ grouped, int N, int M,
+    int start_idx, int G, int slice, int RG,
     int64_t* __restrict__ out_idx, float* __restrict__ out_xyz, uint64_t* __restrict__ words,
     uint32_t* __restrict__ status, uint32_t spin_limit,
     const int64_t* __restrict__ seg, int nseg) {
@@ -372,7 +517,8 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     __shared__ uint4 live_a[kWave * CPL];  // compacted live candidates: m, index, x, y
     __shared__ uint32_t live_z[kWave * CPL];  // and z
     extern __shared__ uint64_t stage[];  // the gathered words (STAGED)
-    constexpr int kPoll = 16;  // loads per lane in flight per poll
+    // loads per lane in flight per poll of a staged gather (32 spill registers)
+    constexpr int kPoll = 16;
 
     // this workgroup's cloud
     int g;
@@ -413,16 +559,67 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     const int wbase = pw * kWave * PPT;       // first slice position of this wave
 
     float px[PPT], py[PPT], pz[PPT];
-    uint32_t pm[PPT];
+    uint32_t pm[PPT], pj[PPT];  // pj: the points' indices (GROUPED)
 #pragma unroll
     for (int p = 0; p < PPT; ++p) {
         const int r = u * PPT + p;
         const bool real = point_wave && r < cnt;
         const size_t j = (size_t)lo + (real ? r : 0);
-        px[p] = xb[3 * j + 0];
-        py[p] = xb[3 * j + 1];
-        pz[p] = xb[3 * j + 2];
+        if constexpr (GROUPED) {
+            const float4 e = grouped[xrow0 + (int64_t)j];
+            px[p] = e.x;
+            py[p] = e.y;
+            pz[p] = e.z;
+            pj[p] = f2u(e.w);
+        } else {
+            px[p] = xb[3 * j + 0];
+            py[p] = xb[3 * j + 1];
+            pz[p] = xb[3 * j + 2];
+        }
         pm[p] = real ? 0x7F800000u : 0u;  // +inf for points, +0 for padding
+    }
+    // GROUPED: the wave's box over its real points, and the largest m of the
+    // wave as of the last exchange (keys only decrease, so it stays an upper
+    // bound until the next); a wave with no real point never folds
+    float bx0 = 0.f, by0 = 0.f, bz0 = 0.f, bx1 = 0.f, by1 = 0.f, bz1 = 0.f;
+    uint32_t wmax = 0x7F800000u;
+    bool wave_real = false;
+    if constexpr (GROUPED) {
+        float l[3] = {INFINITY, INFINITY, INFINITY}, h[3] = {-INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+        for (int p = 0; p < PPT; ++p) {
+            if (point_wave && u * PPT + p < cnt) {
+                l[0] = fminf(l[0], px[p]);
+                l[1] = fminf(l[1], py[p]);
+                l[2] = fminf(l[2], pz[p]);
+                h[0] = fmaxf(h[0], px[p]);
+                h[1] = fmaxf(h[1], py[p]);
+                h[2] = fmaxf(h[2], pz[p]);
+            }
+        }
+        // a NaN coordinate: no box (the wave always folds)
+        bool nan_pt = false;
+#pragma unroll
+        for (int p = 0; p < PPT; ++p)
+            nan_pt |= point_wave && u * PPT + p < cnt && (px[p] != px[p] || py[p] != py[p] || pz[p] != pz[p]);
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
+            for (int off = 32; off >= 1; off >>= 1) {
+                l[a] = fminf(l[a], __shfl_xor(l[a], off, kWave));
+                h[a] = fmaxf(h[a], __shfl_xor(h[a], off, kWave));
+            }
+        // (the lane read takes 32-bit integers: pass the bits)
+        bx0 = u2f(uniform(f2u(l[0])));
+        by0 = u2f(uniform(f2u(l[1])));
+        bz0 = u2f(uniform(f2u(l[2])));
+        bx1 = u2f(uniform(f2u(h[0])));
+        by1 = u2f(uniform(f2u(h[1])));
+        bz1 = u2f(uniform(f2u(h[2])));
+        wave_real = point_wave && cnt > wbase;
+        if (ballot(nan_pt) != 0) {
+            bx0 = by0 = bz0 = -INFINITY;
+            bx1 = by1 = bz1 = INFINITY;
+        }
     }
 
     int64_t* ob = out_idx + orow0;
@@ -477,11 +674,46 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                         }
                     }
                 }
-                for (; a < n; ++a) {
-                    const uint4 c = cen[a];
+                if constexpr (!GROUPED) {
+                    for (; a < n; ++a) {
+                        const uint4 c = cen[a];
 #pragma unroll
-                    for (int p = 0; p < PPT; ++p)
-                        pm[p] = min(pm[p], f2u(s32(u2f(c.x), u2f(c.y), u2f(c.z), px[p], py[p], pz[p])));
+                        for (int p = 0; p < PPT; ++p)
+                            pm[p] = min(pm[p], f2u(s32(u2f(c.x), u2f(c.y), u2f(c.z), px[p], py[p], pz[p])));
+                    }
+                }
+                if (!wave_real) a = n;  // nothing to fold (not GROUPED: a == n already)
+                // GROUPED: up to four centres at a time, their loads in flight
+                // together (for the plain fold this measured slower: 100k
+                // points 1.074 against 1.038 ms)
+                while (a < n) {
+                    const int k = min(n - a, 4);
+                    uint4 cc[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) cc[i] = cen[a + (i < k ? i : 0)];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (i >= k) break;  // wave-uniform
+                        const uint4 c = cc[i];
+                        if constexpr (GROUPED) {
+                            // the centre's lower bound to the box: per axis
+                            // the gap in the distance's own float operations,
+                            // whose rounding is monotone, so it never exceeds
+                            // the distance of any point in the box. At or
+                            // above the wave's largest m, no m of the wave
+                            // changes.
+                            const float X = u2f(c.x), Y = u2f(c.y), Z = u2f(c.z);
+                            const float gx = fmaxf(fmaxf(bx0 - X, X - bx1), 0.f);
+                            const float gy = fmaxf(fmaxf(by0 - Y, Y - by1), 0.f);
+                            const float gz = fmaxf(fmaxf(bz0 - Z, Z - bz1), 0.f);
+                            const float lb = (gx * gx + gy * gy) + gz * gz;
+                            if (lb >= u2f(wmax)) continue;  // wave-uniform; false for NaN
+                        }
+#pragma unroll
+                        for (int p = 0; p < PPT; ++p)
+                            pm[p] = min(pm[p], f2u(s32(u2f(c.x), u2f(c.y), u2f(c.z), px[p], py[p], pz[p])));
+                    }
+                    a += k;
                 }
                 if (d) break;  // done was set after the last count: n is final
                 __builtin_amdgcn_s_sleep(1);
@@ -526,18 +758,29 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 z1 = a1 ? pz[p] : z1;
             }
             const int pos = lo + wbase + lane * PPT;  // index of this thread's first point
+            // index of this thread's point p (-1: none)
+            auto pidx = [&](int p) -> uint32_t {
+                if constexpr (GROUPED) {
+                    uint32_t j = kNone;
+#pragma unroll
+                    for (int q = 0; q < PPT; ++q) j = p == q ? pj[q] : j;
+                    return j;
+                } else {
+                    return (uint32_t)(pos + p);
+                }
+            };
             // the k-th report is a real point only if the wave holds more than
             // k real points (real positions come first and win ties)
             const int reals = cnt - wbase;
             uint32_t am, aj, bm, bj, cm_, cj_;
             int al, bl, cl;
-            wave_max_key(m1, (uint32_t)(pos + p1), true, am, aj, al);
+            wave_max_key(m1, pidx(p1), true, am, aj, al);
+            if constexpr (GROUPED) wmax = am;
             const uint32_t ax = lane_value(f2u(x1), al), ay = lane_value(f2u(y1), al),
                            az = lane_value(f2u(z1), al);
             const bool in1 = lane == al;
             // second: lane al offers its second key, the others their first
-            wave_max_key(in1 ? m2 : m1, (uint32_t)(pos + (in1 ? p2 : p1)), !in1 || p2 >= 0, bm, bj,
-                         bl);
+            wave_max_key(in1 ? m2 : m1, pidx(in1 ? p2 : p1), !in1 || p2 >= 0, bm, bj, bl);
             const uint32_t bx = lane_value(f2u(in1 ? x2 : x1), bl < 0 ? 0 : bl),
                            by = lane_value(f2u(in1 ? y2 : y1), bl < 0 ? 0 : bl),
                            bz = lane_value(f2u(in1 ? z2 : z1), bl < 0 ? 0 : bl);
@@ -546,7 +789,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
             const int taken = (int)in1 + (int)in2;
             const uint32_t nm = taken == 0 ? m1 : (taken == 1 ? m2 : m3);
             const int np = taken == 0 ? p1 : (taken == 1 ? p2 : p3);
-            wave_max_key(nm, (uint32_t)(pos + np), np >= 0, cm_, cj_, cl);
+            wave_max_key(nm, pidx(np), np >= 0, cm_, cj_, cl);
             if (lane == 0) {
                 rep[2 * pw + 0] = make_uint4(am, reals > 0 ? aj : kNone, ax, ay);
                 rep_z[2 * pw + 0] = az;
@@ -606,7 +849,14 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 for (int k = 0; k < RG && alive != 0; ++k) {
                     const bool a = __builtin_amdgcn_inverse_ballot_w64(alive);
                     const uint32_t mx = wave_max_u32(a ? r.x : 0u);
-                    const int l = (int)__builtin_ctzll(alive & ballot(r.x == mx));
+                    uint64_t tm = alive & ballot(r.x == mx);
+                    if (GROUPED && (tm & (tm - 1))) {
+                        // the waves are not in index order: the smallest index
+                        const bool in = (tm >> lane) & 1ull;
+                        const uint32_t jm = ~wave_max_u32(in ? ~r.y : 0u);
+                        tm &= ballot(r.y == jm);
+                    }
+                    const int l = (int)__builtin_ctzll(tm);
                     sel |= 1ull << l;
                     alive &= ~(1ull << l);
                 }
@@ -621,7 +871,10 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 const uint32_t uj = !wl ? kNone : (!p0 ? r0.y : (!p1 ? r1.y : wbd.y));
                 uint32_t gm, gj;
                 int gl;
-                wave_max_key(um, uj, uj != kNone, gm, gj, gl);
+                if constexpr (GROUPED)
+                    wave_max_key_any(um, uj, uj != kNone, gm, gj, gl);
+                else
+                    wave_max_key(um, uj, uj != kNone, gm, gj, gl);
                 // This batch's word set: the three words of candidate q = g * RG
                 // + rank at 3q, then the two of each workgroup's bound (each
                 // workgroup's words are contiguous). The set is sized for Q =
@@ -637,6 +890,13 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 int slot = (int)lanes_below(sel);
                 if ((sel >> (lane ^ 1)) & 1ull)
                     slot += (lane & 1) == 0 ? (pj < r.y ? 1 : 0) : (pj > r.y ? -1 : 0);
+                if constexpr (GROUPED) {
+                    // the waves are not in index order: rank among the
+                    // published reports by index
+                    slot = 0;
+                    for (uint64_t t = sel; t != 0; t &= t - 1)
+                        slot += lane_value(r.y, (int)__builtin_ctzll(t)) < r.y ? 1 : 0;
+                }
                 auto put = [&](uint64_t* w, uint64_t v) {
                     __hip_atomic_store(w, tag8(v, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 };
@@ -758,12 +1018,31 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                             cw1[k] = c[1];
                             cw2[k] = c[2];
                         }
+                        // each lane's best bound over workgroups lane, lane + 64,
+                        // ..., then one reduction over the lanes (not in
+                        // index order: ties go by index)
                         const uint64_t* bw = stage + 3 * Q;
-                        for (int base = 0; base < G; base += kWave) {
-                            const int wg = base + lane;
-                            const bool in = wg < G;
-                            merge_bound(in, in ? (uint32_t)bw[wg * 2 + 0] : 0u,
-                                        in ? (uint32_t)bw[wg * 2 + 1] : kNone);
+                        if (G <= kWave) {
+                            const bool in = lane < G;
+                            merge_bound(in, in ? (uint32_t)bw[lane * 2 + 0] : 0u,
+                                        in ? (uint32_t)bw[lane * 2 + 1] : kNone);
+                        } else {
+                            uint32_t lm = 0, lj = kNone;
+                            for (int wg = lane; wg < G; wg += kWave) {
+                                const uint32_t m = (uint32_t)bw[wg * 2 + 0],
+                                               j = (uint32_t)bw[wg * 2 + 1];
+                                if (j != kNone && (lj == kNone || key_gt(m, j, lm, lj))) {
+                                    lm = m;
+                                    lj = j;
+                                }
+                            }
+                            uint32_t om, oj;
+                            int ol;
+                            wave_max_key_any(lm, lj, lj != kNone, om, oj, ol);
+                            if (ol >= 0 && (beta_j == kNone || key_gt(om, oj, beta_m, beta_j))) {
+                                beta_m = om;
+                                beta_j = oj;
+                            }
                         }
 #pragma unroll
                         for (int k = 0; k < CPL; ++k) {
@@ -1114,11 +1393,12 @@ size_t fps_batch_lds_bytes(int G, int rg) {
     return G > 64 || G * rg > 128 ? (size_t)G * (3 * rg + 2) * 8 : 0;
 }
 
-// The (points per thread, block, candidates per lane) triples that are built.
-template <int PPT_, int BLOCK_, int CPL_, bool STAGED_>
+// The (points per thread, block, candidates per lane, staged, grouped)
+// configurations that are built.
+template <int PPT_, int BLOCK_, int CPL_, bool STAGED_, bool GROUPED_ = false>
 struct BatchCfg {
     static constexpr int PPT = PPT_, BLOCK = BLOCK_, CPL = CPL_;
-    static constexpr bool STAGED = STAGED_;
+    static constexpr bool STAGED = STAGED_, GROUPED = GROUPED_;
 };
 
 template <int P>
@@ -1127,60 +1407,95 @@ using BatchCfgsFor =
                BatchCfg<P, 1024, 1, true>, BatchCfg<P, 1024, 2, true>, BatchCfg<P, 1024, 4, true>,
                BatchCfg<P, 1024, 8, true>, BatchCfg<P, 256, 1, false>, BatchCfg<P, 256, 1, true>>;
 
-using BatchCfgs = decltype(std::tuple_cat(BatchCfgsFor<1>{}, BatchCfgsFor<2>{}, BatchCfgsFor<3>{},
-                                          BatchCfgsFor<4>{}, BatchCfgsFor<5>{}, BatchCfgsFor<6>{},
-                                          BatchCfgsFor<8>{}, BatchCfgsFor<10>{},
-                                          BatchCfgsFor<12>{}, BatchCfgsFor<16>{}));
+// Grouped slices: 1024 threads, 4 to 10 points per thread (slices of at most
+// kGroupMaxSlice points); staged sets have more than 128 candidates.
+template <int P>
+using GroupedCfgsFor =
+    std::tuple<BatchCfg<P, 1024, 1, false, true>, BatchCfg<P, 1024, 2, false, true>,
+               BatchCfg<P, 1024, 2, true, true>, BatchCfg<P, 1024, 4, true, true>,
+               BatchCfg<P, 1024, 8, true, true>>;
+
+using BatchCfgs = decltype(std::tuple_cat(
+    BatchCfgsFor<1>{}, BatchCfgsFor<2>{}, BatchCfgsFor<3>{}, BatchCfgsFor<4>{}, BatchCfgsFor<5>{},
+    BatchCfgsFor<6>{}, BatchCfgsFor<8>{}, BatchCfgsFor<10>{}, BatchCfgsFor<12>{},
+    BatchCfgsFor<16>{}, GroupedCfgsFor<4>{}, GroupedCfgsFor<5>{}, GroupedCfgsFor<6>{},
+    GroupedCfgsFor<8>{}, GroupedCfgsFor<10>{}));
+
+bool fps_batch_group_built(int ppt, int block) {
+    return block == 1024 && (ppt == 4 || ppt == 5 || ppt == 6 || ppt == 8 || ppt == 10);
+}
 
 // Calls fn(Cfg{}) for the built configuration matching the runtime values;
 // false when none does. A launch that needs dynamic LDS stages its words.
 template <typename Fn>
-static bool with_batch_cfg(int ppt, int block, int cpl, size_t lds, Fn&& fn) {
+static bool with_batch_cfg(int ppt, int block, int cpl, size_t lds, bool group, Fn&& fn) {
     const bool staged = lds > 0;
     return std::apply(
         [&](auto... cfg) {
             return ((decltype(cfg)::PPT == ppt && decltype(cfg)::BLOCK == block &&
                      decltype(cfg)::CPL == cpl && decltype(cfg)::STAGED == staged &&
-                     (fn(cfg), true)) ||
+                     decltype(cfg)::GROUPED == group && (fn(cfg), true)) ||
                     ...);
         },
         BatchCfgs{});
 }
 
 // Largest number of batched-FPS workgroups that are resident at once.
-hipError_t fps_batch_capacity(int ppt, int block, int cpl, size_t lds, int cus, int* out) {
+hipError_t fps_batch_capacity(int ppt, int block, int cpl, size_t lds, bool group, int cus,
+                              int* out) {
     hipError_t e = hipErrorInvalidValue;
     int per_cu = 0;
-    with_batch_cfg(ppt, block, cpl, lds, [&](auto cfg) {
+    with_batch_cfg(ppt, block, cpl, lds, group, [&](auto cfg) {
         using C = decltype(cfg);
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, (const void*)fps_batch_kernel<C::PPT, C::BLOCK, C::CPL, C::STAGED>, C::BLOCK,
-            lds);
+            &per_cu,
+            (const void*)fps_batch_kernel<C::PPT, C::BLOCK, C::CPL, C::STAGED, C::GROUPED>,
+            C::BLOCK, lds);
     });
     *out = per_cu * cus;
     return e;
 }
 
-// Dense: B * G workgroups, exchange words after the 256-byte header. Ragged
-// (seg != nullptr): `units` workgroups, `words` = the exchange words (each
-// cloud's record locates its own), `lds` = the largest stage of any cloud;
-// B, N, M, start_idx, G and rg are unused.
+// Bytes of the grouped points (dense clouds with `group`), after the exchange
+// part of the workspace, which is all that the per-call clear touches.
+size_t fps_batch_group_bytes(int64_t B, int64_t N) { return (size_t)B * (size_t)N * 16; }
+
+size_t fps_batch_group_offset(int64_t B, int64_t G, int rg) {
+    return (fps_batch_workspace_bytes(B, G, rg) + 255) & ~(size_t)255;
+}
+
+// Dense: B * G workgroups, exchange words after the 256-byte header, and with
+// `group` the grouped points after them (written first by one workgroup per
+// slice). Ragged (seg != nullptr): `units` workgroups, `words` = the exchange
+// words (each cloud's record locates its own), `lds` = the largest stage of
+// any cloud; B, N, M, start_idx, G, rg and group are unused.
 hipError_t launch_fps_batch(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t start_idx,
                             int64_t* out_idx, float* out_xyz, void* workspace, int G, int ppt,
-                            int block, int rg, int cpl, uint32_t spin_limit, hipStream_t stream,
-                            const int64_t* seg, int nseg, int64_t units, uint64_t* seg_words,
-                            size_t seg_lds) {
+                            int block, int rg, int cpl, bool group, uint32_t spin_limit,
+                            hipStream_t stream, const int64_t* seg, int nseg, int64_t units,
+                            uint64_t* seg_words, size_t seg_lds) {
+    if (seg) group = false;
     const int slice = seg ? 0 : (int)((N + G - 1) / G);
     uint32_t* status = (uint32_t*)workspace;
     uint64_t* words = seg ? seg_words : (uint64_t*)((char*)workspace + 256);
     const size_t lds = seg ? seg_lds : fps_batch_lds_bytes(G, rg);
     const unsigned grid = (unsigned)(seg ? units : B * G);
+    float4* grouped = nullptr;
+    if (group) {
+        if (G < 2 || slice > kGroupMaxSlice || !fps_batch_group_built(ppt, block))
+            return hipErrorInvalidValue;
+        grouped = (float4*)((char*)workspace + fps_batch_group_offset(B, G, rg));
+        hipLaunchKernelGGL((fps_group_kernel<1024>), dim3(grid), dim3(1024), 0, stream, xyz,
+                           (int)N, G, slice, kWave * ppt, grouped);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipError_t e = hipErrorInvalidValue;
-    with_batch_cfg(ppt, block, cpl, lds, [&](auto cfg) {
+    with_batch_cfg(ppt, block, cpl, lds, group, [&](auto cfg) {
         using C = decltype(cfg);
-        hipLaunchKernelGGL((fps_batch_kernel<C::PPT, C::BLOCK, C::CPL, C::STAGED>), dim3(grid),
-                           dim3(C::BLOCK), lds, stream, xyz, (int)N, (int)M, (int)start_idx, G,
-                           slice, rg, out_idx, out_xyz, words, status,
+        hipLaunchKernelGGL((fps_batch_kernel<C::PPT, C::BLOCK, C::CPL, C::STAGED, C::GROUPED>),
+                           dim3(grid), dim3(C::BLOCK), lds, stream, xyz, grouped, (int)N, (int)M,
+                           (int)start_idx, G, slice, rg, out_idx, out_xyz, words, status,
                            spin_limit, seg, nseg);
         e = hipGetLastError();
     });

@@ -260,6 +260,7 @@ struct FpsPlan {
     int block;   // threads per workgroup
     int rg;      // candidates each workgroup publishes per exchange (batch, G > 1)
     int cpl;     // candidates per lane of the certifying wave (batch)
+    bool group;  // slices grouped by position, folds culled per wave (batch)
     int err;     // POINTOPS_OK or why no plan fits
 };
 
@@ -345,10 +346,17 @@ FpsPlan fps_plan_batch(int64_t B, int64_t N, const DeviceInfo& dev) {
             p.cpl = cand <= 64 ? 1 : cand <= 128 ? 2 : cand <= 256 ? 4 : 8;
             if (p.block == 256 && p.cpl > 1) { block = 1024; continue; }
         }
+        // Grouped slices where a centre's fold outweighs its certification
+        // (four or more points per thread); POINTOPS_FPS_GROUP = 0 / 1 turns
+        // the grouping off, or on wherever it is built.
+        const long group_env = env_long("POINTOPS_FPS_GROUP", -1);
+        p.group = G > 1 && slice <= pointops::kFpsGroupMaxSlice &&
+                  pointops::fps_batch_group_built(p.ppt, p.block) &&
+                  (group_env == 1 || (group_env != 0 && p.ppt >= 4));
         int cap = 0;
         hipError_t e = pointops::fps_batch_capacity(p.ppt, p.block, p.cpl,
                                                     pointops::fps_batch_lds_bytes(p.G, p.rg),
-                                                    cus, &cap);
+                                                    p.group, cus, &cap);
         if (e != hipSuccess) { p.err = hip_fail(e, "fps occupancy query"); return p; }
         if (G == 1 || B * G <= cap) {
             p.err = POINTOPS_OK;
@@ -377,9 +385,17 @@ FpsPlan fps_plan(int64_t B, int64_t N, const DeviceInfo& dev) {
     return fps_plan_batch(B, N, dev);
 }
 
-size_t plan_workspace_bytes(int64_t B, const FpsPlan& p) {
+// The part of the workspace that every call clears (status and exchange words).
+size_t plan_clear_bytes(int64_t B, const FpsPlan& p) {
     return p.batch ? pointops::fps_batch_workspace_bytes(B, p.G, p.rg)
                    : pointops::fps_workspace_bytes(B, p.G);
+}
+
+size_t plan_workspace_bytes(int64_t B, int64_t N, const FpsPlan& p) {
+    if (p.batch && p.group)
+        return pointops::fps_batch_group_offset(B, p.G, p.rg) +
+               pointops::fps_batch_group_bytes(B, N);
+    return plan_clear_bytes(B, p);
 }
 
 // The static scratch of pointops_fps_noalloc: FPS's workspace (status word,
@@ -451,7 +467,7 @@ size_t pointops_fps_workspace_bytes(int64_t B, int64_t N, int64_t M) {
     if (current_device(&dev) != POINTOPS_OK) dev = &fallback;
     const FpsPlan p = fps_plan(B, N, *dev);
     g_err[0] = 0;
-    return p.err == POINTOPS_OK ? plan_workspace_bytes(B, p) : 0;
+    return p.err == POINTOPS_OK ? plan_workspace_bytes(B, N, p) : 0;
 }
 
 }  // extern "C"
@@ -480,9 +496,10 @@ int fps_run(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t start_idx
     DeviceInfo* dev = nullptr;
     int st = check_device(device, &dev);
     if (st != POINTOPS_OK) return st;
-    const FpsPlan p = fps_plan(B, N, *dev);
+    FpsPlan p = fps_plan(B, N, *dev);
     if (p.err != POINTOPS_OK) return p.err;
-    const size_t need = plan_workspace_bytes(B, p);
+    if (scratch) p.group = false;  // the static scratch holds the exchange words only
+    const size_t need = plan_workspace_bytes(B, N, p);
     if (scratch) {
         st = static_scratch(device, need, &ws);
         if (st != POINTOPS_OK) return st;
@@ -491,12 +508,12 @@ int fps_run(const float* xyz, int64_t B, int64_t N, int64_t M, int64_t start_idx
                     ws_bytes, need);
     }
     hipStream_t s = (hipStream_t)stream;
-    e = pointops::launch_fps_clear(ws, need, s);
+    e = pointops::launch_fps_clear(ws, plan_clear_bytes(B, p), s);
     if (e != hipSuccess) return hip_fail(e, "fps workspace clear");
     const uint32_t spin = (uint32_t)env_long("POINTOPS_FPS_SPIN_LIMIT", 1L << 22);
     if (p.batch)
         e = pointops::launch_fps_batch(xyz, B, N, M, start_idx, out_idx, out_xyz, ws, p.G,
-                                       p.ppt, p.block, p.rg, p.cpl, spin, s, nullptr, 0, 0,
+                                       p.ppt, p.block, p.rg, p.cpl, p.group, spin, s, nullptr, 0, 0,
                                        nullptr, 0);
     else
         e = pointops::launch_fps(xyz, B, N, M, start_idx, out_idx, out_xyz, ws, p.G, p.ppt,

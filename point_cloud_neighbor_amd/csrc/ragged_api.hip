@@ -302,7 +302,8 @@ RaggedFps plan_fps_ragged(const int64_t* x_off, const int64_t* x_cnt, const int6
         p.cpl = cand <= 64 ? 1 : cand <= 128 ? 2 : cand <= 256 ? 4 : 8;
         if (p.block == 256 && p.cpl > 1) { block = 1024; continue; }
         int cap = 0;
-        hipError_t e = pointops::fps_batch_capacity(p.ppt, p.block, p.cpl, p.lds, dev.cus, &cap);
+        hipError_t e =
+            pointops::fps_batch_capacity(p.ppt, p.block, p.cpl, p.lds, false, dev.cus, &cap);
         if (e != hipSuccess) { p.err = hip_fail(e, "fps occupancy query"); return p; }
         if (multi > cap) {  // fewer, larger slices
             for (int64_t b : active)
@@ -565,7 +566,7 @@ int pointops_fps_ragged(const float* xyz, int64_t rows, const int64_t* x_off,
     const uint32_t spin = (uint32_t)env_long("POINTOPS_FPS_SPIN_LIMIT", 1L << 22);
     if (p.batch)
         e = pointops::launch_fps_batch(xyz, 0, 0, 0, 0, out_idx, out_xyz, workspace, 0, p.ppt,
-                                       p.block, 0, p.cpl, spin, s, table, p.table.nseg,
+                                       p.block, 0, p.cpl, false, spin, s, table, p.table.nseg,
                                        p.table.units, words, p.lds);
     else
         e = pointops::launch_fps(xyz, 0, p.max_n, 0, 0, out_idx, out_xyz, workspace, 1, p.ppt,

@@ -13,7 +13,8 @@ from tests.gpu_util import dev, host
 
 pytestmark = pytest.mark.gpu
 
-ENV = ("POINTOPS_FPS_MODE", "POINTOPS_FPS_WG_PER_CLOUD", "POINTOPS_FPS_RG", "POINTOPS_KNN_GRID",
+ENV = ("POINTOPS_FPS_MODE", "POINTOPS_FPS_WG_PER_CLOUD", "POINTOPS_FPS_RG", "POINTOPS_FPS_GROUP",
+       "POINTOPS_KNN_GRID",
        "POINTOPS_KNN_GRID_WAVE", "POINTOPS_KNN_WAVE", "POINTOPS_BQ_GRID", "POINTOPS_BQ_BUDGET",
        "POINTOPS_BQ_QUERIES_PER_WAVE")
 
@@ -64,6 +65,36 @@ def test_random_fps(gpu, oracle_mod, clean_env, seed):
         got = host(gpu.furthest_point_sample(dev(x), M, st))
         want = oracle_mod.fps(x, M, st, threads=4)
         assert np.array_equal(got, want), (seed, case, B, N, M, st, env)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_fps_grouped(gpu, oracle_mod, clean_env, seed):
+    """Slices of 4 to 10 points per thread, grouped by position with the folds
+    culled per wave (and, for the same shape, not grouped): ties between waves
+    that are no longer in index order, duplicates, samples past the distinct
+    points of the integer clouds."""
+    rng = np.random.default_rng(3000 + seed)
+    lib = gpu._load()
+    for case in range(5):
+        B = int(rng.choice([1, 2]))
+        N = int(rng.choice([8000, 12000, 20000, 30000]))
+        x = cloud(rng, B, N)
+        # 2 or more workgroups of 2881 to 8192 points: 4 to 10 points per thread
+        Gs = [g for g in range(2, 16) if 2880 < -(-N // g) <= 8192]
+        G = int(rng.choice(Gs))
+        M = int(rng.integers(1, 2000 if rng.random() < 0.7 else 4000))
+        st = int(rng.integers(0, N))
+        want = oracle_mod.fps(x, M, st, threads=8)
+        sizes = {}
+        for group in (1, 0):
+            env = {"POINTOPS_FPS_MODE": "batch", "POINTOPS_FPS_WG_PER_CLOUD": G,
+                   "POINTOPS_FPS_RG": int(rng.integers(1, 9)), "POINTOPS_FPS_GROUP": group}
+            clean_env(env)
+            sizes[group] = lib.pointops_fps_workspace_bytes(B, N, M)
+            got = host(gpu.furthest_point_sample(dev(x), M, st))
+            assert np.array_equal(got, want), (seed, case, B, N, M, st, env)
+        # the grouped plan was taken (its workspace holds the grouped points)
+        assert sizes[1] >= sizes[0] + B * N * 16, (seed, case, B, N, G, sizes)
 
 
 @pytest.mark.parametrize("seed", range(6))
