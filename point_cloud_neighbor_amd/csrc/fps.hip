@@ -1286,6 +1286,8 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 certify_fast(std::integral_constant<int, 1>{});
             else if (CPL >= 2 && used <= 2)
                 certify_fast(std::integral_constant<int, (CPL >= 2 ? 2 : 1)>{});
+            else if (CPL >= 4 && used <= 3)
+                certify_fast(std::integral_constant<int, (CPL >= 4 ? 3 : 1)>{});
             else if (CPL >= 4 && used <= 4)
                 certify_fast(std::integral_constant<int, (CPL >= 4 ? 4 : 1)>{});
             else
