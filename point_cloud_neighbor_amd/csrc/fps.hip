@@ -1138,7 +1138,18 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
             // to the bound's can still pass by its index: a block that stops
             // there rewinds to its start, replays the steps that passed and
             // goes on one step at a time with the full test.
-            auto certify_fast = [&](auto c_) {
+            //
+            // As certified centres fold into the candidates, keys fall to the
+            // bound and below, and those candidates can no longer be
+            // certified in this batch. Every eight steps (after a block that
+            // passed) a loop of two or more slots counts the candidates whose
+            // m is at least the bound's (a superset of the live ones); when
+            // they fit in half the slots it compacts them, in the same
+            // lane-major order, and goes on with half the slots. A candidate
+            // dropped this way has m below the bound's and can never be the
+            // certified maximum again; one kept with m equal to it is
+            // harmless (it is tested like any other).
+            auto certify_fast = [&](auto self, auto c_, int nc0) -> void {
                 constexpr int C = decltype(c_)::value;  // slots per lane, <= CPL
                 uint32_t m[C], xs[C], ys[C], zs[C], js[C];
 #pragma unroll
@@ -1150,7 +1161,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                     js[c] = cj[c];
                 }
                 const int limit = min(M - t0, kFpsMaxBatch);
-                int nc = 0;
+                int nc = nc0;
                 auto fold = [&](float X, float Y, float Z) {
 #pragma unroll
                     for (int c = 0; c < C; ++c)
@@ -1251,7 +1262,55 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                     __asm__ __volatile__("" ::: "memory");  // entries before the count
                     __hip_atomic_store(lane == 0 ? &cen_count : &sink_cnt[lane], nc,
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                    if (pass == kCertBlock) continue;
+                    if (pass == kCertBlock) {
+                        if constexpr (C >= 2) {
+                            if (((nc - nc0) & 7) == 0) {
+                                constexpr int H = C / 2;
+                                uint64_t keepm[C];
+                                uint32_t n = 0;
+#pragma unroll
+                                for (int c = 0; c < C; ++c) {
+                                    keepm[c] = ballot(js[c] != kNone && m[c] >= beta_m);
+                                    n += (uint32_t)__popcll(keepm[c]);
+                                }
+                                if (n >= 1 && n <= (uint32_t)(H * kWave)) {
+                                    // position in lane-major order: the kept
+                                    // slots of lower lanes, then this lane's
+                                    // earlier slots
+                                    uint32_t q = 0;
+#pragma unroll
+                                    for (int c = 0; c < C; ++c) q += lanes_below(keepm[c]);
+                                    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                                    for (int c = 0; c < C; ++c) {
+                                        if ((keepm[c] >> lane) & 1ull) {
+                                            live_a[q] = make_uint4(m[c], js[c], xs[c], ys[c]);
+                                            live_z[q] = zs[c];
+                                            ++q;
+                                        }
+                                    }
+                                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                                    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                                    for (int h = 0; h < H; ++h) {
+                                        const int qq = lane * H + h;
+                                        const bool in = qq < (int)n;
+                                        const uint4 e = live_a[in ? qq : 0];
+                                        const uint32_t ez = live_z[in ? qq : 0];
+                                        cm[h] = in ? e.x : 0u;
+                                        cj[h] = in ? e.y : kNone;
+                                        cxv[h] = in ? e.z : 0u;
+                                        cyv[h] = in ? e.w : 0u;
+                                        czv[h] = in ? ez : 0u;
+                                    }
+                                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                                    self(self, std::integral_constant<int, H>{}, nc);
+                                    return;
+                                }
+                            }
+                        }
+                        continue;
+                    }
                     tied = pass < room && ((tie >> pass) & 1u);
                     if (tied) {
 #pragma unroll
@@ -1283,13 +1342,13 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 t = t0 + nc;
             };
             if (used <= 1)
-                certify_fast(std::integral_constant<int, 1>{});
+                certify_fast(certify_fast, std::integral_constant<int, 1>{}, 0);
             else if (CPL >= 2 && used <= 2)
-                certify_fast(std::integral_constant<int, (CPL >= 2 ? 2 : 1)>{});
+                certify_fast(certify_fast, std::integral_constant<int, (CPL >= 2 ? 2 : 1)>{}, 0);
             else if (CPL >= 4 && used <= 3)
-                certify_fast(std::integral_constant<int, (CPL >= 4 ? 3 : 1)>{});
+                certify_fast(certify_fast, std::integral_constant<int, (CPL >= 4 ? 3 : 1)>{}, 0);
             else if (CPL >= 4 && used <= 4)
-                certify_fast(std::integral_constant<int, (CPL >= 4 ? 4 : 1)>{});
+                certify_fast(certify_fast, std::integral_constant<int, (CPL >= 4 ? 4 : 1)>{}, 0);
             else
                 certify(std::integral_constant<int, CPL>{});
         }

@@ -94,6 +94,38 @@ def host_np(t):
     return t.detach().cpu().numpy()
 
 
+@pytest.mark.parametrize("seed", [3, 11])
+def test_fps_nonfinite_grouped(gpu, seed, monkeypatch):
+    """Grouped slices (waves culling folds by their boxes) against the same
+    call without grouping, on clouds with NaN and infinite coordinates. The
+    box bound stays a lower bound there (a wave holding a NaN point always
+    folds; infinite gaps only skip folds whose distances are infinite or
+    NaN), so the two must agree index for index and bit for bit, guards
+    intact."""
+    lib, s = lib_and_stream(gpu)
+    N, M = 20000, 600
+    x = dev(poisoned(seed, N, frac=0.01))
+    monkeypatch.setenv("POINTOPS_FPS_MODE", "batch")
+    monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", "4")  # slices of 5000: 6 points per thread
+    got = {}
+    for group in ("1", "0"):
+        monkeypatch.setenv("POINTOPS_FPS_GROUP", group)
+        out = Guarded((1, M), torch.int64)
+        oxyz = Guarded((1, M, 3), torch.float32)
+        nb = lib.pointops_fps_workspace_bytes(1, N, M)
+        ws = torch.empty(max(1, nb), dtype=torch.uint8, device="cuda")
+        assert lib.pointops_fps(x.data_ptr(), 1, N, M, 0, out.ptr(), oxyz.ptr(),
+                                ws.data_ptr(), ws.numel(), s) == 0
+        torch.cuda.synchronize()
+        gpu.fps_status(ws)
+        got[group] = (out.check(f"fps grouped={group}"),
+                      oxyz.check(f"fps xyz grouped={group}").view(np.uint32), nb)
+    assert got["1"][2] >= got["0"][2] + N * 16  # the grouped plan was taken
+    assert np.array_equal(got["1"][0], got["0"][0])
+    assert np.array_equal(got["1"][1], got["0"][1])
+    assert ((got["1"][0] >= 0) & (got["1"][0] < N)).all()
+
+
 @pytest.mark.parametrize("k,Q,P,grid,env", [
     (16, 3000, 20000, True, {"POINTOPS_KNN_GRID_WAVE": "1"}),
     (16, 12000, 20000, True, {"POINTOPS_KNN_GRID_WAVE": "2"}),
