@@ -507,7 +507,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     __shared__ uint4 cen[kFpsMaxBatch];
     __shared__ uint4 sink_rec[kWave];  // stores of the certifying wave's other lanes
     __shared__ int sink_cnt[kWave];
-    __shared__ int cen_count, cen_done, sh_t, sh_abort;
+    __shared__ int cen_count, cen_done, sh_t, sh_abort, sh_gather_abort, sh_pub;
     // reports of the point waves (m, index, x, y; z) and each wave's bound
     // (m, index), one entry per lane of the reading wave: the entries past the
     // last report or wave stay empty
@@ -632,6 +632,8 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
         cen_done = 1;
         sh_t = 1;
         sh_abort = 0;
+        sh_gather_abort = 0;
+        sh_pub = 0;
         if (g == 0) {
             ob[0] = jbase + start_idx;
             if (oxb) { oxb[0] = sx; oxb[1] = sy; oxb[2] = sz; }
@@ -800,6 +802,59 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
             }
         }
         __syncthreads();
+        // A staged set of more than one wave-0 poll (over 16 loads per lane;
+        // eight candidate slots per lane, up to 2048 words): the point waves
+        // gather it into LDS instead, all of it in one round trip. They start once wave 0 has issued this workgroup's words (a
+        // flag in LDS): polling earlier only adds uncached traffic that slows
+        // the exchange itself.
+        if constexpr (STAGED && CPL >= 8) {
+            if (G > 1 && point_wave && G * (3 * RG + 2) > 16 * kWave) {
+                constexpr int kNpt = (NW - 1) * kWave;
+                constexpr int kHelp = (2048 + kNpt - 1) / kNpt;
+                const uint32_t tag = batch;
+                const int words_total = G * (3 * RG + 2);
+                const uint64_t* set = cw + (size_t)(batch & 1) * fps_set_words(G, RG);
+                uint32_t spins = 0;
+                while (__hip_atomic_load(&sh_pub, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) !=
+                       (int)batch) {
+                    if (++spins > spin_limit) break;  // wave 0 has stopped: its own poll times out too
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                if (words_total > kHelp * kNpt) {
+                    __hip_atomic_store(&sh_gather_abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                } else {
+                    while (true) {
+                        uint64_t v[kHelp];
+#pragma unroll
+                        for (int k = 0; k < kHelp; ++k) {
+                            const int w = u + k * kNpt;
+                            v[k] = w < words_total ? __hip_atomic_load(&set[w], __ATOMIC_RELAXED,
+                                                                       __HIP_MEMORY_SCOPE_AGENT)
+                                                   : tag8(0, tag);
+                        }
+                        bool ready = true;
+#pragma unroll
+                        for (int k = 0; k < kHelp; ++k)
+                            ready &= (uint32_t)(v[k] & 0xFFu) == (tag & 0xFFu);
+                        if (ballot(!ready) == 0) {
+#pragma unroll
+                            for (int k = 0; k < kHelp; ++k) {
+                                const int w = u + k * kNpt;
+                                if (w < words_total) stage[w] = v[k] >> 8;
+                            }
+                            break;
+                        }
+                        if (++spins > spin_limit) {
+                            __hip_atomic_store(&sh_gather_abort, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_WORKGROUP);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                }
+                __syncthreads();  // the set is in LDS (wave 0 meets this after publishing)
+            }
+        }
         if (wave != 0) continue;
 
         // ---- wave 0: exchange, then certify centres ----------------------------
@@ -918,6 +973,9 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 if (lane == 0) {
                     put(set + 3 * Q + 2 * g, gm);
                     put(set + 3 * Q + 2 * g + 1, gj);
+                    if (STAGED && CPL >= 8)
+                        __hip_atomic_store(&sh_pub, (int)batch, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
                 auto poll = [&](uint64_t w) {
                     return __hip_atomic_load(&set[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -982,7 +1040,13 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                     // into LDS, kPoll loads per lane in flight per poll, then
                     // read it back by candidate.
                     const int words_total = 3 * Q + 2 * G;
-                    for (int w0 = 0; w0 < words_total && !abort; w0 += kPoll * kWave) {
+                    const bool coop = CPL >= 8 && words_total > 16 * kWave;
+                    if (coop) {
+                        __syncthreads();  // the point waves' gather (above) is done
+                        abort = (uint32_t)__hip_atomic_load(&sh_gather_abort, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_WORKGROUP);
+                    }
+                    for (int w0 = 0; w0 < words_total && !abort && !coop; w0 += kPoll * kWave) {
                         uint32_t spins = 0;
                         while (true) {
                             uint64_t v[kPoll];
