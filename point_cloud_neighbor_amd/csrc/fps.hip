@@ -358,63 +358,49 @@ __device__ __forceinline__ void wave_max_key_any(uint32_t m, uint32_t j, bool us
 // For the batched kernel on clouds where a centre's fold over a workgroup's
 // points outweighs its certification (several points per thread), each slice
 // is first reordered so that every point wave holds a spatially compact group:
-// the slice's points sorted by the Morton code of their position in the
-// slice's bounding box (ties by index), cut into runs of one wave's capacity,
-// and each run put back in index order. Within a wave, position order is then
-// index order as before, so a wave's tie rules are unchanged; across the waves
-// of a workgroup it is not, and the certifying wave breaks ties by index
-// explicitly. A point wave then folds a centre only if the centre's lower
-// bound to the wave's box is below the largest m in the wave. The result is
-// unchanged: a skipped fold leaves every m of the wave as it was.
+// the slice's points in the Morton order of their cells in the slice's
+// bounding box, cut into runs of one wave's capacity. Position order is then
+// not index order, so wherever the plain kernel lets the first lane or the
+// earlier register win a tie (a thread's best points, a wave's reports, the
+// certifying wave's choice among the waves' reports, the workgroup bound, the
+// order of the published candidates), the grouped kernel compares indices
+// explicitly; padding positions carry no index and lose every tie. A point
+// wave then folds a centre only if the centre's lower bound to the wave's box
+// is below the largest m in the wave. The result is unchanged: a skipped fold
+// leaves every m of the wave as it was.
 
 constexpr int kGroupMaxSlice = kFpsGroupMaxSlice;
 
-// 10-bit coordinate in [lo, hi] (0 for NaN), spread to every third bit.
-__device__ __forceinline__ uint32_t morton_part(float v, float lo, float scale) {
-    float t = (v - lo) * scale;
-    uint32_t q = t >= 1023.f ? 1023u : (t >= 0.f ? (uint32_t)t : 0u);
-    q = (q | (q << 16)) & 0x030000FFu;
-    q = (q | (q << 8)) & 0x0300F00Fu;
-    q = (q | (q << 4)) & 0x030C30C3u;
-    q = (q | (q << 2)) & 0x09249249u;
+// 4-bit coordinate cell in [lo, lo + 16 / scale) (0 for NaN), spread to every
+// third bit: 4096 cells of the slice's box in Morton order.
+__device__ __forceinline__ uint32_t morton4(float v, float lo, float scale) {
+    const float t = (v - lo) * scale;
+    uint32_t q = t >= 15.f ? 15u : (t >= 0.f ? (uint32_t)t : 0u);
+    q = (q | (q << 4)) & 0x0C3u;
+    q = (q | (q << 2)) & 0x249u;
     return q;
 }
 
-// Ascending bitonic sort of n (a power of two) 64-bit keys in LDS by BLOCK threads.
-template <int BLOCK>
-__device__ void lds_bitonic_sort(uint64_t* key, int n) {
-    for (int k = 2; k <= n; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < n; i += BLOCK) {
-                const int l = i ^ j;
-                if (l > i) {
-                    const uint64_t a = key[i], b = key[l];
-                    const bool up = (i & k) == 0;
-                    if ((a > b) == up) {
-                        key[i] = b;
-                        key[l] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
-// One workgroup per slice: writes the slice's points, grouped, as (x, y, z,
-// cloud index) to `grouped` (B x N float4, slice positions in place).
+// One workgroup per slice: a counting sort of the slice's points by their
+// Morton cell (4096 cells of the slice's bounding box; the order inside a
+// cell is whichever the LDS counters hand out), written as (x, y, z, cloud
+// index) to `grouped` (B x N float4, slice positions in place). Runs of one
+// wave's capacity of this order are the point waves' groups.
 template <int BLOCK>
 __global__ __launch_bounds__(BLOCK) void fps_group_kernel(const float* __restrict__ xyz, int N,
-                                                          int G, int slice, int cap,
+                                                          int G, int slice,
                                                           float4* __restrict__ grouped) {
-    __shared__ uint64_t key[kGroupMaxSlice];
-    __shared__ float red[6][BLOCK / kWave];
+    constexpr int kCells = 4096, kPer = kGroupMaxSlice / BLOCK, kNW = BLOCK / kWave;
+    __shared__ uint32_t cell_start[kCells];
+    __shared__ float red[6][kNW];
+    __shared__ uint32_t wsum[kNW];
     const int b = blockIdx.x / G, g = blockIdx.x - b * G;
     const int lo = g * slice;
     const int cnt = min(N, lo + slice) - lo;
     const float* xb = xyz + ((int64_t)b * N + lo) * 3;
     float4* ob = grouped + (int64_t)b * N + lo;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    for (int c = tid; c < kCells; c += BLOCK) cell_start[c] = 0;
     // the slice's bounding box (NaN coordinates take no part: fminf/fmaxf)
     float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
     for (int i = tid; i < cnt; i += BLOCK)
@@ -433,42 +419,62 @@ __global__ __launch_bounds__(BLOCK) void fps_group_kernel(const float* __restric
             red[3 + a][wave] = mx[a];
         }
     __syncthreads();
+    float sc[3];
     for (int a = 0; a < 3; ++a) {
         mn[a] = red[a][0];
         mx[a] = red[3 + a][0];
-        for (int w = 1; w < BLOCK / kWave; ++w) {
+        for (int w = 1; w < kNW; ++w) {
             mn[a] = fminf(mn[a], red[a][w]);
             mx[a] = fmaxf(mx[a], red[3 + a][w]);
         }
-    }
-    float sc[3];
-    for (int a = 0; a < 3; ++a) {
         const float ext = mx[a] - mn[a];
-        sc[a] = ext > 0.f && ext < INFINITY ? 1024.f / ext : 0.f;
+        sc[a] = ext > 0.f && ext < INFINITY ? 16.f / ext : 0.f;
         if (!(mn[a] > -INFINITY)) mn[a] = 0.f;
     }
-    int n2 = 1;
-    while (n2 < cnt) n2 <<= 1;
-    for (int i = tid; i < n2; i += BLOCK) {
-        uint64_t k = ~0ull;
+    // each thread's points: i = tid + r * BLOCK; their cells and order inside
+    uint32_t cell[kPer], within[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int i = tid + r * BLOCK;
         if (i < cnt) {
-            const uint32_t mc = morton_part(xb[3 * i + 0], mn[0], sc[0]) |
-                                (morton_part(xb[3 * i + 1], mn[1], sc[1]) << 1) |
-                                (morton_part(xb[3 * i + 2], mn[2], sc[2]) << 2);
-            k = ((uint64_t)mc << 32) | (uint32_t)i;
+            cell[r] = morton4(xb[3 * i + 0], mn[0], sc[0]) |
+                      (morton4(xb[3 * i + 1], mn[1], sc[1]) << 1) |
+                      (morton4(xb[3 * i + 2], mn[2], sc[2]) << 2);
+            within[r] = atomicAdd(&cell_start[cell[r]], 1u);
         }
-        key[i] = k;
     }
     __syncthreads();
-    lds_bitonic_sort<BLOCK>(key, n2);
-    // rank r in Morton order -> run r / cap; sort again by (run, index)
-    for (int i = tid; i < cnt; i += BLOCK) key[i] = ((uint64_t)(i / cap) << 32) | (uint32_t)key[i];
+    // exclusive scan of the cell counts: kCells / BLOCK consecutive cells per thread
+    constexpr int kCpt = kCells / BLOCK;
+    uint32_t c_[kCpt], run = 0;
+#pragma unroll
+    for (int c = 0; c < kCpt; ++c) {
+        c_[c] = cell_start[tid * kCpt + c];
+        run += c_[c];
+    }
+    uint32_t incl = run;  // inclusive scan over the wave's lanes
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_up((int)incl, off, kWave);
+        if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
-    lds_bitonic_sort<BLOCK>(key, n2);
-    for (int i = tid; i < cnt; i += BLOCK) {
-        const int j = (int)(uint32_t)key[i];
-        ob[i] = make_float4(xb[3 * j + 0], xb[3 * j + 1], xb[3 * j + 2],
-                            __uint_as_float((uint32_t)(lo + j)));
+    uint32_t base = incl - run;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+#pragma unroll
+    for (int c = 0; c < kCpt; ++c) {
+        cell_start[tid * kCpt + c] = base;
+        base += c_[c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int i = tid + r * BLOCK;
+        if (i < cnt) {
+            const uint32_t pos = cell_start[cell[r]] + within[r];
+            ob[pos] = make_float4(xb[3 * i + 0], xb[3 * i + 1], xb[3 * i + 2],
+                                  __uint_as_float((uint32_t)(lo + i)));
+        }
     }
 }
 
@@ -570,7 +576,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
             px[p] = e.x;
             py[p] = e.y;
             pz[p] = e.z;
-            pj[p] = f2u(e.w);
+            pj[p] = real ? f2u(e.w) : kNone;  // padding loses every tie
         } else {
             px[p] = xb[3 * j + 0];
             py[p] = xb[3 * j + 1];
@@ -737,14 +743,29 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
             // largest keys in position order (strict > keeps the earlier,
             // smaller-index point first on ties), with the coordinates of the
             // first two.
+            // (GROUPED: positions are not in index order, so equal keys
+            // compare indices)
             uint32_t m1 = pm[0], m2 = 0, m3 = 0;
             int p1 = 0, p2 = -1, p3 = -1;
             float x1 = px[0], y1 = py[0], z1 = pz[0], x2 = 0.f, y2 = 0.f, z2 = 0.f;
+            uint32_t j1 = pj[0], j2 = kNone, j3 = kNone;  // GROUPED
 #pragma unroll
             for (int p = 1; p < PPT; ++p) {
                 const uint32_t v = pm[p];
-                const bool a1 = v > m1, a2 = !a1 && (p2 < 0 || v > m2),
-                           a3 = !a1 && !a2 && (p3 < 0 || v > m3);
+                bool a1, a2, a3;
+                if constexpr (GROUPED) {
+                    const uint32_t jv = pj[p];
+                    a1 = v > m1 || (v == m1 && jv < j1);
+                    a2 = !a1 && (p2 < 0 || v > m2 || (v == m2 && jv < j2));
+                    a3 = !a1 && !a2 && (p3 < 0 || v > m3 || (v == m3 && jv < j3));
+                    j3 = a1 || a2 ? j2 : (a3 ? jv : j3);
+                    j2 = a1 ? j1 : (a2 ? jv : j2);
+                    j1 = a1 ? jv : j1;
+                } else {
+                    a1 = v > m1;
+                    a2 = !a1 && (p2 < 0 || v > m2);
+                    a3 = !a1 && !a2 && (p3 < 0 || v > m3);
+                }
                 // shift down the entries the new key displaces
                 m3 = a1 || a2 ? m2 : (a3 ? v : m3);
                 p3 = a1 || a2 ? p2 : (a3 ? p : p3);
@@ -776,13 +797,21 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
             const int reals = cnt - wbase;
             uint32_t am, aj, bm, bj, cm_, cj_;
             int al, bl, cl;
-            wave_max_key(m1, pidx(p1), true, am, aj, al);
+            // (GROUPED: lanes are not in index order either)
+            auto wmax_key = [&](uint32_t m, uint32_t j, bool use, uint32_t& om, uint32_t& oj,
+                                int& ol) {
+                if constexpr (GROUPED)
+                    wave_max_key_any(m, j, use, om, oj, ol);
+                else
+                    wave_max_key(m, j, use, om, oj, ol);
+            };
+            wmax_key(m1, pidx(p1), true, am, aj, al);
             if constexpr (GROUPED) wmax = am;
             const uint32_t ax = lane_value(f2u(x1), al), ay = lane_value(f2u(y1), al),
                            az = lane_value(f2u(z1), al);
             const bool in1 = lane == al;
             // second: lane al offers its second key, the others their first
-            wave_max_key(in1 ? m2 : m1, pidx(in1 ? p2 : p1), !in1 || p2 >= 0, bm, bj, bl);
+            wmax_key(in1 ? m2 : m1, pidx(in1 ? p2 : p1), !in1 || p2 >= 0, bm, bj, bl);
             const uint32_t bx = lane_value(f2u(in1 ? x2 : x1), bl < 0 ? 0 : bl),
                            by = lane_value(f2u(in1 ? y2 : y1), bl < 0 ? 0 : bl),
                            bz = lane_value(f2u(in1 ? z2 : z1), bl < 0 ? 0 : bl);
@@ -791,7 +820,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
             const int taken = (int)in1 + (int)in2;
             const uint32_t nm = taken == 0 ? m1 : (taken == 1 ? m2 : m3);
             const int np = taken == 0 ? p1 : (taken == 1 ? p2 : p3);
-            wave_max_key(nm, pidx(np), np >= 0, cm_, cj_, cl);
+            wmax_key(nm, pidx(np), np >= 0, cm_, cj_, cl);
             if (lane == 0) {
                 rep[2 * pw + 0] = make_uint4(am, reals > 0 ? aj : kNone, ax, ay);
                 rep_z[2 * pw + 0] = az;
@@ -1611,7 +1640,7 @@ hipError_t launch_fps_batch(const float* xyz, int64_t B, int64_t N, int64_t M, i
             return hipErrorInvalidValue;
         grouped = (float4*)((char*)workspace + fps_batch_group_offset(B, G, rg));
         hipLaunchKernelGGL((fps_group_kernel<1024>), dim3(grid), dim3(1024), 0, stream, xyz,
-                           (int)N, G, slice, kWave * ppt, grouped);
+                           (int)N, G, slice, grouped);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
