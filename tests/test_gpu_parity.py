@@ -390,19 +390,24 @@ def test_every_output_slot_written(gpu):
     assert not (o < 0).any()
 
 
-@pytest.mark.parametrize("mode", ["batch", "step"])
-def test_fps_bounded_wait_terminates(gpu, mode, monkeypatch):
+@pytest.mark.parametrize("mode,N,G", [("batch", 20000, 8), ("step", 20000, 8),
+                                      ("batch", 400000, None), ("batch", 800000, None)])
+def test_fps_bounded_wait_terminates(gpu, mode, N, G, monkeypatch):
     """A tiny bound on the cross-workgroup wait (forced from the host) makes the
     kernel stop early instead of waiting: the call returns, output slots not
-    reached hold -1 and the rest are valid indices."""
+    reached hold -1 and the rest are valid indices. The two large clouds take
+    256 workgroups, whose 2048 exchange words the point waves gather (after
+    a bounded wait for their own workgroup's words); the larger one also
+    groups its slices."""
     monkeypatch.setenv("POINTOPS_FPS_MODE", mode)
-    monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", "8")
+    if G:
+        monkeypatch.setenv("POINTOPS_FPS_WG_PER_CLOUD", str(G))
     monkeypatch.setenv("POINTOPS_FPS_SPIN_LIMIT", "0")
-    xyz = dev(W.uniform_cube(4, 1, 20000))
-    ws = torch.empty(gpu.fps_workspace_bytes(1, 20000, 500), dtype=torch.uint8, device="cuda")
+    xyz = dev(W.uniform_cube(4, 1, N))
+    ws = torch.empty(gpu.fps_workspace_bytes(1, N, 500), dtype=torch.uint8, device="cuda")
     out = host(gpu.furthest_point_sample(xyz, 500, workspace=ws, check=False))
     torch.cuda.synchronize()
-    assert ((out >= 0) & (out < 20000) | (out == -1)).all()
+    assert ((out >= 0) & (out < N) | (out == -1)).all()
     first_bad = np.argmax(out[0] == -1) if (out == -1).any() else 500
     assert (out[0, first_bad:] == -1).all()
     # the give-up is reported: through the status query of the C ABI and as
