@@ -97,6 +97,44 @@ def test_random_fps_grouped(gpu, oracle_mod, clean_env, seed):
         assert sizes[1] >= sizes[0] + B * N * 16, (seed, case, B, N, G, sizes)
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_random_fps_wide(gpu, oracle_mod, clean_env, seed):
+    """Plans of more than 64 workgroups per cloud (staged exchange words, up
+    to 512 candidates in eight slots per lane; sets of more than 1024 words
+    gathered by the point waves; slices of four or more points per thread
+    grouped by position), forced on clouds with heavy ties."""
+    rng = np.random.default_rng(4000 + seed)
+    for case in range(4):
+        N = int(rng.choice([120000, 300000]))
+        x = cloud(rng, 1, N)
+        G = int(rng.choice([80, 100, 128, 200, 256]))
+        RG = int(rng.choice([r for r in (2, 3, 4) if G * r <= 512]))
+        M = int(rng.integers(100, 1200))
+        st = int(rng.integers(0, N))
+        env = {"POINTOPS_FPS_MODE": "batch", "POINTOPS_FPS_WG_PER_CLOUD": G, "POINTOPS_FPS_RG": RG}
+        clean_env(env)
+        got = host(gpu.furthest_point_sample(dev(x), M, st))
+        want = oracle_mod.fps(x, M, st, threads=8)
+        assert np.array_equal(got, want), (seed, case, N, M, st, env)
+
+
+def test_random_fps_wide_covers_paths():
+    """The shapes of test_random_fps_wide reach the point-wave gather and the
+    grouped slices (checked on the CPU from the same seeded choices)."""
+    seen = set()
+    for seed in range(3):
+        rng = np.random.default_rng(4000 + seed)
+        for case in range(4):
+            N = int(rng.choice([120000, 300000]))
+            cloud(rng, 1, N)
+            G = int(rng.choice([80, 100, 128, 200, 256]))
+            RG = int(rng.choice([r for r in (2, 3, 4) if G * r <= 512]))
+            rng.integers(100, 1200)
+            rng.integers(0, N)
+            seen.add((G * (3 * RG + 2) > 1024, -(-N // G) > 2880))
+    assert (True, True) in seen or ((True, False) in seen and (False, True) in seen), seen
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_random_searches(gpu, oracle_mod, clean_env, seed):
     rng = np.random.default_rng(2000 + seed)
