@@ -928,6 +928,11 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
             } else {
                 // publish this workgroup's RG best reports (in index order) and
                 // its bound: the best of the wave bounds and unpublished reports
+                // the loads the bound and the slots need, issued before the
+                // selection so that their latency hides behind it
+                const uint4 r0 = rep[(2 * lane) & (kWave - 1)];
+                const uint4 r1 = rep[(2 * lane + 1) & (kWave - 1)];
+                const uint32_t pj = rep[lane ^ 1].y;  // the pair's other report
                 uint64_t alive = ballot(r.y != kNone);  // reports not yet taken
                 uint64_t sel = 0;
                 for (int k = 0; k < RG && alive != 0; ++k) {
@@ -946,8 +951,6 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 }
                 // a wave's keys are ordered: report 0 >= report 1 >= bound, so
                 // its best unpublished key is the first of them not published
-                const uint4 r0 = rep[(2 * lane) & (kWave - 1)];
-                const uint4 r1 = rep[(2 * lane + 1) & (kWave - 1)];
                 const bool p0 = (sel >> ((2 * lane) & 63)) & 1ull,
                            p1 = (sel >> ((2 * lane + 1) & 63)) & 1ull;
                 const bool wl = lane < NPW;
@@ -970,7 +973,6 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                 const int nsel = __popcll(sel);
                 // the published slot, in index order: when both reports of a
                 // wave are published, the smaller index takes the first slot
-                const uint32_t pj = rep[lane ^ 1].y;  // the pair's other report
                 int slot = (int)lanes_below(sel);
                 if ((sel >> (lane ^ 1)) & 1ull)
                     slot += (lane & 1) == 0 ? (pj < r.y ? 1 : 0) : (pj > r.y ? -1 : 0);
