@@ -683,11 +683,16 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                     }
                 }
                 if constexpr (!GROUPED) {
-                    for (; a < n; ++a) {
-                        const uint4 c = cen[a];
+                    // the next entry's load goes out while this one folds
+                    if (a < n) {
+                        uint4 c = cen[a];
+                        for (; a < n; ++a) {
+                            const uint4 nx = cen[a + 1 < n ? a + 1 : a];
 #pragma unroll
-                        for (int p = 0; p < PPT; ++p)
-                            pm[p] = min(pm[p], f2u(s32(u2f(c.x), u2f(c.y), u2f(c.z), px[p], py[p], pz[p])));
+                            for (int p = 0; p < PPT; ++p)
+                                pm[p] = min(pm[p], f2u(s32(u2f(c.x), u2f(c.y), u2f(c.z), px[p], py[p], pz[p])));
+                            c = nx;
+                        }
                     }
                 }
                 if (!wave_real) a = n;  // nothing to fold (not GROUPED: a == n already)
