@@ -662,8 +662,6 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
         if (point_wave) {
             // outputs are written here, not by the certifying wave, so that
             // wave never waits on a global store
-            // outputs are written here, not by the certifying wave, so that
-            // wave never waits on a global store
             const bool writer = g == 0 && pw == 0 && out_t0 >= 1;
             int a = 0;
             while (true) {
