@@ -491,6 +491,13 @@ __host__ __device__ __forceinline__ int fps_set_words(int G, int rg) {
 // the points come from the grouped slices (`grouped`) and folds are culled by
 // each wave's box. Each combination is its own kernel, so that none carries
 // another's registers.
+// LDS position of published word w of a set of Q candidates (three words
+// each, candidate-major) and its bounds: word i of candidate q goes to
+// i * Q + q; the bounds keep their order after the 3Q candidate words.
+__device__ __forceinline__ int stage_pos(int w, int Q) {
+    return w < 3 * Q ? (w % 3) * Q + w / 3 : w;
+}
+
 template <int PPT, int BLOCK, int CPL, bool STAGED, bool GROUPED>
 __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     const float* __restrict__ xyz, const float4* __restrict__ grouped, int N, int M,
@@ -522,7 +529,15 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     __shared__ uint2 bnd[kWave];
     __shared__ uint4 live_a[kWave * CPL];  // compacted live candidates: m, index, x, y
     __shared__ uint32_t live_z[kWave * CPL];  // and z
-    extern __shared__ uint64_t stage[];  // the gathered words (STAGED)
+    // the gathered words (STAGED), then the bounds as published. With fewer
+    // than eight slots per lane the candidates' three words go to three
+    // arrays of Q, so reading them back by candidate is a contiguous load per
+    // word (100k points: 1.000 -> 0.982 ms); the eight-slot kernels keep them
+    // candidate by candidate, as published: there the arrays start 4096 bytes
+    // apart (Q = 512), the staging writes of a wave meet in the same banks,
+    // and the 2^20-point cloud measured 4.93 -> 5.07 ms.
+    constexpr bool kSoA = CPL < 8;
+    extern __shared__ uint64_t stage[];
     // loads per lane in flight per poll of a staged gather (32 spill registers)
     constexpr int kPoll = 16;
 
@@ -872,7 +887,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
 #pragma unroll
                             for (int k = 0; k < kHelp; ++k) {
                                 const int w = u + k * kNpt;
-                                if (w < words_total) stage[w] = v[k] >> 8;
+                                if (w < words_total) stage[kSoA ? stage_pos(w, G * RG) : w] = v[k] >> 8;
                             }
                             break;
                         }
@@ -1096,7 +1111,7 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
 #pragma unroll
                                 for (int k = 0; k < kPoll; ++k) {
                                     const int w = w0 + k * kWave + lane;
-                                    if (w < words_total) stage[w] = v[k] >> 8;
+                                    if (w < words_total) stage[kSoA ? stage_pos(w, Q) : w] = v[k] >> 8;
                                 }
                                 break;
                             }
@@ -1111,10 +1126,11 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
 #pragma unroll
                         for (int k = 0; k < CPL; ++k) {
                             const int q = k * kWave + lane;
-                            const uint64_t* c = stage + (q < Q ? q : 0) * 3;
+                            const int qq = q < Q ? q : 0;
+                            const uint64_t* c = stage + (kSoA ? qq : 3 * qq);
                             cw0[k] = c[0];
-                            cw1[k] = c[1];
-                            cw2[k] = c[2];
+                            cw1[k] = c[kSoA ? Q : 1];
+                            cw2[k] = c[kSoA ? 2 * Q : 2];
                         }
                         // each lane's best bound over workgroups lane, lane + 64,
                         // ..., then one reduction over the lanes (not in
