@@ -493,9 +493,11 @@ __host__ __device__ __forceinline__ int fps_set_words(int G, int rg) {
 // another's registers.
 // LDS position of published word w of a set of Q candidates (three words
 // each, candidate-major) and its bounds: word i of candidate q goes to
-// i * Q + q; the bounds keep their order after the 3Q candidate words.
+// i * (Q + kStagePad) + q; the bounds keep their order after the three
+// arrays. The pad moves the arrays' starts to different LDS banks whatever Q.
+constexpr int kStagePad = 8;
 __device__ __forceinline__ int stage_pos(int w, int Q) {
-    return w < 3 * Q ? (w % 3) * Q + w / 3 : w;
+    return w < 3 * Q ? (w % 3) * (Q + kStagePad) + w / 3 : w + 2 * kStagePad;
 }
 
 template <int PPT, int BLOCK, int CPL, bool STAGED, bool GROUPED>
@@ -531,11 +533,10 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
     __shared__ uint32_t live_z[kWave * CPL];  // and z
     // the gathered words (STAGED), then the bounds as published. With fewer
     // than eight slots per lane the candidates' three words go to three
-    // arrays of Q, so reading them back by candidate is a contiguous load per
-    // word (100k points: 1.000 -> 0.982 ms); the eight-slot kernels keep them
-    // candidate by candidate, as published: there the arrays start 4096 bytes
-    // apart (Q = 512), the staging writes of a wave meet in the same banks,
-    // and the 2^20-point cloud measured 4.93 -> 5.07 ms.
+    // arrays (stage_pos), so reading them back by candidate is a contiguous
+    // load per word (100k points: 0.998 -> 0.966 ms); the eight-slot kernels,
+    // whose point waves gather the set, keep the published order (2^20
+    // points: 4.93 -> 5.18 ms with the arrays, 5.07 without the pad).
     constexpr bool kSoA = CPL < 8;
     extern __shared__ uint64_t stage[];
     // loads per lane in flight per poll of a staged gather (32 spill registers)
@@ -1129,13 +1130,13 @@ __global__ __launch_bounds__(BLOCK) void fps_batch_kernel(
                             const int qq = q < Q ? q : 0;
                             const uint64_t* c = stage + (kSoA ? qq : 3 * qq);
                             cw0[k] = c[0];
-                            cw1[k] = c[kSoA ? Q : 1];
-                            cw2[k] = c[kSoA ? 2 * Q : 2];
+                            cw1[k] = c[kSoA ? Q + kStagePad : 1];
+                            cw2[k] = c[kSoA ? 2 * (Q + kStagePad) : 2];
                         }
                         // each lane's best bound over workgroups lane, lane + 64,
                         // ..., then one reduction over the lanes (not in
                         // index order: ties go by index)
-                        const uint64_t* bw = stage + 3 * Q;
+                        const uint64_t* bw = stage + 3 * Q + (kSoA ? 2 * kStagePad : 0);
                         if (G <= kWave) {
                             const bool in = lane < G;
                             merge_bound(in, in ? (uint32_t)bw[lane * 2 + 0] : 0u,
@@ -1565,7 +1566,7 @@ size_t fps_batch_workspace_bytes(int64_t B, int64_t G, int rg) {
 // the staging they save: 100k points, 63 workgroups of 4 candidates, 1.077
 // against 1.040 ms).
 size_t fps_batch_lds_bytes(int G, int rg) {
-    return G > 64 || G * rg > 128 ? (size_t)G * (3 * rg + 2) * 8 : 0;
+    return G > 64 || G * rg > 128 ? ((size_t)G * (3 * rg + 2) + 2 * kStagePad) * 8 : 0;
 }
 
 // The (points per thread, block, candidates per lane, staged, grouped)
